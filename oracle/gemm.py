@@ -1,0 +1,84 @@
+"""Oracle for AllGather-GEMM and GEMM-ReduceScatter (test infrastructure only).
+
+Plain definitions in float64; the swizzled, overlapped method reaches the same
+values up to rounding order because it only reorders tiles and transfers
+(AutoOverlap §6.2/§7.2: the tile-order knobs keep semantics unchanged; DITRON
+§4.4: adapted kernels are bitwise equal to the native ones).
+
+* AllGather-GEMM (DITRON §2 and §4.1, AG-GEMM workload; talk, swizzling
+  section): every rank r holds one row chunk A_r of the activations; after the
+  all-gather each rank computes C = concat(A_0, ..., A_{W-1}) @ B with its own
+  weight shard B.  Chunks are concatenated in rank order, whatever order they
+  arrive in.
+* GEMM-ReduceScatter (DITRON §4.1, GEMM-RS workload; talk, GEMM-ReduceScatter
+  example with per-tile notify and a separate reduce kernel): every rank s
+  computes a full partial product P_s = A_s @ B_s over its K shard; rank r owns
+  rows [r*R, (r+1)*R) of the sum, out_r = sum_s P_s[rows of r].  The sum is taken
+  in ascending s (the reading that makes the result independent of arrival
+  order).  On one GPU only the local partial P_r is computed; the other ranks'
+  slices for rank r arrive as inputs ("remote partials").
+
+Inputs are bf16 bit patterns (uint16) and fp32 arrays from ``seeded_inputs``;
+bf16 -> float64 widening is exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns: the bf16 value is the top half of an fp32."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def gather_rows(a_chunks):
+    """concat_c A_c in rank order (the all-gather's result), as float64."""
+    return np.concatenate([bf16_to_f64(a) for a in a_chunks], axis=0)
+
+
+def ag_gemm(a_chunks, b_kn) -> np.ndarray:
+    """C = concat(A_0..A_{W-1}) @ B, float64.  b_kn is the logical K x N weight."""
+    return gather_rows(a_chunks) @ bf16_to_f64(b_kn)
+
+
+def ag_gemm_rows(a_chunks, b_kn, rows) -> np.ndarray:
+    """Selected rows of C (global row indices), for sampled checks at full size."""
+    rows = np.asarray(rows, dtype=np.int64)
+    R = a_chunks[0].shape[0]
+    a = np.stack([bf16_to_f64(a_chunks[int(i) // R][int(i) % R]) for i in rows])
+    return a @ bf16_to_f64(b_kn)
+
+
+def gemm_partial(a_local, b_kn, rows=None) -> np.ndarray:
+    """Local partial product P = A_local @ B (float64); optionally only some rows."""
+    a = a_local if rows is None else a_local[np.asarray(rows, dtype=np.int64)]
+    return bf16_to_f64(a) @ bf16_to_f64(b_kn)
+
+
+def reduce_slice(local_slice: np.ndarray, remote: dict, world: int, rank: int) -> np.ndarray:
+    """out_r = sum over s = 0..W-1 in ascending order of S_s, with S_r the local slice
+    and S_s (s != r) the partial that rank s computed for rank r's rows."""
+    out = np.zeros_like(local_slice, dtype=np.float64)
+    for s in range(world):
+        term = local_slice if s == rank else np.asarray(remote[s], dtype=np.float64)
+        out = out + term
+    return out
+
+
+def gemm_rs(a_local, b_kn, remote: dict, world: int, rank: int):
+    """(P, out): the full local partial (M x N) and rank's reduced slice (R x N)."""
+    p = gemm_partial(a_local, b_kn)
+    R = p.shape[0] // world
+    out = reduce_slice(p[rank * R:(rank + 1) * R], remote, world, rank)
+    return p, out
+
+
+def gemm_rs_rows(a_local, b_kn, remote: dict, world: int, rank: int, local_rows):
+    """Sampled version: rows are indices inside rank's slice (0..R-1).  Returns
+    (P rows of the slice, out rows)."""
+    R = a_local.shape[0] // world
+    local_rows = np.asarray(local_rows, dtype=np.int64)
+    p = gemm_partial(a_local, b_kn, rank * R + local_rows)
+    sub = {s: np.asarray(v)[local_rows] for s, v in remote.items()}
+    return p, reduce_slice(p, sub, world, rank)

@@ -1,0 +1,129 @@
+"""Pins for oracle.gemm: checks that do not reuse the oracle's own formulas.
+
+* exact rational arithmetic (fractions.Fraction) on tiny shapes, with the
+  classical bound |fl(sum) - sum| <= gamma_K * sum |a||b| for float64 dot
+  products (gamma_K = K u / (1 - K u), u = 2^-53);
+* integer-valued inputs, for which every float64 (and fp32) sum is exact, so the
+  oracle must equal Python integer arithmetic bit for bit -- a wrong chunk
+  order, a transposed operand or an off-by-one row fails exactly;
+* special cases: one chunk is a plain GEMM (torch.matmul in float64); all
+  remote partials zero gives the local slice back; a constructed sum whose value
+  depends on the summation order pins the ascending-rank order of the reduce.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+from oracle import gemm as og
+
+
+def _exact(a_bits, b_bits):
+    a = si.bf16_bits_to_f32(a_bits).astype(np.float64)
+    b = si.bf16_bits_to_f32(b_bits).astype(np.float64)
+    M, K = a.shape
+    N = b.shape[1]
+    c = [[sum(Fraction(float(a[i, k])) * Fraction(float(b[k, j])) for k in range(K))
+          for j in range(N)] for i in range(M)]
+    absum = [[sum(abs(Fraction(float(a[i, k])) * Fraction(float(b[k, j]))) for k in range(K))
+              for j in range(N)] for i in range(M)]
+    return c, absum
+
+
+@pytest.mark.parametrize("world,rows,k,n", [(3, 5, 7, 4), (2, 4, 16, 3), (1, 6, 9, 5)])
+def test_ag_gemm_vs_exact_rational(world, rows, k, n):
+    inp = si.ag_inputs(901, world, rows, n, k, a_std=1.0, b_std=0.5)
+    c = og.ag_gemm(inp.a_chunks, inp.b)
+    a_all = np.concatenate(inp.a_chunks)
+    exact, absum = _exact(a_all, inp.b)
+    u = 2.0 ** -53
+    gamma = k * u / (1 - k * u)
+    for i in range(world * rows):
+        for j in range(n):
+            err = abs(Fraction(float(c[i, j])) - exact[i][j])
+            assert err <= Fraction(gamma) * absum[i][j] + Fraction(1, 2 ** 1074)
+
+
+@pytest.mark.parametrize("world,rows,k,n", [(4, 3, 20, 5), (8, 2, 33, 7)])
+def test_ag_gemm_integer_exact_per_chunk(world, rows, k, n):
+    inp = si.ag_inputs(902, world, rows, n, k, integer=True)
+    c = og.ag_gemm(inp.a_chunks, inp.b)
+    b = si.bf16_bits_to_f32(inp.b).astype(np.int64)
+    for ch in range(world):
+        a = si.bf16_bits_to_f32(inp.a_chunks[ch]).astype(np.int64)
+        for i in range(rows):
+            for j in range(n):
+                want = sum(int(a[i, kk]) * int(b[kk, j]) for kk in range(k))
+                assert c[ch * rows + i, j] == want
+
+
+def test_ag_gemm_rows_matches_full():
+    inp = si.ag_inputs(903, 4, 16, 24, 40)
+    full = og.ag_gemm(inp.a_chunks, inp.b)
+    rows = [0, 15, 16, 33, 63]
+    np.testing.assert_array_equal(og.ag_gemm_rows(inp.a_chunks, inp.b, rows), full[rows])
+
+
+def test_single_chunk_is_plain_gemm():
+    inp = si.ag_inputs(904, 1, 40, 24, 56)
+    c = og.ag_gemm(inp.a_chunks, inp.b)
+    a = torch.from_numpy(si.bf16_bits_to_f32(inp.a_chunks[0])).double()
+    b = torch.from_numpy(si.bf16_bits_to_f32(inp.b)).double()
+    ref = torch.matmul(a, b).numpy()
+    np.testing.assert_allclose(c, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_bf16_widening_known_values():
+    # 0x3F80 = 1.0, 0xC000 = -2.0, 0x3E80 = 0.25, 0x4049 = 3.140625, 0x0000 = 0
+    bits = np.array([0x3F80, 0xC000, 0x3E80, 0x4049, 0x0000], np.uint16)
+    np.testing.assert_array_equal(og.bf16_to_f64(bits), [1.0, -2.0, 0.25, 3.140625, 0.0])
+
+
+@pytest.mark.parametrize("world,rank", [(4, 0), (4, 3), (3, 1)])
+def test_gemm_rs_integer_exact(world, rank):
+    rows, k, n = 3, 10, 4
+    inp = si.rs_inputs(905, world, rank, rows, n, k, integer=True)
+    p, out = og.gemm_rs(inp.a, inp.b, inp.remote, world, rank)
+    a = si.bf16_bits_to_f32(inp.a).astype(np.int64)
+    b = si.bf16_bits_to_f32(inp.b).astype(np.int64)
+    for i in range(world * rows):
+        for j in range(n):
+            assert p[i, j] == sum(int(a[i, kk]) * int(b[kk, j]) for kk in range(k))
+    for i in range(rows):
+        for j in range(n):
+            want = 0
+            for s in range(world):
+                if s == rank:
+                    want += sum(int(a[rank * rows + i, kk]) * int(b[kk, j]) for kk in range(k))
+                else:
+                    want += int(inp.remote[s][i, j])
+            assert out[i, j] == want
+
+
+def test_gemm_rs_zero_remote_gives_local_slice():
+    world, rank, rows = 4, 2, 8
+    inp = si.rs_inputs(906, world, rank, rows, 12, 32, remote_zero=True)
+    p, out = og.gemm_rs(inp.a, inp.b, inp.remote, world, rank)
+    np.testing.assert_array_equal(out, p[rank * rows:(rank + 1) * rows])
+
+
+def test_reduce_order_is_ascending_rank():
+    # S_0 = 2^53, S_1 = 1, S_2 = -2^53 (local, rank 2).  Ascending order gives
+    # (2^53 + 1) -> 2^53 (ties to even), then 0.  Any order that adds the 1 last
+    # gives 1; descending order gives (-2^53 + 1) + 2^53 = 1.
+    local = np.array([[-2.0 ** 53]])
+    remote = {0: np.array([[2.0 ** 53]]), 1: np.array([[1.0]])}
+    out = og.reduce_slice(local, remote, 3, 2)
+    assert out[0, 0] == 0.0
+
+
+def test_gemm_rs_rows_matches_full():
+    world, rank, rows = 4, 1, 16
+    inp = si.rs_inputs(907, world, rank, rows, 20, 24, remote_std=0.3)
+    p, out = og.gemm_rs(inp.a, inp.b, inp.remote, world, rank)
+    sel = [0, 7, 15]
+    ps, outs = og.gemm_rs_rows(inp.a, inp.b, inp.remote, world, rank, sel)
+    np.testing.assert_array_equal(ps, p[rank * rows + np.array(sel)])
+    np.testing.assert_array_equal(outs, out[sel])
