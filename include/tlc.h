@@ -1,0 +1,327 @@
+/*
+ * tlc.h -- C ABI of libtlc: chunk-swizzled AllGather-GEMM, GEMM-ReduceScatter
+ * and AllGather-MoE on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (tile-level computation/communication overlap) runs ONE persistent
+ * tiled GEMM whose tile order follows communication chunks:
+ *   - gather mode (AllGather-GEMM, AG-MoE): every rank computes the tiles of the
+ *     chunk it already holds first, then the other chunks in rank-offset order as
+ *     per-chunk ready flags flip (DITRON paper notes, §3.2 "distributed
+ *     swizzling", gather mode and the rank_id mod local_world_size start;
+ *     Triton-Distributed talk, swizzling section);
+ *   - scatter mode (GEMM-ReduceScatter): tiles bound for remote ranks are produced
+ *     first, the rank's own slice last, into per-destination row slices of the
+ *     partial product, which a reduce kernel then sums into the local slice
+ *     (DITRON §3.2 scatter mode; talk, GEMM-ReduceScatter example: the GEMM
+ *     notifies, a separate reduce kernel waits, two streams).
+ * The other ranks are emulated on one GPU: their chunks are device buffers that
+ * a side stream lands into the local buffers chunk by chunk, then flags a
+ * per-chunk signal (AutoOverlap §5.3, backends 1 "copy engine" and 4/5
+ * "load/store on SMs"; global-memory signals for both).
+ *
+ * Conventions (all entry points)
+ *   - Every call returns tlc_status: 0 = OK, negative = error.  Argument errors
+ *     are detected on the host and returned synchronously; nothing is enqueued
+ *     then.  tlc_last_error() gives a human-readable detail for the calling
+ *     thread.
+ *   - Calls are asynchronous in stream order; no call synchronizes the host,
+ *     except tlc_signals_alloc/free and tlc_read_status.
+ *   - Ownership: the caller owns every buffer.  The library allocates no device
+ *     memory on these paths and keeps no per-call state.
+ *   - Pointers named "device" must point to device-accessible memory of the
+ *     current HIP device; "host" pointers are read during the call only.
+ *   - Streams are hipStream_t values passed as void* (NULL = default stream).
+ *   - Device-side failures (a wait that exceeded its time limit, a plan entry
+ *     outside the output) are written to tlc_signals.status and read after the
+ *     stream is synchronized (tlc_read_status).  The kernels then stop early;
+ *     outputs are undefined.
+ *   - Element types: "bf16" = bfloat16 (raw 16-bit), "f32" = IEEE binary32.
+ *     All matrices are row-major with the stated leading dimension.
+ */
+#ifndef TLC_H
+#define TLC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t tlc_status;
+
+enum {
+  TLC_OK = 0,
+  TLC_ERR_INVALID_ARG = -1, /* NULL pointer, size out of range, inconsistent sizes */
+  TLC_ERR_UNSUPPORTED = -2, /* tile shape / layout / device not supported */
+  TLC_ERR_MISALIGNED = -3,  /* a pointer or row stride not 16-byte aligned */
+  TLC_ERR_CAPACITY = -4,    /* output array too small (tlc_chunk_plan) */
+  TLC_ERR_HIP = -5,         /* a HIP runtime call failed (text in tlc_last_error) */
+  TLC_ERR_TIMEOUT = -6,     /* device: a chunk flag did not reach the epoch in time */
+  TLC_ERR_BAD_PLAN = -7     /* device: a plan entry lies outside the output */
+};
+
+enum { TLC_MODE_AG = 0, TLC_MODE_RS = 1, TLC_MODE_MOE = 2 };
+/* NATURAL: every rank walks tiles from tile 0 (no swizzle).  RANK_OFFSET: the
+ * chunk-following order described above. */
+enum { TLC_ORDER_NATURAL = 0, TLC_ORDER_RANK_OFFSET = 1 };
+/* Layout of a weight operand B of logical shape K x N:
+ * KN = K rows of N contiguous elements; NK = N rows of K contiguous elements. */
+enum { TLC_B_KN = 0, TLC_B_NK = 1 };
+/* How the emulated peers' chunks arrive:
+ *   NONE        -- already in place; the caller has set the flags (compute-only)
+ *   COPY_ENGINE -- one hipMemcpyAsync(DeviceToDeviceNoCU) per chunk on the copy
+ *                  stream, then hipStreamWriteValue32 of the chunk's flag
+ *   CU          -- one copy kernel on the copy stream; its workgroups copy the
+ *                  chunks in landing order and the last one to finish a chunk
+ *                  publishes its flag with a release store                     */
+enum { TLC_LAND_NONE = 0, TLC_LAND_COPY_ENGINE = 1, TLC_LAND_CU = 2 };
+
+#define TLC_MAX_WORLD 32
+
+/* One output tile of the plan, 32 bytes.  Rows [m0, m0+m_rows) and columns
+ * [n0, n0+n_cols) of the output.  expert = -1 for dense GEMMs.  chunk_mask bit
+ * c = the tile reads rows of chunk c (gather, MoE) or writes rows of
+ * destination chunk c (scatter).  key = the primary sort key: wait position
+ * (gather), send position (scatter) or readiness (MoE); 0 in natural order. */
+typedef struct {
+  int32_t m0, n0, m_rows, n_cols;
+  int32_t expert;
+  uint32_t chunk_mask;
+  int32_t key;
+  int32_t reserved; /* 0 */
+} tlc_tile;
+
+/* Signals shared by the copy side and the kernels (device memory; allocate
+ * with tlc_signals_alloc so that it is fine-grained and coherent with the copy
+ * engines).  flags[c] >= epoch  <=>  chunk c has landed for this call.
+ * status[0] = 0 or a negative tlc_status, status[1] = plan index of the tile
+ * that failed, status[2] = chunk it waited for.  land_count is internal to the
+ * CU landing backend (zero between calls). */
+typedef struct {
+  uint32_t flags[TLC_MAX_WORLD];
+  uint32_t land_count[TLC_MAX_WORLD];
+  int32_t status[4];
+  uint32_t reserved[12];
+} tlc_signals;
+
+/* ---------------------------------------------------------------- plan ---- */
+
+/* tlc_plan_desc: a dense gather or scatter GEMM whose M rows are `world`
+ * chunks of `rows_per_chunk` rows (M = world * rows_per_chunk). */
+typedef struct {
+  int32_t mode;           /* TLC_MODE_AG or TLC_MODE_RS */
+  int32_t world;          /* 1 .. TLC_MAX_WORLD */
+  int32_t rank;           /* 0 .. world-1 */
+  int32_t M, N;           /* output size, >= 1 */
+  int32_t rows_per_chunk; /* R >= 1, M == world * R */
+  int32_t bm, bn;         /* tile size, >= 1 */
+  int32_t order;          /* TLC_ORDER_* */
+  int32_t group_m;        /* >= 1: m-tiles per locality band inside a key */
+} tlc_plan_desc;
+
+/* Tile order of the communication-aware scheduler (host code, integers only).
+ *   Gather: chunk c is consumed at position p(c) = (c - rank) mod W; a tile is
+ *   keyed by the largest p of the chunks it reads, so tiles that straddle
+ *   chunks run once their last chunk has landed (Triton-Distributed talk,
+ *   non-perfect tile scheduling).  Scatter: destination c is sent at position
+ *   q(c) = (c - rank - 1) mod W; a tile is keyed by the smallest q of the
+ *   destinations it writes, so the rank's own slice goes last and straddling
+ *   tiles go early.  Ties: (m-tile / group_m, n-tile, m-tile) -- bands of
+ *   group_m m-tiles walked column by column (AutoOverlap §5.4, Fig. 6: intra-
+ *   chunk swizzle for locality).  Natural order: all keys 0.
+ * tiles:   host array of `cap` entries, or NULL to query the count only.
+ * n_tiles: host, receives ceil(M/bm) * ceil(N/bn).
+ * landing_order: host array of world-1 entries or NULL; receives the order in
+ *   which peers' chunks land: rank+1, rank+2, ..., rank-1 (mod W).
+ * Errors: INVALID_ARG (bad desc), CAPACITY (cap < count; *n_tiles is set). */
+tlc_status tlc_chunk_plan(const tlc_plan_desc* desc, tlc_tile* tiles, int64_t cap,
+                          int64_t* n_tiles, int32_t* landing_order);
+
+/* ------------------------------------------------------------- signals ---- */
+
+/* Allocate / free one zeroed tlc_signals block in fine-grained device memory
+ * (synchronous).  *out receives a device pointer. */
+tlc_status tlc_signals_alloc(tlc_signals** out);
+tlc_status tlc_signals_free(tlc_signals* sig);
+/* Enqueue on `stream`: flags[0..world-1] = value (a one-workgroup kernel; no
+ * memset, so it may be captured in a graph).  Used to mark every chunk as
+ * landed for compute-only runs, or to rewind the flags to 0. */
+tlc_status tlc_signals_set(tlc_signals* sig, int32_t world, uint32_t value, void* stream);
+/* Enqueue on `stream`: status[0..3] = 0. */
+tlc_status tlc_signals_clear_status(tlc_signals* sig, void* stream);
+/* Synchronize `stream`, then copy status[0..3] to the host array out[4]. */
+tlc_status tlc_read_status(const tlc_signals* sig, void* stream, int32_t* out);
+
+/* ---------------------------------------------------------- AG-GEMM ------- */
+
+/* C[M x N] (f32) = concat_{c=0..W-1}(A_c) [M x K] (bf16) @ B [K x N] (bf16),
+ * fp32 accumulation (DITRON §4.1 AG-GEMM; the pages' core-level tile GEMM).
+ * Tile shapes: (bm, bn) in {(256,256), (128,128)}; BK = 64.
+ * Requirements: K % 64 == 0, N % 8 == 0, M == world * rows_per_chunk, all
+ * pointers 16-byte aligned.  `plan` is a device copy of tlc_chunk_plan(...)
+ * output for the same (M, N, rows_per_chunk, bm, bn, world, rank), mode AG.
+ * Buffers:
+ *   a      device bf16 M x K, the gathered activations; rows of chunk `rank`
+ *          must be in place before the call; the other chunks' rows are
+ *          written by the landing (or already in place if land == NONE).
+ *          The caller must stream-order the copy stream after earlier readers
+ *          of `a` (the landing overwrites it).
+ *   a_src  host array of `world` device pointers, chunk c's source (R x K
+ *          bf16); entry `rank` is ignored; may be NULL if land == NONE.
+ *   b      device bf16, layout b_layout (KN: ldb = N; NK: ldb = K).
+ *   c      device f32 M x N, ldc = N.
+ *   sig    device tlc_signals; status must be 0 on entry; flags < epoch for the
+ *          chunks that still have to land.
+ * Streams: the GEMM runs on `compute`, the landing on `copy`.
+ * grid: persistent workgroups (0 = default: fewest rounds of tiles over the
+ * compute units, spread evenly).  timeout_ns: per-wait limit (0 = 2 s). */
+typedef struct {
+  const tlc_tile* plan; /* device, n_tiles entries, execution order */
+  int64_t n_tiles;
+  int32_t M, N, K;
+  int32_t world, rank, rows_per_chunk;
+  int32_t bm, bn;
+  void* a;
+  const void* const* a_src;
+  const void* b;
+  int32_t b_layout;
+  float* c;
+  tlc_signals* sig;
+  uint32_t epoch;
+  int32_t land;
+  int32_t grid;
+  int64_t timeout_ns;
+} tlc_ag_args;
+
+tlc_status tlc_ag_gemm(const tlc_ag_args* args, void* compute_stream, void* copy_stream);
+
+/* ---------------------------------------------------------- GEMM-RS ------- */
+
+/* Scatter-mode GEMM then reduce (DITRON §4.1 GEMM-RS; talk, GEMM-ReduceScatter
+ * example).  P[M x N] (f32) = A [M x K] (bf16, local K shard) @ B [K x N];
+ * the row chunk P[c] = rows [c R, (c+1) R) is the partial bound for rank c.
+ * out[R x N] (f32) = sum over s = 0..W-1 in ascending s of S_s, S_rank = P[rank]
+ * and S_s = landing[s] (the partial rank s computed for this rank's rows).
+ * Requirements as tlc_ag_gemm plus N % 4 == 0.  plan: mode RS.
+ *   remote_src / landing: host arrays of `world` device pointers (R x N f32);
+ *   entries `rank` are ignored; remote_src may be NULL if land == NONE (then
+ *   landing[s] must already hold the data and flags be >= epoch).
+ * The GEMM and then the reduce run on `compute`; the reduce waits in-kernel for
+ * the remote partials' flags.  */
+typedef struct {
+  const tlc_tile* plan;
+  int64_t n_tiles;
+  int32_t M, N, K;
+  int32_t world, rank, rows_per_chunk;
+  int32_t bm, bn;
+  const void* a;
+  const void* b;
+  int32_t b_layout;
+  float* partials;
+  const float* const* remote_src;
+  float* const* landing;
+  float* out;
+  tlc_signals* sig;
+  uint32_t epoch;
+  int32_t land;
+  int32_t grid;
+  int64_t timeout_ns;
+} tlc_rs_args;
+
+tlc_status tlc_gemm_rs(const tlc_rs_args* args, void* compute_stream, void* copy_stream);
+
+/* The reduce step alone (same arguments; the GEMM is not run). */
+tlc_status tlc_rs_reduce(const tlc_rs_args* args, void* compute_stream, void* copy_stream);
+
+/* ------------------------------------------------------------ AG-MoE ------ */
+
+/* Routing for AG-MoE, on the device (DITRON §3.1 device level: chunk sizes
+ * computed at run time for MoE routing; talk, "MoE dynamic sorting").
+ * For T = world * tokens_per_chunk tokens and E experts:
+ *   topk[T x k]  experts with the largest logits, largest first, equal logits
+ *                -> lower expert index first;
+ *   gates[T x k] softmax over the selected logits (f32);
+ *   counts[E], offsets[E+1] (exclusive prefix sum);
+ *   row_token[T*k]  token of every grouped-GEMM row, expert-major, inside an
+ *                   expert ordered by (p(chunk of token), token) with
+ *                   p(c) = (c - rank) mod world;
+ *   slot[T x k]  the grouped-GEMM row of (token, j-th expert);
+ *   plan, *n_tiles_dev: grouped-GEMM tiles (bm x bn over each expert's rows and
+ *                N columns), ordered by (readiness, expert, m-tile, n-tile), with
+ *                readiness = largest p of the tiles' tokens (0 in natural
+ *                order); chunk_mask = chunks of the tile's tokens.
+ * Limits: E <= 64 (one expert per lane of a wavefront), k <= E, k <= 16,
+ * T <= 2^20, bm in {128, 256}.  plan_cap >= tlc_moe_plan_capacity(...).
+ * All arrays are device memory; `workspace` is device memory of at least
+ * tlc_moe_workspace_bytes(T, k, E, bm) bytes (contents need not be initialised). */
+typedef struct {
+  const float* logits; /* device f32 T x E */
+  int32_t tokens_per_chunk, world, rank, experts, topk;
+  int32_t N, bm, bn, order;
+  int32_t* topk_idx;
+  float* gates;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* slot;
+  tlc_tile* plan;
+  int64_t plan_cap;
+  int32_t* n_tiles_dev;
+  void* workspace;
+} tlc_moe_route_args;
+
+int64_t tlc_moe_plan_capacity(int32_t T, int32_t topk, int32_t experts, int32_t N, int32_t bm,
+                              int32_t bn);
+int64_t tlc_moe_workspace_bytes(int32_t T, int32_t topk, int32_t experts, int32_t bm);
+tlc_status tlc_moe_route(const tlc_moe_route_args* args, void* stream);
+
+/* Y[(T*k) x N] (f32): Y[i] = X[row_token[i]] (bf16, 1 x H) @ W_e (bf16, H x N)
+ * for the expert e whose row segment holds i.  X is the gathered token matrix
+ * (T x H, chunk c = rows [c Tc, (c+1) Tc)); chunks land as in tlc_ag_gemm.
+ * w: device bf16, E stacked matrices, layout w_layout (KN: E x H x N; NK:
+ * E x N x H).  Tiles come from tlc_moe_route (plan, n_tiles_dev).
+ * Requirements: H % 64 == 0, N % 8 == 0, 16-byte aligned pointers. */
+typedef struct {
+  const tlc_tile* plan;
+  const int32_t* n_tiles_dev;
+  int64_t plan_cap;
+  const int32_t* row_token;
+  int32_t tokens_per_chunk, world, rank, experts, topk;
+  int32_t H, N;
+  int32_t bm, bn;
+  void* x;
+  const void* const* x_src;
+  const void* w;
+  int32_t w_layout;
+  float* y;
+  tlc_signals* sig;
+  uint32_t epoch;
+  int32_t land;
+  int32_t grid;
+  int64_t timeout_ns;
+} tlc_moe_args;
+
+tlc_status tlc_ag_moe(const tlc_moe_args* args, void* compute_stream, void* copy_stream);
+
+/* ------------------------------------------------------------ misc -------- */
+
+/* Land the peers' chunks only (the copy side of tlc_ag_gemm / tlc_gemm_rs,
+ * no GEMM): for c in landing order (rank+1, ..., rank-1 mod W) copies
+ * `bytes_per_chunk` bytes from src[c] to dst[c] and then raises
+ * sig->flags[c] to epoch.  dst, src: host arrays of `world` device pointers,
+ * 16-byte aligned; entries `rank` are ignored.  bytes_per_chunk % 16 == 0.
+ * land: TLC_LAND_COPY_ENGINE or TLC_LAND_CU.  Used for copy-only timings. */
+tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_chunk,
+                    int32_t world, int32_t rank, tlc_signals* sig, uint32_t epoch, int32_t land,
+                    void* copy_stream);
+
+const char* tlc_status_string(tlc_status s);
+const char* tlc_last_error(void);
+/* Library version, e.g. 100 = 0.1.0. */
+int32_t tlc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TLC_H */

@@ -1,0 +1,91 @@
+"""The C-ABI library loads and exports every function include/tlc.h declares
+(no compute calls: no GPU is needed), and host-side argument validation
+returns synchronous error codes."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from tile_level_communication_amd import tlc
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tlc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tlc_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    assert set(names) == set(tlc.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    L = tlc.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert C.cast(getattr(L, name), C.c_void_p).value
+
+
+def test_version_and_strings():
+    assert tlc.version() == 100
+    assert tlc.status_string(tlc.ERR_TIMEOUT).startswith("timeout")
+    assert tlc.status_string(0) == "ok"
+
+
+def test_struct_sizes_match_header():
+    assert C.sizeof(tlc.Tile) == 32
+    assert C.sizeof(tlc.PlanDesc) == 40
+
+
+def _ag_args(**over):
+    base = dict(plan=None, n_tiles=0, M=256, N=256, K=512, world=2, rank=0, rows_per_chunk=128,
+                bm=128, bn=128, a=None, a_src=None, b=None, b_layout=tlc.B_KN, c=None, sig=None,
+                epoch=1, land=tlc.LAND_NONE, grid=0, timeout_ns=0)
+    base.update(over)
+    return tlc.AGArgs(**base)
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(world=0), tlc.ERR_INVALID_ARG),
+    (dict(rank=2), tlc.ERR_INVALID_ARG),
+    (dict(M=255), tlc.ERR_INVALID_ARG),
+    (dict(K=500), tlc.ERR_UNSUPPORTED),
+    (dict(N=250, M=256), tlc.ERR_UNSUPPORTED),
+    (dict(bm=64, bn=64), tlc.ERR_UNSUPPORTED),
+    (dict(b_layout=7), tlc.ERR_INVALID_ARG),
+    (dict(), tlc.ERR_INVALID_ARG),                       # NULL operands
+    (dict(a=16, b=32, c=48, sig=64, n_tiles=4), tlc.ERR_INVALID_ARG),   # NULL plan
+    (dict(a=8, b=32, c=48, sig=64), tlc.ERR_MISALIGNED),
+    (dict(a=16, b=32, c=48, sig=64, land=9), tlc.ERR_INVALID_ARG),
+    (dict(a=16, b=32, c=48, sig=64, land=tlc.LAND_CU), tlc.ERR_INVALID_ARG),  # no a_src
+])
+def test_ag_gemm_argument_errors(over, want):
+    args = _ag_args(**over)
+    s = tlc.lib().tlc_ag_gemm(C.byref(args), None, None)
+    assert s == want, tlc.last_error()
+    assert tlc.last_error()
+
+
+def test_plan_capacity_and_query():
+    d = tlc.PlanDesc(tlc.MODE_AG, 8, 3, 8192, 3200, 1024, 256, 256, tlc.ORDER_RANK_OFFSET, 4)
+    n = C.c_int64(0)
+    assert tlc.lib().tlc_chunk_plan(C.byref(d), None, 0, C.byref(n), None) == 0
+    assert n.value == 32 * 13
+    tiles = (tlc.Tile * 10)()
+    assert tlc.lib().tlc_chunk_plan(C.byref(d), tiles, 10, C.byref(n), None) == tlc.ERR_CAPACITY
+    bad = tlc.PlanDesc(tlc.MODE_AG, 8, 8, 8192, 3200, 1024, 256, 256, 1, 1)
+    assert tlc.lib().tlc_chunk_plan(C.byref(bad), None, 0, C.byref(n), None) == tlc.ERR_INVALID_ARG
+    bad = tlc.PlanDesc(tlc.MODE_AG, 8, 0, 8190, 3200, 1024, 256, 256, 1, 1)
+    assert tlc.lib().tlc_chunk_plan(C.byref(bad), None, 0, C.byref(n), None) == tlc.ERR_INVALID_ARG
+    bad = tlc.PlanDesc(tlc.MODE_MOE, 8, 0, 8192, 3200, 1024, 256, 256, 1, 1)
+    assert tlc.lib().tlc_chunk_plan(C.byref(bad), None, 0, C.byref(n), None) == tlc.ERR_INVALID_ARG
+
+
+def test_moe_sizes():
+    assert tlc.moe_plan_capacity(4096, 8, 64, 768, 256, 256) == (4096 * 8 // 256 + 64) * 3
+    assert tlc.moe_workspace_bytes(4096, 8, 64, 256) >= 4096 * 8 + 65 * 4 + 2 * 192 * 4
+    assert tlc.moe_plan_capacity(0, 8, 64, 768, 256, 256) == 0

@@ -1,0 +1,154 @@
+"""AllGather-GEMM on the GPU (through the C ABI) against the float64 oracle.
+
+Small shapes span several tiles with ragged edges and a tile that straddles two
+chunks; every rank; both weight layouts; all three landing modes.  Integer-
+valued inputs are compared bit for bit.  The full Qwen3-32B-like FFN-up shape
+(8 chunks of 1024 x 5120, weight 5120 x 3200) is checked on sampled rows with
+normal inputs and in full with integer inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+from oracle import gemm as og
+from tests.parity import absmax_bf16, check_close, check_exact, log
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tile_level_communication_amd import tlc
+    from tile_level_communication_amd.workloads import AGProblem
+else:  # collected on CPU-only hosts, never run there
+    from tile_level_communication_amd import tlc  # noqa: F401
+
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2}
+
+SHAPES = [
+    # name, W, R, K, N, tile
+    ("w2_256x256x512_t128", 2, 128, 512, 256, 128),
+    ("w2_256x256x512_t256_straddle", 2, 128, 512, 256, 256),
+    ("w3_ragged_600x392x320_t256", 3, 200, 320, 392, 256),
+    ("w5_ragged_385x136x128_t128", 5, 77, 128, 136, 128),
+]
+
+
+def _run(inp, rank, tile, layout, land, **kw):
+    prob = AGProblem(inp.a_chunks, inp.b, rank, tile, tile, layout, **kw)
+    if land == tlc.LAND_NONE:
+        prob.place_all()
+    else:
+        prob.poison_remote()
+    prob.run(land)
+    torch.cuda.synchronize()
+    st = prob.sig.read_status()
+    assert st[0] == 0, f"device status {st}"
+    return prob, prob.c.cpu().numpy()
+
+
+@pytest.mark.parametrize("land", list(LANDS))
+@pytest.mark.parametrize("layout", [0, 1], ids=["KN", "NK"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_ag_small_parity(shape, layout, land):
+    name, W, R, K, N, tile = shape
+    for integer in (False, True):
+        inp = si.ag_inputs(100 + W, W, R, N, K, integer=integer)
+        ref = og.ag_gemm(inp.a_chunks, inp.b)
+        for rank in range(W):
+            log(f"[ag] {name} layout={layout} land={land} int={integer} rank={rank}")
+            _, c = _run(inp, rank, tile, layout, LANDS[land])
+            if integer:
+                check_exact(c, ref, name)
+            else:
+                check_close(c, ref, K, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), name)
+
+
+def test_ag_tile_order_does_not_change_bits():
+    W, R, K, N = 4, 160, 256, 520
+    inp = si.ag_inputs(120, W, R, N, K)
+    outs = []
+    for order in (tlc.ORDER_NATURAL, tlc.ORDER_RANK_OFFSET):
+        for group_m in (1, 4):
+            for grid in (0, 1, 7):
+                log(f"[ag order] order={order} group_m={group_m} grid={grid}")
+                prob = AGProblem(inp.a_chunks, inp.b, 2, 128, 128, tlc.B_KN, order=order, group_m=group_m)
+                prob.poison_remote()
+                prob.run(tlc.LAND_COPY_ENGINE, grid=grid)
+                torch.cuda.synchronize()
+                assert prob.sig.read_status()[0] == 0
+                outs.append(prob.c.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    check_close(outs[0], og.ag_gemm(inp.a_chunks, inp.b), K, absmax_bf16(inp.a_chunks),
+                absmax_bf16(inp.b), "order")
+
+
+@pytest.mark.parametrize("land", ["copy_engine", "cu"])
+def test_ag_fresh_data_every_call(land):
+    """Landed data changes between calls (and the landing rows are poisoned
+    before each call): a read of stale or not-yet-landed data fails."""
+    W, R, K, N = 4, 128, 256, 256
+    inp1 = si.ag_inputs(130, W, R, N, K)
+    inp2 = si.ag_inputs(131, W, R, N, K)
+    inp2.a_chunks[1] = inp1.a_chunks[1]  # the local chunk (rank 1) stays the same
+    prob = AGProblem(inp1.a_chunks, inp1.b, 1, 128, 128)
+    for it, inp in enumerate([inp1, inp2, inp1, inp2]):
+        log(f"[ag fresh] land={land} iteration={it}")
+        for c in range(W):
+            prob.a_src[c].copy_(torch.from_numpy(inp.a_chunks[c].view(np.int16)).view(torch.bfloat16))
+        prob.poison_remote()
+        prob.run(LANDS[land])
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        check_close(prob.c.cpu().numpy(), og.ag_gemm(inp.a_chunks, inp1.b), K,
+                    absmax_bf16(inp.a_chunks), absmax_bf16(inp1.b), f"iter{it}")
+
+
+def test_ag_timeout_reports_status():
+    """A chunk whose flag never reaches the epoch: the kernel gives up after
+    the time limit, reports TIMEOUT with the chunk, and every workgroup exits."""
+    W, R, K, N = 2, 128, 128, 128
+    inp = si.ag_inputs(140, W, R, N, K)
+    prob = AGProblem(inp.a_chunks, inp.b, 0, 128, 128)
+    prob.place_all()
+    log("[ag timeout] flags left below the epoch, 2 ms limit")
+    prob.run(tlc.LAND_NONE, timeout_ns=2_000_000, preset_flags=False)
+    st = prob.sig.read_status(prob.streams.compute)
+    assert st[0] == tlc.ERR_TIMEOUT and st[2] == 1, st
+    prob.sig.clear_status()
+    prob.run(tlc.LAND_NONE)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    check_close(prob.c.cpu().numpy(), og.ag_gemm(inp.a_chunks, inp.b), K, absmax_bf16(inp.a_chunks),
+                absmax_bf16(inp.b), "after timeout")
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_ag_qwen3_ffn_up_full_size(rank):
+    wl = si.WORKLOADS[2]
+    log(f"[ag full] {wl.name} rank={rank}: generating inputs")
+    inp = si.workload_inputs(2)
+    prob = AGProblem(inp.a_chunks, inp.b, rank, 256, 256, tlc.B_KN)
+    prob.poison_remote()
+    log(f"[ag full] {wl.name} rank={rank}: run (copy engine landing)")
+    prob.run(tlc.LAND_COPY_ENGINE)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    c = prob.c
+    rng = np.random.default_rng(rank)
+    rows = np.unique(np.concatenate([
+        [0, 1, 255, 256, 1023, 1024, 4095, 4096, 8191],
+        [ch * 1024 + o for ch in range(8) for o in (0, 511, 1023)],
+        rng.integers(0, 8192, 40)]))
+    got = c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
+    ref = og.ag_gemm_rows(inp.a_chunks, inp.b, rows)
+    check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), "cfg full rows")
+    # integer-valued inputs: the whole output bit for bit
+    log(f"[ag full] {wl.name} rank={rank}: integer inputs, full compare")
+    ii = si.workload_inputs(2, integer=True)
+    prob = AGProblem(ii.a_chunks, ii.b, rank, 256, 256, tlc.B_KN)
+    prob.poison_remote()
+    prob.run(tlc.LAND_CU)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    check_exact(prob.c.cpu().numpy(), og.ag_gemm(ii.a_chunks, ii.b), "cfg full integer")

@@ -1,0 +1,103 @@
+"""AG-MoE on the GPU (through the C ABI) against the oracle: routing arrays and
+the readiness-sorted tile list bit for bit, gates within 1e-6, the grouped GEMM
+within the GEMM tolerance (integer inputs bit for bit)."""
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+from oracle import moe as om
+from oracle import plan as op
+from tests.parity import absmax_bf16, check_close, check_exact, log
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tile_level_communication_amd import tlc
+    from tile_level_communication_amd.workloads import MoEProblem
+
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2}
+
+
+def _check_routing(prob, ref, order):
+    np.testing.assert_array_equal(prob.topk_idx.cpu().numpy(), ref["topk"])
+    np.testing.assert_array_equal(prob.counts.cpu().numpy(), ref["counts"])
+    np.testing.assert_array_equal(prob.offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(prob.row_token.cpu().numpy(), ref["row_token"])
+    np.testing.assert_array_equal(prob.slot.cpu().numpy(), ref["slot"])
+    g = prob.gates.cpu().numpy().astype(np.float64)
+    assert np.abs(g - ref["gates"]).max() <= 1e-6
+    n = int(prob.n_tiles_dev.cpu().item())
+    want = op.moe_plan(ref["counts"], ref["offsets"], ref["row_token"], prob.Tc, prob.world, prob.rank,
+                       prob.N, prob.bm, prob.bn, order)
+    got = prob.plan[:n].cpu().numpy().astype(np.int64)
+    got[:, 5] &= 0xFFFFFFFF
+    assert n == len(want)
+    np.testing.assert_array_equal(got, np.array(want, dtype=np.int64))
+
+
+SMALL = [
+    # name, W, Tc, H, N, E, k, tile
+    ("w4_t64_e16_k4_h128_n136_t128", 4, 16, 128, 136, 16, 4, 128),
+    ("w2_t80_e64_k8_h192_n256_t256", 2, 40, 192, 256, 64, 8, 256),
+    ("w8_t256_e8_k2_h64_n512_t128", 8, 32, 64, 512, 8, 2, 128),
+]
+
+
+@pytest.mark.parametrize("land", list(LANDS))
+@pytest.mark.parametrize("layout", [0, 1], ids=["KN", "NK"])
+@pytest.mark.parametrize("shape", SMALL, ids=[s[0] for s in SMALL])
+def test_moe_small_parity(shape, layout, land):
+    name, W, Tc, H, N, E, k, tile = shape
+    for integer in (False, True):
+        inp = si.moe_inputs(300 + W, W, Tc, H, N, E, integer=integer)
+        for rank in sorted({0, W - 1, W // 2}):
+            for order in (tlc.ORDER_RANK_OFFSET, tlc.ORDER_NATURAL):
+                log(f"[moe] {name} layout={layout} land={land} int={integer} rank={rank} order={order}")
+                ref = om.route(inp.logits, k, W, rank, Tc)
+                prob = MoEProblem(inp.x_chunks, inp.logits, inp.w, rank, k, tile, tile, layout, order)
+                if LANDS[land] == 0:
+                    prob.place_all()
+                else:
+                    prob.poison_remote()
+                prob.run(LANDS[land])
+                torch.cuda.synchronize()
+                assert prob.sig.read_status()[0] == 0
+                _check_routing(prob, ref, order)
+                y_ref = om.grouped_gemm(inp.x_chunks, inp.w, ref["offsets"], ref["row_token"])
+                y = prob.y.cpu().numpy()
+                if integer:
+                    check_exact(y, y_ref, name)
+                else:
+                    check_close(y, y_ref, H, absmax_bf16(inp.x_chunks), absmax_bf16(inp.w), name)
+
+
+def test_moe_ties_route_to_lower_expert():
+    W, Tc, H, N, E, k = 2, 32, 64, 128, 16, 4
+    inp = si.moe_inputs(320, W, Tc, H, N, E)
+    inp.logits[:] = np.round(inp.logits * 2) / 2      # many exact ties
+    log("[moe ties]")
+    ref = om.route(inp.logits, k, W, 1, Tc)
+    prob = MoEProblem(inp.x_chunks, inp.logits, inp.w, 1, k, 128, 128)
+    prob.poison_remote()
+    prob.run(tlc.LAND_COPY_ENGINE)
+    torch.cuda.synchronize()
+    _check_routing(prob, ref, tlc.ORDER_RANK_OFFSET)
+
+
+@pytest.mark.parametrize("rank", [0, 5])
+def test_moe_full_size(rank):
+    wl = si.WORKLOADS[4]
+    log(f"[moe full] {wl.name} rank={rank}")
+    inp = si.workload_inputs(4)
+    ref = om.route(inp.logits, wl.topk, wl.world, rank, wl.rows_per_chunk)
+    prob = MoEProblem(inp.x_chunks, inp.logits, inp.w, rank, wl.topk, 256, 256, tlc.B_KN)
+    prob.poison_remote()
+    prob.run(tlc.LAND_COPY_ENGINE)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    _check_routing(prob, ref, tlc.ORDER_RANK_OFFSET)
+    assert int(ref["counts"].sum()) == 4096 * 8
+    y_ref = om.grouped_gemm(inp.x_chunks, inp.w, ref["offsets"], ref["row_token"])
+    check_close(prob.y.cpu().numpy(), y_ref, wl.k, absmax_bf16(inp.x_chunks), absmax_bf16(inp.w),
+                "moe full")

@@ -1,0 +1,504 @@
+// libtlc entry points: argument validation, landing enqueue, kernel launches.
+// See include/tlc.h for the contract of every function.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "tlc_internal.h"
+
+namespace tlc {
+
+namespace {
+thread_local char g_err[512] = "";
+std::mutex g_info_mu;
+DeviceInfo g_info[64];
+bool g_info_ok[64] = {};
+constexpr int kReserveCUs = 8;  // one CU per XCD left for copy/signal kernels
+constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
+}  // namespace
+
+tlc_status fail(tlc_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tlc_status ok() {
+  g_err[0] = '\0';
+  return TLC_OK;
+}
+
+tlc_status device_info(DeviceInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TLC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(TLC_ERR_UNSUPPORTED, "device id %d", dev);
+  std::lock_guard<std::mutex> lk(g_info_mu);
+  if (!g_info_ok[dev]) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(TLC_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    DeviceInfo info;
+    info.cus = prop.multiProcessorCount;
+    int khz = 0;
+    e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    info.wall_khz = (e == hipSuccess && khz > 0) ? khz : 100000;
+    info.arch_ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_info[dev] = info;
+    g_info_ok[dev] = true;
+  }
+  *out = g_info[dev];
+  if (!out->arch_ok) return fail(TLC_ERR_UNSUPPORTED, "libtlc kernels are built for gfx950 only");
+  return TLC_OK;
+}
+
+int default_grid(int64_t n_tiles, int avail) {
+  if (n_tiles <= 0 || avail <= 0) return 1;
+  const int64_t rounds = (n_tiles + avail - 1) / avail;
+  int64_t g = (n_tiles + rounds - 1) / rounds;
+  g = ((g + 7) / 8) * 8;
+  if (g > avail) g = avail;
+  return static_cast<int>(g);
+}
+
+}  // namespace tlc
+
+using namespace tlc;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ticks_for(int64_t ns, const DeviceInfo& info) {
+  if (ns <= 0) ns = kDefaultTimeoutNs;
+  return ns / 1000 * info.wall_khz / 1000 + 1;
+}
+
+tlc_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TLC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return TLC_OK;
+}
+
+// Enqueue the emulated peers' chunk transfers on `copy` in landing order
+// (rank+1, rank+2, ... mod W) and raise each chunk's flag to `epoch` after
+// its bytes.
+tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, int64_t bytes,
+                           int world, int rank, tlc_signals* sig, uint32_t epoch, void* copy,
+                           const DeviceInfo& info) {
+  if (land == TLC_LAND_NONE || world == 1) return TLC_OK;
+  hipStream_t s = static_cast<hipStream_t>(copy);
+  if (land == TLC_LAND_COPY_ENGINE) {
+    for (int i = 1; i < world; ++i) {
+      const int c = (rank + i) % world;
+      tlc_status st = hip_check(hipMemcpyAsync(dst[c], src[c], static_cast<size_t>(bytes),
+                                               hipMemcpyDeviceToDeviceNoCU, s),
+                                "hipMemcpyAsync(landing)");
+      if (st) return st;
+      st = hip_check(hipStreamWriteValue32(s, &sig->flags[c], epoch, 0), "hipStreamWriteValue32");
+      if (st) return st;
+    }
+    return TLC_OK;
+  }
+  LandParams p;
+  memset(&p, 0, sizeof(p));
+  p.n_chunks = world - 1;
+  for (int i = 1; i < world; ++i) {
+    const int c = (rank + i) % world;
+    p.order[i - 1] = c;
+    p.src[c] = static_cast<const uint4*>(src[c]);
+    p.dst[c] = static_cast<uint4*>(dst[c]);
+  }
+  p.vec_per_chunk = bytes / 16;
+  p.sig = sig;
+  p.epoch = epoch;
+  int grid = info.cus / 4;
+  if (grid < 8) grid = 8;
+  return launch_land_cu(p, grid, copy);
+}
+
+tlc_status check_land_args(int land, const void* const* src, const void* const* dst, int world,
+                           int rank, int64_t bytes, const char* who) {
+  if (land != TLC_LAND_NONE && land != TLC_LAND_COPY_ENGINE && land != TLC_LAND_CU)
+    return fail(TLC_ERR_INVALID_ARG, "%s: land %d unknown", who, land);
+  if (land == TLC_LAND_NONE) return TLC_OK;
+  if (!src || !dst) return fail(TLC_ERR_INVALID_ARG, "%s: landing needs source and destination arrays", who);
+  if (bytes % 16 != 0) return fail(TLC_ERR_MISALIGNED, "%s: chunk bytes %lld not a multiple of 16", who,
+                                   static_cast<long long>(bytes));
+  for (int c = 0; c < world; ++c) {
+    if (c == rank) continue;
+    if (!src[c] || !dst[c]) return fail(TLC_ERR_INVALID_ARG, "%s: chunk %d pointer is NULL", who, c);
+    if (!aligned16(src[c]) || !aligned16(dst[c]))
+      return fail(TLC_ERR_MISALIGNED, "%s: chunk %d pointer not 16-byte aligned", who, c);
+  }
+  return TLC_OK;
+}
+
+tlc_status check_dense(const char* who, int32_t M, int32_t N, int32_t K, int32_t world, int32_t rank,
+                       int32_t R, int32_t bm, int32_t bn, int32_t b_layout, const tlc_tile* plan,
+                       int64_t n_tiles, const void* a, const void* b, const void* c,
+                       const tlc_signals* sig) {
+  if (world < 1 || world > TLC_MAX_WORLD) return fail(TLC_ERR_INVALID_ARG, "%s: world %d", who, world);
+  if (rank < 0 || rank >= world) return fail(TLC_ERR_INVALID_ARG, "%s: rank %d", who, rank);
+  if (M < 1 || N < 1 || K < 1 || R < 1) return fail(TLC_ERR_INVALID_ARG, "%s: sizes must be >= 1", who);
+  if (static_cast<int64_t>(world) * R != M)
+    return fail(TLC_ERR_INVALID_ARG, "%s: M %d != world %d * rows_per_chunk %d", who, M, world, R);
+  if (K % 64 != 0) return fail(TLC_ERR_UNSUPPORTED, "%s: K %d is not a multiple of 64", who, K);
+  if (N % 8 != 0) return fail(TLC_ERR_UNSUPPORTED, "%s: N %d is not a multiple of 8", who, N);
+  if (!((bm == 256 && bn == 256) || (bm == 128 && bn == 128)))
+    return fail(TLC_ERR_UNSUPPORTED, "%s: tile %dx%d not built (256x256, 128x128)", who, bm, bn);
+  if (b_layout != TLC_B_KN && b_layout != TLC_B_NK)
+    return fail(TLC_ERR_INVALID_ARG, "%s: b_layout %d", who, b_layout);
+  if (static_cast<int64_t>(M) * K >= (1LL << 31) || static_cast<int64_t>(K) * N >= (1LL << 31))
+    return fail(TLC_ERR_UNSUPPORTED, "%s: operand with >= 2^31 elements", who);
+  if (n_tiles < 0) return fail(TLC_ERR_INVALID_ARG, "%s: n_tiles < 0", who);
+  if ((n_tiles > 0 && !plan) || !a || !b || !c || !sig)
+    return fail(TLC_ERR_INVALID_ARG, "%s: NULL plan, operand, output or signals", who);
+  if (!aligned16(a) || !aligned16(b) || !aligned16(c))
+    return fail(TLC_ERR_MISALIGNED, "%s: operands must be 16-byte aligned", who);
+  return TLC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tlc_status tlc_signals_alloc(tlc_signals** out) {
+  if (!out) return fail(TLC_ERR_INVALID_ARG, "tlc_signals_alloc: NULL out");
+  void* p = nullptr;
+  tlc_status st = hip_check(hipExtMallocWithFlags(&p, sizeof(tlc_signals), hipDeviceMallocFinegrained),
+                            "hipExtMallocWithFlags(fine-grained)");
+  if (st) return st;
+  st = hip_check(hipMemset(p, 0, sizeof(tlc_signals)), "hipMemset(signals)");
+  if (st) {
+    (void)hipFree(p);
+    return st;
+  }
+  st = hip_check(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  if (st) return st;
+  *out = static_cast<tlc_signals*>(p);
+  return ok();
+}
+
+tlc_status tlc_signals_free(tlc_signals* sig) {
+  if (!sig) return ok();
+  tlc_status st = hip_check(hipFree(sig), "hipFree(signals)");
+  return st ? st : ok();
+}
+
+tlc_status tlc_signals_set(tlc_signals* sig, int32_t world, uint32_t value, void* stream) {
+  if (!sig || world < 1 || world > TLC_MAX_WORLD)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_signals_set: bad arguments");
+  tlc_status st = launch_signals_set(sig, world, value, stream);
+  return st ? st : ok();
+}
+
+tlc_status tlc_signals_clear_status(tlc_signals* sig, void* stream) {
+  if (!sig) return fail(TLC_ERR_INVALID_ARG, "tlc_signals_clear_status: NULL");
+  tlc_status st = launch_status_clear(sig, stream);
+  return st ? st : ok();
+}
+
+tlc_status tlc_read_status(const tlc_signals* sig, void* stream, int32_t* out) {
+  if (!sig || !out) return fail(TLC_ERR_INVALID_ARG, "tlc_read_status: NULL");
+  tlc_status st = hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
+  if (st) return st;
+  st = hip_check(hipMemcpy(out, sig->status, 4 * sizeof(int32_t), hipMemcpyDeviceToHost), "hipMemcpy(status)");
+  return st ? st : ok();
+}
+
+tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_chunk, int32_t world,
+                    int32_t rank, tlc_signals* sig, uint32_t epoch, int32_t land, void* copy_stream) {
+  if (world < 1 || world > TLC_MAX_WORLD || rank < 0 || rank >= world || !sig || bytes_per_chunk < 0)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_land: bad world/rank/signals/size");
+  if (land == TLC_LAND_NONE) return fail(TLC_ERR_INVALID_ARG, "tlc_land: land must be COPY_ENGINE or CU");
+  tlc_status st = check_land_args(land, src, dst, world, rank, bytes_per_chunk, "tlc_land");
+  if (st) return st;
+  DeviceInfo info;
+  st = device_info(&info);
+  if (st) return st;
+  st = enqueue_landing(land, dst, src, bytes_per_chunk, world, rank, sig, epoch, copy_stream, info);
+  return st ? st : ok();
+}
+
+tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* copy_stream) {
+  if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_ag_gemm: NULL args");
+  tlc_status st = check_dense("tlc_ag_gemm", a->M, a->N, a->K, a->world, a->rank, a->rows_per_chunk,
+                              a->bm, a->bn, a->b_layout, a->plan, a->n_tiles, a->a, a->b, a->c, a->sig);
+  if (st) return st;
+  const int64_t chunk_bytes = static_cast<int64_t>(a->rows_per_chunk) * a->K * 2;
+  void* dst[TLC_MAX_WORLD];
+  for (int c = 0; c < a->world; ++c) dst[c] = static_cast<char*>(a->a) + c * chunk_bytes;
+  st = check_land_args(a->land, a->a_src, dst, a->world, a->rank, chunk_bytes, "tlc_ag_gemm");
+  if (st) return st;
+  DeviceInfo info;
+  st = device_info(&info);
+  if (st) return st;
+
+  st = enqueue_landing(a->land, dst, a->a_src, chunk_bytes, a->world, a->rank, a->sig, a->epoch,
+                       copy_stream, info);
+  if (st) return st;
+  if (a->n_tiles == 0) return ok();
+
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.plan = a->plan;
+  p.n_tiles = a->n_tiles;
+  p.a = static_cast<const uint16_t*>(a->a);
+  p.b = static_cast<const uint16_t*>(a->b);
+  p.c = a->c;
+  p.M = a->M;
+  p.N = a->N;
+  p.K = a->K;
+  p.lda = a->K;
+  p.ldb = a->b_layout == TLC_B_NK ? a->K : a->N;
+  p.ldc = a->N;
+  p.no_wait_mask = 1u << a->rank;
+  p.do_wait = 1;
+  p.sig = a->sig;
+  p.epoch = a->epoch;
+  p.timeout_ticks = ticks_for(a->timeout_ns, info);
+  const int avail = a->land == TLC_LAND_NONE ? info.cus : info.cus - kReserveCUs;
+  int grid = a->grid > 0 ? a->grid : default_grid(a->n_tiles, avail);
+  p.xcd_remap = grid % 8 == 0;
+  st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
+  return st ? st : ok();
+}
+
+static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* copy_stream,
+                            bool run_gemm) {
+  if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: NULL args");
+  tlc_status st = check_dense("tlc_gemm_rs", a->M, a->N, a->K, a->world, a->rank, a->rows_per_chunk,
+                              a->bm, a->bn, a->b_layout, a->plan, a->n_tiles, a->a, a->b,
+                              a->partials, a->sig);
+  if (st) return st;
+  if (a->N % 4 != 0) return fail(TLC_ERR_UNSUPPORTED, "tlc_gemm_rs: N %% 4 != 0");
+  if (!a->out || !aligned16(a->out)) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: out NULL or misaligned");
+  if (a->world > 1 && !a->landing) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: NULL landing array");
+  for (int s = 0; s < a->world; ++s) {
+    if (s == a->rank) continue;
+    if (!a->landing[s] || !aligned16(a->landing[s]))
+      return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: landing[%d] NULL or misaligned", s);
+  }
+  const int64_t slice = static_cast<int64_t>(a->rows_per_chunk) * a->N;
+  const int64_t slice_bytes = slice * 4;
+  int land = run_gemm ? a->land : TLC_LAND_NONE;
+  st = check_land_args(land, reinterpret_cast<const void* const*>(a->remote_src),
+                       reinterpret_cast<const void* const*>(a->landing), a->world, a->rank, slice_bytes,
+                       "tlc_gemm_rs");
+  if (st) return st;
+  DeviceInfo info;
+  st = device_info(&info);
+  if (st) return st;
+
+  st = enqueue_landing(land, reinterpret_cast<void* const*>(a->landing),
+                       reinterpret_cast<const void* const*>(a->remote_src), slice_bytes, a->world,
+                       a->rank, a->sig, a->epoch, copy_stream, info);
+  if (st) return st;
+
+  if (run_gemm && a->n_tiles > 0) {
+    GemmParams p;
+    memset(&p, 0, sizeof(p));
+    p.plan = a->plan;
+    p.n_tiles = a->n_tiles;
+    p.a = static_cast<const uint16_t*>(a->a);
+    p.b = static_cast<const uint16_t*>(a->b);
+    p.c = a->partials;
+    p.M = a->M;
+    p.N = a->N;
+    p.K = a->K;
+    p.lda = a->K;
+    p.ldb = a->b_layout == TLC_B_NK ? a->K : a->N;
+    p.ldc = a->N;
+    p.do_wait = 0;
+    p.sig = a->sig;
+    p.epoch = a->epoch;
+    p.timeout_ticks = ticks_for(a->timeout_ns, info);
+    int grid = a->grid > 0 ? a->grid : default_grid(a->n_tiles, info.cus);
+    p.xcd_remap = grid % 8 == 0;
+    st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
+    if (st) return st;
+  }
+
+  ReduceParams r;
+  memset(&r, 0, sizeof(r));
+  for (int s = 0; s < a->world; ++s)
+    r.src[s] = s == a->rank ? a->partials + a->rank * slice : a->landing[s];
+  r.out = a->out;
+  r.n_vec4 = slice / 4;
+  r.world = a->world;
+  r.wait_mask = ((a->world == 32) ? 0xFFFFFFFFu : ((1u << a->world) - 1u)) & ~(1u << a->rank);
+  r.sig = a->sig;
+  r.epoch = a->epoch;
+  r.timeout_ticks = ticks_for(a->timeout_ns, info);
+  int rgrid = info.cus * 4;
+  const int64_t need = (r.n_vec4 + 255) / 256;
+  if (need < rgrid) rgrid = static_cast<int>(need > 0 ? need : 1);
+  st = launch_reduce(r, rgrid, compute_stream);
+  return st ? st : ok();
+}
+
+tlc_status tlc_gemm_rs(const tlc_rs_args* a, void* compute_stream, void* copy_stream) {
+  return rs_common(a, compute_stream, copy_stream, true);
+}
+
+tlc_status tlc_rs_reduce(const tlc_rs_args* a, void* compute_stream, void* copy_stream) {
+  return rs_common(a, compute_stream, copy_stream, false);
+}
+
+int64_t tlc_moe_plan_capacity(int32_t T, int32_t topk, int32_t experts, int32_t N, int32_t bm, int32_t bn) {
+  if (T < 1 || topk < 1 || experts < 1 || N < 1 || bm < 1 || bn < 1) return 0;
+  return moe_max_pairs(T, topk, experts, bm) * ((N + bn - 1) / bn);
+}
+
+int64_t tlc_moe_workspace_bytes(int32_t T, int32_t topk, int32_t experts, int32_t bm) {
+  if (T < 1 || topk < 1 || experts < 1 || bm < 1) return 0;
+  const int64_t pairs = moe_max_pairs(T, topk, experts, bm);
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  return up(static_cast<int64_t>(T) * 8) + up((experts + 1) * 4LL) + up(pairs * 4) + up(pairs * 4);
+}
+
+tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
+  if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: NULL args");
+  if (a->world < 1 || a->world > TLC_MAX_WORLD || a->rank < 0 || a->rank >= a->world)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: world/rank");
+  if (a->experts < 1 || a->experts > 64 || a->topk < 1 || a->topk > a->experts || a->topk > 16)
+    return fail(TLC_ERR_UNSUPPORTED, "tlc_moe_route: experts %d (<= 64), topk %d (<= min(E, 16))",
+                a->experts, a->topk);
+  if (a->tokens_per_chunk < 1) return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: tokens_per_chunk");
+  const int64_t T = static_cast<int64_t>(a->world) * a->tokens_per_chunk;
+  if (T > (1 << 20)) return fail(TLC_ERR_UNSUPPORTED, "tlc_moe_route: T > 2^20");
+  if (a->N < 1 || !(a->bm == 128 || a->bm == 256) || a->bn < 1)
+    return fail(TLC_ERR_UNSUPPORTED, "tlc_moe_route: N/bm/bn");
+  if (a->order != TLC_ORDER_NATURAL && a->order != TLC_ORDER_RANK_OFFSET)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: order");
+  if (!a->logits || !a->topk_idx || !a->gates || !a->counts || !a->offsets || !a->row_token ||
+      !a->slot || !a->plan || !a->n_tiles_dev || !a->workspace)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: NULL array");
+  const int64_t cap = tlc_moe_plan_capacity(static_cast<int32_t>(T), a->topk, a->experts, a->N, a->bm, a->bn);
+  if (a->plan_cap < cap)
+    return fail(TLC_ERR_CAPACITY, "tlc_moe_route: plan_cap %lld < %lld", static_cast<long long>(a->plan_cap),
+                static_cast<long long>(cap));
+  if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0)
+    return fail(TLC_ERR_MISALIGNED, "tlc_moe_route: workspace not 256-byte aligned");
+  MoeDev d;
+  memset(&d, 0, sizeof(d));
+  d.logits = a->logits;
+  d.T = static_cast<int32_t>(T);
+  d.E = a->experts;
+  d.k = a->topk;
+  d.Tc = a->tokens_per_chunk;
+  d.world = a->world;
+  d.rank = a->rank;
+  d.N = a->N;
+  d.bm = a->bm;
+  d.bn = a->bn;
+  d.order = a->order;
+  d.ntiles_n = (a->N + a->bn - 1) / a->bn;
+  d.max_pairs = static_cast<int32_t>(moe_max_pairs(d.T, d.k, d.E, d.bm));
+  d.topk = a->topk_idx;
+  d.gates = a->gates;
+  d.counts = a->counts;
+  d.offsets = a->offsets;
+  d.row_token = a->row_token;
+  d.slot = a->slot;
+  d.plan = a->plan;
+  d.n_tiles = a->n_tiles_dev;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  char* ws = static_cast<char*>(a->workspace);
+  d.member = reinterpret_cast<unsigned long long*>(ws);
+  ws += up(T * 8);
+  d.pstart = reinterpret_cast<int32_t*>(ws);
+  ws += up((d.E + 1) * 4LL);
+  d.pair_key = reinterpret_cast<int32_t*>(ws);
+  ws += up(d.max_pairs * 4LL);
+  d.pair_mask = reinterpret_cast<uint32_t*>(ws);
+  DeviceInfo info;
+  tlc_status st = device_info(&info);
+  if (st) return st;
+  st = launch_moe_route(d, stream);
+  return st ? st : ok();
+}
+
+tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* copy_stream) {
+  if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: NULL args");
+  if (a->world < 1 || a->world > TLC_MAX_WORLD || a->rank < 0 || a->rank >= a->world)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: world/rank");
+  if (a->experts < 1 || a->topk < 1 || a->tokens_per_chunk < 1 || a->H < 1 || a->N < 1)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: sizes must be >= 1");
+  if (a->H % 64 != 0 || a->N % 8 != 0)
+    return fail(TLC_ERR_UNSUPPORTED, "tlc_ag_moe: H %% 64 and N %% 8 must be 0");
+  if (!((a->bm == 256 && a->bn == 256) || (a->bm == 128 && a->bn == 128)))
+    return fail(TLC_ERR_UNSUPPORTED, "tlc_ag_moe: tile %dx%d not built", a->bm, a->bn);
+  if (a->w_layout != TLC_B_KN && a->w_layout != TLC_B_NK)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: w_layout");
+  const int64_t T = static_cast<int64_t>(a->world) * a->tokens_per_chunk;
+  if (T * a->H >= (1LL << 31)) return fail(TLC_ERR_UNSUPPORTED, "tlc_ag_moe: T*H >= 2^31");
+  if (!a->plan || !a->n_tiles_dev || !a->row_token || !a->x || !a->w || !a->y || !a->sig)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: NULL array");
+  if (!aligned16(a->x) || !aligned16(a->w) || !aligned16(a->y))
+    return fail(TLC_ERR_MISALIGNED, "tlc_ag_moe: operands must be 16-byte aligned");
+  const int64_t chunk_bytes = static_cast<int64_t>(a->tokens_per_chunk) * a->H * 2;
+  void* dst[TLC_MAX_WORLD];
+  for (int c = 0; c < a->world; ++c) dst[c] = static_cast<char*>(a->x) + c * chunk_bytes;
+  tlc_status st = check_land_args(a->land, a->x_src, dst, a->world, a->rank, chunk_bytes, "tlc_ag_moe");
+  if (st) return st;
+  DeviceInfo info;
+  st = device_info(&info);
+  if (st) return st;
+  st = enqueue_landing(a->land, dst, a->x_src, chunk_bytes, a->world, a->rank, a->sig, a->epoch,
+                       copy_stream, info);
+  if (st) return st;
+
+  GemmParams p;
+  memset(&p, 0, sizeof(p));
+  p.plan = a->plan;
+  p.n_tiles_dev = a->n_tiles_dev;
+  p.n_tiles = a->plan_cap;
+  p.a = static_cast<const uint16_t*>(a->x);
+  p.b = static_cast<const uint16_t*>(a->w);
+  p.c = a->y;
+  p.row_token = a->row_token;
+  p.M = static_cast<int32_t>(T * a->topk);
+  p.N = a->N;
+  p.K = a->H;
+  p.lda = a->H;
+  p.ldb = a->w_layout == TLC_B_NK ? a->H : a->N;
+  p.ldc = a->N;
+  p.b_expert_stride = static_cast<int64_t>(a->H) * a->N;
+  p.no_wait_mask = 1u << a->rank;
+  p.do_wait = 1;
+  p.sig = a->sig;
+  p.epoch = a->epoch;
+  p.timeout_ticks = ticks_for(a->timeout_ns, info);
+  const int avail = a->land == TLC_LAND_NONE ? info.cus : info.cus - kReserveCUs;
+  // The tile count is only known on the device: use every available CU.
+  int grid = a->grid > 0 ? a->grid : (avail >= 8 ? avail / 8 * 8 : avail);
+  p.xcd_remap = grid % 8 == 0;
+  st = launch_gemm(p, a->bm, a->bn, a->w_layout, KIND_MOE, grid, compute_stream);
+  return st ? st : ok();
+}
+
+const char* tlc_status_string(tlc_status s) {
+  switch (s) {
+    case TLC_OK: return "ok";
+    case TLC_ERR_INVALID_ARG: return "invalid argument";
+    case TLC_ERR_UNSUPPORTED: return "unsupported";
+    case TLC_ERR_MISALIGNED: return "misaligned";
+    case TLC_ERR_CAPACITY: return "capacity too small";
+    case TLC_ERR_HIP: return "HIP runtime error";
+    case TLC_ERR_TIMEOUT: return "timeout waiting for a chunk";
+    case TLC_ERR_BAD_PLAN: return "plan entry outside the output";
+    default: return "unknown status";
+  }
+}
+
+const char* tlc_last_error(void) { return g_err; }
+
+int32_t tlc_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Kernels around the GEMM: the scatter-mode reduce, the CU landing backend
+// and the signal helpers.
+//
+// Reduce (GEMM-ReduceScatter, second half): out = S_0 + S_1 + ... + S_{W-1}
+// element-wise in ascending rank order, where S_rank is this rank's own row
+// chunk of the partial product and S_s (s != rank) the partial that rank s
+// produced for these rows.  It starts once the remote partials' flags reach the
+// epoch (Triton-Distributed talk, GEMM-ReduceScatter example: the reduce
+// kernel waits on per-tile notifications; here the GEMM precedes the reduce in
+// stream order, so only the landed partials are waited for).  float4 loads and
+// stores, grid-stride; HBM-bound.
+//
+// CU landing (AutoOverlap §5.3, backends 4/5: transfers by load/store on SMs,
+// signalled through global memory): workgroups copy the chunks in landing
+// order; each workgroup publishes its part of a chunk with a release fence and
+// an arrival count, and the last arrival raises the chunk's flag.
+#include <hip/hip_runtime.h>
+
+#include "device_sync.h"
+#include "tlc_internal.h"
+
+namespace tlc {
+namespace {
+
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
+  __shared__ int s_abort;
+  if (p.wait_mask) {
+    if (threadIdx.x == 0) s_abort = wait_chunks(p.sig, p.wait_mask, p.epoch, p.timeout_ticks, -1);
+    __syncthreads();
+    if (s_abort) return;
+  }
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < p.n_vec4;
+       i += stride) {
+    float4 acc = reinterpret_cast<const float4*>(p.src[0])[i];
+    for (int s = 1; s < p.world; ++s) {
+      const float4 v = reinterpret_cast<const float4*>(p.src[s])[i];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    reinterpret_cast<float4*>(p.out)[i] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void land_kernel(LandParams p) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int i = 0; i < p.n_chunks; ++i) {
+    const int c = p.order[i];
+    const uint4* src = p.src[c];
+    uint4* dst = p.dst[c];
+    for (int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+         v < p.vec_per_chunk; v += stride)
+      dst[v] = src[v];
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->land_count[c], 1u, __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == gridDim.x - 1) {
+        __hip_atomic_store(&p.sig->land_count[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.sig->flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+  }
+}
+
+__global__ void signals_set_kernel(tlc_signals* sig, int world, uint32_t value) {
+  const int c = threadIdx.x;
+  if (c < world) __hip_atomic_store(&sig->flags[c], value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__global__ void status_clear_kernel(tlc_signals* sig) {
+  const int i = threadIdx.x;
+  if (i < 4) __hip_atomic_store(&sig->status[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+tlc_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TLC_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+tlc_status launch_reduce(const ReduceParams& p, int grid, void* stream) {
+  hipLaunchKernelGGL(reduce_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  return check_launch("reduce");
+}
+
+tlc_status launch_land_cu(const LandParams& p, int grid, void* stream) {
+  hipLaunchKernelGGL(land_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  return check_launch("land");
+}
+
+tlc_status launch_signals_set(tlc_signals* sig, int world, uint32_t value, void* stream) {
+  hipLaunchKernelGGL(signals_set_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), sig,
+                     world, value);
+  return check_launch("signals_set");
+}
+
+tlc_status launch_status_clear(tlc_signals* sig, void* stream) {
+  hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), sig);
+  return check_launch("status_clear");
+}
+
+}  // namespace tlc

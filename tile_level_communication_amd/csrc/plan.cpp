@@ -1,0 +1,105 @@
+// Host tile planner: the order in which the persistent GEMM visits its tiles.
+//
+// Gather mode follows the rank-offset start of DITRON's distributed swizzle
+// (paper notes, §3.2: execution starts at rank_id mod local_world_size, and the
+// compiler issues remote fetches early so local HBM acts as a cache of remote
+// memory).  Scatter mode produces remote-bound tiles first and the local slice
+// last (§3.2 scatter mode; Triton-Distributed talk, swizzling section).  Tiles
+// that straddle chunk boundaries are keyed by the last chunk they wait for
+// (gather) or the first destination they feed (scatter), per the talk's
+// section on non-perfect tile scheduling.  Inside one key the tiles go band by
+// band (group_m m-tiles wide), column by column, keeping operand reuse close in
+// time (AutoOverlap §5.4 / Fig. 6, intra-chunk swizzle for locality).
+#include <algorithm>
+#include <vector>
+
+#include "tlc_internal.h"
+
+namespace {
+
+struct Keyed {
+  int32_t key, band, nt, mt;
+  tlc_tile tile;
+};
+
+bool key_less(const Keyed& x, const Keyed& y) {
+  if (x.key != y.key) return x.key < y.key;
+  if (x.band != y.band) return x.band < y.band;
+  if (x.nt != y.nt) return x.nt < y.nt;
+  return x.mt < y.mt;
+}
+
+int32_t mod(int64_t a, int32_t w) {
+  int64_t r = a % w;
+  return static_cast<int32_t>(r < 0 ? r + w : r);
+}
+
+}  // namespace
+
+extern "C" tlc_status tlc_chunk_plan(const tlc_plan_desc* d, tlc_tile* tiles, int64_t cap,
+                                     int64_t* n_tiles, int32_t* landing_order) {
+  using tlc::fail;
+  if (!d || !n_tiles) return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: NULL desc or n_tiles");
+  if (d->mode != TLC_MODE_AG && d->mode != TLC_MODE_RS)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: mode %d is not AG or RS", d->mode);
+  if (d->world < 1 || d->world > TLC_MAX_WORLD)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: world %d outside 1..%d", d->world,
+                TLC_MAX_WORLD);
+  if (d->rank < 0 || d->rank >= d->world)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: rank %d outside 0..%d", d->rank,
+                d->world - 1);
+  if (d->M < 1 || d->N < 1 || d->rows_per_chunk < 1 || d->bm < 1 || d->bn < 1 || d->group_m < 1)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: sizes must be >= 1");
+  if (static_cast<int64_t>(d->world) * d->rows_per_chunk != d->M)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: M=%d != world %d * rows_per_chunk %d", d->M,
+                d->world, d->rows_per_chunk);
+  if (d->order != TLC_ORDER_NATURAL && d->order != TLC_ORDER_RANK_OFFSET)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: order %d unknown", d->order);
+
+  const int32_t W = d->world, r = d->rank, R = d->rows_per_chunk;
+  const int64_t mtiles = (d->M + d->bm - 1) / d->bm;
+  const int64_t ntiles = (d->N + d->bn - 1) / d->bn;
+  const int64_t count = mtiles * ntiles;
+  *n_tiles = count;
+  if (landing_order)
+    for (int32_t i = 1; i < W; ++i) landing_order[i - 1] = (r + i) % W;
+  if (!tiles) return tlc::ok();
+  if (cap < count)
+    return fail(TLC_ERR_CAPACITY, "tlc_chunk_plan: capacity %lld < %lld tiles",
+                static_cast<long long>(cap), static_cast<long long>(count));
+
+  std::vector<Keyed> v;
+  v.reserve(static_cast<size_t>(count));
+  for (int64_t mt = 0; mt < mtiles; ++mt) {
+    const int32_t m0 = static_cast<int32_t>(mt * d->bm);
+    const int32_t rows = std::min<int32_t>(d->bm, d->M - m0);
+    const int32_t c_first = m0 / R, c_last = (m0 + rows - 1) / R;
+    uint32_t mask = 0;
+    int32_t key_ag = 0, key_rs = W;
+    for (int32_t c = c_first; c <= c_last; ++c) {
+      mask |= 1u << c;
+      key_ag = std::max(key_ag, mod(c - r, W));       // consume position, latest
+      key_rs = std::min(key_rs, mod(c - r - 1, W));   // send position, earliest
+    }
+    int32_t key = d->order == TLC_ORDER_NATURAL ? 0 : (d->mode == TLC_MODE_AG ? key_ag : key_rs);
+    for (int64_t nt = 0; nt < ntiles; ++nt) {
+      Keyed k;
+      k.key = key;
+      k.band = static_cast<int32_t>(mt / d->group_m);
+      k.nt = static_cast<int32_t>(nt);
+      k.mt = static_cast<int32_t>(mt);
+      k.tile.m0 = m0;
+      k.tile.n0 = static_cast<int32_t>(nt * d->bn);
+      k.tile.m_rows = rows;
+      k.tile.n_cols = std::min<int32_t>(d->bn, d->N - k.tile.n0);
+      k.tile.expert = -1;
+      k.tile.chunk_mask = mask;
+      k.tile.key = key;
+      k.tile.reserved = 0;
+      v.push_back(k);
+    }
+  }
+  std::sort(v.begin(), v.end(), key_less);
+  for (size_t i = 0; i < v.size(); ++i) tiles[i] = v[i].tile;
+  return tlc::ok();
+}

@@ -1,0 +1,103 @@
+// Internal declarations shared by the library's translation units (not part of
+// the public ABI; see include/tlc.h for the entry points).
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+
+#include <hip/hip_runtime.h>
+
+#include "tlc.h"
+
+namespace tlc {
+
+// Sets the thread's last-error text and returns `s` (for `return fail(...)`).
+tlc_status fail(tlc_status s, const char* fmt, ...);
+tlc_status ok();
+
+// Device facts cached per device id (compute units, wall-clock rate).
+struct DeviceInfo {
+  int cus = 0;
+  int64_t wall_khz = 0;
+  int arch_ok = 0;  // gfx950
+};
+tlc_status device_info(DeviceInfo* out);
+
+// Parameters of the tiled GEMM kernels (one struct for all modes).
+struct GemmParams {
+  const tlc_tile* plan;
+  const int32_t* n_tiles_dev;  // MoE: tile count written by the routing kernels
+  int64_t n_tiles;             // dense: tile count; MoE: plan capacity
+  const uint16_t* a;           // gathered A (AG), local A (RS), tokens X (MoE)
+  const uint16_t* b;           // weight, or stacked expert weights (MoE)
+  float* c;                    // output
+  const int32_t* row_token;    // MoE only
+  int32_t M, N, K;
+  int64_t lda, ldb, ldc;
+  int64_t b_expert_stride;     // MoE: elements between experts' weights
+  uint32_t no_wait_mask;       // chunks that are never waited for (the local one)
+  int32_t do_wait;
+  tlc_signals* sig;
+  uint32_t epoch;
+  int64_t timeout_ticks;
+  int32_t xcd_remap;
+};
+
+enum GemmKind { KIND_DENSE = 0, KIND_MOE = 1 };
+
+// Launch the persistent tiled GEMM: bm x bn in {256x256, 128x128}.
+tlc_status launch_gemm(const GemmParams& p, int bm, int bn, int b_layout, int kind, int grid,
+                       void* stream);
+
+struct ReduceParams {
+  const float* src[TLC_MAX_WORLD];  // S_0 .. S_{W-1}
+  float* out;
+  int64_t n_vec4;                   // elements / 4
+  int32_t world;
+  uint32_t wait_mask;               // chunks whose flags must reach epoch first
+  tlc_signals* sig;
+  uint32_t epoch;
+  int64_t timeout_ticks;
+};
+tlc_status launch_reduce(const ReduceParams& p, int grid, void* stream);
+
+struct LandParams {
+  const uint4* src[TLC_MAX_WORLD];
+  uint4* dst[TLC_MAX_WORLD];
+  int32_t order[TLC_MAX_WORLD];
+  int32_t n_chunks;
+  int64_t vec_per_chunk;  // 16-byte units per chunk
+  tlc_signals* sig;
+  uint32_t epoch;
+};
+tlc_status launch_land_cu(const LandParams& p, int grid, void* stream);
+
+tlc_status launch_signals_set(tlc_signals* sig, int world, uint32_t value, void* stream);
+tlc_status launch_status_clear(tlc_signals* sig, void* stream);
+
+struct MoeDev {
+  const float* logits;
+  int32_t T, E, k, Tc, world, rank, N, bm, bn, order, ntiles_n, max_pairs;
+  int32_t* topk;
+  float* gates;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* slot;
+  tlc_tile* plan;
+  int32_t* n_tiles;
+  unsigned long long* member;  // workspace: T masks
+  int32_t* pstart;             // workspace: E + 1
+  int32_t* pair_key;           // workspace: max_pairs
+  uint32_t* pair_mask;         // workspace: max_pairs
+};
+
+int64_t moe_max_pairs(int32_t T, int32_t topk, int32_t experts, int32_t bm);
+tlc_status launch_moe_route(const MoeDev& d, void* stream);
+
+// Default persistent grid: the fewest rounds of tiles over the CUs, with the
+// tiles spread evenly over that many rounds (rounded up to a multiple of 8).
+int default_grid(int64_t n_tiles, int cus);
+
+}  // namespace tlc

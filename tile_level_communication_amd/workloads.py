@@ -1,0 +1,257 @@
+"""Device-side set-up of the three operations around the libtlc calls.
+
+Each problem object owns its device buffers (torch tensors on the ROCm device),
+its tile plan (built by ``tlc_chunk_plan`` or, for MoE, by ``tlc_moe_route`` on
+the device) and a ``tlc_signals`` block, and exposes ``run()`` which enqueues
+one call of the operation.  The emulated peers' data lives in separate source
+buffers; every ``run()`` with landing enabled copies it in again and raises the
+epoch, so each call waits for fresh arrivals.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import tlc
+
+
+def to_bf16(bits: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> a bf16 tensor on `device`."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def to_f32(x: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def weight_layout(b_kn: torch.Tensor, b_layout: int) -> torch.Tensor:
+    """A K x N weight stored as K x N (KN) or as its N x K transpose (NK)."""
+    return b_kn.contiguous() if b_layout == tlc.B_KN else b_kn.t().contiguous()
+
+
+class Streams:
+    """A compute stream (torch's current one) and a side copy stream, both at
+    the default priority."""
+
+    def __init__(self, device):
+        self.compute = torch.cuda.current_stream(device)
+        self.copy = torch.cuda.Stream(device=device)
+
+    def begin(self):
+        # the landing may only overwrite buffers once earlier work is done
+        self.copy.wait_stream(self.compute)
+
+    def end(self):
+        self.compute.wait_stream(self.copy)
+
+
+class AGProblem:
+    def __init__(self, a_chunks, b_kn, rank, bm=256, bn=256, b_layout=tlc.B_KN,
+                 order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda"):
+        self.device = torch.device(device)
+        self.world = len(a_chunks)
+        self.rank = rank
+        self.R, self.K = a_chunks[0].shape
+        self.N = b_kn.shape[1]
+        self.M = self.world * self.R
+        self.bm, self.bn, self.b_layout = bm, bn, b_layout
+        self.a_src = [to_bf16(a, self.device) for a in a_chunks]
+        self.a = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=self.device)
+        self.a[rank * self.R:(rank + 1) * self.R].copy_(self.a_src[rank])
+        self.b = weight_layout(to_bf16(b_kn, self.device), b_layout)
+        self.c = torch.empty((self.M, self.N), dtype=torch.float32, device=self.device)
+        tiles, self.landing_order = tlc.chunk_plan(tlc.MODE_AG, self.world, rank, self.M, self.N,
+                                                   self.R, bm, bn, order, group_m)
+        self.tiles = tiles
+        self.plan = torch.from_numpy(tiles).to(self.device)
+        self.n_tiles = int(tiles.shape[0])
+        self.sig = tlc.Signals()
+        self.epoch = 0
+        self.streams = Streams(self.device)
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+    def place_all(self):
+        """Copy every chunk into the gathered buffer (for compute-only runs)."""
+        for c in range(self.world):
+            self.a[c * self.R:(c + 1) * self.R].copy_(self.a_src[c])
+
+    def poison_remote(self):
+        """Fill the rows the landing will write with NaN (stale-read detector)."""
+        for c in range(self.world):
+            if c != self.rank:
+                self.a[c * self.R:(c + 1) * self.R].fill_(float("nan"))
+
+    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, preset_flags=None):
+        """Enqueue one AG-GEMM.  With land == LAND_NONE the flags are raised to the
+        new epoch first (chunks must already be in place) unless preset_flags is
+        False."""
+        self.epoch += 1
+        s = self.streams
+        if land == tlc.LAND_NONE and preset_flags is not False:
+            self.sig.set(self.world, self.epoch, s.compute)
+        s.begin()
+        tlc.ag_gemm(self.plan, self.n_tiles, self.M, self.N, self.K, self.world, self.rank, self.R,
+                    self.bm, self.bn, self.a, self.a_src if land != tlc.LAND_NONE else None,
+                    self.b, self.b_layout, self.c, self.sig, self.epoch, land, s.compute, s.copy,
+                    grid, timeout_ns)
+        s.end()
+
+    def land_only(self, land=tlc.LAND_COPY_ENGINE):
+        self.epoch += 1
+        s = self.streams
+        s.begin()
+        dst = [self.a[c * self.R:(c + 1) * self.R] for c in range(self.world)]
+        tlc.land(dst, self.a_src, self.R * self.K * 2, self.world, self.rank, self.sig, self.epoch,
+                 land, s.copy)
+        s.end()
+
+
+class RSProblem:
+    def __init__(self, a, b_kn, remote: dict, world, rank, bm=256, bn=256, b_layout=tlc.B_KN,
+                 order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda"):
+        self.device = torch.device(device)
+        self.world, self.rank = world, rank
+        self.M, self.K = a.shape
+        self.N = b_kn.shape[1]
+        self.R = self.M // world
+        self.bm, self.bn, self.b_layout = bm, bn, b_layout
+        self.a = to_bf16(a, self.device)
+        self.b = weight_layout(to_bf16(b_kn, self.device), b_layout)
+        self.partials = torch.empty((self.M, self.N), dtype=torch.float32, device=self.device)
+        self.out = torch.empty((self.R, self.N), dtype=torch.float32, device=self.device)
+        self.remote_src = [None] * world
+        self.landing = [None] * world
+        for s in range(world):
+            if s != rank:
+                self.remote_src[s] = to_f32(remote[s], self.device)
+                self.landing[s] = torch.empty((self.R, self.N), dtype=torch.float32, device=self.device)
+        tiles, self.landing_order = tlc.chunk_plan(tlc.MODE_RS, world, rank, self.M, self.N, self.R,
+                                                   bm, bn, order, group_m)
+        self.tiles = tiles
+        self.plan = torch.from_numpy(tiles).to(self.device)
+        self.n_tiles = int(tiles.shape[0])
+        self.sig = tlc.Signals()
+        self.epoch = 0
+        self.streams = Streams(self.device)
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.M * self.N * self.K
+
+    @property
+    def reduce_bytes(self) -> int:
+        return (self.world + 1) * self.R * self.N * 4
+
+    def place_all(self):
+        for s in range(self.world):
+            if s != self.rank:
+                self.landing[s].copy_(self.remote_src[s])
+
+    def poison_remote(self):
+        for s in range(self.world):
+            if s != self.rank:
+                self.landing[s].fill_(float("nan"))
+
+    def _args(self):
+        return (self.plan, self.n_tiles, self.M, self.N, self.K, self.world, self.rank, self.R,
+                self.bm, self.bn, self.a, self.b, self.b_layout, self.partials)
+
+    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0):
+        self.epoch += 1
+        s = self.streams
+        if land == tlc.LAND_NONE:
+            self.sig.set(self.world, self.epoch, s.compute)
+        s.begin()
+        tlc.gemm_rs(*self._args(), self.remote_src if land != tlc.LAND_NONE else None, self.landing,
+                    self.out, self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns)
+        s.end()
+
+    def reduce_only(self, timeout_ns=0):
+        self.epoch += 1
+        s = self.streams
+        self.sig.set(self.world, self.epoch, s.compute)
+        tlc.rs_reduce(*self._args(), None, self.landing, self.out, self.sig, self.epoch,
+                      tlc.LAND_NONE, s.compute, s.copy, 0, timeout_ns)
+
+    def land_only(self, land=tlc.LAND_COPY_ENGINE):
+        self.epoch += 1
+        s = self.streams
+        s.begin()
+        tlc.land(self.landing, self.remote_src, self.R * self.N * 4, self.world, self.rank, self.sig,
+                 self.epoch, land, s.copy)
+        s.end()
+
+
+class MoEProblem:
+    def __init__(self, x_chunks, logits, w_ekn, rank, topk, bm=256, bn=256, b_layout=tlc.B_KN,
+                 order=tlc.ORDER_RANK_OFFSET, device="cuda"):
+        self.device = torch.device(device)
+        dev = self.device
+        self.world = len(x_chunks)
+        self.rank = rank
+        self.Tc, self.H = x_chunks[0].shape
+        self.T = self.world * self.Tc
+        self.E, _, self.N = w_ekn.shape
+        self.k = topk
+        self.bm, self.bn, self.b_layout, self.order = bm, bn, b_layout, order
+        self.x_src = [to_bf16(x, dev) for x in x_chunks]
+        self.x = torch.empty((self.T, self.H), dtype=torch.bfloat16, device=dev)
+        self.x[rank * self.Tc:(rank + 1) * self.Tc].copy_(self.x_src[rank])
+        w = to_bf16(w_ekn, dev)
+        self.w = w.contiguous() if b_layout == tlc.B_KN else w.transpose(1, 2).contiguous()
+        self.logits = to_f32(logits, dev)
+        T, k, E = self.T, self.k, self.E
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.topk_idx = torch.empty((T, k), **i32)
+        self.gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty((E,), **i32)
+        self.offsets = torch.empty((E + 1,), **i32)
+        self.row_token = torch.empty((T * k,), **i32)
+        self.slot = torch.empty((T, k), **i32)
+        self.plan_cap = tlc.moe_plan_capacity(T, k, E, self.N, bm, bn)
+        self.plan = torch.empty((self.plan_cap, 8), **i32)
+        self.n_tiles_dev = torch.zeros((1,), **i32)
+        ws = tlc.moe_workspace_bytes(T, k, E, bm)
+        self.workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        self.y = torch.empty((T * k, self.N), dtype=torch.float32, device=dev)
+        self.sig = tlc.Signals()
+        self.epoch = 0
+        self.streams = Streams(dev)
+
+    @property
+    def flops(self) -> float:
+        return 2.0 * self.T * self.k * self.N * self.H
+
+    def place_all(self):
+        for c in range(self.world):
+            self.x[c * self.Tc:(c + 1) * self.Tc].copy_(self.x_src[c])
+
+    def poison_remote(self):
+        for c in range(self.world):
+            if c != self.rank:
+                self.x[c * self.Tc:(c + 1) * self.Tc].fill_(float("nan"))
+
+    def route(self):
+        s = self.streams
+        tlc.moe_route(self.logits, self.Tc, self.world, self.rank, self.E, self.k, self.N, self.bm,
+                      self.bn, self.order, self.topk_idx, self.gates, self.counts, self.offsets,
+                      self.row_token, self.slot, self.plan, self.plan_cap, self.n_tiles_dev,
+                      self.workspace, s.compute)
+
+    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, do_route=True):
+        self.epoch += 1
+        s = self.streams
+        if land == tlc.LAND_NONE:
+            self.sig.set(self.world, self.epoch, s.compute)
+        s.begin()
+        if do_route:
+            self.route()
+        tlc.ag_moe(self.plan, self.n_tiles_dev, self.plan_cap, self.row_token, self.Tc, self.world,
+                   self.rank, self.E, self.k, self.H, self.N, self.bm, self.bn, self.x,
+                   self.x_src if land != tlc.LAND_NONE else None, self.w, self.b_layout, self.y,
+                   self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns)
+        s.end()
