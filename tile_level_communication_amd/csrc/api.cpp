@@ -16,7 +16,12 @@ thread_local char g_err[512] = "";
 std::mutex g_info_mu;
 DeviceInfo g_info[64];
 bool g_info_ok[64] = {};
-constexpr int kReserveCUs = 8;  // one CU per XCD left for copy/signal kernels
+// CUs the persistent GEMM leaves free while it may wait for landings: the CU
+// landing kernel needs a few; the copy-engine path raises each flag with
+// hipStreamWriteValue32, which the runtime executes as a small kernel, and that
+// kernel must find a free CU while the GEMM's workgroups spin.
+constexpr int kReserveCUsLandCU = 8;
+constexpr int kReserveCUsCopyEngine = 48;
 constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
 }  // namespace
 
@@ -55,6 +60,11 @@ tlc_status device_info(DeviceInfo* out) {
   *out = g_info[dev];
   if (!out->arch_ok) return fail(TLC_ERR_UNSUPPORTED, "libtlc kernels are built for gfx950 only");
   return TLC_OK;
+}
+
+int reserve_for(int land) {
+  return land == TLC_LAND_COPY_ENGINE ? kReserveCUsCopyEngine
+                                      : (land == TLC_LAND_CU ? kReserveCUsLandCU : 0);
 }
 
 int default_grid(int64_t n_tiles, int avail) {
@@ -262,7 +272,7 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* copy_st
   p.sig = a->sig;
   p.epoch = a->epoch;
   p.timeout_ticks = ticks_for(a->timeout_ns, info);
-  const int avail = a->land == TLC_LAND_NONE ? info.cus : info.cus - kReserveCUs;
+  const int avail = info.cus - reserve_for(a->land);
   int grid = a->grid > 0 ? a->grid : default_grid(a->n_tiles, avail);
   p.xcd_remap = grid % 8 == 0;
   st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
@@ -475,7 +485,7 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* copy_st
   p.sig = a->sig;
   p.epoch = a->epoch;
   p.timeout_ticks = ticks_for(a->timeout_ns, info);
-  const int avail = a->land == TLC_LAND_NONE ? info.cus : info.cus - kReserveCUs;
+  const int avail = info.cus - reserve_for(a->land);
   // The tile count is only known on the device: use every available CU.
   int grid = a->grid > 0 ? a->grid : (avail >= 8 ? avail / 8 * 8 : avail);
   p.xcd_remap = grid % 8 == 0;

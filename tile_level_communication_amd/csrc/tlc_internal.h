@@ -99,5 +99,7 @@ tlc_status launch_moe_route(const MoeDev& d, void* stream);
 // Default persistent grid: the fewest rounds of tiles over the CUs, with the
 // tiles spread evenly over that many rounds (rounded up to a multiple of 8).
 int default_grid(int64_t n_tiles, int cus);
+// CUs left free by the persistent GEMM for the given landing mode.
+int reserve_for(int land);
 
 }  // namespace tlc
