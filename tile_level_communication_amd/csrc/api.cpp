@@ -473,6 +473,7 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* copy_st
   p.b = static_cast<const uint16_t*>(a->w);
   p.c = a->y;
   p.row_token = a->row_token;
+  p.a_rows = T;
   p.M = static_cast<int32_t>(T * a->topk);
   p.N = a->N;
   p.K = a->H;

@@ -1,10 +1,10 @@
 // Persistent, plan-driven bf16 GEMM for gfx950 (MFMA 32x32x16 bf16 -> fp32).
 //
-// One workgroup (4 wavefronts, 2 x 2) owns one BM x BN output tile at a time
-// and walks the tile list in plan order: slot s takes tiles s, s + G, s + 2G,
-// ... where G is the grid size.  Slots are spread so that each XCD (8 per
-// MI355X; workgroups are dealt to XCDs round-robin) gets a contiguous run of
-// the plan, keeping the operands that neighbouring tiles share in the same L2.
+// A workgroup owns one output tile at a time and walks the tile list in plan
+// order: slot s takes tiles s, s + G, s + 2G, ... where G is the grid size.
+// Slots are spread so that each XCD (8 per MI355X; workgroups are dealt to
+// XCDs round-robin) gets a contiguous run of the plan, keeping the operands
+// that neighbouring tiles share in the same L2.
 //
 // Before touching a tile's A rows, the workgroup waits until every chunk the
 // tile reads has landed (flag >= epoch), with a bounded spin that reports a
@@ -13,12 +13,17 @@
 // low-level signal wait with scope, memory semantics and expected value;
 // AutoOverlap §5.2: only the tiles that consume a chunk wait for it).
 //
-// K loop: BK = 64, two LDS stages.  Each stage is filled with 128-bit global
-// loads (A rows and, for an N x K weight, B rows are K-contiguous; a K x N
-// weight is transposed 8 x 8 in registers on its way to LDS) and read back as
-// 128-bit MFMA fragments.  LDS rows are 64 bf16 = eight 16-byte chunks stored
-// at chunk ^ (row & 7), so the eight lanes of a fragment read or a row write
-// always hit eight different 16-byte bank groups.
+// Two tile cores:
+//  * 256 x 256 (the default): 8 wavefronts (2 x 4), 128 x 64 per wavefront,
+//    two per SIMD so that one wave's MFMAs cover the other's LDS reads.
+//    Operands go global -> LDS with buffer loads that write LDS directly (no
+//    register staging), BK = 64, two stages of 64 KB.  A rows (and N x K
+//    weight rows) are 64 bf16 = eight 16-byte chunks per LDS row, chunk c of
+//    row r stored at c ^ ((r >> 1) & 7): the 16 lanes that one LDS cycle
+//    serves read 16 different bank groups.  A K x N weight is kept K-major in
+//    LDS (512-byte rows, chunk c of row k at c ^ 2(k & 15)) and transposed on
+//    the way to the registers with ds_read_b64_tr_b16.
+//  * 128 x 128 (small problems): 4 wavefronts, register-staged loads.
 #include <hip/hip_runtime.h>
 
 #include "device_sync.h"
@@ -204,10 +209,195 @@ struct Tile {
   }
 };
 
-template <int BM, int BN, int B_NK, int KIND>
-__global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
-  __shared__ u32x4 lds[2 * (BM + BN) * 8];
-  __shared__ int s_abort;
+// ---------------------------------------------------------------------------
+// 256 x 256 core, 8 wavefronts, direct-to-LDS operand loads.
+// ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+#define TLC_LDS __attribute__((address_space(3)))
+
+// Buffer resource with wave-uniform fields (readfirstlane), so that the
+// compiler keeps it in scalar registers.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0),
+                                           static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           0x00020000);
+}
+
+// 16 bytes per lane from global memory straight into LDS at base + 16 * lane.
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, TLC_LDS void* lds, uint32_t voff,
+                                  uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+}
+
+template <int B_NK, int KIND>
+struct Tile8w {
+  static constexpr int BM = 256, BN = 256, WM = 128, WN = 64, FM = 4, FN = 2, NT = 512;
+  __device__ static int swz(int row) { return (row >> 1) & 7; }
+
+  __device__ static void run(const GemmParams& p, const tlc_tile& tl, TLC_LDS u32x4* A0,
+                             TLC_LDS u32x4* A1, TLC_LDS u32x4* B0, TLC_LDS u32x4* B1) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const uint32_t lda2 = static_cast<uint32_t>(p.lda) * 2, ldb2 = static_cast<uint32_t>(p.ldb) * 2;
+
+    // ---- global sources of the 4 A blocks and 4 B blocks (1 KB each) this
+    // wave fills per stage; rows outside the tile are clamped into it ----
+    __amdgpu_buffer_rsrc_t ra;
+    uint32_t a_off[4];
+    if (KIND == KIND_MOE) {
+      ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * lda2);
+    } else {
+      ra = make_rsrc(p.a + static_cast<int64_t>(tl.m0) * p.lda, static_cast<uint32_t>(tl.m_rows) * lda2);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int row = (wave * 4 + q) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(row);
+      row = row < tl.m_rows ? row : tl.m_rows - 1;
+      const uint32_t src_row = KIND == KIND_MOE ? static_cast<uint32_t>(p.row_token[tl.m0 + row])
+                                                 : static_cast<uint32_t>(row);
+      a_off[q] = src_row * lda2 + kc * 16;
+    }
+    const uint16_t* bexp = p.b + (KIND == KIND_MOE ? tl.expert * p.b_expert_stride : 0);
+    __amdgpu_buffer_rsrc_t rb;
+    uint32_t b_off[4];
+    if constexpr (B_NK) {
+      rb = make_rsrc(bexp + static_cast<int64_t>(tl.n0) * p.ldb, static_cast<uint32_t>(tl.n_cols) * ldb2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int row = (wave * 4 + q) * 8 + (lane >> 3);
+        const int kc = (lane & 7) ^ swz(row);
+        row = row < tl.n_cols ? row : tl.n_cols - 1;
+        b_off[q] = row * ldb2 + kc * 16;
+      }
+    } else {
+      rb = make_rsrc(bexp + tl.n0, static_cast<uint32_t>(p.K) * ldb2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = (wave * 4 + q) * 2 + (lane >> 5);
+        int n = ((lane & 31) ^ (2 * (k & 15))) * 8;
+        n = n < tl.n_cols ? n : tl.n_cols - 8;
+        b_off[q] = k * ldb2 + n * 2;
+      }
+    }
+    const uint32_t b_step = B_NK ? 128u : 64u * ldb2;
+    auto issue = [&](int kt, TLC_LDS u32x4* As, TLC_LDS u32x4* Bs) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        load_lds16(ra, (TLC_LDS void*)(As + (wave * 4 + q) * 64), a_off[q], kt * 128u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        load_lds16(rb, (TLC_LDS void*)(Bs + (wave * 4 + q) * 64), b_off[q], kt * b_step);
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    const int h = lane >> 5;
+    const int s_lane = swz(lane & 31);
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto fread = [&](const TLC_LDS u32x4* As, const TLC_LDS u32x4* Bs, int ks, int slot) {
+      const int phys = (ks * 2 + h) ^ s_lane;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[slot][i] = __builtin_bit_cast(
+            bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)As +
+                                            (wm * WM + i * 32 + (lane & 31)) * 128 + phys * 16));
+      if constexpr (B_NK) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          fb[slot][j] = __builtin_bit_cast(
+              bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)Bs +
+                                              (wn * WN + j * 32 + (lane & 31)) * 128 + phys * 16));
+      } else {
+        // Lane l needs B[k = 16 ks + 8 (l / 32) + t][n] for t = 0..7 (n = l % 32 of the block):
+        // two transposing reads, each giving 4 consecutive k of one column.
+        const int g = lane >> 4, i16 = lane & 15;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          v4i16 hv[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int k = ks * 16 + 8 * (g >> 1) + 4 * hh + (i16 >> 2);
+            const int n = wn * WN + j * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+            const int pc = (n >> 3) ^ (2 * (k & 15));
+            hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (TLC_LDS v4i16*)((const TLC_LDS char*)Bs + k * 512 + pc * 16 + (n & 7) * 2));
+          }
+          const v8i16 v = {hv[0][0], hv[0][1], hv[0][2], hv[0][3], hv[1][0], hv[1][1], hv[1][2], hv[1][3]};
+          fb[slot][j] = __builtin_bit_cast(bf16x8, v);
+        }
+      }
+    };
+    // One BK = 64 stage: fragments for step ks+1 are requested before the
+    // MFMAs of step ks are issued (the scheduling barriers keep that order).
+    auto compute = [&](const TLC_LDS u32x4* As, const TLC_LDS u32x4* Bs) {
+      fread(As, Bs, 0, 0);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int sl = ks & 1;
+        if (ks < 3) fread(As, Bs, ks + 1, sl ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // LDS-writing buffer loads are tracked by vmcnt: wait for this wave's, then
+    // the barrier covers the other waves'.
+    auto stage_done = [&]() {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    };
+
+    const int KT = p.K / 64;
+    issue(0, A0, B0);
+    stage_done();
+    for (int kt = 0; kt < KT; kt += 2) {
+      if (kt + 1 < KT) issue(kt + 1, A1, B1);
+      compute(A0, B0);
+      stage_done();
+      if (kt + 1 < KT) {
+        if (kt + 2 < KT) issue(kt + 2, A0, B0);
+        compute(A1, B1);
+        stage_done();
+      }
+    }
+
+    // ---- epilogue: fp32 to C, one 32-bit lane offset plus per-element
+    // constants; edge tiles masked ----
+    int lane_off = (wm * WM + 4 * (lane >> 5)) * static_cast<int>(p.ldc) + wn * WN + (lane & 31);
+    asm volatile("" : "+v"(lane_off));
+    float* cbase = p.c + static_cast<int64_t>(tl.m0) * p.ldc + tl.n0;
+    const bool full = tl.m_rows == BM && tl.n_cols == BN;
+    const int lrow = wm * WM + 4 * (lane >> 5), lcol = wn * WN + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int rr = i * 32 + 8 * (e >> 2) + (e & 3);
+          const int cc = j * 32;
+          if (full || (lrow + rr < tl.m_rows && lcol + cc < tl.n_cols))
+            cbase[lane_off + rr * static_cast<int>(p.ldc) + cc] = acc[i][j][e];
+        }
+  }
+};
+
+// Walks the plan: validation, chunk waits, then `run_tile(tile)`.
+template <int BM, int BN, int KIND, typename RunTile>
+__device__ inline void tile_loop(const GemmParams& p, int* s_abort, RunTile run_tile) {
   const int G = gridDim.x;
   int slot = blockIdx.x;
   if (p.xcd_remap) slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
@@ -217,8 +407,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
     const tlc_tile tl = p.plan[t];
     const bool bad = tl.m_rows < 1 || tl.n_cols < 1 || tl.m0 < 0 || tl.n0 < 0 ||
                      tl.m0 + tl.m_rows > p.M || tl.n0 + tl.n_cols > p.N || tl.m_rows > BM ||
-                     tl.n_cols > BN || (tl.n_cols & 7) != 0 ||
-                     (KIND == KIND_MOE && tl.expert < 0);
+                     tl.n_cols > BN || (tl.n_cols & 7) != 0 || (KIND == KIND_MOE && tl.expert < 0);
     if (bad) {
       if (threadIdx.x == 0) report(p.sig, TLC_ERR_BAD_PLAN, t);
       break;
@@ -226,21 +415,42 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
     if (p.do_wait) {
       const uint32_t need = tl.chunk_mask & ~seen;
       if (need) {
-        if (threadIdx.x == 0) s_abort = wait_chunks(p.sig, need, p.epoch, p.timeout_ticks, t);
+        if (threadIdx.x == 0) *s_abort = wait_chunks(p.sig, need, p.epoch, p.timeout_ticks, t);
         __syncthreads();
-        const int abort = s_abort;
+        const int abort = *s_abort;
         if (abort) break;
         seen |= need;
       }
     }
-    Tile<BM, BN, B_NK, KIND>::run(p, tl, lds);
+    run_tile(tl);
   }
+}
+
+template <int B_NK, int KIND>
+__global__ __launch_bounds__(512) void gemm_kernel_8w(GemmParams p) {
+  __shared__ u32x4 A0[2048], A1[2048], B0[2048], B1[2048];
+  __shared__ int s_abort;
+  tile_loop<256, 256, KIND>(p, &s_abort, [&](const tlc_tile& tl) {
+    Tile8w<B_NK, KIND>::run(p, tl, (TLC_LDS u32x4*)A0, (TLC_LDS u32x4*)A1, (TLC_LDS u32x4*)B0,
+                            (TLC_LDS u32x4*)B1);
+  });
+}
+
+template <int BM, int BN, int B_NK, int KIND>
+__global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
+  __shared__ u32x4 lds[2 * (BM + BN) * 8];
+  __shared__ int s_abort;
+  tile_loop<BM, BN, KIND>(p, &s_abort, [&](const tlc_tile& tl) { Tile<BM, BN, B_NK, KIND>::run(p, tl, lds); });
 }
 
 template <int BM, int BN, int B_NK, int KIND>
 tlc_status launch_one(const GemmParams& p, int grid, void* stream) {
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, B_NK, KIND>), dim3(grid), dim3(THREADS), 0,
-                     static_cast<hipStream_t>(stream), p);
+  if constexpr (BM == 256 && BN == 256)
+    hipLaunchKernelGGL((gemm_kernel_8w<B_NK, KIND>), dim3(grid), dim3(512), 0,
+                       static_cast<hipStream_t>(stream), p);
+  else
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, B_NK, KIND>), dim3(grid), dim3(THREADS), 0,
+                       static_cast<hipStream_t>(stream), p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TLC_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return ok();

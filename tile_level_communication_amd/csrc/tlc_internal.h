@@ -33,6 +33,7 @@ struct GemmParams {
   const uint16_t* b;           // weight, or stacked expert weights (MoE)
   float* c;                    // output
   const int32_t* row_token;    // MoE only
+  int64_t a_rows;              // MoE: rows of the token matrix (bounds of the gathered loads)
   int32_t M, N, K;
   int64_t lda, ldb, ldc;
   int64_t b_expert_stride;     // MoE: elements between experts' weights
