@@ -1,18 +1,23 @@
 #!/usr/bin/env python3
-"""Benchmark: chunk-swizzled AllGather-GEMM on one MI355X.
+"""Benchmark of the chunk-swizzled overlap path on one MI355X.
 
-Workload (default): the Qwen3-32B-like FFN-up AllGather-GEMM -- 8 chunks of
-1024 x 5120 bf16 activations gathered into A (8192 x 5120), weight shard
-B 5120 x 3200 bf16, C = A @ B in fp32.  One step = one pass of the whole path:
-the 7 peer chunks land on a side stream (copy engine, one transfer per chunk,
-then the chunk's flag), while the persistent tile-swizzled GEMM on the compute
-stream starts with the local chunk and consumes the others as their flags
-flip.  Inputs are seeded synthetic data already resident in HBM.
+Default workload (--workload ag): the Qwen3-32B-like FFN-up AllGather-GEMM --
+8 chunks of 1024 x 5120 bf16 activations gathered into A (8192 x 5120), weight
+shard B 5120 x 3200 bf16 (K x N), C = A @ B in fp32.  One step = one pass of the
+whole path: the 7 peer chunks land on a side stream through the copy engine (one
+transfer per chunk, then the chunk's flag), while the persistent tile-swizzled
+GEMM on the compute stream starts with the local chunk and consumes the others
+as their flags flip.  Inputs are seeded synthetic data resident in HBM.
 
-Reported (one JSON line): fused TFLOP/s (value), the GEMM kernel's roofline
-(MFMA bf16 peak 2.5 PFLOP/s), compute-only and copy-only times and the overlap
-efficiency eta = max(compute-only, copy-only) / fused, and the CPU oracle
-timed on a bounded sample (cpu_baseline).
+Other workloads (--workload rs | rs_long | moe) time GEMM-ReduceScatter (4096 x
+4096 x 2048, 4 chunks; 131072 x 5120 x 3200, 8 chunks) and AG-MoE (4096 tokens,
+64 experts, top-8) the same way; the default line is the AG-GEMM one.
+
+The JSON line carries: fused TFLOP/s (value), compute-only and copy-only times,
+overlap efficiency eta = max(compute-only, copy-only) / fused, the roofline of
+the dominant kernel (the persistent GEMM with every chunk resident, timed with
+HIP events on its stream; bf16 MFMA peak 2.5 PFLOP/s), and the CPU oracle timed
+on a bounded sample (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -28,6 +33,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4}
 
 
 def parse():
@@ -35,20 +41,20 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ag", choices=list(WORKLOAD_ID))
     ap.add_argument("--land", default="copy_engine", choices=["copy_engine", "cu"])
     ap.add_argument("--layout", default="KN", choices=["KN", "NK"])
     ap.add_argument("--tile", type=int, default=256)
     ap.add_argument("--group-m", type=int, default=4)
     ap.add_argument("--grid", type=int, default=0)
+    ap.add_argument("--copy-streams", type=int, default=1)
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--profile-only", action="store_true",
-                    help="run the fused loop only (for rocprofv3), print nothing else")
     return ap.parse_args()
 
 
-def timed(fn, steps, warmup, torch, streams):
+def timed(fn, steps, warmup, torch):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -59,9 +65,28 @@ def timed(fn, steps, warmup, torch, streams):
     return (time.perf_counter() - t0) / steps
 
 
-def cpu_baseline(inp, budget_s):
-    """The float64 oracle on a bounded sample of the workload: whole 1024-row
-    chunks of C, as many as fit in about `budget_s` seconds."""
+class KernelTimer:
+    """HIP events around one launch on the stream the kernel runs on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream, self.pairs = torch, stream, []
+
+    def __call__(self, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        fn()
+        e1.record(self.stream)
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self, skip):
+        import numpy as np
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs[skip:]]))
+
+
+def cpu_baseline(kind, inp, budget_s, rank=0):
+    """The float64 oracle on a bounded sample of the workload (whole row blocks
+    of the output, as many as fit in about `budget_s` seconds)."""
     import numpy as np
     from oracle import gemm as og
     try:
@@ -69,118 +94,42 @@ def cpu_baseline(inp, budget_s):
         threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:
         threads = os.cpu_count() or 1
-    K, N = inp.b.shape
-    R = inp.a_chunks[0].shape[0]
     flops = 0.0
-    chunks = 0
+    blocks = 0
     t0 = time.perf_counter()
-    while True:
-        c = chunks % len(inp.a_chunks)
-        og.ag_gemm_rows(inp.a_chunks, inp.b, np.arange(c * R, (c + 1) * R))
-        flops += 2.0 * R * N * K
-        chunks += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    if kind == "ag":
+        K, N = inp.b.shape
+        R = inp.a_chunks[0].shape[0]
+        while True:
+            c = blocks % len(inp.a_chunks)
+            og.ag_gemm_rows(inp.a_chunks, inp.b, np.arange(c * R, (c + 1) * R))
+            flops += 2.0 * R * N * K
+            blocks += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        what = f"{blocks} row chunks of {R}x{N} (K={K}) of C"
+    else:  # rs: rows of the local slice (partial GEMM + reduce)
+        K, N = inp.b.shape
+        W = len(inp.remote) + 1
+        R = inp.a.shape[0] // W
+        rows = 256
+        while True:
+            start = (blocks * rows) % R
+            og.gemm_rs_rows(inp.a, inp.b, inp.remote, W, rank, np.arange(start, start + rows))
+            flops += 2.0 * rows * N * K
+            blocks += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        what = f"{blocks} blocks of {rows} rows of the reduced slice (K={K}, N={N})"
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{chunks} row chunks of {R}x{N} (K={K}) of C, float64, {dt:.1f} s"}
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "sample": f"{what}, float64, {dt:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU's share of the method (the other ranks are emulated on "
-              "the same GPU); runs on more than one GPU are not supported.", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
-    import torch
-
-    import seeded_inputs as si
-    from tile_level_communication_amd import tlc
-    from tile_level_communication_amd.workloads import AGProblem
-
-    wl = si.WORKLOADS[2]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    inp = si.workload_inputs(2)
-    layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
-    land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
-    prob = AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
-                     group_m=args.group_m, device=dev)
-    compute = torch.cuda.Stream(device=dev)
-    copy = torch.cuda.Stream(device=dev)
-    prob.streams.compute = compute
-    prob.streams.copy = copy
-    flops = prob.flops
-    call = dict(plan=prob.plan, n_tiles=prob.n_tiles, M=prob.M, N=prob.N, K=prob.K, world=prob.world,
-                rank=prob.rank, rows_per_chunk=prob.R, bm=args.tile, bn=args.tile, a=prob.a,
-                b=prob.b, b_layout=layout, c=prob.c, sig=prob.sig)
-    ev_pairs = []
-    torch.cuda.synchronize()
-
-    def fused():
-        prob.epoch += 1
-        copy.wait_stream(compute)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(compute)
-        tlc.ag_gemm(**call, a_src=prob.a_src, epoch=prob.epoch, land=land, compute_stream=compute,
-                    copy_stream=copy, grid=args.grid)
-        e1.record(compute)
-        compute.wait_stream(copy)
-        ev_pairs.append((e0, e1))
-
-    if args.profile_only:
-        timed(fused, args.steps, args.warmup, torch, None)
-        return
-
-    # fused: landing + GEMM
-    t_fused = timed(fused, args.steps, args.warmup, torch, None)
-    durs = [a.elapsed_time(b) for a, b in ev_pairs[args.warmup:]]
-    gemm_fused_ms = float(np.mean(durs))
-
-    # compute-only: all chunks in place, flags preset once
-    prob.place_all()
-    prob.epoch += 1
-    fixed_epoch = prob.epoch
-    prob.sig.set(prob.world, fixed_epoch, compute)
-    torch.cuda.synchronize()
-    ev_pairs.clear()
-
-    def compute_only():
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(compute)
-        tlc.ag_gemm(**call, a_src=None, epoch=fixed_epoch, land=tlc.LAND_NONE,
-                    compute_stream=compute, copy_stream=copy, grid=args.grid)
-        e1.record(compute)
-        ev_pairs.append((e0, e1))
-
-    t_comp = timed(compute_only, args.steps, args.warmup, torch, None)
-    gemm_comp_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_pairs[args.warmup:]]))
-
-    # copy-only: the same landing sequence, no GEMM
-    dst = [prob.a[c * prob.R:(c + 1) * prob.R] for c in range(prob.world)]
-
-    def copy_only():
-        prob.epoch += 1
-        copy.wait_stream(compute)
-        tlc.land(dst, prob.a_src, prob.R * prob.K * 2, prob.world, prob.rank, prob.sig, prob.epoch,
-                 land, copy)
-        compute.wait_stream(copy)
-
-    t_copy = timed(copy_only, args.steps, args.warmup, torch, None)
-
-    # device status of a final fused call (timeouts or plan errors would show here)
-    torch.cuda.synchronize()
-    fused()
-    status = prob.sig.read_status(compute)
-
-    value = flops / t_fused / 1e12
-    achieved = flops / (gemm_fused_ms * 1e-3) / 1e12
-    eta = max(t_comp, t_copy) / t_fused
+def base_line(args, value, t_fused, extra):
     line = {
-        "metric": "AG-GEMM TFLOP/s @1 GPU (fused landing + chunk-swizzled GEMM), % bf16 MFMA peak, overlap efficiency",
+        "metric": "AG-GEMM / GEMM-RS TFLOP/s @1 GPU (fused landing + chunk-swizzled GEMM), "
+                  "% bf16 MFMA peak, overlap efficiency",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -192,24 +141,240 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, bf16)",
+    }
+    line.update(extra)
+    return line
+
+
+def run_ag(args, torch, tlc, si, workloads):
+    wl = si.WORKLOADS[2]
+    dev = torch.device("cuda:0")
+    inp = si.workload_inputs(2)
+    layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
+    land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
+    prob = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
+                               group_m=args.group_m, device=dev)
+    compute = torch.cuda.Stream(device=dev)
+    copies = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.copy_streams))]
+    prob.streams.compute = compute
+    prob.streams.copies = copies
+    flops = prob.flops
+    call = dict(plan=prob.plan, n_tiles=prob.n_tiles, M=prob.M, N=prob.N, K=prob.K, world=prob.world,
+                rank=prob.rank, rows_per_chunk=prob.R, bm=args.tile, bn=args.tile, a=prob.a,
+                b=prob.b, b_layout=layout, c=prob.c, sig=prob.sig)
+    torch.cuda.synchronize()
+    fused_t = KernelTimer(torch, compute)
+
+    def fused():
+        workloads.next_epoch(prob)
+        for c in copies:
+            c.wait_stream(compute)
+        fused_t(lambda: tlc.ag_gemm(**call, a_src=prob.a_src, epoch=prob.epoch, land=land,
+                                    compute_stream=compute, copy_stream=copies, grid=args.grid))
+        for c in copies:
+            compute.wait_stream(c)
+
+    t_fused = timed(fused, args.steps, args.warmup, torch)
+    gemm_fused_ms = fused_t.mean_ms(args.warmup)
+
+    # compute-only: every chunk in place, no flag checks (land NONE, epoch 0)
+    prob.place_all()
+    torch.cuda.synchronize()
+    comp_t = KernelTimer(torch, compute)
+
+    def compute_only():
+        comp_t(lambda: tlc.ag_gemm(**call, a_src=None, epoch=0, land=tlc.LAND_NONE,
+                                   compute_stream=compute, copy_stream=None, grid=args.grid))
+
+    t_comp = timed(compute_only, args.steps, args.warmup, torch)
+    gemm_comp_ms = comp_t.mean_ms(args.warmup)
+
+    # copy-only: the same landing sequence, no GEMM
+    dst = [prob.a[c * prob.R:(c + 1) * prob.R] for c in range(prob.world)]
+
+    def copy_only():
+        workloads.next_epoch(prob)
+        for c in copies:
+            c.wait_stream(compute)
+        tlc.land(dst, prob.a_src, prob.R * prob.K * 2, prob.world, prob.rank, prob.sig, prob.epoch,
+                 land, copies)
+        for c in copies:
+            compute.wait_stream(c)
+
+    t_copy = timed(copy_only, args.steps, args.warmup, torch)
+    torch.cuda.synchronize()
+    fused()
+    status = prob.sig.read_status(compute)
+    achieved = flops / (gemm_comp_ms * 1e-3) / 1e12
+    extra = {
         "config": {"workload": wl.name, "M": prob.M, "N": prob.N, "K": prob.K, "world": prob.world,
                    "rank": prob.rank, "tile": [args.tile, args.tile, 64], "b_layout": args.layout,
-                   "landing": args.land, "group_m": args.group_m, "n_tiles": prob.n_tiles,
+                   "landing": args.land, "copy_streams": len(copies), "group_m": args.group_m,
+                   "n_tiles": prob.n_tiles,
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "gemm_kernel<256,256,KN,dense> (fused mode)"},
-        "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                     "traffic": None,
+                     "kernel": "gemm_kernel_8w<KN,dense,no-wait> (every chunk resident)"},
+        "pct_peak": round(100 * flops / t_fused / 1e12 / PEAK_BF16_TFLOPS, 2),
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
         "gemm_kernel_ms": {"fused": round(gemm_fused_ms, 4), "compute_only": round(gemm_comp_ms, 4)},
         "copy_only_ms": round(t_copy * 1e3, 4),
-        "copy_gbs": round(7 * prob.R * prob.K * 2 / t_copy / 1e9, 1),
-        "overlap_efficiency": round(eta, 4),
+        "copy_gbs": round((prob.world - 1) * prob.R * prob.K * 2 / t_copy / 1e9, 1),
+        "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,
     }
+    line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline("ag", inp, args.cpu_seconds)
+    return line
+
+
+def run_rs(args, torch, tlc, si, workloads, wid):
+    wl = si.WORKLOADS[wid]
+    dev = torch.device("cuda:0")
+    inp = si.workload_inputs(wid, rank=args.rank)
+    layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
+    land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
+    prob = workloads.RSProblem(inp.a, inp.b, inp.remote, wl.world, args.rank, args.tile, args.tile,
+                               layout, group_m=args.group_m, device=dev)
+    compute = torch.cuda.Stream(device=dev)
+    copies = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.copy_streams))]
+    prob.streams.compute = compute
+    prob.streams.copies = copies
+    flops = prob.flops
+    torch.cuda.synchronize()
+    steps, warm = args.steps, args.warmup
+
+    def fused():
+        workloads.next_epoch(prob)
+        for c in copies:
+            c.wait_stream(compute)
+        tlc.gemm_rs(*prob._args(), prob.remote_src, prob.landing, prob.out, prob.sig, prob.epoch,
+                    land, compute, copies, args.grid)
+        for c in copies:
+            compute.wait_stream(c)
+
+    t_fused = timed(fused, steps, warm, torch)
+    prob.place_all()
+    prob.sig.set(prob.world, tlc.EPOCH_MAX, compute)
+    torch.cuda.synchronize()
+    comp_t = KernelTimer(torch, compute)
+
+    def compute_only():
+        comp_t(lambda: tlc.gemm_rs(*prob._args(), None, prob.landing, prob.out, prob.sig,
+                                   tlc.EPOCH_MAX, tlc.LAND_NONE, compute, None, args.grid))
+
+    t_comp = timed(compute_only, steps, warm, torch)
+    red_t = KernelTimer(torch, compute)
+
+    def reduce_only():
+        red_t(lambda: tlc.rs_reduce(*prob._args(), None, prob.landing, prob.out, prob.sig,
+                                    tlc.EPOCH_MAX, tlc.LAND_NONE, compute))
+
+    timed(reduce_only, steps, warm, torch)
+    red_ms = red_t.mean_ms(warm)
+
+    def copy_only():
+        workloads.next_epoch(prob)
+        for c in copies:
+            c.wait_stream(compute)
+        tlc.land(prob.landing, prob.remote_src, prob.R * prob.N * 4, prob.world, prob.rank, prob.sig,
+                 prob.epoch, land, copies)
+        for c in copies:
+            compute.wait_stream(c)
+
+    t_copy = timed(copy_only, steps, warm, torch)
+    torch.cuda.synchronize()
+    status = prob.sig.read_status(compute)
+    gemm_ms = comp_t.mean_ms(warm) - red_ms
+    gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
+    red_gbs = prob.reduce_bytes / (red_ms * 1e-3) / 1e9
+    extra = {
+        "config": {"workload": wl.name, "M": prob.M, "N": prob.N, "K": prob.K, "world": prob.world,
+                   "rank": prob.rank, "tile": [args.tile, args.tile, 64], "b_layout": args.layout,
+                   "landing": args.land, "copy_streams": len(copies), "n_tiles": prob.n_tiles,
+                   "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "gemm_kernel_8w (scatter order, no waits)"},
+        "reduce_roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(red_gbs / PEAK_HBM_GBS, 4),
+                            "kernel": "reduce_kernel", "ms": round(red_ms, 4)},
+        "compute_only_ms": round(t_comp * 1e3, 4),
+        "compute_only_tflops": round(flops / t_comp / 1e12, 2),
+        "copy_only_ms": round(t_copy * 1e3, 4),
+        "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
+        "device_status": status,
+    }
+    line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline("rs", inp, args.cpu_seconds, args.rank)
+    return line
+
+
+def run_moe(args, torch, tlc, si, workloads):
+    wl = si.WORKLOADS[4]
+    dev = torch.device("cuda:0")
+    inp = si.workload_inputs(4)
+    layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
+    land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
+    prob = workloads.MoEProblem(inp.x_chunks, inp.logits, inp.w, args.rank, wl.topk, args.tile,
+                                args.tile, layout, device=dev)
+    compute = torch.cuda.Stream(device=dev)
+    copies = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.copy_streams))]
+    prob.streams.compute = compute
+    prob.streams.copies = copies
+    flops = prob.flops
+    torch.cuda.synchronize()
+
+    def fused():
+        prob.run(land, grid=args.grid)
+
+    t_fused = timed(fused, args.steps, args.warmup, torch)
+    prob.place_all()
+    torch.cuda.synchronize()
+
+    def compute_only():
+        prob.route()
+        tlc.ag_moe(prob.plan, prob.n_tiles_dev, prob.plan_cap, prob.row_token, prob.Tc, prob.world,
+                   prob.rank, prob.E, prob.k, prob.H, prob.N, prob.bm, prob.bn, prob.x, None, prob.w,
+                   prob.b_layout, prob.y, prob.sig, 0, tlc.LAND_NONE, compute, None, args.grid)
+
+    t_comp = timed(compute_only, args.steps, args.warmup, torch)
+    torch.cuda.synchronize()
+    status = prob.sig.read_status(compute)
+    extra = {
+        "config": {"workload": wl.name, "tokens": prob.T, "experts": prob.E, "topk": prob.k,
+                   "H": prob.H, "N": prob.N, "world": prob.world, "rank": prob.rank,
+                   "landing": args.land, "n_tiles": int(prob.n_tiles_dev.item()),
+                   "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
+        "compute_only_ms": round(t_comp * 1e3, 4),
+        "compute_only_tflops": round(flops / t_comp / 1e12, 2),
+        "device_status": status,
+    }
+    return base_line(args, flops / t_fused / 1e12, t_fused, extra)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the method (the other ranks are emulated on "
+              "the same GPU); runs on more than one GPU are not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import seeded_inputs as si
+    from tile_level_communication_amd import tlc, workloads
+
+    torch.cuda.set_device(0)
+    if args.workload == "ag":
+        line = run_ag(args, torch, tlc, si, workloads)
+    elif args.workload == "moe":
+        line = run_moe(args, torch, tlc, si, workloads)
+    else:
+        line = run_rs(args, torch, tlc, si, workloads, WORKLOAD_ID[args.workload])
     print(json.dumps(line), flush=True)
 
 

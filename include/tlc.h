@@ -31,6 +31,12 @@
  *   - Pointers named "device" must point to device-accessible memory of the
  *     current HIP device; "host" pointers are read during the call only.
  *   - Streams are hipStream_t values passed as void* (NULL = default stream).
+ *     The landing side takes a host array of n_copy_streams >= 1 streams:
+ *     with the copy engine, the i-th chunk in landing order is copied on
+ *     copy_streams[i % n] (several streams let several copy engines work at
+ *     once, as several links would); the CU landing kernel runs on
+ *     copy_streams[0].  The caller orders the copy streams after earlier
+ *     readers of the landing buffers, and later readers after them.
  *   - Device-side failures (a wait that exceeded its time limit, a plan entry
  *     outside the output) are written to tlc_signals.status and read after the
  *     stream is synchronized (tlc_read_status).  The kernels then stop early;
@@ -70,8 +76,9 @@ enum { TLC_ORDER_NATURAL = 0, TLC_ORDER_RANK_OFFSET = 1 };
 enum { TLC_B_KN = 0, TLC_B_NK = 1 };
 /* How the emulated peers' chunks arrive:
  *   NONE        -- already in place; the caller has set the flags (compute-only)
- *   COPY_ENGINE -- one hipMemcpyAsync(DeviceToDeviceNoCU) per chunk on the copy
- *                  stream, then hipStreamWriteValue32 of the chunk's flag
+ *   COPY_ENGINE -- one hipMemcpyAsync(DeviceToDeviceNoCU) per chunk on a copy
+ *                  stream, then a 4-byte copy-engine transfer of the epoch into
+ *                  the chunk's flag (epoch in 1..TLC_EPOCH_MAX)
  *   CU          -- one copy kernel on the copy stream; its workgroups copy the
  *                  chunks in landing order and the last one to finish a chunk
  *                  publishes its flag with a release store                     */
@@ -92,17 +99,25 @@ typedef struct {
   int32_t reserved; /* 0 */
 } tlc_tile;
 
+/* Copy-engine landings raise a chunk's flag with a second copy-engine transfer
+ * of 4 bytes from a table of epoch values held in the signals block, so no
+ * compute unit is involved; epochs are therefore limited to 1..TLC_EPOCH_MAX
+ * in that mode (rewind the flags to 0 with tlc_signals_set, then restart at 1). */
+#define TLC_EPOCH_MAX 4096
+
 /* Signals shared by the copy side and the kernels (device memory; allocate
  * with tlc_signals_alloc so that it is fine-grained and coherent with the copy
  * engines).  flags[c] >= epoch  <=>  chunk c has landed for this call.
  * status[0] = 0 or a negative tlc_status, status[1] = plan index of the tile
  * that failed, status[2] = chunk it waited for.  land_count is internal to the
- * CU landing backend (zero between calls). */
+ * CU landing backend (zero between calls).  epoch_table[i] = i + 1, written
+ * once by tlc_signals_alloc. */
 typedef struct {
   uint32_t flags[TLC_MAX_WORLD];
   uint32_t land_count[TLC_MAX_WORLD];
   int32_t status[4];
-  uint32_t reserved[12];
+  uint32_t reserved[60];
+  uint32_t epoch_table[TLC_EPOCH_MAX];
 } tlc_signals;
 
 /* ---------------------------------------------------------------- plan ---- */
@@ -172,8 +187,10 @@ tlc_status tlc_read_status(const tlc_signals* sig, void* stream, int32_t* out);
  *   b      device bf16, layout b_layout (KN: ldb = N; NK: ldb = K).
  *   c      device f32 M x N, ldc = N.
  *   sig    device tlc_signals; status must be 0 on entry; flags < epoch for the
- *          chunks that still have to land.
- * Streams: the GEMM runs on `compute`, the landing on `copy`.
+ *          chunks that still have to land.  With land == TLC_LAND_NONE and
+ *          epoch == 0 the kernel does not look at the flags at all (every
+ *          chunk must already be in place): the plain compute-only GEMM.
+ * Streams: the GEMM runs on `compute_stream`, the landing on the copy streams.
  * grid: persistent workgroups (0 = default: fewest rounds of tiles over the
  * compute units, spread evenly).  timeout_ns: per-wait limit (0 = 2 s). */
 typedef struct {
@@ -194,7 +211,8 @@ typedef struct {
   int64_t timeout_ns;
 } tlc_ag_args;
 
-tlc_status tlc_ag_gemm(const tlc_ag_args* args, void* compute_stream, void* copy_stream);
+tlc_status tlc_ag_gemm(const tlc_ag_args* args, void* compute_stream, void* const* copy_streams,
+                       int32_t n_copy_streams);
 
 /* ---------------------------------------------------------- GEMM-RS ------- */
 
@@ -229,10 +247,12 @@ typedef struct {
   int64_t timeout_ns;
 } tlc_rs_args;
 
-tlc_status tlc_gemm_rs(const tlc_rs_args* args, void* compute_stream, void* copy_stream);
+tlc_status tlc_gemm_rs(const tlc_rs_args* args, void* compute_stream, void* const* copy_streams,
+                       int32_t n_copy_streams);
 
-/* The reduce step alone (same arguments; the GEMM is not run). */
-tlc_status tlc_rs_reduce(const tlc_rs_args* args, void* compute_stream, void* copy_stream);
+/* The reduce step alone, on `compute_stream` (same arguments; neither the GEMM
+ * nor the landing is run: landing[s] must hold the data, flags >= epoch). */
+tlc_status tlc_rs_reduce(const tlc_rs_args* args, void* compute_stream);
 
 /* ------------------------------------------------------------ AG-MoE ------ */
 
@@ -302,7 +322,8 @@ typedef struct {
   int64_t timeout_ns;
 } tlc_moe_args;
 
-tlc_status tlc_ag_moe(const tlc_moe_args* args, void* compute_stream, void* copy_stream);
+tlc_status tlc_ag_moe(const tlc_moe_args* args, void* compute_stream, void* const* copy_streams,
+                      int32_t n_copy_streams);
 
 /* ------------------------------------------------------------ misc -------- */
 
@@ -314,7 +335,7 @@ tlc_status tlc_ag_moe(const tlc_moe_args* args, void* compute_stream, void* copy
  * land: TLC_LAND_COPY_ENGINE or TLC_LAND_CU.  Used for copy-only timings. */
 tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_chunk,
                     int32_t world, int32_t rank, tlc_signals* sig, uint32_t epoch, int32_t land,
-                    void* copy_stream);
+                    void* const* copy_streams, int32_t n_copy_streams);
 
 const char* tlc_status_string(tlc_status s);
 const char* tlc_last_error(void);

@@ -65,7 +65,7 @@ def _ag_args(**over):
 ])
 def test_ag_gemm_argument_errors(over, want):
     args = _ag_args(**over)
-    s = tlc.lib().tlc_ag_gemm(C.byref(args), None, None)
+    s = tlc.lib().tlc_ag_gemm(C.byref(args), None, None, 0)
     assert s == want, tlc.last_error()
     assert tlc.last_error()
 

@@ -152,3 +152,22 @@ def test_ag_qwen3_ffn_up_full_size(rank):
     torch.cuda.synchronize()
     assert prob.sig.read_status()[0] == 0
     check_exact(prob.c.cpu().numpy(), og.ag_gemm(ii.a_chunks, ii.b), "cfg full integer")
+
+
+def test_ag_epoch_rewind_copy_engine():
+    """Copy-engine flags come from a table of TLC_EPOCH_MAX epochs: calls across
+    the end of the table rewind the flags and stay correct."""
+    W, R, K, N = 3, 128, 128, 256
+    inp = si.ag_inputs(150, W, R, N, K)
+    prob = AGProblem(inp.a_chunks, inp.b, 2, 128, 128)
+    prob.epoch = tlc.EPOCH_MAX - 2
+    prob.sig.set(W, prob.epoch, prob.streams.compute)
+    ref = og.ag_gemm(inp.a_chunks, inp.b)
+    for it in range(4):
+        log(f"[ag epoch rewind] call {it}, epoch before {prob.epoch}")
+        prob.poison_remote()
+        prob.run(tlc.LAND_COPY_ENGINE)
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        check_close(prob.c.cpu().numpy(), ref, K, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), f"call{it}")
+    assert prob.epoch == 2

@@ -17,9 +17,9 @@ std::mutex g_info_mu;
 DeviceInfo g_info[64];
 bool g_info_ok[64] = {};
 // CUs the persistent GEMM leaves free while it may wait for landings: the CU
-// landing kernel needs a few; the copy-engine path raises each flag with
-// hipStreamWriteValue32, which the runtime executes as a small kernel, and that
-// kernel must find a free CU while the GEMM's workgroups spin.
+// landing kernel needs a few; on the copy-engine path the runtime may still
+// run the 4-byte flag transfers as small kernels, which must find a free CU
+// while the GEMM's workgroups spin.
 constexpr int kReserveCUsLandCU = 8;
 constexpr int kReserveCUsCopyEngine = 48;
 constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
@@ -98,18 +98,21 @@ tlc_status hip_check(hipError_t e, const char* what) {
 // (rank+1, rank+2, ... mod W) and raise each chunk's flag to `epoch` after
 // its bytes.
 tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, int64_t bytes,
-                           int world, int rank, tlc_signals* sig, uint32_t epoch, void* copy,
-                           const DeviceInfo& info) {
+                           int world, int rank, tlc_signals* sig, uint32_t epoch,
+                           void* const* copy_streams, int n_copy_streams, const DeviceInfo& info) {
   if (land == TLC_LAND_NONE || world == 1) return TLC_OK;
-  hipStream_t s = static_cast<hipStream_t>(copy);
   if (land == TLC_LAND_COPY_ENGINE) {
     for (int i = 1; i < world; ++i) {
       const int c = (rank + i) % world;
+      hipStream_t s = static_cast<hipStream_t>(copy_streams[(i - 1) % n_copy_streams]);
       tlc_status st = hip_check(hipMemcpyAsync(dst[c], src[c], static_cast<size_t>(bytes),
                                                hipMemcpyDeviceToDeviceNoCU, s),
                                 "hipMemcpyAsync(landing)");
       if (st) return st;
-      st = hip_check(hipStreamWriteValue32(s, &sig->flags[c], epoch, 0), "hipStreamWriteValue32");
+      // the flag follows the data on the same copy engine queue
+      st = hip_check(hipMemcpyAsync(&sig->flags[c], &sig->epoch_table[epoch - 1], sizeof(uint32_t),
+                                    hipMemcpyDeviceToDeviceNoCU, s),
+                     "hipMemcpyAsync(flag)");
       if (st) return st;
     }
     return TLC_OK;
@@ -128,14 +131,20 @@ tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, i
   p.epoch = epoch;
   int grid = info.cus / 4;
   if (grid < 8) grid = 8;
-  return launch_land_cu(p, grid, copy);
+  return launch_land_cu(p, grid, copy_streams[0]);
 }
 
 tlc_status check_land_args(int land, const void* const* src, const void* const* dst, int world,
-                           int rank, int64_t bytes, const char* who) {
+                           int rank, int64_t bytes, const char* who, void* const* copy_streams,
+                           int n_copy_streams, uint32_t epoch) {
   if (land != TLC_LAND_NONE && land != TLC_LAND_COPY_ENGINE && land != TLC_LAND_CU)
     return fail(TLC_ERR_INVALID_ARG, "%s: land %d unknown", who, land);
   if (land == TLC_LAND_NONE) return TLC_OK;
+  if (!copy_streams || n_copy_streams < 1)
+    return fail(TLC_ERR_INVALID_ARG, "%s: landing needs n_copy_streams >= 1 streams", who);
+  if (land == TLC_LAND_COPY_ENGINE && (epoch < 1 || epoch > TLC_EPOCH_MAX))
+    return fail(TLC_ERR_INVALID_ARG, "%s: copy-engine landing needs 1 <= epoch <= %d (got %u)", who,
+                TLC_EPOCH_MAX, epoch);
   if (!src || !dst) return fail(TLC_ERR_INVALID_ARG, "%s: landing needs source and destination arrays", who);
   if (bytes % 16 != 0) return fail(TLC_ERR_MISALIGNED, "%s: chunk bytes %lld not a multiple of 16", who,
                                    static_cast<long long>(bytes));
@@ -184,6 +193,13 @@ tlc_status tlc_signals_alloc(tlc_signals** out) {
                             "hipExtMallocWithFlags(fine-grained)");
   if (st) return st;
   st = hip_check(hipMemset(p, 0, sizeof(tlc_signals)), "hipMemset(signals)");
+  if (!st) {
+    static uint32_t table[TLC_EPOCH_MAX];
+    for (uint32_t i = 0; i < TLC_EPOCH_MAX; ++i) table[i] = i + 1;
+    st = hip_check(hipMemcpy(static_cast<tlc_signals*>(p)->epoch_table, table, sizeof(table),
+                             hipMemcpyHostToDevice),
+                   "hipMemcpy(epoch table)");
+  }
   if (st) {
     (void)hipFree(p);
     return st;
@@ -222,20 +238,24 @@ tlc_status tlc_read_status(const tlc_signals* sig, void* stream, int32_t* out) {
 }
 
 tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_chunk, int32_t world,
-                    int32_t rank, tlc_signals* sig, uint32_t epoch, int32_t land, void* copy_stream) {
+                    int32_t rank, tlc_signals* sig, uint32_t epoch, int32_t land,
+                    void* const* copy_streams, int32_t n_copy_streams) {
   if (world < 1 || world > TLC_MAX_WORLD || rank < 0 || rank >= world || !sig || bytes_per_chunk < 0)
     return fail(TLC_ERR_INVALID_ARG, "tlc_land: bad world/rank/signals/size");
   if (land == TLC_LAND_NONE) return fail(TLC_ERR_INVALID_ARG, "tlc_land: land must be COPY_ENGINE or CU");
-  tlc_status st = check_land_args(land, src, dst, world, rank, bytes_per_chunk, "tlc_land");
+  tlc_status st = check_land_args(land, src, dst, world, rank, bytes_per_chunk, "tlc_land",
+                                  copy_streams, n_copy_streams, epoch);
   if (st) return st;
   DeviceInfo info;
   st = device_info(&info);
   if (st) return st;
-  st = enqueue_landing(land, dst, src, bytes_per_chunk, world, rank, sig, epoch, copy_stream, info);
+  st = enqueue_landing(land, dst, src, bytes_per_chunk, world, rank, sig, epoch, copy_streams,
+                       n_copy_streams, info);
   return st ? st : ok();
 }
 
-tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* copy_stream) {
+tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* copy_streams,
+                       int32_t n_copy_streams) {
   if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_ag_gemm: NULL args");
   tlc_status st = check_dense("tlc_ag_gemm", a->M, a->N, a->K, a->world, a->rank, a->rows_per_chunk,
                               a->bm, a->bn, a->b_layout, a->plan, a->n_tiles, a->a, a->b, a->c, a->sig);
@@ -243,14 +263,15 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* copy_st
   const int64_t chunk_bytes = static_cast<int64_t>(a->rows_per_chunk) * a->K * 2;
   void* dst[TLC_MAX_WORLD];
   for (int c = 0; c < a->world; ++c) dst[c] = static_cast<char*>(a->a) + c * chunk_bytes;
-  st = check_land_args(a->land, a->a_src, dst, a->world, a->rank, chunk_bytes, "tlc_ag_gemm");
+  st = check_land_args(a->land, a->a_src, dst, a->world, a->rank, chunk_bytes, "tlc_ag_gemm",
+                       copy_streams, n_copy_streams, a->epoch);
   if (st) return st;
   DeviceInfo info;
   st = device_info(&info);
   if (st) return st;
 
   st = enqueue_landing(a->land, dst, a->a_src, chunk_bytes, a->world, a->rank, a->sig, a->epoch,
-                       copy_stream, info);
+                       copy_streams, n_copy_streams, info);
   if (st) return st;
   if (a->n_tiles == 0) return ok();
 
@@ -268,19 +289,20 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* copy_st
   p.ldb = a->b_layout == TLC_B_NK ? a->K : a->N;
   p.ldc = a->N;
   p.no_wait_mask = 1u << a->rank;
-  p.do_wait = 1;
+  // land == NONE with epoch 0: every chunk is resident, nothing to wait for
+  p.do_wait = !(a->land == TLC_LAND_NONE && a->epoch == 0);
   p.sig = a->sig;
   p.epoch = a->epoch;
   p.timeout_ticks = ticks_for(a->timeout_ns, info);
-  const int avail = info.cus - reserve_for(a->land);
+  const int avail = info.cus - (p.do_wait ? reserve_for(a->land) : 0);
   int grid = a->grid > 0 ? a->grid : default_grid(a->n_tiles, avail);
   p.xcd_remap = grid % 8 == 0;
   st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
   return st ? st : ok();
 }
 
-static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* copy_stream,
-                            bool run_gemm) {
+static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* const* copy_streams,
+                            int n_copy_streams, bool run_gemm) {
   if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: NULL args");
   tlc_status st = check_dense("tlc_gemm_rs", a->M, a->N, a->K, a->world, a->rank, a->rows_per_chunk,
                               a->bm, a->bn, a->b_layout, a->plan, a->n_tiles, a->a, a->b,
@@ -299,7 +321,7 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
   int land = run_gemm ? a->land : TLC_LAND_NONE;
   st = check_land_args(land, reinterpret_cast<const void* const*>(a->remote_src),
                        reinterpret_cast<const void* const*>(a->landing), a->world, a->rank, slice_bytes,
-                       "tlc_gemm_rs");
+                       "tlc_gemm_rs", copy_streams, n_copy_streams, a->epoch);
   if (st) return st;
   DeviceInfo info;
   st = device_info(&info);
@@ -307,7 +329,7 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
 
   st = enqueue_landing(land, reinterpret_cast<void* const*>(a->landing),
                        reinterpret_cast<const void* const*>(a->remote_src), slice_bytes, a->world,
-                       a->rank, a->sig, a->epoch, copy_stream, info);
+                       a->rank, a->sig, a->epoch, copy_streams, n_copy_streams, info);
   if (st) return st;
 
   if (run_gemm && a->n_tiles > 0) {
@@ -328,7 +350,8 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
     p.sig = a->sig;
     p.epoch = a->epoch;
     p.timeout_ticks = ticks_for(a->timeout_ns, info);
-    int grid = a->grid > 0 ? a->grid : default_grid(a->n_tiles, info.cus);
+    // the GEMM does not wait, but the landing running beside it may need CUs
+    int grid = a->grid > 0 ? a->grid : default_grid(a->n_tiles, info.cus - reserve_for(land));
     p.xcd_remap = grid % 8 == 0;
     st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
     if (st) return st;
@@ -352,12 +375,13 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
   return st ? st : ok();
 }
 
-tlc_status tlc_gemm_rs(const tlc_rs_args* a, void* compute_stream, void* copy_stream) {
-  return rs_common(a, compute_stream, copy_stream, true);
+tlc_status tlc_gemm_rs(const tlc_rs_args* a, void* compute_stream, void* const* copy_streams,
+                       int32_t n_copy_streams) {
+  return rs_common(a, compute_stream, copy_streams, n_copy_streams, true);
 }
 
-tlc_status tlc_rs_reduce(const tlc_rs_args* a, void* compute_stream, void* copy_stream) {
-  return rs_common(a, compute_stream, copy_stream, false);
+tlc_status tlc_rs_reduce(const tlc_rs_args* a, void* compute_stream) {
+  return rs_common(a, compute_stream, nullptr, 0, false);
 }
 
 int64_t tlc_moe_plan_capacity(int32_t T, int32_t topk, int32_t experts, int32_t N, int32_t bm, int32_t bn) {
@@ -434,7 +458,8 @@ tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
   return st ? st : ok();
 }
 
-tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* copy_stream) {
+tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* copy_streams,
+                      int32_t n_copy_streams) {
   if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: NULL args");
   if (a->world < 1 || a->world > TLC_MAX_WORLD || a->rank < 0 || a->rank >= a->world)
     return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: world/rank");
@@ -455,13 +480,14 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* copy_st
   const int64_t chunk_bytes = static_cast<int64_t>(a->tokens_per_chunk) * a->H * 2;
   void* dst[TLC_MAX_WORLD];
   for (int c = 0; c < a->world; ++c) dst[c] = static_cast<char*>(a->x) + c * chunk_bytes;
-  tlc_status st = check_land_args(a->land, a->x_src, dst, a->world, a->rank, chunk_bytes, "tlc_ag_moe");
+  tlc_status st = check_land_args(a->land, a->x_src, dst, a->world, a->rank, chunk_bytes, "tlc_ag_moe",
+                                  copy_streams, n_copy_streams, a->epoch);
   if (st) return st;
   DeviceInfo info;
   st = device_info(&info);
   if (st) return st;
   st = enqueue_landing(a->land, dst, a->x_src, chunk_bytes, a->world, a->rank, a->sig, a->epoch,
-                       copy_stream, info);
+                       copy_streams, n_copy_streams, info);
   if (st) return st;
 
   GemmParams p;
@@ -482,11 +508,11 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* copy_st
   p.ldc = a->N;
   p.b_expert_stride = static_cast<int64_t>(a->H) * a->N;
   p.no_wait_mask = 1u << a->rank;
-  p.do_wait = 1;
+  p.do_wait = !(a->land == TLC_LAND_NONE && a->epoch == 0);
   p.sig = a->sig;
   p.epoch = a->epoch;
   p.timeout_ticks = ticks_for(a->timeout_ns, info);
-  const int avail = info.cus - reserve_for(a->land);
+  const int avail = info.cus - (p.do_wait ? reserve_for(a->land) : 0);
   // The tile count is only known on the device: use every available CU.
   int grid = a->grid > 0 ? a->grid : (avail >= 8 ? avail / 8 * 8 : avail);
   p.xcd_remap = grid % 8 == 0;

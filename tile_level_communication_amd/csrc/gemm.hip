@@ -396,7 +396,7 @@ struct Tile8w {
 };
 
 // Walks the plan: validation, chunk waits, then `run_tile(tile)`.
-template <int BM, int BN, int KIND, typename RunTile>
+template <int BM, int BN, int KIND, int WAIT, typename RunTile>
 __device__ inline void tile_loop(const GemmParams& p, int* s_abort, RunTile run_tile) {
   const int G = gridDim.x;
   int slot = blockIdx.x;
@@ -412,7 +412,7 @@ __device__ inline void tile_loop(const GemmParams& p, int* s_abort, RunTile run_
       if (threadIdx.x == 0) report(p.sig, TLC_ERR_BAD_PLAN, t);
       break;
     }
-    if (p.do_wait) {
+    if (WAIT) {
       const uint32_t need = tl.chunk_mask & ~seen;
       if (need) {
         if (threadIdx.x == 0) *s_abort = wait_chunks(p.sig, need, p.epoch, p.timeout_ticks, t);
@@ -426,31 +426,39 @@ __device__ inline void tile_loop(const GemmParams& p, int* s_abort, RunTile run_
   }
 }
 
-template <int B_NK, int KIND>
+template <int B_NK, int KIND, int WAIT>
 __global__ __launch_bounds__(512) void gemm_kernel_8w(GemmParams p) {
   __shared__ u32x4 A0[2048], A1[2048], B0[2048], B1[2048];
   __shared__ int s_abort;
-  tile_loop<256, 256, KIND>(p, &s_abort, [&](const tlc_tile& tl) {
+  tile_loop<256, 256, KIND, WAIT>(p, &s_abort, [&](const tlc_tile& tl) {
     Tile8w<B_NK, KIND>::run(p, tl, (TLC_LDS u32x4*)A0, (TLC_LDS u32x4*)A1, (TLC_LDS u32x4*)B0,
                             (TLC_LDS u32x4*)B1);
   });
 }
 
-template <int BM, int BN, int B_NK, int KIND>
+template <int BM, int BN, int B_NK, int KIND, int WAIT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
   __shared__ u32x4 lds[2 * (BM + BN) * 8];
   __shared__ int s_abort;
-  tile_loop<BM, BN, KIND>(p, &s_abort, [&](const tlc_tile& tl) { Tile<BM, BN, B_NK, KIND>::run(p, tl, lds); });
+  tile_loop<BM, BN, KIND, WAIT>(p, &s_abort, [&](const tlc_tile& tl) { Tile<BM, BN, B_NK, KIND>::run(p, tl, lds); });
+}
+
+template <int BM, int BN, int B_NK, int KIND, int WAIT>
+void launch_kernel(const GemmParams& p, int grid, void* stream) {
+  if constexpr (BM == 256 && BN == 256)
+    hipLaunchKernelGGL((gemm_kernel_8w<B_NK, KIND, WAIT>), dim3(grid), dim3(512), 0,
+                       static_cast<hipStream_t>(stream), p);
+  else
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, B_NK, KIND, WAIT>), dim3(grid), dim3(THREADS), 0,
+                       static_cast<hipStream_t>(stream), p);
 }
 
 template <int BM, int BN, int B_NK, int KIND>
 tlc_status launch_one(const GemmParams& p, int grid, void* stream) {
-  if constexpr (BM == 256 && BN == 256)
-    hipLaunchKernelGGL((gemm_kernel_8w<B_NK, KIND>), dim3(grid), dim3(512), 0,
-                       static_cast<hipStream_t>(stream), p);
+  if (p.do_wait)
+    launch_kernel<BM, BN, B_NK, KIND, 1>(p, grid, stream);
   else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, B_NK, KIND>), dim3(grid), dim3(THREADS), 0,
-                       static_cast<hipStream_t>(stream), p);
+    launch_kernel<BM, BN, B_NK, KIND, 0>(p, grid, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TLC_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
   return ok();

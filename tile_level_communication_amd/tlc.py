@@ -24,6 +24,7 @@ ORDER_NATURAL, ORDER_RANK_OFFSET = 0, 1
 B_KN, B_NK = 0, 1
 LAND_NONE, LAND_COPY_ENGINE, LAND_CU = 0, 1, 2
 MAX_WORLD = 32
+EPOCH_MAX = 4096
 
 EXPORTS = [
     "tlc_chunk_plan", "tlc_signals_alloc", "tlc_signals_free", "tlc_signals_set",
@@ -119,11 +120,11 @@ def lib() -> C.CDLL:
         L.tlc_signals_clear_status.restype = st
         L.tlc_read_status.argtypes = [vp, vp, C.POINTER(C.c_int32)]
         L.tlc_read_status.restype = st
-        L.tlc_ag_gemm.argtypes = [C.POINTER(AGArgs), vp, vp]
+        L.tlc_ag_gemm.argtypes = [C.POINTER(AGArgs), vp, C.POINTER(vp), C.c_int32]
         L.tlc_ag_gemm.restype = st
-        L.tlc_gemm_rs.argtypes = [C.POINTER(RSArgs), vp, vp]
+        L.tlc_gemm_rs.argtypes = [C.POINTER(RSArgs), vp, C.POINTER(vp), C.c_int32]
         L.tlc_gemm_rs.restype = st
-        L.tlc_rs_reduce.argtypes = [C.POINTER(RSArgs), vp, vp]
+        L.tlc_rs_reduce.argtypes = [C.POINTER(RSArgs), vp]
         L.tlc_rs_reduce.restype = st
         L.tlc_moe_plan_capacity.argtypes = [C.c_int32] * 6
         L.tlc_moe_plan_capacity.restype = C.c_int64
@@ -131,10 +132,10 @@ def lib() -> C.CDLL:
         L.tlc_moe_workspace_bytes.restype = C.c_int64
         L.tlc_moe_route.argtypes = [C.POINTER(MoERouteArgs), vp]
         L.tlc_moe_route.restype = st
-        L.tlc_ag_moe.argtypes = [C.POINTER(MoEArgs), vp, vp]
+        L.tlc_ag_moe.argtypes = [C.POINTER(MoEArgs), vp, C.POINTER(vp), C.c_int32]
         L.tlc_ag_moe.restype = st
         L.tlc_land.argtypes = [C.POINTER(vp), C.POINTER(vp), C.c_int64, C.c_int32, C.c_int32, vp,
-                               C.c_uint32, C.c_int32, vp]
+                               C.c_uint32, C.c_int32, C.POINTER(vp), C.c_int32]
         L.tlc_land.restype = st
         L.tlc_status_string.argtypes = [st]
         L.tlc_status_string.restype = C.c_char_p
@@ -177,6 +178,17 @@ def _stream(s) -> int:
     if isinstance(s, int):
         return s
     return s.cuda_stream
+
+
+def _streams(s):
+    """A stream, a list of streams or None -> (host array of hipStream_t, count)."""
+    if s is None:
+        return None, 0
+    items = list(s) if isinstance(s, (list, tuple)) else [s]
+    arr = (C.c_void_p * len(items))()
+    for i, x in enumerate(items):
+        arr[i] = _stream(x) or None
+    return arr, len(items)
 
 
 def _ptr_array(items, world):
@@ -242,12 +254,13 @@ def signals_alloc() -> Signals:
 
 def ag_gemm(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, a_src, b, b_layout, c,
             sig: Signals, epoch, land, compute_stream=None, copy_stream=None, grid=0, timeout_ns=0):
-    """tlc_ag_gemm.  a_src: list of `world` device tensors (entry `rank` unused) or None."""
+    """tlc_ag_gemm.  a_src: list of `world` device tensors (entry `rank` unused) or None.
+    copy_stream: one stream or a list of streams for the landing."""
     src = _ptr_array(a_src, world) if a_src is not None else None
     args = AGArgs(_ptr(plan), n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, _ptr(a), src,
                   _ptr(b), b_layout, _ptr(c), sig.ptr, epoch, land, grid, timeout_ns)
-    _check(lib().tlc_ag_gemm(C.byref(args), _stream(compute_stream), _stream(copy_stream)),
-           "tlc_ag_gemm")
+    cs, n = _streams(copy_stream)
+    _check(lib().tlc_ag_gemm(C.byref(args), _stream(compute_stream), cs, n), "tlc_ag_gemm")
 
 
 def _rs_args(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout, partials,
@@ -265,8 +278,8 @@ def gemm_rs(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b
     """tlc_gemm_rs.  remote_src, landing: lists of `world` device tensors (entry `rank` unused)."""
     args = _rs_args(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout,
                     partials, remote_src, landing, out, sig, epoch, land, grid, timeout_ns)
-    _check(lib().tlc_gemm_rs(C.byref(args), _stream(compute_stream), _stream(copy_stream)),
-           "tlc_gemm_rs")
+    cs, n = _streams(copy_stream)
+    _check(lib().tlc_gemm_rs(C.byref(args), _stream(compute_stream), cs, n), "tlc_gemm_rs")
 
 
 def rs_reduce(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout, partials,
@@ -275,8 +288,7 @@ def rs_reduce(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b,
     """tlc_rs_reduce: the reduce step only."""
     args = _rs_args(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout,
                     partials, remote_src, landing, out, sig, epoch, land, grid, timeout_ns)
-    _check(lib().tlc_rs_reduce(C.byref(args), _stream(compute_stream), _stream(copy_stream)),
-           "tlc_rs_reduce")
+    _check(lib().tlc_rs_reduce(C.byref(args), _stream(compute_stream)), "tlc_rs_reduce")
 
 
 # ---------------------------------------------------------------- AG-MoE ----
@@ -306,12 +318,13 @@ def ag_moe(plan, n_tiles_dev, plan_cap, row_token, tokens_per_chunk, world, rank
     args = MoEArgs(_ptr(plan), _ptr(n_tiles_dev), plan_cap, _ptr(row_token), tokens_per_chunk,
                    world, rank, experts, topk, H, N, bm, bn, _ptr(x), src, _ptr(w), w_layout,
                    _ptr(y), sig.ptr, epoch, land, grid, timeout_ns)
-    _check(lib().tlc_ag_moe(C.byref(args), _stream(compute_stream), _stream(copy_stream)),
-           "tlc_ag_moe")
+    cs, n = _streams(copy_stream)
+    _check(lib().tlc_ag_moe(C.byref(args), _stream(compute_stream), cs, n), "tlc_ag_moe")
 
 
 def land(dst, src, bytes_per_chunk, world, rank, sig: Signals, epoch, land_kind, copy_stream=None):
     d = _ptr_array(dst, world)
     s = _ptr_array(src, world)
-    _check(lib().tlc_land(d, s, bytes_per_chunk, world, rank, sig.ptr, epoch, land_kind,
-                          _stream(copy_stream)), "tlc_land")
+    cs, n = _streams(copy_stream)
+    _check(lib().tlc_land(d, s, bytes_per_chunk, world, rank, sig.ptr, epoch, land_kind, cs, n),
+           "tlc_land")

@@ -31,19 +31,40 @@ def weight_layout(b_kn: torch.Tensor, b_layout: int) -> torch.Tensor:
 
 
 class Streams:
-    """A compute stream (torch's current one) and a side copy stream, both at
-    the default priority."""
+    """A compute stream (torch's current one) and `n_copy` side copy streams,
+    all at the default priority.  Two copy streams let two copy engines land
+    chunks at once."""
 
-    def __init__(self, device):
+    def __init__(self, device, n_copy: int = 2):
         self.compute = torch.cuda.current_stream(device)
-        self.copy = torch.cuda.Stream(device=device)
+        self.copies = [torch.cuda.Stream(device=device) for _ in range(n_copy)]
+
+    @property
+    def copy(self):
+        return self.copies
 
     def begin(self):
         # the landing may only overwrite buffers once earlier work is done
-        self.copy.wait_stream(self.compute)
+        for c in self.copies:
+            c.wait_stream(self.compute)
 
     def end(self):
-        self.compute.wait_stream(self.copy)
+        for c in self.copies:
+            self.compute.wait_stream(c)
+
+
+def next_epoch(prob) -> int:
+    """Advance the problem's epoch; copy-engine flags are raised from a table of
+    TLC_EPOCH_MAX values, so past the end the flags are rewound to 0 and the
+    epochs restart at 1."""
+    prob.epoch += 1
+    if prob.epoch > tlc.EPOCH_MAX:
+        prob.streams.compute.synchronize()
+        for c in prob.streams.copies:
+            c.synchronize()
+        prob.sig.set(prob.world, 0, prob.streams.compute)
+        prob.epoch = 1
+    return prob.epoch
 
 
 class AGProblem:
@@ -89,7 +110,7 @@ class AGProblem:
         """Enqueue one AG-GEMM.  With land == LAND_NONE the flags are raised to the
         new epoch first (chunks must already be in place) unless preset_flags is
         False."""
-        self.epoch += 1
+        next_epoch(self)
         s = self.streams
         if land == tlc.LAND_NONE and preset_flags is not False:
             self.sig.set(self.world, self.epoch, s.compute)
@@ -101,7 +122,7 @@ class AGProblem:
         s.end()
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
-        self.epoch += 1
+        next_epoch(self)
         s = self.streams
         s.begin()
         dst = [self.a[c * self.R:(c + 1) * self.R] for c in range(self.world)]
@@ -161,7 +182,7 @@ class RSProblem:
                 self.bm, self.bn, self.a, self.b, self.b_layout, self.partials)
 
     def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0):
-        self.epoch += 1
+        next_epoch(self)
         s = self.streams
         if land == tlc.LAND_NONE:
             self.sig.set(self.world, self.epoch, s.compute)
@@ -171,14 +192,14 @@ class RSProblem:
         s.end()
 
     def reduce_only(self, timeout_ns=0):
-        self.epoch += 1
+        next_epoch(self)
         s = self.streams
         self.sig.set(self.world, self.epoch, s.compute)
         tlc.rs_reduce(*self._args(), None, self.landing, self.out, self.sig, self.epoch,
-                      tlc.LAND_NONE, s.compute, s.copy, 0, timeout_ns)
+                      tlc.LAND_NONE, s.compute, None, 0, timeout_ns)
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
-        self.epoch += 1
+        next_epoch(self)
         s = self.streams
         s.begin()
         tlc.land(self.landing, self.remote_src, self.R * self.N * 4, self.world, self.rank, self.sig,
@@ -243,7 +264,7 @@ class MoEProblem:
                       self.workspace, s.compute)
 
     def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, do_route=True):
-        self.epoch += 1
+        next_epoch(self)
         s = self.streams
         if land == tlc.LAND_NONE:
             self.sig.set(self.world, self.epoch, s.compute)
