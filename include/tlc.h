@@ -36,7 +36,10 @@
  *     copy_streams[i % n] (several streams let several copy engines work at
  *     once, as several links would); the CU landing kernel runs on
  *     copy_streams[0].  The caller orders the copy streams after earlier
- *     readers of the landing buffers, and later readers after them.
+ *     readers of the landing buffers, and later readers after them.  The
+ *     landing is always enqueued before the kernels that wait for it: when
+ *     two streams share one hardware queue the work then runs one after the
+ *     other instead of waiting forever.
  *   - Device-side failures (a wait that exceeded its time limit, a plan entry
  *     outside the output) are written to tlc_signals.status and read after the
  *     stream is synchronized (tlc_read_status).  The kernels then stop early;
@@ -209,6 +212,12 @@ typedef struct {
   int32_t land;
   int32_t grid;
   int64_t timeout_ns;
+  /* Optional debug trace (NULL = off): device int64 array of n_tiles x 4,
+   * entry t = {workgroup, wall-clock at wait start, at wait end, at tile end}
+   * for the tile at plan index t; wall clock = the device's constant-rate
+   * counter (hipDeviceAttributeWallClockRate).  Entries of tiles not run keep
+   * their previous contents. */
+  int64_t* trace;
 } tlc_ag_args;
 
 tlc_status tlc_ag_gemm(const tlc_ag_args* args, void* compute_stream, void* const* copy_streams,

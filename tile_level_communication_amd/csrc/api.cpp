@@ -129,8 +129,9 @@ tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, i
   p.vec_per_chunk = bytes / 16;
   p.sig = sig;
   p.epoch = epoch;
-  int grid = info.cus / 4;
-  if (grid < 8) grid = 8;
+  // a few workgroups: each one holds a CU's wave slots that a GEMM workgroup
+  // (two waves per SIMD at 256 registers) could otherwise use
+  const int grid = 32;
   return launch_land_cu(p, grid, copy_streams[0]);
 }
 
@@ -270,6 +271,9 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   st = device_info(&info);
   if (st) return st;
 
+  // The producer is always enqueued before the consumer: two streams may share
+  // one hardware queue, and a GEMM queued ahead of its own landing there would
+  // wait on flags that can never be raised.
   st = enqueue_landing(a->land, dst, a->a_src, chunk_bytes, a->world, a->rank, a->sig, a->epoch,
                        copy_streams, n_copy_streams, info);
   if (st) return st;
@@ -294,6 +298,7 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   p.sig = a->sig;
   p.epoch = a->epoch;
   p.timeout_ticks = ticks_for(a->timeout_ns, info);
+  p.trace = a->trace;
   const int avail = info.cus - (p.do_wait ? reserve_for(a->land) : 0);
   int grid = a->grid > 0 ? a->grid : default_grid(a->n_tiles, avail);
   p.xcd_remap = grid % 8 == 0;

@@ -412,6 +412,8 @@ __device__ inline void tile_loop(const GemmParams& p, int* s_abort, RunTile run_
       if (threadIdx.x == 0) report(p.sig, TLC_ERR_BAD_PLAN, t);
       break;
     }
+    int64_t t_wait0 = 0, t_wait1 = 0;
+    if (p.trace && threadIdx.x == 0) t_wait0 = static_cast<int64_t>(wall_clock64());
     if (WAIT) {
       const uint32_t need = tl.chunk_mask & ~seen;
       if (need) {
@@ -422,7 +424,15 @@ __device__ inline void tile_loop(const GemmParams& p, int* s_abort, RunTile run_
         seen |= need;
       }
     }
+    if (p.trace && threadIdx.x == 0) t_wait1 = static_cast<int64_t>(wall_clock64());
     run_tile(tl);
+    if (p.trace && threadIdx.x == 0) {
+      int64_t* e = p.trace + 4 * t;
+      e[0] = blockIdx.x;
+      e[1] = t_wait0;
+      e[2] = t_wait1;
+      e[3] = static_cast<int64_t>(wall_clock64());
+    }
   }
 }
 

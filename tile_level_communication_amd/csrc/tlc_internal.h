@@ -43,6 +43,7 @@ struct GemmParams {
   uint32_t epoch;
   int64_t timeout_ticks;
   int32_t xcd_remap;
+  int64_t* trace;              // optional: n_tiles x {wg, wait start, wait end, done}
 };
 
 enum GemmKind { KIND_DENSE = 0, KIND_MOE = 1 };

@@ -59,7 +59,7 @@ class AGArgs(C.Structure):
                 ("a", C.c_void_p), ("a_src", C.POINTER(C.c_void_p)), ("b", C.c_void_p),
                 ("b_layout", C.c_int32), ("c", C.c_void_p), ("sig", C.c_void_p),
                 ("epoch", C.c_uint32), ("land", C.c_int32), ("grid", C.c_int32),
-                ("timeout_ns", C.c_int64)]
+                ("timeout_ns", C.c_int64), ("trace", C.c_void_p)]
 
 
 class RSArgs(C.Structure):
@@ -253,12 +253,13 @@ def signals_alloc() -> Signals:
 # ------------------------------------------------------------- AG-GEMM ------
 
 def ag_gemm(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, a_src, b, b_layout, c,
-            sig: Signals, epoch, land, compute_stream=None, copy_stream=None, grid=0, timeout_ns=0):
+            sig: Signals, epoch, land, compute_stream=None, copy_stream=None, grid=0, timeout_ns=0,
+            trace=None):
     """tlc_ag_gemm.  a_src: list of `world` device tensors (entry `rank` unused) or None.
     copy_stream: one stream or a list of streams for the landing."""
     src = _ptr_array(a_src, world) if a_src is not None else None
     args = AGArgs(_ptr(plan), n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, _ptr(a), src,
-                  _ptr(b), b_layout, _ptr(c), sig.ptr, epoch, land, grid, timeout_ns)
+                  _ptr(b), b_layout, _ptr(c), sig.ptr, epoch, land, grid, timeout_ns, _ptr(trace))
     cs, n = _streams(copy_stream)
     _check(lib().tlc_ag_gemm(C.byref(args), _stream(compute_stream), cs, n), "tlc_ag_gemm")
 

@@ -106,7 +106,7 @@ class AGProblem:
             if c != self.rank:
                 self.a[c * self.R:(c + 1) * self.R].fill_(float("nan"))
 
-    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, preset_flags=None):
+    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, preset_flags=None, trace=None):
         """Enqueue one AG-GEMM.  With land == LAND_NONE the flags are raised to the
         new epoch first (chunks must already be in place) unless preset_flags is
         False."""
@@ -118,7 +118,7 @@ class AGProblem:
         tlc.ag_gemm(self.plan, self.n_tiles, self.M, self.N, self.K, self.world, self.rank, self.R,
                     self.bm, self.bn, self.a, self.a_src if land != tlc.LAND_NONE else None,
                     self.b, self.b_layout, self.c, self.sig, self.epoch, land, s.compute, s.copy,
-                    grid, timeout_ns)
+                    grid, timeout_ns, trace)
         s.end()
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
