@@ -89,17 +89,26 @@ enum { TLC_LAND_NONE = 0, TLC_LAND_COPY_ENGINE = 1, TLC_LAND_CU = 2 };
 
 #define TLC_MAX_WORLD 32
 
-/* One output tile of the plan, 32 bytes.  Rows [m0, m0+m_rows) and columns
+/* One work unit of the plan, 32 bytes: an output tile, or one K range of a
+ * tile that is split along K.  Rows [m0, m0+m_rows) and columns
  * [n0, n0+n_cols) of the output.  expert = -1 for dense GEMMs.  chunk_mask bit
  * c = the tile reads rows of chunk c (gather, MoE) or writes rows of
  * destination chunk c (scatter).  key = the primary sort key: wait position
- * (gather), send position (scatter) or readiness (MoE); 0 in natural order. */
+ * (gather), send position (scatter) or readiness (MoE); 0 in natural order.
+ * split = 0 for a whole tile; for a tile split into S K ranges (2 <= S <= 255)
+ * unit s (0 <= s < S) has split = S | s << 8 | f << 16, where f numbers the
+ * split tiles 0, 1, ... in plan order.  Unit s covers the 64-wide K steps
+ * [s*KT/S, (s+1)*KT/S) (integer division, KT = K/64); the S units of a tile
+ * are adjacent in the plan.  Each unit writes its fp32 partial tile to a
+ * workspace slot; the last of the S units to finish adds the S partials in
+ * ascending s and stores the tile, so the result does not depend on which
+ * workgroup ran which unit or in which order they finished. */
 typedef struct {
   int32_t m0, n0, m_rows, n_cols;
   int32_t expert;
   uint32_t chunk_mask;
   int32_t key;
-  int32_t reserved; /* 0 */
+  uint32_t split; /* 0, or S | s << 8 | f << 16 (see above) */
 } tlc_tile;
 
 /* Copy-engine landings raise a chunk's flag with a second copy-engine transfer
@@ -113,13 +122,16 @@ typedef struct {
  * engines).  flags[c] >= epoch  <=>  chunk c has landed for this call.
  * status[0] = 0 or a negative tlc_status, status[1] = plan index of the tile
  * that failed, status[2] = chunk it waited for.  land_count is internal to the
- * CU landing backend (zero between calls).  epoch_table[i] = i + 1, written
- * once by tlc_signals_alloc. */
+ * CU landing backend, work_next / work_done to the GEMM's dynamic work queue
+ * (all zero between calls; the last workgroup of a launch resets them).
+ * epoch_table[i] = i + 1, written once by tlc_signals_alloc.  One GEMM call
+ * at a time per signals block. */
 typedef struct {
   uint32_t flags[TLC_MAX_WORLD];
   uint32_t land_count[TLC_MAX_WORLD];
   int32_t status[4];
-  uint32_t reserved[60];
+  uint32_t work_next, work_done;
+  uint32_t reserved[58];
   uint32_t epoch_table[TLC_EPOCH_MAX];
 } tlc_signals;
 
@@ -136,6 +148,9 @@ typedef struct {
   int32_t bm, bn;         /* tile size, >= 1 */
   int32_t order;          /* TLC_ORDER_* */
   int32_t group_m;        /* >= 1: m-tiles per locality band inside a key */
+  int32_t split_k;        /* 0 or 1: no split; 2..255: tiles with key >= split_from
+                             are split into split_k K ranges */
+  int32_t split_from;     /* first key whose tiles are split (>= 0) */
 } tlc_plan_desc;
 
 /* Tile order of the communication-aware scheduler (host code, integers only).
@@ -148,13 +163,26 @@ typedef struct {
  *   tiles go early.  Ties: (m-tile / group_m, n-tile, m-tile) -- bands of
  *   group_m m-tiles walked column by column (AutoOverlap §5.4, Fig. 6: intra-
  *   chunk swizzle for locality).  Natural order: all keys 0.
+ *   A tile with key >= split_from (split_k >= 2) becomes split_k adjacent
+ *   units, one per K range, so that the work that depends on the last chunks
+ *   can spread over every compute unit.
  * tiles:   host array of `cap` entries, or NULL to query the count only.
- * n_tiles: host, receives ceil(M/bm) * ceil(N/bn).
+ * n_tiles: host, receives the number of units: ceil(M/bm) * ceil(N/bn) plus
+ *   (split_k - 1) per split tile.
  * landing_order: host array of world-1 entries or NULL; receives the order in
  *   which peers' chunks land: rank+1, rank+2, ..., rank-1 (mod W).
  * Errors: INVALID_ARG (bad desc), CAPACITY (cap < count; *n_tiles is set). */
 tlc_status tlc_chunk_plan(const tlc_plan_desc* desc, tlc_tile* tiles, int64_t cap,
                           int64_t* n_tiles, int32_t* landing_order);
+
+/* Bytes of the workspace a plan with `n_split_tiles` split tiles of split_k
+ * units needs: one block per split tile, a 256-byte header (its arrival
+ * counter) followed by split_k fp32 partial tiles of bm x bn, so
+ * n_split_tiles * (256 + split_k * bm * bn * 4).  0 if there is no split tile.
+ * The caller allocates it in device memory (256-byte aligned) and zero-fills it
+ * once; each call leaves the counters at zero again, except after a device
+ * error (TIMEOUT, BAD_PLAN), after which it must be zero-filled before reuse. */
+int64_t tlc_split_workspace_bytes(int64_t n_split_tiles, int32_t split_k, int32_t bm, int32_t bn);
 
 /* ------------------------------------------------------------- signals ---- */
 
@@ -193,9 +221,18 @@ tlc_status tlc_read_status(const tlc_signals* sig, void* stream, int32_t* out);
  *          chunks that still have to land.  With land == TLC_LAND_NONE and
  *          epoch == 0 the kernel does not look at the flags at all (every
  *          chunk must already be in place): the plain compute-only GEMM.
+ *   workspace  device, tlc_split_workspace_bytes(...) bytes for the plan's
+ *          split tiles (zero-filled before first use), or NULL / 0 bytes if the
+ *          plan splits no tile.  A split tile whose slot lies beyond
+ *          workspace_bytes is reported as BAD_PLAN.
  * Streams: the GEMM runs on `compute_stream`, the landing on the copy streams.
- * grid: persistent workgroups (0 = default: fewest rounds of tiles over the
- * compute units, spread evenly).  timeout_ns: per-wait limit (0 = 2 s). */
+ * grid: persistent workgroups (0 = every compute unit the landing leaves free).
+ * schedule: TLC_SCHED_DYNAMIC -- workgroups take the next unit in plan order
+ *   from a counter in `sig` as they become free (units that wait for a late
+ *   chunk then do not hold back the ones behind them); TLC_SCHED_STATIC --
+ *   workgroup slot g runs units g, g + grid, g + 2 grid, ...
+ * timeout_ns: per-wait limit (0 = 2 s). */
+enum { TLC_SCHED_DYNAMIC = 0, TLC_SCHED_STATIC = 1 };
 typedef struct {
   const tlc_tile* plan; /* device, n_tiles entries, execution order */
   int64_t n_tiles;
@@ -212,6 +249,9 @@ typedef struct {
   int32_t land;
   int32_t grid;
   int64_t timeout_ns;
+  void* workspace;
+  int64_t workspace_bytes;
+  int32_t schedule;
   /* Optional debug trace (NULL = off): device int64 array of n_tiles x 4,
    * entry t = {workgroup, wall-clock at wait start, at wait end, at tile end}
    * for the tile at plan index t; wall clock = the device's constant-rate
@@ -254,6 +294,9 @@ typedef struct {
   int32_t land;
   int32_t grid;
   int64_t timeout_ns;
+  void* workspace;         /* as in tlc_ag_args */
+  int64_t workspace_bytes;
+  int32_t schedule;
 } tlc_rs_args;
 
 tlc_status tlc_gemm_rs(const tlc_rs_args* args, void* compute_stream, void* const* copy_streams,
@@ -329,6 +372,7 @@ typedef struct {
   int32_t land;
   int32_t grid;
   int64_t timeout_ns;
+  int32_t schedule; /* TLC_SCHED_* as in tlc_ag_args (MoE tiles are never split) */
 } tlc_moe_args;
 
 tlc_status tlc_ag_moe(const tlc_moe_args* args, void* compute_stream, void* const* copy_streams,
@@ -348,7 +392,7 @@ tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_
 
 const char* tlc_status_string(tlc_status s);
 const char* tlc_last_error(void);
-/* Library version, e.g. 100 = 0.1.0. */
+/* Library version, e.g. 110 = 0.1.10. */
 int32_t tlc_version(void);
 
 #ifdef __cplusplus

@@ -31,14 +31,14 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tlc.version() == 100
+    assert tlc.version() == 110
     assert tlc.status_string(tlc.ERR_TIMEOUT).startswith("timeout")
     assert tlc.status_string(0) == "ok"
 
 
 def test_struct_sizes_match_header():
     assert C.sizeof(tlc.Tile) == 32
-    assert C.sizeof(tlc.PlanDesc) == 40
+    assert C.sizeof(tlc.PlanDesc) == 48
 
 
 def _ag_args(**over):
@@ -62,6 +62,9 @@ def _ag_args(**over):
     (dict(a=8, b=32, c=48, sig=64), tlc.ERR_MISALIGNED),
     (dict(a=16, b=32, c=48, sig=64, land=9), tlc.ERR_INVALID_ARG),
     (dict(a=16, b=32, c=48, sig=64, land=tlc.LAND_CU), tlc.ERR_INVALID_ARG),  # no a_src
+    (dict(a=16, b=32, c=48, sig=64, schedule=5), tlc.ERR_INVALID_ARG),
+    (dict(a=16, b=32, c=48, sig=64, workspace_bytes=1024), tlc.ERR_INVALID_ARG),  # NULL workspace
+    (dict(a=16, b=32, c=48, sig=64, workspace=4112, workspace_bytes=1024), tlc.ERR_MISALIGNED),
 ])
 def test_ag_gemm_argument_errors(over, want):
     args = _ag_args(**over)
@@ -83,6 +86,21 @@ def test_plan_capacity_and_query():
     assert tlc.lib().tlc_chunk_plan(C.byref(bad), None, 0, C.byref(n), None) == tlc.ERR_INVALID_ARG
     bad = tlc.PlanDesc(tlc.MODE_MOE, 8, 0, 8192, 3200, 1024, 256, 256, 1, 1)
     assert tlc.lib().tlc_chunk_plan(C.byref(bad), None, 0, C.byref(n), None) == tlc.ERR_INVALID_ARG
+    bad = tlc.PlanDesc(tlc.MODE_AG, 8, 0, 8192, 3200, 1024, 256, 256, 1, 1, 256, 0)
+    assert tlc.lib().tlc_chunk_plan(C.byref(bad), None, 0, C.byref(n), None) == tlc.ERR_INVALID_ARG
+    bad = tlc.PlanDesc(tlc.MODE_AG, 8, 0, 8192, 3200, 1024, 256, 256, 1, 1, 4, -1)
+    assert tlc.lib().tlc_chunk_plan(C.byref(bad), None, 0, C.byref(n), None) == tlc.ERR_INVALID_ARG
+    # split: 52 tiles per chunk, chunks at key >= 6 split four ways -> +2 * 52 * 3 units
+    d = tlc.PlanDesc(tlc.MODE_AG, 8, 3, 8192, 3200, 1024, 256, 256, tlc.ORDER_RANK_OFFSET, 4, 4, 6)
+    assert tlc.lib().tlc_chunk_plan(C.byref(d), None, 0, C.byref(n), None) == 0
+    assert n.value == 32 * 13 + 2 * 52 * 3
+
+
+def test_split_workspace_bytes():
+    assert tlc.split_workspace_bytes(0, 4, 256, 256) == 0
+    assert tlc.split_workspace_bytes(10, 1, 256, 256) == 0
+    assert tlc.split_workspace_bytes(10, 4, 256, 256) == 10 * (256 + 4 * 256 * 256 * 4)
+    assert tlc.split_workspace_bytes(3, 2, 128, 128) == 3 * (256 + 2 * 128 * 128 * 4)
 
 
 def test_moe_sizes():

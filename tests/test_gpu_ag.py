@@ -104,6 +104,56 @@ def test_ag_fresh_data_every_call(land):
                     absmax_bf16(inp.a_chunks), absmax_bf16(inp1.b), f"iter{it}")
 
 
+@pytest.mark.parametrize("sched", ["dynamic", "static"])
+@pytest.mark.parametrize("split", [(2, 0), (3, 1)], ids=["s2_from0", "s3_from1"])
+@pytest.mark.parametrize("land", ["copy_engine", "cu"])
+def test_ag_split_parity(land, split, sched):
+    """Tiles split along K (one K range per unit, fixup in split order), both
+    schedules; K = 128 with three splits leaves one unit an empty K range."""
+    schedule = tlc.SCHED_DYNAMIC if sched == "dynamic" else tlc.SCHED_STATIC
+    for (name, W, R, K, N, tile) in SHAPES:
+        for integer in (False, True):
+            inp = si.ag_inputs(160 + W, W, R, N, K, integer=integer)
+            ref = og.ag_gemm(inp.a_chunks, inp.b)
+            for rank in sorted({0, W - 1}):
+                log(f"[ag split] {name} land={land} split={split} sched={sched} int={integer} rank={rank}")
+                prob, c = _run(inp, rank, tile, tlc.B_KN, LANDS[land], split_k=split[0],
+                               split_from=split[1], schedule=schedule)
+                if integer:
+                    check_exact(c, ref, name)
+                else:
+                    check_close(c, ref, K, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), name)
+                # the workspace counters are back at zero: a second call is right too
+                prob.poison_remote()
+                prob.run(LANDS[land])
+                torch.cuda.synchronize()
+                assert prob.sig.read_status()[0] == 0
+                c2 = prob.c.cpu().numpy()
+                assert np.array_equal(c2.view(np.uint32), c.view(np.uint32))
+
+
+def test_ag_split_result_independent_of_schedule():
+    """With a fixed split, the output bits do not depend on schedule, grid or
+    which workgroup finished a tile's units last."""
+    W, R, K, N = 4, 160, 512, 520
+    inp = si.ag_inputs(170, W, R, N, K)
+    outs = []
+    for schedule in (tlc.SCHED_DYNAMIC, tlc.SCHED_STATIC):
+        for grid in (0, 1, 3, 16):
+            log(f"[ag split bits] schedule={schedule} grid={grid}")
+            prob = AGProblem(inp.a_chunks, inp.b, 2, 128, 128, tlc.B_KN, split_k=4, split_from=0,
+                             schedule=schedule)
+            prob.poison_remote()
+            prob.run(tlc.LAND_COPY_ENGINE, grid=grid)
+            torch.cuda.synchronize()
+            assert prob.sig.read_status()[0] == 0
+            outs.append(prob.c.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    check_close(outs[0], og.ag_gemm(inp.a_chunks, inp.b), K, absmax_bf16(inp.a_chunks),
+                absmax_bf16(inp.b), "split bits")
+
+
 def test_ag_timeout_reports_status():
     """A chunk whose flag never reaches the epoch: the kernel gives up after
     the time limit, reports TIMEOUT with the chunk, and every workgroup exits."""
@@ -143,10 +193,19 @@ def test_ag_qwen3_ffn_up_full_size(rank):
     got = c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
     ref = og.ag_gemm_rows(inp.a_chunks, inp.b, rows)
     check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), "cfg full rows")
+    # the late chunks split along K (the bench's schedule)
+    log(f"[ag full] {wl.name} rank={rank}: split 4 from key 1, dynamic schedule")
+    prob = AGProblem(inp.a_chunks, inp.b, rank, 256, 256, tlc.B_KN, split_k=4, split_from=1)
+    prob.poison_remote()
+    prob.run(tlc.LAND_COPY_ENGINE)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    got = prob.c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
+    check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), "cfg full rows split")
     # integer-valued inputs: the whole output bit for bit
     log(f"[ag full] {wl.name} rank={rank}: integer inputs, full compare")
     ii = si.workload_inputs(2, integer=True)
-    prob = AGProblem(ii.a_chunks, ii.b, rank, 256, 256, tlc.B_KN)
+    prob = AGProblem(ii.a_chunks, ii.b, rank, 256, 256, tlc.B_KN, split_k=4, split_from=2)
     prob.poison_remote()
     prob.run(tlc.LAND_CU)
     torch.cuda.synchronize()

@@ -25,8 +25,8 @@ SHAPES = [
 ]
 
 
-def _run(inp, W, rank, tile, layout, land):
-    prob = RSProblem(inp.a, inp.b, inp.remote, W, rank, tile, tile, layout)
+def _run(inp, W, rank, tile, layout, land, **kw):
+    prob = RSProblem(inp.a, inp.b, inp.remote, W, rank, tile, tile, layout, **kw)
     if land == 0:
         prob.place_all()
     else:
@@ -125,3 +125,25 @@ def test_rs_ffn_down_128k_sampled(rank):
     rows = np.array([c * R + o for c in range(wl.world) for o in (0, R // 2, R - 1)])
     got = prob.partials[torch.from_numpy(rows).to(prob.out.device)].cpu().numpy()
     check_close(got, og.gemm_partial(inp.a, inp.b, rows), wl.k, am, bm, "partial rows")
+
+
+@pytest.mark.parametrize("sched", ["dynamic", "static"])
+@pytest.mark.parametrize("split", [(2, 0), (3, 2)], ids=["s2_from0", "s3_from2"])
+def test_rs_split_parity(split, sched):
+    """Tiles split along K: partial slots, in-order fixup; integer inputs exact."""
+    schedule = tlc.SCHED_DYNAMIC if sched == "dynamic" else tlc.SCHED_STATIC
+    for (name, W, R, K, N, tile) in SHAPES:
+        for integer in (False, True):
+            rank = W - 1
+            log(f"[rs split] {name} split={split} sched={sched} int={integer}")
+            inp = si.rs_inputs(220 + W, W, rank, R, N, K, remote_std=0.5, integer=integer)
+            p_ref, out_ref = og.gemm_rs(inp.a, inp.b, inp.remote, W, rank)
+            _, p, out = _run(inp, W, rank, tile, tlc.B_KN, tlc.LAND_COPY_ENGINE, split_k=split[0],
+                             split_from=split[1], schedule=schedule)
+            if integer:
+                check_exact(p, p_ref, name + " partials")
+                check_exact(out, out_ref, name + " out")
+            else:
+                am, bm = absmax_bf16(inp.a), absmax_bf16(inp.b)
+                check_close(p, p_ref, K, am, bm, name + " partials")
+                check_close(out, out_ref, K, am, bm, name + " out")

@@ -16,7 +16,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "plan_cases.json")
 @pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
 def test_library_matches_golden(case):
     tiles, landing = tlc.chunk_plan(case["mode"], case["world"], case["rank"], case["M"], case["N"],
-                                    case["R"], case["bm"], case["bn"], case["order"], case["group_m"])
+                                    case["R"], case["bm"], case["bn"], case["order"], case["group_m"],
+                                    case.get("split_k", 0), case.get("split_from", 0))
     assert tiles.tolist() == case["tiles"]
     assert landing == case["landing"]
 
@@ -48,3 +49,19 @@ def test_full_size_plans_match_oracle():
             lib_tiles, _ = tlc.chunk_plan(mode, W, rank, W * R, N, R, bm, bm, tlc.ORDER_RANK_OFFSET, 4)
             ref_tiles, _ = op.chunk_plan(mode, W, rank, W * R, N, R, bm, bm, op.ORDER_RANK_OFFSET, 4)
             assert np.array_equal(lib_tiles.astype(np.int64), np.array(ref_tiles, dtype=np.int64))
+
+
+@pytest.mark.parametrize("mode", [tlc.MODE_AG, tlc.MODE_RS])
+@pytest.mark.parametrize("split_k,split_from", [(2, 0), (3, 1), (4, 6), (5, 7), (255, 2)])
+def test_library_split_matches_oracle(mode, split_k, split_from):
+    for (W, R, N, bm) in [(8, 1024, 3200, 256), (3, 200, 392, 256), (5, 77, 136, 128)]:
+        for rank in (0, W - 1):
+            lib_tiles, _ = tlc.chunk_plan(mode, W, rank, W * R, N, R, bm, bm, tlc.ORDER_RANK_OFFSET, 4,
+                                          split_k, split_from)
+            ref_tiles, _ = op.chunk_plan(mode, W, rank, W * R, N, R, bm, bm, op.ORDER_RANK_OFFSET, 4,
+                                         split_k, split_from)
+            got = lib_tiles.astype(np.int64) & 0xFFFFFFFF
+            ref = np.array(ref_tiles, dtype=np.int64) & 0xFFFFFFFF
+            assert np.array_equal(got, ref)
+            assert tlc.split_tiles(lib_tiles) == sum(1 for t in ref_tiles if (t[7] & 0xFF) >= 2 and
+                                                     ((t[7] >> 8) & 0xFF) == 0)

@@ -16,12 +16,14 @@ thread_local char g_err[512] = "";
 std::mutex g_info_mu;
 DeviceInfo g_info[64];
 bool g_info_ok[64] = {};
-// CUs the persistent GEMM leaves free while it may wait for landings: the CU
-// landing kernel needs a few; on the copy-engine path the runtime may still
-// run the 4-byte flag transfers as small kernels, which must find a free CU
-// while the GEMM's workgroups spin.
+// CUs the persistent GEMM leaves free while it may wait for landings.  The CU
+// landing kernel is enqueued first and needs only a few.  On the copy-engine
+// path the runtime runs each 4-byte flag transfer as a small kernel with
+// 1024-thread workgroups, which has to find a CU that no GEMM workgroup holds
+// while those workgroups spin; with fewer than one free CU per shader engine
+// (8 XCDs x 4) that placement stalled now and then until the wait timed out.
 constexpr int kReserveCUsLandCU = 8;
-constexpr int kReserveCUsCopyEngine = 48;
+constexpr int kReserveCUsCopyEngine = 32;
 constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
 }  // namespace
 
@@ -183,6 +185,34 @@ tlc_status check_dense(const char* who, int32_t M, int32_t N, int32_t K, int32_t
   return TLC_OK;
 }
 
+// Work distribution and split-tile workspace of one GEMM launch: checked with
+// the other arguments, applied when the launch parameters are filled in.
+tlc_status check_schedule(int32_t schedule, const void* ws, int64_t ws_bytes, const char* who) {
+  if (schedule != TLC_SCHED_DYNAMIC && schedule != TLC_SCHED_STATIC)
+    return fail(TLC_ERR_INVALID_ARG, "%s: schedule %d unknown", who, schedule);
+  if (ws_bytes < 0 || (ws_bytes > 0 && !ws))
+    return fail(TLC_ERR_INVALID_ARG, "%s: workspace NULL with %lld bytes", who,
+                static_cast<long long>(ws_bytes));
+  if (ws && reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(TLC_ERR_MISALIGNED, "%s: workspace not 256-byte aligned", who);
+  return TLC_OK;
+}
+
+void set_schedule(GemmParams* p, int32_t schedule, void* ws, int64_t ws_bytes) {
+  p->dynamic = schedule == TLC_SCHED_DYNAMIC;
+  p->split_ws = static_cast<char*>(ws);
+  p->split_bytes = ws ? ws_bytes : 0;
+}
+
+// Persistent grid: every CU left free (dynamic: no more workgroups than
+// units), or the evenly spread static default.
+int pick_grid(int requested, int dynamic, int64_t n_units, int avail) {
+  if (requested > 0) return requested;
+  if (avail < 1) avail = 1;
+  if (dynamic) return static_cast<int>(n_units < avail ? (n_units > 0 ? n_units : 1) : avail);
+  return default_grid(n_units, avail);
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,6 +291,8 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   tlc_status st = check_dense("tlc_ag_gemm", a->M, a->N, a->K, a->world, a->rank, a->rows_per_chunk,
                               a->bm, a->bn, a->b_layout, a->plan, a->n_tiles, a->a, a->b, a->c, a->sig);
   if (st) return st;
+  st = check_schedule(a->schedule, a->workspace, a->workspace_bytes, "tlc_ag_gemm");
+  if (st) return st;
   const int64_t chunk_bytes = static_cast<int64_t>(a->rows_per_chunk) * a->K * 2;
   void* dst[TLC_MAX_WORLD];
   for (int c = 0; c < a->world; ++c) dst[c] = static_cast<char*>(a->a) + c * chunk_bytes;
@@ -299,8 +331,9 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   p.epoch = a->epoch;
   p.timeout_ticks = ticks_for(a->timeout_ns, info);
   p.trace = a->trace;
+  set_schedule(&p, a->schedule, a->workspace, a->workspace_bytes);
   const int avail = info.cus - (p.do_wait ? reserve_for(a->land) : 0);
-  int grid = a->grid > 0 ? a->grid : default_grid(a->n_tiles, avail);
+  const int grid = pick_grid(a->grid, p.dynamic, a->n_tiles, avail);
   p.xcd_remap = grid % 8 == 0;
   st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
   return st ? st : ok();
@@ -312,6 +345,8 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
   tlc_status st = check_dense("tlc_gemm_rs", a->M, a->N, a->K, a->world, a->rank, a->rows_per_chunk,
                               a->bm, a->bn, a->b_layout, a->plan, a->n_tiles, a->a, a->b,
                               a->partials, a->sig);
+  if (st) return st;
+  st = check_schedule(a->schedule, a->workspace, a->workspace_bytes, "tlc_gemm_rs");
   if (st) return st;
   if (a->N % 4 != 0) return fail(TLC_ERR_UNSUPPORTED, "tlc_gemm_rs: N %% 4 != 0");
   if (!a->out || !aligned16(a->out)) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: out NULL or misaligned");
@@ -355,8 +390,9 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
     p.sig = a->sig;
     p.epoch = a->epoch;
     p.timeout_ticks = ticks_for(a->timeout_ns, info);
+    set_schedule(&p, a->schedule, a->workspace, a->workspace_bytes);
     // the GEMM does not wait, but the landing running beside it may need CUs
-    int grid = a->grid > 0 ? a->grid : default_grid(a->n_tiles, info.cus - reserve_for(land));
+    const int grid = pick_grid(a->grid, p.dynamic, a->n_tiles, info.cus - reserve_for(land));
     p.xcd_remap = grid % 8 == 0;
     st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
     if (st) return st;
@@ -482,6 +518,7 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
     return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: NULL array");
   if (!aligned16(a->x) || !aligned16(a->w) || !aligned16(a->y))
     return fail(TLC_ERR_MISALIGNED, "tlc_ag_moe: operands must be 16-byte aligned");
+  if (check_schedule(a->schedule, nullptr, 0, "tlc_ag_moe")) return TLC_ERR_INVALID_ARG;
   const int64_t chunk_bytes = static_cast<int64_t>(a->tokens_per_chunk) * a->H * 2;
   void* dst[TLC_MAX_WORLD];
   for (int c = 0; c < a->world; ++c) dst[c] = static_cast<char*>(a->x) + c * chunk_bytes;
@@ -517,6 +554,7 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
   p.sig = a->sig;
   p.epoch = a->epoch;
   p.timeout_ticks = ticks_for(a->timeout_ns, info);
+  set_schedule(&p, a->schedule, nullptr, 0);
   const int avail = info.cus - (p.do_wait ? reserve_for(a->land) : 0);
   // The tile count is only known on the device: use every available CU.
   int grid = a->grid > 0 ? a->grid : (avail >= 8 ? avail / 8 * 8 : avail);
@@ -541,6 +579,6 @@ const char* tlc_status_string(tlc_status s) {
 
 const char* tlc_last_error(void) { return g_err; }
 
-int32_t tlc_version(void) { return 100; }
+int32_t tlc_version(void) { return 110; }
 
 }  // extern "C"

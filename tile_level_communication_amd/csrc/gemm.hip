@@ -1,10 +1,15 @@
 // Persistent, plan-driven bf16 GEMM for gfx950 (MFMA 32x32x16 bf16 -> fp32).
 //
-// A workgroup owns one output tile at a time and walks the tile list in plan
-// order: slot s takes tiles s, s + G, s + 2G, ... where G is the grid size.
-// Slots are spread so that each XCD (8 per MI355X; workgroups are dealt to
-// XCDs round-robin) gets a contiguous run of the plan, keeping the operands
-// that neighbouring tiles share in the same L2.
+// A workgroup owns one work unit at a time -- an output tile, or one K range
+// of a tile split along K -- and walks the unit list in plan order.  With the
+// dynamic schedule it takes the next unit from a counter as soon as it is
+// free; with the static one slot s takes units s, s + G, s + 2G, ... (G = grid
+// size), the slots spread so that each XCD (8 per MI355X; workgroups are dealt
+// to XCDs round-robin) gets a contiguous run of the plan.
+//
+// A unit of a split tile writes its fp32 partial to a workspace slot and counts
+// itself in; the last unit of the tile adds the partials in ascending split
+// index and stores the tile, so results do not depend on the schedule.
 //
 // Before touching a tile's A rows, the workgroup waits until every chunk the
 // tile reads has landed (flag >= epoch), with a bounded spin that reports a
@@ -53,6 +58,79 @@ __device__ inline void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
   }
 }
 
+// K steps [kt0, kt1) of a unit (all KT steps for a whole tile).
+__device__ inline void unit_k_range(uint32_t split, int KT, int* kt0, int* kt1) {
+  const int S = static_cast<int>(split & 0xFFu);
+  if (S < 2) {
+    *kt0 = 0;
+    *kt1 = KT;
+    return;
+  }
+  const int s = static_cast<int>((split >> 8) & 0xFFu);
+  *kt0 = s * KT / S;
+  *kt1 = (s + 1) * KT / S;
+}
+
+// Split-tile epilogue.  Returns true when the caller is to store the tile:
+// always for a whole tile; for a split tile only in the workgroup that counted
+// itself in last, after acc has been replaced by the sum of the S partials in
+// ascending split index.  Partial slots hold each thread's accumulators as
+// float4s, index (block * 4 + quarter) * NT + thread, so that both writes and
+// reads are 16 bytes per lane, consecutive over the workgroup.
+template <int NT, int FM, int FN>
+__device__ inline bool split_epilogue(const GemmParams& p, const tlc_tile& tl,
+                                      f32x16 (&acc)[FM][FN], int* s_flag) {
+  const uint32_t S = tl.split & 0xFFu;
+  if (S < 2) return true;
+  const uint32_t s = (tl.split >> 8) & 0xFFu, f = tl.split >> 16;
+  const int tid = threadIdx.x;
+  constexpr int PER = FM * FN * 4;  // float4s per thread = tile floats / (4 NT)
+  char* block = p.split_ws + static_cast<int64_t>(f) * (256 + static_cast<int64_t>(S) * NT * PER * 16);
+  uint32_t* counter = reinterpret_cast<uint32_t*>(block);
+  float4* slots = reinterpret_cast<float4*>(block + 256);
+  float4* mine = slots + static_cast<int64_t>(s) * NT * PER;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        mine[((i * FN + j) * 4 + q) * NT + tid] =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+  __threadfence();  // the partial is visible device-wide before the count
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == S - 1;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  if (!*s_flag) return false;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t idx = ((i * FN + j) * 4 + q) * NT + tid;
+        float4 v = slots[idx];
+        for (uint32_t u = 1; u < S; ++u) {
+          const float4 w = slots[static_cast<int64_t>(u) * NT * PER + idx];
+          v.x += w.x;
+          v.y += w.y;
+          v.z += w.z;
+          v.w += w.w;
+        }
+        acc[i][j][4 * q] = v.x;
+        acc[i][j][4 * q + 1] = v.y;
+        acc[i][j][4 * q + 2] = v.z;
+        acc[i][j][4 * q + 3] = v.w;
+      }
+  return true;
+}
+
 template <int BM, int BN, int B_NK, int KIND>
 struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2;  // per-wave sub-tile
@@ -64,7 +142,7 @@ struct Tile {
   static_assert(A_PT >= 1 && B_ROWS_PT >= 1, "tile too small");
   static_assert(B_BLOCKS <= THREADS, "one 8x8 block per thread at most");
 
-  __device__ static void run(const GemmParams& p, const tlc_tile& tl, u32x4* lds) {
+  __device__ static void run(const GemmParams& p, const tlc_tile& tl, u32x4* lds, int* s_flag) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -157,13 +235,16 @@ struct Tile {
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    const int KT = p.K / BK;
-    gload(0);
-    swrite(0);
+    int kt0, kt1;
+    unit_k_range(tl.split, p.K / BK, &kt0, &kt1);
+    if (kt0 < kt1) {
+      gload(kt0);
+      swrite(0);
+    }
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) gload(kt + 1);
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int cur = (kt - kt0) & 1;
+      if (kt + 1 < kt1) gload(kt + 1);
       const u32x4* as = As + cur * LDS_A;
       const u32x4* bs = Bs + cur * LDS_B;
 #pragma unroll
@@ -189,9 +270,10 @@ struct Tile {
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < KT) swrite(cur ^ 1);
+      if (kt + 1 < kt1) swrite(cur ^ 1);
       __syncthreads();
     }
+    if (!split_epilogue<THREADS>(p, tl, acc, s_flag)) return;
 
     // ---- epilogue: fp32 tile to C, masked at the tile's edges ----
     float* cbase = p.c + static_cast<int64_t>(tl.m0) * p.ldc + tl.n0;
@@ -240,7 +322,8 @@ struct Tile8w {
   __device__ static int swz(int row) { return (row >> 1) & 7; }
 
   __device__ static void run(const GemmParams& p, const tlc_tile& tl, TLC_LDS u32x4* A0,
-                             TLC_LDS u32x4* A1, TLC_LDS u32x4* B0, TLC_LDS u32x4* B1) {
+                             TLC_LDS u32x4* A1, TLC_LDS u32x4* B0, TLC_LDS u32x4* B1,
+                             int* s_flag) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const uint32_t lda2 = static_cast<uint32_t>(p.lda) * 2, ldb2 = static_cast<uint32_t>(p.ldb) * 2;
@@ -360,19 +443,21 @@ struct Tile8w {
       __syncthreads();
     };
 
-    const int KT = p.K / 64;
-    issue(0, A0, B0);
+    int kt0, kt1;
+    unit_k_range(tl.split, p.K / 64, &kt0, &kt1);
+    if (kt0 < kt1) issue(kt0, A0, B0);
     stage_done();
-    for (int kt = 0; kt < KT; kt += 2) {
-      if (kt + 1 < KT) issue(kt + 1, A1, B1);
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      if (kt + 1 < kt1) issue(kt + 1, A1, B1);
       compute(A0, B0);
       stage_done();
-      if (kt + 1 < KT) {
-        if (kt + 2 < KT) issue(kt + 2, A0, B0);
+      if (kt + 1 < kt1) {
+        if (kt + 2 < kt1) issue(kt + 2, A0, B0);
         compute(A1, B1);
         stage_done();
       }
     }
+    if (!split_epilogue<NT>(p, tl, acc, s_flag)) return;
 
     // ---- epilogue: fp32 to C, one 32-bit lane offset plus per-element
     // constants; edge tiles masked ----
@@ -395,19 +480,41 @@ struct Tile8w {
   }
 };
 
-// Walks the plan: validation, chunk waits, then `run_tile(tile)`.
+// Walks the plan: takes units (dynamic counter or static slots), validates
+// them, waits for their chunks, then `run_tile(unit)`.
+struct LoopShared {
+  int abort;
+  int split_last;
+  int64_t next[2];
+};
+
 template <int BM, int BN, int KIND, int WAIT, typename RunTile>
-__device__ inline void tile_loop(const GemmParams& p, int* s_abort, RunTile run_tile) {
+__device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile run_tile) {
   const int G = gridDim.x;
-  int slot = blockIdx.x;
-  if (p.xcd_remap) slot = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
   const int64_t n_tiles = KIND == KIND_MOE ? static_cast<int64_t>(*p.n_tiles_dev) : p.n_tiles;
   uint32_t seen = p.no_wait_mask;
-  for (int64_t t = slot; t < n_tiles; t += G) {
+  int64_t t;
+  if (p.dynamic) {
+    if (threadIdx.x == 0)
+      sh->next[0] = __hip_atomic_fetch_add(&p.sig->work_next, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    t = sh->next[0];
+  } else {
+    t = p.xcd_remap ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  }
+  for (int it = 1; t < n_tiles; ++it) {
     const tlc_tile tl = p.plan[t];
+    const uint32_t S = tl.split & 0xFFu;
+    const bool bad_split =
+        tl.split != 0 &&
+        (S < 2 || ((tl.split >> 8) & 0xFFu) >= S ||
+         static_cast<int64_t>((tl.split >> 16) + 1) * (256 + static_cast<int64_t>(S) * BM * BN * 4) >
+             p.split_bytes);
     const bool bad = tl.m_rows < 1 || tl.n_cols < 1 || tl.m0 < 0 || tl.n0 < 0 ||
                      tl.m0 + tl.m_rows > p.M || tl.n0 + tl.n_cols > p.N || tl.m_rows > BM ||
-                     tl.n_cols > BN || (tl.n_cols & 7) != 0 || (KIND == KIND_MOE && tl.expert < 0);
+                     tl.n_cols > BN || (tl.n_cols & 7) != 0 || (KIND == KIND_MOE && tl.expert < 0) ||
+                     bad_split;
     if (bad) {
       if (threadIdx.x == 0) report(p.sig, TLC_ERR_BAD_PLAN, t);
       break;
@@ -417,15 +524,18 @@ __device__ inline void tile_loop(const GemmParams& p, int* s_abort, RunTile run_
     if (WAIT) {
       const uint32_t need = tl.chunk_mask & ~seen;
       if (need) {
-        if (threadIdx.x == 0) *s_abort = wait_chunks(p.sig, need, p.epoch, p.timeout_ticks, t);
+        if (threadIdx.x == 0) sh->abort = wait_chunks(p.sig, need, p.epoch, p.timeout_ticks, t);
         __syncthreads();
-        const int abort = *s_abort;
-        if (abort) break;
+        if (sh->abort) break;
         seen |= need;
       }
     }
+    // claim the next unit now: the counter's round trip overlaps this unit
+    if (p.dynamic && threadIdx.x == 0)
+      sh->next[it & 1] = __hip_atomic_fetch_add(&p.sig->work_next, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
     if (p.trace && threadIdx.x == 0) t_wait1 = static_cast<int64_t>(wall_clock64());
-    run_tile(tl);
+    run_tile(tl, &sh->split_last);  // has workgroup barriers: next[] is visible after it
     if (p.trace && threadIdx.x == 0) {
       int64_t* e = p.trace + 4 * t;
       e[0] = blockIdx.x;
@@ -433,24 +543,39 @@ __device__ inline void tile_loop(const GemmParams& p, int* s_abort, RunTile run_
       e[2] = t_wait1;
       e[3] = static_cast<int64_t>(wall_clock64());
     }
+    t = p.dynamic ? sh->next[it & 1] : t + G;
+  }
+  if (p.dynamic) {
+    // the last workgroup out rewinds the counters for the next launch
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->work_done, 1u, __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == static_cast<uint32_t>(G) - 1) {
+        __hip_atomic_store(&p.sig->work_next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.sig->work_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 }
 
 template <int B_NK, int KIND, int WAIT>
 __global__ __launch_bounds__(512) void gemm_kernel_8w(GemmParams p) {
   __shared__ u32x4 A0[2048], A1[2048], B0[2048], B1[2048];
-  __shared__ int s_abort;
-  tile_loop<256, 256, KIND, WAIT>(p, &s_abort, [&](const tlc_tile& tl) {
+  __shared__ LoopShared sh;
+  tile_loop<256, 256, KIND, WAIT>(p, &sh, [&](const tlc_tile& tl, int* s_flag) {
     Tile8w<B_NK, KIND>::run(p, tl, (TLC_LDS u32x4*)A0, (TLC_LDS u32x4*)A1, (TLC_LDS u32x4*)B0,
-                            (TLC_LDS u32x4*)B1);
+                            (TLC_LDS u32x4*)B1, s_flag);
   });
 }
 
 template <int BM, int BN, int B_NK, int KIND, int WAIT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
   __shared__ u32x4 lds[2 * (BM + BN) * 8];
-  __shared__ int s_abort;
-  tile_loop<BM, BN, KIND, WAIT>(p, &s_abort, [&](const tlc_tile& tl) { Tile<BM, BN, B_NK, KIND>::run(p, tl, lds); });
+  __shared__ LoopShared sh;
+  tile_loop<BM, BN, KIND, WAIT>(p, &sh, [&](const tlc_tile& tl, int* s_flag) {
+    Tile<BM, BN, B_NK, KIND>::run(p, tl, lds, s_flag);
+  });
 }
 
 template <int BM, int BN, int B_NK, int KIND, int WAIT>

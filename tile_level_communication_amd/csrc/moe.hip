@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void sort_kernel(MoeDev d) {
         tl.expert = e;
         tl.chunk_mask = d.pair_mask[q];
         tl.key = tid;
-        tl.reserved = 0;
+        tl.split = 0;
         d.plan[out++] = tl;
       }
     }

@@ -10,6 +10,12 @@
 // section on non-perfect tile scheduling.  Inside one key the tiles go band by
 // band (group_m m-tiles wide), column by column, keeping operand reuse close in
 // time (AutoOverlap §5.4 / Fig. 6, intra-chunk swizzle for locality).
+//
+// Tiles whose key is at or past split_from are cut into split_k K ranges that
+// follow each other in the plan.  This is not from the pages: a 256 x 256 tile
+// over K = 5120 is a long unit of work, and the tiles that depend on the last
+// chunk would otherwise run on only as many compute units as that chunk has
+// tiles, after everything else has finished.
 #include <algorithm>
 #include <vector>
 
@@ -55,21 +61,16 @@ extern "C" tlc_status tlc_chunk_plan(const tlc_plan_desc* d, tlc_tile* tiles, in
                 d->world, d->rows_per_chunk);
   if (d->order != TLC_ORDER_NATURAL && d->order != TLC_ORDER_RANK_OFFSET)
     return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: order %d unknown", d->order);
+  if (d->split_k < 0 || d->split_k > 255 || d->split_from < 0)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: split_k %d outside 0..255 or split_from %d < 0",
+                d->split_k, d->split_from);
 
   const int32_t W = d->world, r = d->rank, R = d->rows_per_chunk;
   const int64_t mtiles = (d->M + d->bm - 1) / d->bm;
   const int64_t ntiles = (d->N + d->bn - 1) / d->bn;
-  const int64_t count = mtiles * ntiles;
-  *n_tiles = count;
-  if (landing_order)
-    for (int32_t i = 1; i < W; ++i) landing_order[i - 1] = (r + i) % W;
-  if (!tiles) return tlc::ok();
-  if (cap < count)
-    return fail(TLC_ERR_CAPACITY, "tlc_chunk_plan: capacity %lld < %lld tiles",
-                static_cast<long long>(cap), static_cast<long long>(count));
-
+  const int32_t S = d->split_k >= 2 ? d->split_k : 1;
   std::vector<Keyed> v;
-  v.reserve(static_cast<size_t>(count));
+  v.reserve(static_cast<size_t>(mtiles * ntiles));
   for (int64_t mt = 0; mt < mtiles; ++mt) {
     const int32_t m0 = static_cast<int32_t>(mt * d->bm);
     const int32_t rows = std::min<int32_t>(d->bm, d->M - m0);
@@ -95,11 +96,48 @@ extern "C" tlc_status tlc_chunk_plan(const tlc_plan_desc* d, tlc_tile* tiles, in
       k.tile.expert = -1;
       k.tile.chunk_mask = mask;
       k.tile.key = key;
-      k.tile.reserved = 0;
+      k.tile.split = 0;
       v.push_back(k);
     }
   }
   std::sort(v.begin(), v.end(), key_less);
-  for (size_t i = 0; i < v.size(); ++i) tiles[i] = v[i].tile;
+
+  int64_t count = 0;
+  for (const Keyed& k : v) count += (S > 1 && k.key >= d->split_from) ? S : 1;
+  *n_tiles = count;
+  if (landing_order)
+    for (int32_t i = 1; i < W; ++i) landing_order[i - 1] = (r + i) % W;
+  if (!tiles) return tlc::ok();
+  if (cap < count)
+    return fail(TLC_ERR_CAPACITY, "tlc_chunk_plan: capacity %lld < %lld units",
+                static_cast<long long>(cap), static_cast<long long>(count));
+  int64_t out = 0;
+  uint32_t fix = 0;
+  for (const Keyed& k : v) {
+    if (S > 1 && k.key >= d->split_from) {
+      if (fix > 0xFFFFu)
+        return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: more than 65536 split tiles");
+      for (int32_t u = 0; u < S; ++u) {
+        tiles[out] = k.tile;
+        tiles[out].split = static_cast<uint32_t>(S) | (static_cast<uint32_t>(u) << 8) | (fix << 16);
+        ++out;
+      }
+      ++fix;
+    } else {
+      tiles[out++] = k.tile;
+    }
+  }
   return tlc::ok();
 }
+
+extern "C" int64_t tlc_split_workspace_bytes(int64_t n_split_tiles, int32_t split_k, int32_t bm,
+                                             int32_t bn) {
+  if (n_split_tiles <= 0 || split_k < 2 || bm < 1 || bn < 1) return 0;
+  return n_split_tiles * tlc::split_block_bytes(split_k, bm, bn);
+}
+
+namespace tlc {
+int64_t split_block_bytes(int32_t split_k, int32_t bm, int32_t bn) {
+  return 256 + static_cast<int64_t>(split_k) * bm * bn * 4;
+}
+}  // namespace tlc

@@ -44,7 +44,13 @@ struct GemmParams {
   int64_t timeout_ticks;
   int32_t xcd_remap;
   int64_t* trace;              // optional: n_tiles x {wg, wait start, wait end, done}
+  int32_t dynamic;             // 1: units from the work counter in sig; 0: slot-strided
+  char* split_ws;              // split tiles' blocks: 256-byte counter header + S partials
+  int64_t split_bytes;         // bytes of split_ws
 };
+
+// Bytes of one split tile's workspace block (counter header + split_k partials).
+int64_t split_block_bytes(int32_t split_k, int32_t bm, int32_t bn);
 
 enum GemmKind { KIND_DENSE = 0, KIND_MOE = 1 };
 

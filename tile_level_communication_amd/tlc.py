@@ -23,6 +23,7 @@ MODE_AG, MODE_RS, MODE_MOE = 0, 1, 2
 ORDER_NATURAL, ORDER_RANK_OFFSET = 0, 1
 B_KN, B_NK = 0, 1
 LAND_NONE, LAND_COPY_ENGINE, LAND_CU = 0, 1, 2
+SCHED_DYNAMIC, SCHED_STATIC = 0, 1
 MAX_WORLD = 32
 EPOCH_MAX = 4096
 
@@ -30,7 +31,7 @@ EXPORTS = [
     "tlc_chunk_plan", "tlc_signals_alloc", "tlc_signals_free", "tlc_signals_set",
     "tlc_signals_clear_status", "tlc_read_status", "tlc_ag_gemm", "tlc_gemm_rs", "tlc_rs_reduce",
     "tlc_moe_plan_capacity", "tlc_moe_workspace_bytes", "tlc_moe_route", "tlc_ag_moe", "tlc_land",
-    "tlc_status_string", "tlc_last_error", "tlc_version",
+    "tlc_status_string", "tlc_last_error", "tlc_version", "tlc_split_workspace_bytes",
 ]
 
 
@@ -43,13 +44,14 @@ class TLCError(RuntimeError):
 class Tile(C.Structure):
     _fields_ = [("m0", C.c_int32), ("n0", C.c_int32), ("m_rows", C.c_int32), ("n_cols", C.c_int32),
                 ("expert", C.c_int32), ("chunk_mask", C.c_uint32), ("key", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("split", C.c_uint32)]
 
 
 class PlanDesc(C.Structure):
     _fields_ = [("mode", C.c_int32), ("world", C.c_int32), ("rank", C.c_int32), ("M", C.c_int32),
                 ("N", C.c_int32), ("rows_per_chunk", C.c_int32), ("bm", C.c_int32),
-                ("bn", C.c_int32), ("order", C.c_int32), ("group_m", C.c_int32)]
+                ("bn", C.c_int32), ("order", C.c_int32), ("group_m", C.c_int32),
+                ("split_k", C.c_int32), ("split_from", C.c_int32)]
 
 
 class AGArgs(C.Structure):
@@ -59,7 +61,8 @@ class AGArgs(C.Structure):
                 ("a", C.c_void_p), ("a_src", C.POINTER(C.c_void_p)), ("b", C.c_void_p),
                 ("b_layout", C.c_int32), ("c", C.c_void_p), ("sig", C.c_void_p),
                 ("epoch", C.c_uint32), ("land", C.c_int32), ("grid", C.c_int32),
-                ("timeout_ns", C.c_int64), ("trace", C.c_void_p)]
+                ("timeout_ns", C.c_int64), ("workspace", C.c_void_p),
+                ("workspace_bytes", C.c_int64), ("schedule", C.c_int32), ("trace", C.c_void_p)]
 
 
 class RSArgs(C.Structure):
@@ -70,7 +73,8 @@ class RSArgs(C.Structure):
                 ("partials", C.c_void_p), ("remote_src", C.POINTER(C.c_void_p)),
                 ("landing", C.POINTER(C.c_void_p)), ("out", C.c_void_p), ("sig", C.c_void_p),
                 ("epoch", C.c_uint32), ("land", C.c_int32), ("grid", C.c_int32),
-                ("timeout_ns", C.c_int64)]
+                ("timeout_ns", C.c_int64), ("workspace", C.c_void_p),
+                ("workspace_bytes", C.c_int64), ("schedule", C.c_int32)]
 
 
 class MoERouteArgs(C.Structure):
@@ -91,7 +95,7 @@ class MoEArgs(C.Structure):
                 ("x", C.c_void_p), ("x_src", C.POINTER(C.c_void_p)), ("w", C.c_void_p),
                 ("w_layout", C.c_int32), ("y", C.c_void_p), ("sig", C.c_void_p),
                 ("epoch", C.c_uint32), ("land", C.c_int32), ("grid", C.c_int32),
-                ("timeout_ns", C.c_int64)]
+                ("timeout_ns", C.c_int64), ("schedule", C.c_int32)]
 
 
 _lib = None
@@ -143,6 +147,8 @@ def lib() -> C.CDLL:
         L.tlc_last_error.restype = C.c_char_p
         L.tlc_version.argtypes = []
         L.tlc_version.restype = C.c_int32
+        L.tlc_split_workspace_bytes.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32]
+        L.tlc_split_workspace_bytes.restype = C.c_int64
         _lib = L
     return _lib
 
@@ -201,9 +207,10 @@ def _ptr_array(items, world):
 # ------------------------------------------------------------------ plan ----
 
 def chunk_plan(mode, world, rank, M, N, rows_per_chunk, bm, bn, order=ORDER_RANK_OFFSET,
-               group_m=1):
-    """tlc_chunk_plan.  Returns (tiles: int32 ndarray [n_tiles, 8], landing_order: list)."""
-    d = PlanDesc(mode, world, rank, M, N, rows_per_chunk, bm, bn, order, group_m)
+               group_m=1, split_k=0, split_from=0):
+    """tlc_chunk_plan.  Returns (units: int32 ndarray [n_units, 8], landing_order: list)."""
+    d = PlanDesc(mode, world, rank, M, N, rows_per_chunk, bm, bn, order, group_m, split_k,
+                 split_from)
     n = C.c_int64(0)
     _check(lib().tlc_chunk_plan(C.byref(d), None, 0, C.byref(n), None), "tlc_chunk_plan")
     tiles = (Tile * max(n.value, 1))()
@@ -211,6 +218,16 @@ def chunk_plan(mode, world, rank, M, N, rows_per_chunk, bm, bn, order=ORDER_RANK
     _check(lib().tlc_chunk_plan(C.byref(d), tiles, n.value, C.byref(n), land), "tlc_chunk_plan")
     arr = np.ctypeslib.as_array(C.cast(tiles, C.POINTER(C.c_int32)), shape=(max(n.value, 1), 8))
     return arr[:n.value].copy(), [int(land[i]) for i in range(world - 1)]
+
+
+def split_tiles(plan) -> int:
+    """Number of split tiles in a unit list (units with split index 0 and S >= 2)."""
+    sp = np.asarray(plan)[:, 7].astype(np.int64) & 0xFFFFFFFF
+    return int(np.count_nonzero(((sp & 0xFF) >= 2) & (((sp >> 8) & 0xFF) == 0)))
+
+
+def split_workspace_bytes(n_split_tiles, split_k, bm, bn) -> int:
+    return int(lib().tlc_split_workspace_bytes(n_split_tiles, split_k, bm, bn))
 
 
 # --------------------------------------------------------------- signals ----
@@ -254,31 +271,37 @@ def signals_alloc() -> Signals:
 
 def ag_gemm(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, a_src, b, b_layout, c,
             sig: Signals, epoch, land, compute_stream=None, copy_stream=None, grid=0, timeout_ns=0,
-            trace=None):
+            trace=None, workspace=None, schedule=SCHED_DYNAMIC):
     """tlc_ag_gemm.  a_src: list of `world` device tensors (entry `rank` unused) or None.
-    copy_stream: one stream or a list of streams for the landing."""
+    copy_stream: one stream or a list of streams for the landing.  workspace: a
+    zero-filled device tensor for split plans (or None)."""
     src = _ptr_array(a_src, world) if a_src is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = AGArgs(_ptr(plan), n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, _ptr(a), src,
-                  _ptr(b), b_layout, _ptr(c), sig.ptr, epoch, land, grid, timeout_ns, _ptr(trace))
+                  _ptr(b), b_layout, _ptr(c), sig.ptr, epoch, land, grid, timeout_ns,
+                  _ptr(workspace), ws_bytes, schedule, _ptr(trace))
     cs, n = _streams(copy_stream)
     _check(lib().tlc_ag_gemm(C.byref(args), _stream(compute_stream), cs, n), "tlc_ag_gemm")
 
 
 def _rs_args(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout, partials,
-             remote_src, landing, out, sig, epoch, land, grid, timeout_ns):
+             remote_src, landing, out, sig, epoch, land, grid, timeout_ns, workspace=None,
+             schedule=SCHED_DYNAMIC):
     src = _ptr_array(remote_src, world) if remote_src is not None else None
     lnd = _ptr_array(landing, world) if landing is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return RSArgs(_ptr(plan), n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, _ptr(a),
                   _ptr(b), b_layout, _ptr(partials), src, lnd, _ptr(out), sig.ptr, epoch, land,
-                  grid, timeout_ns)
+                  grid, timeout_ns, _ptr(workspace), ws_bytes, schedule)
 
 
 def gemm_rs(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout, partials,
             remote_src, landing, out, sig: Signals, epoch, land, compute_stream=None,
-            copy_stream=None, grid=0, timeout_ns=0):
+            copy_stream=None, grid=0, timeout_ns=0, workspace=None, schedule=SCHED_DYNAMIC):
     """tlc_gemm_rs.  remote_src, landing: lists of `world` device tensors (entry `rank` unused)."""
     args = _rs_args(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout,
-                    partials, remote_src, landing, out, sig, epoch, land, grid, timeout_ns)
+                    partials, remote_src, landing, out, sig, epoch, land, grid, timeout_ns,
+                    workspace, schedule)
     cs, n = _streams(copy_stream)
     _check(lib().tlc_gemm_rs(C.byref(args), _stream(compute_stream), cs, n), "tlc_gemm_rs")
 
@@ -314,11 +337,11 @@ def moe_route(logits, tokens_per_chunk, world, rank, experts, topk, N, bm, bn, o
 
 def ag_moe(plan, n_tiles_dev, plan_cap, row_token, tokens_per_chunk, world, rank, experts, topk, H,
            N, bm, bn, x, x_src, w, w_layout, y, sig: Signals, epoch, land, compute_stream=None,
-           copy_stream=None, grid=0, timeout_ns=0):
+           copy_stream=None, grid=0, timeout_ns=0, schedule=SCHED_DYNAMIC):
     src = _ptr_array(x_src, world) if x_src is not None else None
     args = MoEArgs(_ptr(plan), _ptr(n_tiles_dev), plan_cap, _ptr(row_token), tokens_per_chunk,
                    world, rank, experts, topk, H, N, bm, bn, _ptr(x), src, _ptr(w), w_layout,
-                   _ptr(y), sig.ptr, epoch, land, grid, timeout_ns)
+                   _ptr(y), sig.ptr, epoch, land, grid, timeout_ns, schedule)
     cs, n = _streams(copy_stream)
     _check(lib().tlc_ag_moe(C.byref(args), _stream(compute_stream), cs, n), "tlc_ag_moe")
 

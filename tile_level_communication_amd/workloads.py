@@ -67,9 +67,19 @@ def next_epoch(prob) -> int:
     return prob.epoch
 
 
+def split_workspace(tiles, split_k, bm, bn, device):
+    """Zero-filled workspace for the plan's split tiles (None if none is split)."""
+    n = tlc.split_tiles(tiles)
+    if n == 0:
+        return None
+    nbytes = tlc.split_workspace_bytes(n, split_k, bm, bn)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 class AGProblem:
     def __init__(self, a_chunks, b_kn, rank, bm=256, bn=256, b_layout=tlc.B_KN,
-                 order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda"):
+                 order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda", split_k=0, split_from=0,
+                 schedule=tlc.SCHED_DYNAMIC):
         self.device = torch.device(device)
         self.world = len(a_chunks)
         self.rank = rank
@@ -83,10 +93,13 @@ class AGProblem:
         self.b = weight_layout(to_bf16(b_kn, self.device), b_layout)
         self.c = torch.empty((self.M, self.N), dtype=torch.float32, device=self.device)
         tiles, self.landing_order = tlc.chunk_plan(tlc.MODE_AG, self.world, rank, self.M, self.N,
-                                                   self.R, bm, bn, order, group_m)
+                                                   self.R, bm, bn, order, group_m, split_k,
+                                                   split_from)
         self.tiles = tiles
         self.plan = torch.from_numpy(tiles).to(self.device)
         self.n_tiles = int(tiles.shape[0])
+        self.workspace = split_workspace(tiles, split_k, bm, bn, self.device)
+        self.schedule = schedule
         self.sig = tlc.Signals()
         self.epoch = 0
         self.streams = Streams(self.device)
@@ -118,7 +131,7 @@ class AGProblem:
         tlc.ag_gemm(self.plan, self.n_tiles, self.M, self.N, self.K, self.world, self.rank, self.R,
                     self.bm, self.bn, self.a, self.a_src if land != tlc.LAND_NONE else None,
                     self.b, self.b_layout, self.c, self.sig, self.epoch, land, s.compute, s.copy,
-                    grid, timeout_ns, trace)
+                    grid, timeout_ns, trace, self.workspace, self.schedule)
         s.end()
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
@@ -133,7 +146,8 @@ class AGProblem:
 
 class RSProblem:
     def __init__(self, a, b_kn, remote: dict, world, rank, bm=256, bn=256, b_layout=tlc.B_KN,
-                 order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda"):
+                 order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda", split_k=0, split_from=0,
+                 schedule=tlc.SCHED_DYNAMIC):
         self.device = torch.device(device)
         self.world, self.rank = world, rank
         self.M, self.K = a.shape
@@ -151,10 +165,12 @@ class RSProblem:
                 self.remote_src[s] = to_f32(remote[s], self.device)
                 self.landing[s] = torch.empty((self.R, self.N), dtype=torch.float32, device=self.device)
         tiles, self.landing_order = tlc.chunk_plan(tlc.MODE_RS, world, rank, self.M, self.N, self.R,
-                                                   bm, bn, order, group_m)
+                                                   bm, bn, order, group_m, split_k, split_from)
         self.tiles = tiles
         self.plan = torch.from_numpy(tiles).to(self.device)
         self.n_tiles = int(tiles.shape[0])
+        self.workspace = split_workspace(tiles, split_k, bm, bn, self.device)
+        self.schedule = schedule
         self.sig = tlc.Signals()
         self.epoch = 0
         self.streams = Streams(self.device)
@@ -188,7 +204,8 @@ class RSProblem:
             self.sig.set(self.world, self.epoch, s.compute)
         s.begin()
         tlc.gemm_rs(*self._args(), self.remote_src if land != tlc.LAND_NONE else None, self.landing,
-                    self.out, self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns)
+                    self.out, self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns,
+                    self.workspace, self.schedule)
         s.end()
 
     def reduce_only(self, timeout_ns=0):
