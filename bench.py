@@ -48,6 +48,11 @@ def parse():
     ap.add_argument("--group-m", type=int, default=4)
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--copy-streams", type=int, default=1)
+    ap.add_argument("--split-k", type=int, default=None,
+                    help="K ranges per split tile (default: 4 for ag, none otherwise)")
+    ap.add_argument("--split-from", type=int, default=None,
+                    help="first key (chunk position) whose tiles are split (default 1)")
+    ap.add_argument("--schedule", default="dynamic", choices=["dynamic", "static"])
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -152,8 +157,14 @@ def run_ag(args, torch, tlc, si, workloads):
     inp = si.workload_inputs(2)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
     land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
+    # fused plan: the last chunk's tiles cut in two along K, so that the tail
+    # after the last landing runs on twice as many compute units
+    split_k = 2 if args.split_k is None else args.split_k
+    split_from = 7 if args.split_from is None else args.split_from
+    schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
     prob = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
-                               group_m=args.group_m, device=dev)
+                               group_m=args.group_m, device=dev, split_k=split_k,
+                               split_from=split_from, schedule=schedule)
     compute = torch.cuda.Stream(device=dev)
     copies = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.copy_streams))]
     prob.streams.compute = compute
@@ -161,61 +172,80 @@ def run_ag(args, torch, tlc, si, workloads):
     flops = prob.flops
     call = dict(plan=prob.plan, n_tiles=prob.n_tiles, M=prob.M, N=prob.N, K=prob.K, world=prob.world,
                 rank=prob.rank, rows_per_chunk=prob.R, bm=args.tile, bn=args.tile, a=prob.a,
-                b=prob.b, b_layout=layout, c=prob.c, sig=prob.sig)
+                b=prob.b, b_layout=layout, c=prob.c, sig=prob.sig, workspace=prob.workspace,
+                schedule=schedule)
     torch.cuda.synchronize()
+
+    def fused_step(land_kind, timer=None):
+        def step():
+            workloads.next_epoch(prob)
+            for c in copies:
+                c.wait_stream(compute)
+            run = lambda: tlc.ag_gemm(**call, a_src=prob.a_src, epoch=prob.epoch, land=land_kind,
+                                      compute_stream=compute, copy_stream=copies, grid=args.grid)
+            timer(run) if timer else run()
+            for c in copies:
+                compute.wait_stream(c)
+        return step
+
     fused_t = KernelTimer(torch, compute)
-
-    def fused():
-        workloads.next_epoch(prob)
-        for c in copies:
-            c.wait_stream(compute)
-        fused_t(lambda: tlc.ag_gemm(**call, a_src=prob.a_src, epoch=prob.epoch, land=land,
-                                    compute_stream=compute, copy_stream=copies, grid=args.grid))
-        for c in copies:
-            compute.wait_stream(c)
-
-    t_fused = timed(fused, args.steps, args.warmup, torch)
+    t_fused = timed(fused_step(land, fused_t), args.steps, args.warmup, torch)
     gemm_fused_ms = fused_t.mean_ms(args.warmup)
+    status = prob.sig.read_status(compute)
 
-    # compute-only: every chunk in place, no flag checks (land NONE, epoch 0)
-    prob.place_all()
+    # the same step with the other landing backend (reported beside the headline)
+    other = tlc.LAND_CU if land == tlc.LAND_COPY_ENGINE else tlc.LAND_COPY_ENGINE
+    t_fused_other = timed(fused_step(other), args.steps, args.warmup, torch)
+    status_other = prob.sig.read_status(compute)
+
+    def copy_only_step(land_kind):
+        dst = [prob.a[c * prob.R:(c + 1) * prob.R] for c in range(prob.world)]
+
+        def step():
+            workloads.next_epoch(prob)
+            for c in copies:
+                c.wait_stream(compute)
+            tlc.land(dst, prob.a_src, prob.R * prob.K * 2, prob.world, prob.rank, prob.sig,
+                     prob.epoch, land_kind, copies)
+            for c in copies:
+                compute.wait_stream(c)
+        return step
+
+    t_copy = timed(copy_only_step(land), args.steps, args.warmup, torch)
+    t_copy_other = timed(copy_only_step(other), args.steps, args.warmup, torch)
+
+    # compute-only: the GEMM alone, every chunk in place, no flag checks (land
+    # NONE, epoch 0), whole tiles, static schedule -- its fastest configuration
+    comp = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
+                               group_m=args.group_m, device=dev, schedule=tlc.SCHED_STATIC)
+    comp.place_all()
+    comp.c = prob.c
     torch.cuda.synchronize()
     comp_t = KernelTimer(torch, compute)
+    ccall = dict(call, plan=comp.plan, n_tiles=comp.n_tiles, a=comp.a, sig=comp.sig, workspace=None,
+                 schedule=tlc.SCHED_STATIC)
 
     def compute_only():
-        comp_t(lambda: tlc.ag_gemm(**call, a_src=None, epoch=0, land=tlc.LAND_NONE,
-                                   compute_stream=compute, copy_stream=None, grid=args.grid))
+        comp_t(lambda: tlc.ag_gemm(**ccall, a_src=None, epoch=0, land=tlc.LAND_NONE,
+                                   compute_stream=compute, copy_stream=None, grid=0))
 
     t_comp = timed(compute_only, args.steps, args.warmup, torch)
     gemm_comp_ms = comp_t.mean_ms(args.warmup)
-
-    # copy-only: the same landing sequence, no GEMM
-    dst = [prob.a[c * prob.R:(c + 1) * prob.R] for c in range(prob.world)]
-
-    def copy_only():
-        workloads.next_epoch(prob)
-        for c in copies:
-            c.wait_stream(compute)
-        tlc.land(dst, prob.a_src, prob.R * prob.K * 2, prob.world, prob.rank, prob.sig, prob.epoch,
-                 land, copies)
-        for c in copies:
-            compute.wait_stream(c)
-
-    t_copy = timed(copy_only, args.steps, args.warmup, torch)
     torch.cuda.synchronize()
-    fused()
-    status = prob.sig.read_status(compute)
     achieved = flops / (gemm_comp_ms * 1e-3) / 1e12
+    names = {tlc.LAND_COPY_ENGINE: "copy_engine", tlc.LAND_CU: "cu"}
     extra = {
         "config": {"workload": wl.name, "M": prob.M, "N": prob.N, "K": prob.K, "world": prob.world,
                    "rank": prob.rank, "tile": [args.tile, args.tile, 64], "b_layout": args.layout,
                    "landing": args.land, "copy_streams": len(copies), "group_m": args.group_m,
-                   "n_tiles": prob.n_tiles,
+                   "n_units": prob.n_tiles, "split_k": split_k, "split_from": split_from,
+                   "schedule": args.schedule,
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None,
-                     "kernel": "gemm_kernel_8w<KN,dense,no-wait> (every chunk resident)"},
+                     "kernel": "gemm_kernel_8w<KN,dense,no-wait>: compute-only launch, whole tiles, "
+                               "static schedule, every chunk resident"},
         "pct_peak": round(100 * flops / t_fused / 1e12 / PEAK_BF16_TFLOPS, 2),
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
@@ -224,6 +254,11 @@ def run_ag(args, torch, tlc, si, workloads):
         "copy_gbs": round((prob.world - 1) * prob.R * prob.K * 2 / t_copy / 1e9, 1),
         "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,
+        "other_landing": {"landing": names[other], "value": round(flops / t_fused_other / 1e12, 2),
+                          "ms_per_step": round(t_fused_other * 1e3, 4),
+                          "copy_only_ms": round(t_copy_other * 1e3, 4),
+                          "overlap_efficiency": round(max(t_comp, t_copy_other) / t_fused_other, 4),
+                          "device_status": status_other},
     }
     line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
     if not args.no_cpu_baseline:
@@ -237,8 +272,13 @@ def run_rs(args, torch, tlc, si, workloads, wid):
     inp = si.workload_inputs(wid, rank=args.rank)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
     land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
+    split_k = 0 if args.split_k is None else args.split_k
+    split_from = 1 if args.split_from is None else args.split_from
+    schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
     prob = workloads.RSProblem(inp.a, inp.b, inp.remote, wl.world, args.rank, args.tile, args.tile,
-                               layout, group_m=args.group_m, device=dev)
+                               layout, group_m=args.group_m, device=dev, split_k=split_k,
+                               split_from=split_from, schedule=schedule)
+    ws = dict(workspace=prob.workspace, schedule=schedule)
     compute = torch.cuda.Stream(device=dev)
     copies = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.copy_streams))]
     prob.streams.compute = compute
@@ -252,7 +292,7 @@ def run_rs(args, torch, tlc, si, workloads, wid):
         for c in copies:
             c.wait_stream(compute)
         tlc.gemm_rs(*prob._args(), prob.remote_src, prob.landing, prob.out, prob.sig, prob.epoch,
-                    land, compute, copies, args.grid)
+                    land, compute, copies, args.grid, **ws)
         for c in copies:
             compute.wait_stream(c)
 
@@ -264,7 +304,7 @@ def run_rs(args, torch, tlc, si, workloads, wid):
 
     def compute_only():
         comp_t(lambda: tlc.gemm_rs(*prob._args(), None, prob.landing, prob.out, prob.sig,
-                                   tlc.EPOCH_MAX, tlc.LAND_NONE, compute, None, args.grid))
+                                   tlc.EPOCH_MAX, tlc.LAND_NONE, compute, None, args.grid, **ws))
 
     t_comp = timed(compute_only, steps, warm, torch)
     red_t = KernelTimer(torch, compute)
@@ -294,7 +334,8 @@ def run_rs(args, torch, tlc, si, workloads, wid):
     extra = {
         "config": {"workload": wl.name, "M": prob.M, "N": prob.N, "K": prob.K, "world": prob.world,
                    "rank": prob.rank, "tile": [args.tile, args.tile, 64], "b_layout": args.layout,
-                   "landing": args.land, "copy_streams": len(copies), "n_tiles": prob.n_tiles,
+                   "landing": args.land, "copy_streams": len(copies), "n_units": prob.n_tiles,
+                   "split_k": split_k, "split_from": split_from, "schedule": args.schedule,
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
@@ -340,7 +381,8 @@ def run_moe(args, torch, tlc, si, workloads):
         prob.route()
         tlc.ag_moe(prob.plan, prob.n_tiles_dev, prob.plan_cap, prob.row_token, prob.Tc, prob.world,
                    prob.rank, prob.E, prob.k, prob.H, prob.N, prob.bm, prob.bn, prob.x, None, prob.w,
-                   prob.b_layout, prob.y, prob.sig, 0, tlc.LAND_NONE, compute, None, args.grid)
+                   prob.b_layout, prob.y, prob.sig, 0, tlc.LAND_NONE, compute, None, args.grid,
+                   schedule=tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC)
 
     t_comp = timed(compute_only, args.steps, args.warmup, torch)
     torch.cuda.synchronize()

@@ -16,13 +16,14 @@ thread_local char g_err[512] = "";
 std::mutex g_info_mu;
 DeviceInfo g_info[64];
 bool g_info_ok[64] = {};
-// CUs the persistent GEMM leaves free while it may wait for landings.  The CU
-// landing kernel is enqueued first and needs only a few.  On the copy-engine
-// path the runtime runs each 4-byte flag transfer as a small kernel with
-// 1024-thread workgroups, which has to find a CU that no GEMM workgroup holds
-// while those workgroups spin; with fewer than one free CU per shader engine
-// (8 XCDs x 4) that placement stalled now and then until the wait timed out.
-constexpr int kReserveCUsLandCU = 8;
+// CUs the persistent GEMM leaves free while it may wait for landings.  The
+// landing's kernels -- the CU copy kernel, or on the copy-engine path the
+// runtime's kernel for each 4-byte flag transfer (1024-thread workgroups) --
+// have to find CUs that no GEMM workgroup holds while those workgroups spin
+// (a GEMM workgroup takes all the registers of its CU).  With fewer than one
+// free CU per shader engine (8 XCDs x 4) their placement stalled now and then
+// until the wait timed out, even when the landing kernel was dispatched first.
+constexpr int kReserveCUsLandCU = 32;
 constexpr int kReserveCUsCopyEngine = 32;
 constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
 }  // namespace
@@ -131,9 +132,10 @@ tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, i
   p.vec_per_chunk = bytes / 16;
   p.sig = sig;
   p.epoch = epoch;
-  // a few workgroups: each one holds a CU's wave slots that a GEMM workgroup
-  // (two waves per SIMD at 256 registers) could otherwise use
-  const int grid = 32;
+  // one 1024-thread workgroup per CU the GEMM leaves free (a CU that holds a
+  // landing workgroup cannot also hold a GEMM workgroup: those take all of a
+  // CU's registers)
+  const int grid = kReserveCUsLandCU;
   return launch_land_cu(p, grid, copy_streams[0]);
 }
 

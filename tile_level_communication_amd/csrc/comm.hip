@@ -44,18 +44,44 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
   }
 }
 
-__global__ __launch_bounds__(256) void land_kernel(LandParams p) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+// Each workgroup copies blocks of LAND_THREADS * LAND_UNROLL 16-byte units of a
+// chunk: every thread first loads LAND_UNROLL units (consecutive threads read
+// consecutive units), then stores them, so each CU keeps 128 KB of reads in
+// flight.  The source is read once (non-temporal loads); the destination is
+// stored normally, since the GEMM reads it next.
+constexpr int LAND_THREADS = 1024;
+constexpr int LAND_UNROLL = 8;
+typedef unsigned int land_vec __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(LAND_THREADS) void land_kernel(LandParams p) {
+  const int64_t block = static_cast<int64_t>(LAND_THREADS) * LAND_UNROLL;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * block;
   for (int i = 0; i < p.n_chunks; ++i) {
     const int c = p.order[i];
-    const uint4* src = p.src[c];
-    uint4* dst = p.dst[c];
-    for (int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-         v < p.vec_per_chunk; v += stride)
-      dst[v] = src[v];
-    __threadfence();
+    const land_vec* src = reinterpret_cast<const land_vec*>(p.src[c]);
+    land_vec* dst = reinterpret_cast<land_vec*>(p.dst[c]);
+    const int64_t n = p.vec_per_chunk;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * block + threadIdx.x; base < n;
+         base += stride) {
+      land_vec v[LAND_UNROLL];
+#pragma unroll
+      for (int u = 0; u < LAND_UNROLL; ++u) {
+        const int64_t k = base + static_cast<int64_t>(u) * LAND_THREADS;
+        if (k < n) v[u] = __builtin_nontemporal_load(src + k);
+      }
+#pragma unroll
+      for (int u = 0; u < LAND_UNROLL; ++u) {
+        const int64_t k = base + static_cast<int64_t>(u) * LAND_THREADS;
+        if (k < n) dst[k] = v[u];
+      }
+    }
+    // every wave's stores have reached the cache; one thread then releases
+    // them device-wide (a release writes back the whole L2 once, instead of
+    // once per wave) and counts the workgroup in
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
+      __atomic_thread_fence(__ATOMIC_RELEASE);
       const uint32_t prev = __hip_atomic_fetch_add(&p.sig->land_count[c], 1u, __ATOMIC_ACQ_REL,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (prev == gridDim.x - 1) {
@@ -90,7 +116,7 @@ tlc_status launch_reduce(const ReduceParams& p, int grid, void* stream) {
 }
 
 tlc_status launch_land_cu(const LandParams& p, int grid, void* stream) {
-  hipLaunchKernelGGL(land_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), p);
+  hipLaunchKernelGGL(land_kernel, dim3(grid), dim3(LAND_THREADS), 0, static_cast<hipStream_t>(stream), p);
   return check_launch("land");
 }
 

@@ -74,33 +74,43 @@ __device__ inline void unit_k_range(uint32_t split, int KT, int* kt0, int* kt1) 
 // Split-tile epilogue.  Returns true when the caller is to store the tile:
 // always for a whole tile; for a split tile only in the workgroup that counted
 // itself in last, after acc has been replaced by the sum of the S partials in
-// ascending split index.  Partial slots hold each thread's accumulators as
-// float4s, index (block * 4 + quarter) * NT + thread, so that both writes and
-// reads are 16 bytes per lane, consecutive over the workgroup.
+// ascending split index.  Partial slots hold each thread's accumulators at
+// index (element * NT + thread), so every store and load instruction of a
+// wavefront covers 256 consecutive bytes.
+//
+// The units of one tile may run on different XCDs, whose L2 caches are not
+// coherent with each other.  Partials are therefore written and read with
+// device-scope atomic stores and loads, which the hardware keeps coherent
+// across XCDs without a full L2 write-back, and each wave waits for its stores
+// to complete before the workgroup counts itself in.
 template <int NT, int FM, int FN>
 __device__ inline bool split_epilogue(const GemmParams& p, const tlc_tile& tl,
                                       f32x16 (&acc)[FM][FN], int* s_flag) {
   const uint32_t S = tl.split & 0xFFu;
   if (S < 2) return true;
   const uint32_t s = (tl.split >> 8) & 0xFFu, f = tl.split >> 16;
-  const int tid = threadIdx.x;
-  constexpr int PER = FM * FN * 4;  // float4s per thread = tile floats / (4 NT)
-  char* block = p.split_ws + static_cast<int64_t>(f) * (256 + static_cast<int64_t>(S) * NT * PER * 16);
+  // an opaque copy of the thread index: keeps the compiler from computing the
+  // partial-slot addresses before the K loop and holding them across it
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  constexpr int PER = FM * FN * 16;  // floats per thread = tile floats / NT
+  static_assert((FM * FN) % 2 == 0, "blocks are summed in pairs");
+  char* block = p.split_ws + static_cast<int64_t>(f) * (256 + static_cast<int64_t>(S) * NT * PER * 4);
   uint32_t* counter = reinterpret_cast<uint32_t*>(block);
-  float4* slots = reinterpret_cast<float4*>(block + 256);
-  float4* mine = slots + static_cast<int64_t>(s) * NT * PER;
+  float* slots = reinterpret_cast<float*>(block + 256);
+  float* mine = slots + static_cast<int64_t>(s) * NT * PER + tid;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        mine[((i * FN + j) * 4 + q) * NT + tid] =
-            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-  __threadfence();  // the partial is visible device-wide before the count
+      for (int e = 0; e < 16; ++e)
+        __hip_atomic_store(mine + ((i * FN + j) * 16 + e) * NT, acc[i][j][e], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial has landed
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL,
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == S - 1;
     if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -108,26 +118,34 @@ __device__ inline bool split_epilogue(const GemmParams& p, const tlc_tile& tl,
   }
   __syncthreads();
   if (!*s_flag) return false;
+  // Sum in ascending split index, two 32 x 32 blocks (32 values per thread)
+  // per batch of independent loads, so that each batch costs one round trip.
+  const float* all = slots + tid;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int b = 0; b < FM * FN; b += 2) {
+    f32x16& x0 = acc[b / FN][b % FN];
+    f32x16& x1 = acc[(b + 1) / FN][(b + 1) % FN];
+    const float* p0 = all + static_cast<int64_t>(b) * 16 * NT;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int e = 0; e < 16; ++e) {
+      x0[e] = __hip_atomic_load(p0 + e * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      x1[e] = __hip_atomic_load(p0 + (16 + e) * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (uint32_t u = 1; u < S; ++u) {
+      const float* pu = p0 + static_cast<int64_t>(u) * NT * PER;
+      float t0[16], t1[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t idx = ((i * FN + j) * 4 + q) * NT + tid;
-        float4 v = slots[idx];
-        for (uint32_t u = 1; u < S; ++u) {
-          const float4 w = slots[static_cast<int64_t>(u) * NT * PER + idx];
-          v.x += w.x;
-          v.y += w.y;
-          v.z += w.z;
-          v.w += w.w;
-        }
-        acc[i][j][4 * q] = v.x;
-        acc[i][j][4 * q + 1] = v.y;
-        acc[i][j][4 * q + 2] = v.z;
-        acc[i][j][4 * q + 3] = v.w;
+      for (int e = 0; e < 16; ++e) {
+        t0[e] = __hip_atomic_load(pu + e * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t1[e] = __hip_atomic_load(pu + (16 + e) * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x0[e] += t0[e];
+        x1[e] += t1[e];
+      }
+    }
+  }
   return true;
 }
 
