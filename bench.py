@@ -52,7 +52,8 @@ def parse():
                     help="K ranges per split tile (default: 4 for ag, none otherwise)")
     ap.add_argument("--split-from", type=int, default=None,
                     help="first key (chunk position) whose tiles are split (default 1)")
-    ap.add_argument("--schedule", default="dynamic", choices=["dynamic", "static"])
+    ap.add_argument("--schedule", default=None, choices=["dynamic", "static"],
+                    help="work distribution (default: dynamic for ag and moe, static for rs)")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -161,6 +162,7 @@ def run_ag(args, torch, tlc, si, workloads):
     # after the last landing runs on twice as many compute units
     split_k = 2 if args.split_k is None else args.split_k
     split_from = 7 if args.split_from is None else args.split_from
+    args.schedule = args.schedule or "dynamic"
     schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
     prob = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
                                group_m=args.group_m, device=dev, split_k=split_k,
@@ -274,6 +276,7 @@ def run_rs(args, torch, tlc, si, workloads, wid):
     land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
     split_k = 0 if args.split_k is None else args.split_k
     split_from = 1 if args.split_from is None else args.split_from
+    args.schedule = args.schedule or "static"
     schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
     prob = workloads.RSProblem(inp.a, inp.b, inp.remote, wl.world, args.rank, args.tile, args.tile,
                                layout, group_m=args.group_m, device=dev, split_k=split_k,
@@ -361,6 +364,7 @@ def run_moe(args, torch, tlc, si, workloads):
     inp = si.workload_inputs(4)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
     land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
+    schedule = tlc.SCHED_STATIC if args.schedule == "static" else tlc.SCHED_DYNAMIC
     prob = workloads.MoEProblem(inp.x_chunks, inp.logits, inp.w, args.rank, wl.topk, args.tile,
                                 args.tile, layout, device=dev)
     compute = torch.cuda.Stream(device=dev)
@@ -370,30 +374,45 @@ def run_moe(args, torch, tlc, si, workloads):
     flops = prob.flops
     torch.cuda.synchronize()
 
-    def fused():
-        prob.run(land, grid=args.grid)
+    # fused step: routing on the compute stream while the peers' tokens land,
+    # then the readiness-sorted grouped GEMM consuming chunks as they arrive
+    t_fused = timed(lambda: prob.run(land, grid=args.grid), args.steps, args.warmup, torch)
+    status = prob.sig.read_status(compute)
 
-    t_fused = timed(fused, args.steps, args.warmup, torch)
+    t_copy = timed(lambda: prob.land_only(land), args.steps, args.warmup, torch)
+
     prob.place_all()
     torch.cuda.synchronize()
+    route_t = KernelTimer(torch, compute)
+    gemm_t = KernelTimer(torch, compute)
 
     def compute_only():
-        prob.route()
-        tlc.ag_moe(prob.plan, prob.n_tiles_dev, prob.plan_cap, prob.row_token, prob.Tc, prob.world,
-                   prob.rank, prob.E, prob.k, prob.H, prob.N, prob.bm, prob.bn, prob.x, None, prob.w,
-                   prob.b_layout, prob.y, prob.sig, 0, tlc.LAND_NONE, compute, None, args.grid,
-                   schedule=tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC)
+        route_t(prob.route)
+        gemm_t(lambda: tlc.ag_moe(prob.plan, prob.n_tiles_dev, prob.plan_cap, prob.row_token, prob.Tc,
+                                  prob.world, prob.rank, prob.E, prob.k, prob.H, prob.N, prob.bm,
+                                  prob.bn, prob.x, None, prob.w, prob.b_layout, prob.y, prob.sig, 0,
+                                  tlc.LAND_NONE, compute, None, args.grid, schedule=schedule))
 
     t_comp = timed(compute_only, args.steps, args.warmup, torch)
     torch.cuda.synchronize()
-    status = prob.sig.read_status(compute)
+    gemm_ms = gemm_t.mean_ms(args.warmup)
+    route_ms = route_t.mean_ms(args.warmup)
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
     extra = {
         "config": {"workload": wl.name, "tokens": prob.T, "experts": prob.E, "topk": prob.k,
                    "H": prob.H, "N": prob.N, "world": prob.world, "rank": prob.rank,
-                   "landing": args.land, "n_tiles": int(prob.n_tiles_dev.item()),
+                   "landing": args.land, "tile": [args.tile, args.tile, 64],
+                   "n_tiles": int(prob.n_tiles_dev.item()), "schedule": args.schedule or "dynamic",
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "gemm_kernel_8w<KN,moe,no-wait>: grouped GEMM, every chunk resident"},
+        "route_ms": round(route_ms, 4),
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
+        "copy_only_ms": round(t_copy * 1e3, 4),
+        "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,
     }
     return base_line(args, flops / t_fused / 1e12, t_fused, extra)

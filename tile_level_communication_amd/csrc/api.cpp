@@ -436,7 +436,8 @@ int64_t tlc_moe_workspace_bytes(int32_t T, int32_t topk, int32_t experts, int32_
   if (T < 1 || topk < 1 || experts < 1 || bm < 1) return 0;
   const int64_t pairs = moe_max_pairs(T, topk, experts, bm);
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  return up(static_cast<int64_t>(T) * 8) + up((experts + 1) * 4LL) + up(pairs * 4) + up(pairs * 4);
+  return up(static_cast<int64_t>(T) * 8) + up((experts + 1) * 4LL) + up(pairs * 4) + up(pairs * 4) +
+         up((T + 63) / 64 * static_cast<int64_t>(experts) * 4);
 }
 
 tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
@@ -494,6 +495,8 @@ tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
   d.pair_key = reinterpret_cast<int32_t*>(ws);
   ws += up(d.max_pairs * 4LL);
   d.pair_mask = reinterpret_cast<uint32_t*>(ws);
+  ws += up(d.max_pairs * 4LL);
+  d.blk = reinterpret_cast<int32_t*>(ws);
   DeviceInfo info;
   tlc_status st = device_info(&info);
   if (st) return st;

@@ -511,16 +511,10 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
   const int G = gridDim.x;
   const int64_t n_tiles = KIND == KIND_MOE ? static_cast<int64_t>(*p.n_tiles_dev) : p.n_tiles;
   uint32_t seen = p.no_wait_mask;
-  int64_t t;
-  if (p.dynamic) {
-    if (threadIdx.x == 0)
-      sh->next[0] = __hip_atomic_fetch_add(&p.sig->work_next, 1u, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    t = sh->next[0];
-  } else {
-    t = p.xcd_remap ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  }
+  // The first unit of every workgroup is its slot (no counter traffic while all
+  // workgroups start at once); the dynamic schedule then hands out units
+  // G, G+1, ... from the counter as workgroups become free.
+  int64_t t = p.xcd_remap ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   for (int it = 1; t < n_tiles; ++it) {
     const tlc_tile tl = p.plan[t];
     const uint32_t S = tl.split & 0xFFu;
@@ -550,8 +544,8 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
     }
     // claim the next unit now: the counter's round trip overlaps this unit
     if (p.dynamic && threadIdx.x == 0)
-      sh->next[it & 1] = __hip_atomic_fetch_add(&p.sig->work_next, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+      sh->next[it & 1] = G + static_cast<int64_t>(__hip_atomic_fetch_add(
+                                 &p.sig->work_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     if (p.trace && threadIdx.x == 0) t_wait1 = static_cast<int64_t>(wall_clock64());
     run_tile(tl, &sh->split_last);  // has workgroup barriers: next[] is visible after it
     if (p.trace && threadIdx.x == 0) {
@@ -564,10 +558,14 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
     t = p.dynamic ? sh->next[it & 1] : t + G;
   }
   if (p.dynamic) {
-    // the last workgroup out rewinds the counters for the next launch
+    // the last workgroup out rewinds the counters for the next launch.  Relaxed
+    // order suffices: each workgroup's last claim has returned before it counts
+    // itself out, and the next launch sees the rewound values at the kernel
+    // boundary.  (An acquire-release here would write back the L2 once per
+    // workgroup.)
     __syncthreads();
     if (threadIdx.x == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->work_done, 1u, __ATOMIC_ACQ_REL,
+      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->work_done, 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (prev == static_cast<uint32_t>(G) - 1) {
         __hip_atomic_store(&p.sig->work_next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

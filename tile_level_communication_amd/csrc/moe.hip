@@ -8,16 +8,24 @@
 // Everything here is integer or order-only work except the gate softmax; it is
 // deterministic: no atomics whose order could change a result.
 //
-//   topk_kernel   one wavefront per token, one expert per lane (E <= 64):
-//                 k rounds of a butterfly arg-max (ties -> lower expert),
-//                 softmax over the k winners, a 64-bit membership mask.
-//   count_kernel  one wavefront per expert: ballots over the membership masks.
-//   list_kernel   one wavefront per expert: offsets, then the expert's rows in
-//                 (p(chunk), token) order via ballot prefix counts; slot[t][j].
-//   pair_kernel   one wavefront per (expert, m-tile): readiness key and chunk
-//                 mask over the tile's rows.
-//   sort_kernel   one workgroup: stable counting sort of the (expert, m-tile)
-//                 pairs by key, expanded over the n-tiles.
+// Tokens are visited in arrival order: the local chunk first, then rank+1,
+// rank+2, ... (position a = p(c) * Tc + token offset), in blocks of 64.
+//
+//   topk_kernel     one wavefront per token, one expert per lane (E <= 64):
+//                   k rounds of a butterfly arg-max (ties -> lower expert),
+//                   softmax over the k winners, a 64-bit membership mask.
+//   block_count     one wavefront per block of 64 arrival positions: for each
+//                   expert, how many of the block's tokens chose it.
+//   scan_kernel     one wavefront: per expert, the prefix of those counts over
+//                   the blocks; counts, offsets and m-tile starts over experts.
+//   scatter_kernel  one wavefront per block: each (token, expert) pair's row =
+//                   offsets[e] + rows of e in earlier blocks + earlier lanes of
+//                   this block; row_token and slot.
+//   pair_kernel     one wavefront per (expert, m-tile): readiness key and chunk
+//                   mask over the tile's rows.
+//   sort_kernel     one workgroup: stable counting sort of the (expert, m-tile)
+//                   pairs by key (ballot ranks per wavefront, carried over
+//                   batches of pairs), expanded over the n-tiles.
 #include <hip/hip_runtime.h>
 
 #include "tlc_internal.h"
@@ -78,48 +86,87 @@ __global__ __launch_bounds__(256) void topk_kernel(MoeDev d) {
   }
 }
 
-__global__ __launch_bounds__(64) void count_kernel(MoeDev d) {
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x;
-  int total = 0;
-  for (int base = 0; base < d.T; base += 64) {
-    const int t = base + lane;
-    const bool in = t < d.T && ((d.member[t] >> e) & 1ull);
-    total += __popcll(__ballot(in));
-  }
-  if (lane == 0) d.counts[e] = total;
+// Token at arrival position a (0 <= a < T).
+__device__ inline int arrival_token(const MoeDev& d, int a) {
+  const int pos = a / d.Tc;
+  const int c = (d.rank + pos) % d.world;
+  return c * d.Tc + (a - pos * d.Tc);
 }
 
-__global__ __launch_bounds__(64) void list_kernel(MoeDev d) {
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x;
-  int off = 0, pst = 0;
-  for (int i = 0; i < e; ++i) {
-    off += d.counts[i];
-    pst += (d.counts[i] + d.bm - 1) / d.bm;
+__global__ __launch_bounds__(64) void block_count_kernel(MoeDev d) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int a = b * 64 + lane;
+  const unsigned long long m = a < d.T ? d.member[arrival_token(d, a)] : 0ull;
+  int mine = 0;
+  for (int e = 0; e < d.E; ++e) {
+    const int n = __popcll(__ballot((m >> e) & 1ull));
+    if (lane == e) mine = n;
   }
-  if (lane == 0) {
-    d.offsets[e] = off;
-    d.pstart[e] = pst;
-    if (e == d.E - 1) {
-      d.offsets[d.E] = off + d.counts[e];
-      d.pstart[d.E] = pst + (d.counts[e] + d.bm - 1) / d.bm;
+  if (lane < d.E) d.blk[static_cast<int64_t>(b) * d.E + lane] = mine;
+}
+
+__global__ __launch_bounds__(64) void scan_kernel(MoeDev d) {
+  const int e = threadIdx.x;
+  const int NB = (d.T + 63) / 64;
+  int run = 0;
+  // per expert (lane), exclusive prefix of the block counts, 16 blocks per batch
+  for (int b0 = 0; b0 < NB; b0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      v[i] = (e < d.E && b0 + i < NB) ? d.blk[static_cast<int64_t>(b0 + i) * d.E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (e < d.E && b0 + i < NB) d.blk[static_cast<int64_t>(b0 + i) * d.E + e] = run;
+      run += v[i];
     }
   }
-  int row = off;
-  for (int pos = 0; pos < d.world; ++pos) {
-    const int c = (d.rank + pos) % d.world;
-    for (int base = c * d.Tc; base < (c + 1) * d.Tc; base += 64) {
-      const int t = base + lane;
-      const bool in = t < (c + 1) * d.Tc && ((d.member[t] >> e) & 1ull);
-      const unsigned long long bal = __ballot(in);
-      if (in) {
-        const int r = row + __popcll(bal & ((1ull << lane) - 1ull));
-        d.row_token[r] = t;
-        for (int j = 0; j < d.k; ++j)
-          if (d.topk[static_cast<int64_t>(t) * d.k + j] == e) d.slot[static_cast<int64_t>(t) * d.k + j] = r;
-      }
-      row += __popcll(bal);
+  const int cnt = e < d.E ? run : 0;
+  const int tiles = (cnt + d.bm - 1) / d.bm;
+  // exclusive scans over the experts (lanes)
+  int off = cnt, pst = tiles;
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    const int o = __shfl_up(off, sh), q = __shfl_up(pst, sh);
+    if (e >= sh) {
+      off += o;
+      pst += q;
+    }
+  }
+  if (e < d.E) {
+    d.counts[e] = cnt;
+    d.offsets[e] = off - cnt;
+    d.pstart[e] = pst - tiles;
+    if (e == d.E - 1) {
+      d.offsets[d.E] = off;
+      d.pstart[d.E] = pst;
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void scatter_kernel(MoeDev d) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int a = b * 64 + lane;
+  const bool valid = a < d.T;
+  const int t = valid ? arrival_token(d, a) : 0;
+  const unsigned long long m = valid ? d.member[t] : 0ull;
+  // lane e holds the first row of expert e for this block
+  const int base = lane < d.E ? d.offsets[lane] + d.blk[static_cast<int64_t>(b) * d.E + lane] : 0;
+  int sel[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    sel[j] = (valid && j < d.k) ? d.topk[static_cast<int64_t>(t) * d.k + j] : -1;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int e = 0; e < d.E; ++e) {
+    const bool in = (m >> e) & 1ull;
+    const unsigned long long bal = __ballot(in);
+    const int first = __shfl(base, e);
+    if (in) {
+      const int r = first + __popcll(bal & below);
+      d.row_token[r] = t;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (sel[j] == e) d.slot[static_cast<int64_t>(t) * d.k + j] = r;
     }
   }
 }
@@ -156,32 +203,49 @@ __global__ __launch_bounds__(256) void pair_kernel(MoeDev d) {
   }
 }
 
-__global__ __launch_bounds__(256) void sort_kernel(MoeDev d) {
+__global__ __launch_bounds__(1024) void sort_kernel(MoeDev d) {
+  constexpr int NW = 16;  // wavefronts per workgroup
   __shared__ int bucket[TLC_MAX_WORLD + 1];
+  __shared__ int carry[TLC_MAX_WORLD];
+  __shared__ int wave_cnt[NW][TLC_MAX_WORLD];
   const int P = d.pstart[d.E];
   const int W = d.world;
-  const int tid = threadIdx.x;
-  if (tid < W) {
-    int n = 0;
-    for (int q = 0; q < P; ++q) n += d.pair_key[q] == tid;
-    bucket[tid + 1] = n;
-  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid <= TLC_MAX_WORLD) bucket[tid] = 0;
+  if (tid < TLC_MAX_WORLD) carry[tid] = 0;
+  __syncthreads();
+  for (int q = tid; q < P; q += blockDim.x) atomicAdd(&bucket[d.pair_key[q] + 1], 1);
   __syncthreads();
   if (tid == 0) {
-    bucket[0] = 0;
     for (int w = 0; w < W; ++w) bucket[w + 1] += bucket[w];
     *d.n_tiles = P * d.ntiles_n;
   }
   __syncthreads();
-  if (tid < W) {
-    int out = bucket[tid] * d.ntiles_n;
-    int e = 0;
-    for (int q = 0; q < P; ++q) {
-      while (d.pstart[e + 1] <= q) ++e;
-      if (d.pair_key[q] != tid) continue;
+  // stable ranks: pairs in q order, a batch of blockDim.x pairs at a time
+  for (int q0 = 0; q0 < P; q0 += blockDim.x) {
+    const int q = q0 + tid;
+    const bool valid = q < P;
+    const int key = valid ? d.pair_key[q] : -1;
+    int local = 0;
+    for (int w = 0; w < W; ++w) {
+      const unsigned long long bal = __ballot(key == w);
+      if (key == w) local = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wave_cnt[wave][w] = __popcll(bal);
+    }
+    __syncthreads();
+    if (valid) {
+      int rank = carry[key] + local;
+      for (int v = 0; v < wave; ++v) rank += wave_cnt[v][key];
+      int lo = 0, hi = d.E - 1;  // expert e with pstart[e] <= q < pstart[e+1]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (d.pstart[mid] <= q) lo = mid; else hi = mid - 1;
+      }
+      const int e = lo;
       const int mt = q - d.pstart[e];
       const int m0 = d.offsets[e] + mt * d.bm;
       const int rows = min(d.bm, d.counts[e] - mt * d.bm);
+      const int out = (bucket[key] + rank) * d.ntiles_n;
       for (int nt = 0; nt < d.ntiles_n; ++nt) {
         tlc_tile tl;
         tl.m0 = m0;
@@ -190,11 +254,18 @@ __global__ __launch_bounds__(256) void sort_kernel(MoeDev d) {
         tl.n_cols = min(d.bn, d.N - nt * d.bn);
         tl.expert = e;
         tl.chunk_mask = d.pair_mask[q];
-        tl.key = tid;
+        tl.key = key;
         tl.split = 0;
-        d.plan[out++] = tl;
+        d.plan[out + nt] = tl;
       }
     }
+    __syncthreads();
+    if (tid < W) {
+      int add = 0;
+      for (int v = 0; v < NW; ++v) add += wave_cnt[v][tid];
+      carry[tid] += add;
+    }
+    __syncthreads();
   }
 }
 
@@ -206,11 +277,13 @@ int64_t moe_max_pairs(int32_t T, int32_t topk, int32_t experts, int32_t bm) {
 
 tlc_status launch_moe_route(const MoeDev& d, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nb = (d.T + 63) / 64;
   hipLaunchKernelGGL(topk_kernel, dim3((d.T + 3) / 4), dim3(256), 0, s, d);
-  hipLaunchKernelGGL(count_kernel, dim3(d.E), dim3(64), 0, s, d);
-  hipLaunchKernelGGL(list_kernel, dim3(d.E), dim3(64), 0, s, d);
+  hipLaunchKernelGGL(block_count_kernel, dim3(nb), dim3(64), 0, s, d);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64), 0, s, d);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(64), 0, s, d);
   hipLaunchKernelGGL(pair_kernel, dim3((d.max_pairs + 3) / 4), dim3(256), 0, s, d);
-  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(256), 0, s, d);
+  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, s, d);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TLC_ERR_HIP, "moe route launch: %s", hipGetErrorString(e));
   return ok();

@@ -99,6 +99,7 @@ struct MoeDev {
   int32_t* pstart;             // workspace: E + 1
   int32_t* pair_key;           // workspace: max_pairs
   uint32_t* pair_mask;         // workspace: max_pairs
+  int32_t* blk;                // workspace: ceil(T/64) x E block counts, then their prefixes
 };
 
 int64_t moe_max_pairs(int32_t T, int32_t topk, int32_t experts, int32_t bm);

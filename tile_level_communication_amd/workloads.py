@@ -293,3 +293,12 @@ class MoEProblem:
                    self.x_src if land != tlc.LAND_NONE else None, self.w, self.b_layout, self.y,
                    self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns)
         s.end()
+
+    def land_only(self, land=tlc.LAND_COPY_ENGINE):
+        next_epoch(self)
+        s = self.streams
+        s.begin()
+        dst = [self.x[c * self.Tc:(c + 1) * self.Tc] for c in range(self.world)]
+        tlc.land(dst, self.x_src, self.Tc * self.H * 2, self.world, self.rank, self.sig, self.epoch,
+                 land, s.copy)
+        s.end()
