@@ -33,6 +33,11 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+# HBM bytes of one compute-only AG-GEMM launch (gemm_kernel_8w<KN, dense, no-wait>,
+# whole tiles, static schedule) from the rocprofv3 FETCH_SIZE and WRITE_SIZE passes
+# recorded in profiles/gemm_kernel_8w_ag_ffn_up_8192x3200x5120.md, scaled by the
+# plain-copy calibration factor 1.000.  Re-measure whenever that kernel changes.
+AG_COMPUTE_TRAFFIC_BYTES = (220280.2 + 102400.0) * 1024
 WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4}
 
 
@@ -245,7 +250,10 @@ def run_ag(args, torch, tlc, si, workloads):
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": (round(AG_COMPUTE_TRAFFIC_BYTES) if args.tile == 256
+                                 and args.layout == "KN" else None),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
+                     "algorithmic_bytes": prob.M * prob.K * 2 + prob.K * prob.N * 2 + prob.M * prob.N * 4,
                      "kernel": "gemm_kernel_8w<KN,dense,no-wait>: compute-only launch, whole tiles, "
                                "static schedule, every chunk resident"},
         "pct_peak": round(100 * flops / t_fused / 1e12 / PEAK_BF16_TFLOPS, 2),
