@@ -151,6 +151,7 @@ typedef struct {
   int32_t split_k;        /* 0 or 1: no split; 2..255: tiles with key >= split_from
                              are split into split_k K ranges */
   int32_t split_from;     /* first key whose tiles are split (>= 0) */
+  int32_t sub_chunks;     /* gather mode: 0 or 1, or S >= 2 sub-chunks per rank (see below) */
 } tlc_plan_desc;
 
 /* Tile order of the communication-aware scheduler (host code, integers only).
@@ -166,11 +167,18 @@ typedef struct {
  *   A tile with key >= split_from (split_k >= 2) becomes split_k adjacent
  *   units, one per K range, so that the work that depends on the last chunks
  *   can spread over every compute unit.
+ *   Sub-chunks (gather mode, S = sub_chunks >= 2, R % S == 0, world * S <= 32):
+ *   every rank's chunk lands as S pieces of R/S rows, each with its own flag
+ *   (DITRON §4.3 and Fig. 11 chunk split factor).  The plan is then the one of
+ *   world * S chunks of R/S rows with rank * S as the local one: chunk_mask
+ *   and key refer to sub-chunks c' = row / (R/S), consumed at position
+ *   (c' - rank * S) mod (world * S).
  * tiles:   host array of `cap` entries, or NULL to query the count only.
  * n_tiles: host, receives the number of units: ceil(M/bm) * ceil(N/bn) plus
  *   (split_k - 1) per split tile.
- * landing_order: host array of world-1 entries or NULL; receives the order in
- *   which peers' chunks land: rank+1, rank+2, ..., rank-1 (mod W).
+ * landing_order: host array of (world-1) * S entries (S = 1 without sub-chunks)
+ *   or NULL; receives the order in which peers' (sub-)chunks land:
+ *   rank+1, rank+2, ..., rank-1 (mod W), each as its S sub-chunks in order.
  * Errors: INVALID_ARG (bad desc), CAPACITY (cap < count; *n_tiles is set). */
 tlc_status tlc_chunk_plan(const tlc_plan_desc* desc, tlc_tile* tiles, int64_t cap,
                           int64_t* n_tiles, int32_t* landing_order);
@@ -252,6 +260,10 @@ typedef struct {
   void* workspace;
   int64_t workspace_bytes;
   int32_t schedule;
+  /* 0 or 1, or S >= 2: the landing moves every peer chunk as S pieces of
+   * rows_per_chunk / S rows, each raising its own flag (flags[c * S + j]); the
+   * plan must be built with the same sub_chunks.  world * S <= 32. */
+  int32_t sub_chunks;
   /* Optional debug trace (NULL = off): device int64 array of n_tiles x 4,
    * entry t = {workgroup, wall-clock at wait start, at wait end, at tile end}
    * for the tile at plan index t; wall clock = the device's constant-rate

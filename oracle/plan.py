@@ -75,14 +75,16 @@ def send_pos(c: int, world: int, rank: int) -> int:
     return (c - rank - 1) % world
 
 
-def landing_order(world: int, rank: int):
-    """Order in which the peers' chunks arrive: rank+1, rank+2, ..., rank-1 (mod W)."""
-    return [(rank + i) % world for i in range(1, world)]
+def landing_order(world: int, rank: int, n_local: int = 1):
+    """Order in which the peers' chunks arrive: rank+1, rank+2, ..., rank-1 (mod W).
+    With sub-chunks, `world` counts sub-chunks and the n_local ones from `rank` on
+    are the local rank's own."""
+    return [(rank + i) % world for i in range(n_local, world)]
 
 
 def chunk_plan(mode: int, world: int, rank: int, M: int, N: int, rows_per_chunk: int,
                bm: int, bn: int, order: int = ORDER_RANK_OFFSET, group_m: int = 1,
-               split_k: int = 0, split_from: int = 0):
+               split_k: int = 0, split_from: int = 0, sub_chunks: int = 0):
     """Unit list in execution order for a dense gather (AG) or scatter (RS) GEMM.
 
     Sort key: (key, mt // group_m, nt, mt), where key = max consume_pos over the
@@ -90,9 +92,19 @@ def chunk_plan(mode: int, world: int, rank: int, M: int, N: int, rows_per_chunk:
     natural (un-swizzled) order is requested.  Python's sort is stable and the
     key is total, so the order is unique.  With split_k >= 2, each tile whose
     key >= split_from then becomes split_k adjacent units (split index 0 first).
+
+    Sub-chunks (gather mode, DITRON §4.3 / Fig. 11 chunk split factor): each
+    rank's chunk arrives as S pieces of R/S rows with their own flags, so chunks,
+    positions and masks are those of world*S pieces, rank*S being the first local
+    one; the S local pieces are the rank's own (never landed).
     """
     assert mode in (AG, RS)
     assert M == world * rows_per_chunk
+    S = sub_chunks if sub_chunks and sub_chunks > 1 else 1
+    if S > 1:
+        assert mode == AG and rows_per_chunk % S == 0 and world * S <= 32
+    n_local = S
+    world, rank, rows_per_chunk = world * S, rank * S, rows_per_chunk // S
     tiles = []
     for (mt, nt, m0, n0, mr, nc) in dense_tiles(M, N, bm, bn):
         cs = chunk_set(m0, mr, rows_per_chunk)
@@ -117,7 +129,7 @@ def chunk_plan(mode: int, world: int, rank: int, M: int, N: int, rows_per_chunk:
             n_split += 1
         else:
             units.append(t)
-    return units, landing_order(world, rank)
+    return units, landing_order(world, rank, n_local)
 
 
 def split_k_range(split: int, K: int, bk: int = 64):

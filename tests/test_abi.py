@@ -38,7 +38,7 @@ def test_version_and_strings():
 
 def test_struct_sizes_match_header():
     assert C.sizeof(tlc.Tile) == 32
-    assert C.sizeof(tlc.PlanDesc) == 48
+    assert C.sizeof(tlc.PlanDesc) == 52
 
 
 def _ag_args(**over):

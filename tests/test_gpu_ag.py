@@ -154,6 +154,27 @@ def test_ag_split_result_independent_of_schedule():
                 absmax_bf16(inp.b), "split bits")
 
 
+@pytest.mark.parametrize("sub", [2, 4])
+@pytest.mark.parametrize("land", ["copy_engine", "cu"])
+def test_ag_subchunk_parity(land, sub):
+    """Each peer chunk lands as `sub` pieces with their own flags; tiles wait
+    for exactly the pieces their rows read (straddling tiles included)."""
+    for (name, W, R, K, N, tile) in [("w2_256x256x512_t128", 2, 128, 512, 256, 128),
+                                     ("w4_512x264x192_t256", 4, 128, 192, 264, 256),
+                                     ("w8_1024x136x128_t128", 8, 128, 128, 136, 128)]:
+        for integer in (False, True):
+            inp = si.ag_inputs(180 + W, W, R, N, K, integer=integer)
+            ref = og.ag_gemm(inp.a_chunks, inp.b)
+            for rank in sorted({0, W - 1}):
+                log(f"[ag sub] {name} land={land} sub={sub} int={integer} rank={rank}")
+                _, c = _run(inp, rank, tile, tlc.B_KN, LANDS[land], sub_chunks=sub, split_k=2,
+                            split_from=W * sub - 1)
+                if integer:
+                    check_exact(c, ref, name)
+                else:
+                    check_close(c, ref, K, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), name)
+
+
 def test_ag_timeout_reports_status():
     """A chunk whose flag never reaches the epoch: the kernel gives up after
     the time limit, reports TIMEOUT with the chunk, and every workgroup exits."""

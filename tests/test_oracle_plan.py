@@ -25,7 +25,8 @@ def _cases():
 def test_golden_orders(case):
     tiles, landing = op.chunk_plan(case["mode"], case["world"], case["rank"], case["M"], case["N"],
                                    case["R"], case["bm"], case["bn"], case["order"], case["group_m"],
-                                    case.get("split_k", 0), case.get("split_from", 0))
+                                    case.get("split_k", 0), case.get("split_from", 0),
+                                    case.get("sub_chunks", 0))
     assert [list(t) for t in tiles] == case["tiles"]
     assert landing == case["landing"]
 
@@ -147,3 +148,20 @@ def test_split_units_brute(mode, S, split_from):
             assert units[i] == t
             i += 1
     assert i == len(units)
+
+
+@pytest.mark.parametrize("S", [2, 4])
+def test_subchunk_plan_brute(S):
+    """Sub-chunks: every tile's key is the largest consume position of the
+    R/S-row pieces its rows touch (found row by row), local pieces first."""
+    world, rank, R, N, bm, bn = 4, 2, 8, 10, 4, 4
+    M = world * R
+    tiles, landing = op.chunk_plan(op.AG, world, rank, M, N, R, bm, bn, sub_chunks=S)
+    P = R // S
+    for (m0, n0, mr, nc, e, mask, key, z) in tiles:
+        pieces = {i // P for i in range(m0, m0 + mr)}
+        assert mask == sum(1 << c for c in pieces)
+        assert key == max((c - rank * S) % (world * S) for c in pieces)
+    assert landing == [(rank * S + i) % (world * S) for i in range(S, world * S)]
+    keys = [t[6] for t in tiles]
+    assert keys == sorted(keys)

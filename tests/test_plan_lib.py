@@ -17,7 +17,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "plan_cases.json")
 def test_library_matches_golden(case):
     tiles, landing = tlc.chunk_plan(case["mode"], case["world"], case["rank"], case["M"], case["N"],
                                     case["R"], case["bm"], case["bn"], case["order"], case["group_m"],
-                                    case.get("split_k", 0), case.get("split_from", 0))
+                                    case.get("split_k", 0), case.get("split_from", 0),
+                                    case.get("sub_chunks", 0))
     assert tiles.tolist() == case["tiles"]
     assert landing == case["landing"]
 
@@ -65,3 +66,27 @@ def test_library_split_matches_oracle(mode, split_k, split_from):
             assert np.array_equal(got, ref)
             assert tlc.split_tiles(lib_tiles) == sum(1 for t in ref_tiles if (t[7] & 0xFF) >= 2 and
                                                      ((t[7] >> 8) & 0xFF) == 0)
+
+
+@pytest.mark.parametrize("sub", [2, 4])
+@pytest.mark.parametrize("split_k,split_from", [(0, 0), (2, 5)])
+def test_library_subchunks_match_oracle(sub, split_k, split_from):
+    for (W, R, N, bm) in [(8, 1024, 3200, 256), (2, 128, 256, 128), (4, 96, 136, 128)]:
+        for rank in range(W):
+            lib_tiles, lib_land = tlc.chunk_plan(tlc.MODE_AG, W, rank, W * R, N, R, bm, bm,
+                                                 tlc.ORDER_RANK_OFFSET, 4, split_k, split_from, sub)
+            ref_tiles, ref_land = op.chunk_plan(op.AG, W, rank, W * R, N, R, bm, bm,
+                                                op.ORDER_RANK_OFFSET, 4, split_k, split_from, sub)
+            got = lib_tiles.astype(np.int64) & 0xFFFFFFFF
+            ref = np.array(ref_tiles, dtype=np.int64) & 0xFFFFFFFF
+            assert np.array_equal(got, ref)
+            assert lib_land == ref_land
+
+
+def test_subchunk_argument_errors():
+    with pytest.raises(tlc.TLCError):
+        tlc.chunk_plan(tlc.MODE_RS, 4, 0, 400, 64, 100, 128, 128, sub_chunks=2)   # gather only
+    with pytest.raises(tlc.TLCError):
+        tlc.chunk_plan(tlc.MODE_AG, 4, 0, 400, 64, 100, 128, 128, sub_chunks=3)   # R % S
+    with pytest.raises(tlc.TLCError):
+        tlc.chunk_plan(tlc.MODE_AG, 8, 0, 8192, 64, 1024, 256, 256, sub_chunks=8)  # W * S > 32

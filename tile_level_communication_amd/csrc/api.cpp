@@ -98,16 +98,16 @@ tlc_status hip_check(hipError_t e, const char* what) {
 }
 
 // Enqueue the emulated peers' chunk transfers on `copy` in landing order
-// (rank+1, rank+2, ... mod W) and raise each chunk's flag to `epoch` after
-// its bytes.
+// (rank+n_local, rank+n_local+1, ... mod W: the n_local chunks from `rank` on
+// are already in place) and raise each chunk's flag to `epoch` after its bytes.
 tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, int64_t bytes,
-                           int world, int rank, tlc_signals* sig, uint32_t epoch,
+                           int world, int rank, int n_local, tlc_signals* sig, uint32_t epoch,
                            void* const* copy_streams, int n_copy_streams, const DeviceInfo& info) {
-  if (land == TLC_LAND_NONE || world == 1) return TLC_OK;
+  if (land == TLC_LAND_NONE || world <= n_local) return TLC_OK;
   if (land == TLC_LAND_COPY_ENGINE) {
-    for (int i = 1; i < world; ++i) {
+    for (int i = n_local; i < world; ++i) {
       const int c = (rank + i) % world;
-      hipStream_t s = static_cast<hipStream_t>(copy_streams[(i - 1) % n_copy_streams]);
+      hipStream_t s = static_cast<hipStream_t>(copy_streams[(i - n_local) % n_copy_streams]);
       tlc_status st = hip_check(hipMemcpyAsync(dst[c], src[c], static_cast<size_t>(bytes),
                                                hipMemcpyDeviceToDeviceNoCU, s),
                                 "hipMemcpyAsync(landing)");
@@ -122,10 +122,10 @@ tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, i
   }
   LandParams p;
   memset(&p, 0, sizeof(p));
-  p.n_chunks = world - 1;
-  for (int i = 1; i < world; ++i) {
+  p.n_chunks = world - n_local;
+  for (int i = n_local; i < world; ++i) {
     const int c = (rank + i) % world;
-    p.order[i - 1] = c;
+    p.order[i - n_local] = c;
     p.src[c] = static_cast<const uint4*>(src[c]);
     p.dst[c] = static_cast<uint4*>(dst[c]);
   }
@@ -141,7 +141,7 @@ tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, i
 
 tlc_status check_land_args(int land, const void* const* src, const void* const* dst, int world,
                            int rank, int64_t bytes, const char* who, void* const* copy_streams,
-                           int n_copy_streams, uint32_t epoch) {
+                           int n_copy_streams, uint32_t epoch, int n_local = 1) {
   if (land != TLC_LAND_NONE && land != TLC_LAND_COPY_ENGINE && land != TLC_LAND_CU)
     return fail(TLC_ERR_INVALID_ARG, "%s: land %d unknown", who, land);
   if (land == TLC_LAND_NONE) return TLC_OK;
@@ -154,7 +154,7 @@ tlc_status check_land_args(int land, const void* const* src, const void* const* 
   if (bytes % 16 != 0) return fail(TLC_ERR_MISALIGNED, "%s: chunk bytes %lld not a multiple of 16", who,
                                    static_cast<long long>(bytes));
   for (int c = 0; c < world; ++c) {
-    if (c == rank) continue;
+    if ((c - rank + world) % world < n_local) continue;
     if (!src[c] || !dst[c]) return fail(TLC_ERR_INVALID_ARG, "%s: chunk %d pointer is NULL", who, c);
     if (!aligned16(src[c]) || !aligned16(dst[c]))
       return fail(TLC_ERR_MISALIGNED, "%s: chunk %d pointer not 16-byte aligned", who, c);
@@ -282,7 +282,7 @@ tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_
   DeviceInfo info;
   st = device_info(&info);
   if (st) return st;
-  st = enqueue_landing(land, dst, src, bytes_per_chunk, world, rank, sig, epoch, copy_streams,
+  st = enqueue_landing(land, dst, src, bytes_per_chunk, world, rank, 1, sig, epoch, copy_streams,
                        n_copy_streams, info);
   return st ? st : ok();
 }
@@ -295,11 +295,28 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   if (st) return st;
   st = check_schedule(a->schedule, a->workspace, a->workspace_bytes, "tlc_ag_gemm");
   if (st) return st;
-  const int64_t chunk_bytes = static_cast<int64_t>(a->rows_per_chunk) * a->K * 2;
+  // Sub-chunks: each rank's chunk lands and is flagged as S pieces of R/S rows,
+  // so W*S flags, the local rank's S pieces never waited for.
+  const int S = a->sub_chunks > 1 ? a->sub_chunks : 1;
+  if (a->sub_chunks < 0 || a->rows_per_chunk % S != 0 ||
+      static_cast<int64_t>(a->world) * S > TLC_MAX_WORLD)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_ag_gemm: sub_chunks %d (rows_per_chunk %% S, world * S <= %d)",
+                a->sub_chunks, TLC_MAX_WORLD);
+  if (a->land != TLC_LAND_NONE && a->world > 1 && !a->a_src)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_ag_gemm: landing needs source and destination arrays");
+  const int Wf = a->world * S, rf = a->rank * S;
+  const int64_t chunk_bytes = static_cast<int64_t>(a->rows_per_chunk / S) * a->K * 2;
   void* dst[TLC_MAX_WORLD];
-  for (int c = 0; c < a->world; ++c) dst[c] = static_cast<char*>(a->a) + c * chunk_bytes;
-  st = check_land_args(a->land, a->a_src, dst, a->world, a->rank, chunk_bytes, "tlc_ag_gemm",
-                       copy_streams, n_copy_streams, a->epoch);
+  const void* src[TLC_MAX_WORLD];
+  for (int c = 0; c < Wf; ++c) {
+    dst[c] = static_cast<char*>(a->a) + c * chunk_bytes;
+    const int owner = c / S;
+    const void* base = a->a_src ? a->a_src[owner] : nullptr;
+    src[c] = (base && owner != a->rank) ? static_cast<const char*>(base) + (c % S) * chunk_bytes
+                                        : nullptr;
+  }
+  st = check_land_args(a->land, src, dst, Wf, rf, chunk_bytes, "tlc_ag_gemm", copy_streams,
+                       n_copy_streams, a->epoch, S);
   if (st) return st;
   DeviceInfo info;
   st = device_info(&info);
@@ -308,8 +325,8 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   // The producer is always enqueued before the consumer: two streams may share
   // one hardware queue, and a GEMM queued ahead of its own landing there would
   // wait on flags that can never be raised.
-  st = enqueue_landing(a->land, dst, a->a_src, chunk_bytes, a->world, a->rank, a->sig, a->epoch,
-                       copy_streams, n_copy_streams, info);
+  st = enqueue_landing(a->land, dst, src, chunk_bytes, Wf, rf, S, a->sig, a->epoch, copy_streams,
+                       n_copy_streams, info);
   if (st) return st;
   if (a->n_tiles == 0) return ok();
 
@@ -326,7 +343,7 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   p.lda = a->K;
   p.ldb = a->b_layout == TLC_B_NK ? a->K : a->N;
   p.ldc = a->N;
-  p.no_wait_mask = 1u << a->rank;
+  p.no_wait_mask = ((S == 32 ? 0u : (1u << S)) - 1u) << rf;
   // land == NONE with epoch 0: every chunk is resident, nothing to wait for
   p.do_wait = !(a->land == TLC_LAND_NONE && a->epoch == 0);
   p.sig = a->sig;
@@ -371,7 +388,7 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
 
   st = enqueue_landing(land, reinterpret_cast<void* const*>(a->landing),
                        reinterpret_cast<const void* const*>(a->remote_src), slice_bytes, a->world,
-                       a->rank, a->sig, a->epoch, copy_streams, n_copy_streams, info);
+                       a->rank, 1, a->sig, a->epoch, copy_streams, n_copy_streams, info);
   if (st) return st;
 
   if (run_gemm && a->n_tiles > 0) {
@@ -533,7 +550,7 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
   DeviceInfo info;
   st = device_info(&info);
   if (st) return st;
-  st = enqueue_landing(a->land, dst, a->x_src, chunk_bytes, a->world, a->rank, a->sig, a->epoch,
+  st = enqueue_landing(a->land, dst, a->x_src, chunk_bytes, a->world, a->rank, 1, a->sig, a->epoch,
                        copy_streams, n_copy_streams, info);
   if (st) return st;
 

@@ -64,8 +64,15 @@ extern "C" tlc_status tlc_chunk_plan(const tlc_plan_desc* d, tlc_tile* tiles, in
   if (d->split_k < 0 || d->split_k > 255 || d->split_from < 0)
     return fail(TLC_ERR_INVALID_ARG, "tlc_chunk_plan: split_k %d outside 0..255 or split_from %d < 0",
                 d->split_k, d->split_from);
+  const int32_t SC = d->sub_chunks > 1 ? d->sub_chunks : 1;
+  if (d->sub_chunks < 0 || (SC > 1 && (d->mode != TLC_MODE_AG || d->rows_per_chunk % SC != 0 ||
+                                       static_cast<int64_t>(d->world) * SC > TLC_MAX_WORLD)))
+    return fail(TLC_ERR_INVALID_ARG,
+                "tlc_chunk_plan: sub_chunks %d needs gather mode, rows_per_chunk %% S == 0, "
+                "world * S <= %d", d->sub_chunks, TLC_MAX_WORLD);
 
-  const int32_t W = d->world, r = d->rank, R = d->rows_per_chunk;
+  // with sub-chunks, the plan of world * S chunks of R / S rows, local chunk rank * S
+  const int32_t W = d->world * SC, r = d->rank * SC, R = d->rows_per_chunk / SC;
   const int64_t mtiles = (d->M + d->bm - 1) / d->bm;
   const int64_t ntiles = (d->N + d->bn - 1) / d->bn;
   const int32_t S = d->split_k >= 2 ? d->split_k : 1;
@@ -106,7 +113,7 @@ extern "C" tlc_status tlc_chunk_plan(const tlc_plan_desc* d, tlc_tile* tiles, in
   for (const Keyed& k : v) count += (S > 1 && k.key >= d->split_from) ? S : 1;
   *n_tiles = count;
   if (landing_order)
-    for (int32_t i = 1; i < W; ++i) landing_order[i - 1] = (r + i) % W;
+    for (int32_t i = SC; i < W; ++i) landing_order[i - SC] = (r + i) % W;
   if (!tiles) return tlc::ok();
   if (cap < count)
     return fail(TLC_ERR_CAPACITY, "tlc_chunk_plan: capacity %lld < %lld units",

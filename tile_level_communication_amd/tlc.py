@@ -51,7 +51,7 @@ class PlanDesc(C.Structure):
     _fields_ = [("mode", C.c_int32), ("world", C.c_int32), ("rank", C.c_int32), ("M", C.c_int32),
                 ("N", C.c_int32), ("rows_per_chunk", C.c_int32), ("bm", C.c_int32),
                 ("bn", C.c_int32), ("order", C.c_int32), ("group_m", C.c_int32),
-                ("split_k", C.c_int32), ("split_from", C.c_int32)]
+                ("split_k", C.c_int32), ("split_from", C.c_int32), ("sub_chunks", C.c_int32)]
 
 
 class AGArgs(C.Structure):
@@ -62,7 +62,8 @@ class AGArgs(C.Structure):
                 ("b_layout", C.c_int32), ("c", C.c_void_p), ("sig", C.c_void_p),
                 ("epoch", C.c_uint32), ("land", C.c_int32), ("grid", C.c_int32),
                 ("timeout_ns", C.c_int64), ("workspace", C.c_void_p),
-                ("workspace_bytes", C.c_int64), ("schedule", C.c_int32), ("trace", C.c_void_p)]
+                ("workspace_bytes", C.c_int64), ("schedule", C.c_int32), ("sub_chunks", C.c_int32),
+                ("trace", C.c_void_p)]
 
 
 class RSArgs(C.Structure):
@@ -207,17 +208,18 @@ def _ptr_array(items, world):
 # ------------------------------------------------------------------ plan ----
 
 def chunk_plan(mode, world, rank, M, N, rows_per_chunk, bm, bn, order=ORDER_RANK_OFFSET,
-               group_m=1, split_k=0, split_from=0):
+               group_m=1, split_k=0, split_from=0, sub_chunks=0):
     """tlc_chunk_plan.  Returns (units: int32 ndarray [n_units, 8], landing_order: list)."""
     d = PlanDesc(mode, world, rank, M, N, rows_per_chunk, bm, bn, order, group_m, split_k,
-                 split_from)
+                 split_from, sub_chunks)
     n = C.c_int64(0)
     _check(lib().tlc_chunk_plan(C.byref(d), None, 0, C.byref(n), None), "tlc_chunk_plan")
     tiles = (Tile * max(n.value, 1))()
-    land = (C.c_int32 * max(world - 1, 1))()
+    n_land = (world - 1) * max(sub_chunks, 1)
+    land = (C.c_int32 * max(n_land, 1))()
     _check(lib().tlc_chunk_plan(C.byref(d), tiles, n.value, C.byref(n), land), "tlc_chunk_plan")
     arr = np.ctypeslib.as_array(C.cast(tiles, C.POINTER(C.c_int32)), shape=(max(n.value, 1), 8))
-    return arr[:n.value].copy(), [int(land[i]) for i in range(world - 1)]
+    return arr[:n.value].copy(), [int(land[i]) for i in range(n_land)]
 
 
 def split_tiles(plan) -> int:
@@ -271,7 +273,7 @@ def signals_alloc() -> Signals:
 
 def ag_gemm(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, a_src, b, b_layout, c,
             sig: Signals, epoch, land, compute_stream=None, copy_stream=None, grid=0, timeout_ns=0,
-            trace=None, workspace=None, schedule=SCHED_DYNAMIC):
+            trace=None, workspace=None, schedule=SCHED_DYNAMIC, sub_chunks=0):
     """tlc_ag_gemm.  a_src: list of `world` device tensors (entry `rank` unused) or None.
     copy_stream: one stream or a list of streams for the landing.  workspace: a
     zero-filled device tensor for split plans (or None)."""
@@ -279,7 +281,7 @@ def ag_gemm(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, a_sr
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = AGArgs(_ptr(plan), n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, _ptr(a), src,
                   _ptr(b), b_layout, _ptr(c), sig.ptr, epoch, land, grid, timeout_ns,
-                  _ptr(workspace), ws_bytes, schedule, _ptr(trace))
+                  _ptr(workspace), ws_bytes, schedule, sub_chunks, _ptr(trace))
     cs, n = _streams(copy_stream)
     _check(lib().tlc_ag_gemm(C.byref(args), _stream(compute_stream), cs, n), "tlc_ag_gemm")
 

@@ -79,9 +79,10 @@ def split_workspace(tiles, split_k, bm, bn, device):
 class AGProblem:
     def __init__(self, a_chunks, b_kn, rank, bm=256, bn=256, b_layout=tlc.B_KN,
                  order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda", split_k=0, split_from=0,
-                 schedule=tlc.SCHED_DYNAMIC):
+                 schedule=tlc.SCHED_DYNAMIC, sub_chunks=0):
         self.device = torch.device(device)
         self.world = len(a_chunks)
+        self.sub_chunks = sub_chunks
         self.rank = rank
         self.R, self.K = a_chunks[0].shape
         self.N = b_kn.shape[1]
@@ -94,7 +95,7 @@ class AGProblem:
         self.c = torch.empty((self.M, self.N), dtype=torch.float32, device=self.device)
         tiles, self.landing_order = tlc.chunk_plan(tlc.MODE_AG, self.world, rank, self.M, self.N,
                                                    self.R, bm, bn, order, group_m, split_k,
-                                                   split_from)
+                                                   split_from, sub_chunks)
         self.tiles = tiles
         self.plan = torch.from_numpy(tiles).to(self.device)
         self.n_tiles = int(tiles.shape[0])
@@ -131,7 +132,7 @@ class AGProblem:
         tlc.ag_gemm(self.plan, self.n_tiles, self.M, self.N, self.K, self.world, self.rank, self.R,
                     self.bm, self.bn, self.a, self.a_src if land != tlc.LAND_NONE else None,
                     self.b, self.b_layout, self.c, self.sig, self.epoch, land, s.compute, s.copy,
-                    grid, timeout_ns, trace, self.workspace, self.schedule)
+                    grid, timeout_ns, trace, self.workspace, self.schedule, self.sub_chunks)
         s.end()
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
