@@ -4,10 +4,12 @@
 Default workload (--workload ag): the Qwen3-32B-like FFN-up AllGather-GEMM --
 8 chunks of 1024 x 5120 bf16 activations gathered into A (8192 x 5120), weight
 shard B 5120 x 3200 bf16 (K x N), C = A @ B in fp32.  One step = one pass of the
-whole path: the 7 peer chunks land on a side stream through the copy engine (one
-transfer per chunk, then the chunk's flag), while the persistent tile-swizzled
-GEMM on the compute stream starts with the local chunk and consumes the others
-as their flags flip.  Inputs are seeded synthetic data resident in HBM.
+whole path: the 7 peer chunks land on a side stream with hipMemcpyAsync (one
+device-to-device transfer per chunk, then a 4-byte transfer raising the chunk's
+flag), while the persistent tile-swizzled GEMM on the compute stream starts with
+the local chunk and consumes the others as their flags flip.  The same step with
+the transfers forced onto the SDMA engines and with the library's own copy
+kernel is reported beside it.  Inputs are seeded synthetic data resident in HBM.
 
 Other workloads (--workload rs | rs_long | moe) time GEMM-ReduceScatter (4096 x
 4096 x 2048, 4 chunks; 131072 x 5120 x 3200, 8 chunks) and AG-MoE (4096 tokens,
@@ -47,7 +49,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ag", choices=list(WORKLOAD_ID))
-    ap.add_argument("--land", default="copy_engine", choices=["copy_engine", "cu"])
+    ap.add_argument("--land", default="memcpy", choices=["memcpy", "copy_engine", "cu"],
+                    help="memcpy: hipMemcpyAsync device-to-device on the side stream (default); "
+                         "copy_engine: the same forced onto the SDMA engines (NoCU); cu: our copy kernel")
     ap.add_argument("--layout", default="KN", choices=["KN", "NK"])
     ap.add_argument("--tile", type=int, default=256)
     ap.add_argument("--group-m", type=int, default=4)
@@ -57,6 +61,8 @@ def parse():
                     help="K ranges per split tile (default: 4 for ag, none otherwise)")
     ap.add_argument("--split-from", type=int, default=None,
                     help="first key (chunk position) whose tiles are split (default 1)")
+    ap.add_argument("--sub-chunks", type=int, default=None,
+                    help="ag: land every peer chunk as S pieces with their own flags (default 1)")
     ap.add_argument("--schedule", default=None, choices=["dynamic", "static"],
                     help="work distribution (default: dynamic for ag and moe, static for rs)")
     ap.add_argument("--rank", type=int, default=0)
@@ -162,16 +168,19 @@ def run_ag(args, torch, tlc, si, workloads):
     dev = torch.device("cuda:0")
     inp = si.workload_inputs(2)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
-    land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
-    # fused plan: the last chunk's tiles cut in two along K, so that the tail
-    # after the last landing runs on twice as many compute units
-    split_k = 2 if args.split_k is None else args.split_k
+    land = {"copy_engine": tlc.LAND_COPY_ENGINE, "cu": tlc.LAND_CU, "memcpy": tlc.LAND_MEMCPY}[args.land]
+    # fused plan: whole tiles; with the slow SDMA landing the last chunk's tiles
+    # are cut in two along K, so that the tail after the last landing runs on
+    # twice as many compute units
+    split_k = (2 if land == tlc.LAND_COPY_ENGINE else 0) if args.split_k is None else args.split_k
     split_from = 7 if args.split_from is None else args.split_from
     args.schedule = args.schedule or "dynamic"
     schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
+    sub = 1 if args.sub_chunks is None else args.sub_chunks
     prob = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
                                group_m=args.group_m, device=dev, split_k=split_k,
-                               split_from=split_from, schedule=schedule)
+                               split_from=split_from * sub + (sub - 1), schedule=schedule,
+                               sub_chunks=sub)
     compute = torch.cuda.Stream(device=dev)
     copies = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.copy_streams))]
     prob.streams.compute = compute
@@ -180,7 +189,7 @@ def run_ag(args, torch, tlc, si, workloads):
     call = dict(plan=prob.plan, n_tiles=prob.n_tiles, M=prob.M, N=prob.N, K=prob.K, world=prob.world,
                 rank=prob.rank, rows_per_chunk=prob.R, bm=args.tile, bn=args.tile, a=prob.a,
                 b=prob.b, b_layout=layout, c=prob.c, sig=prob.sig, workspace=prob.workspace,
-                schedule=schedule)
+                schedule=schedule, sub_chunks=sub)
     torch.cuda.synchronize()
 
     def fused_step(land_kind, timer=None):
@@ -200,26 +209,29 @@ def run_ag(args, torch, tlc, si, workloads):
     gemm_fused_ms = fused_t.mean_ms(args.warmup)
     status = prob.sig.read_status(compute)
 
-    # the same step with the other landing backend (reported beside the headline)
-    other = tlc.LAND_CU if land == tlc.LAND_COPY_ENGINE else tlc.LAND_COPY_ENGINE
-    t_fused_other = timed(fused_step(other), args.steps, args.warmup, torch)
-    status_other = prob.sig.read_status(compute)
+    # the same step with the other landing backends (reported beside the headline)
+    names = {tlc.LAND_COPY_ENGINE: "copy_engine", tlc.LAND_CU: "cu", tlc.LAND_MEMCPY: "memcpy"}
+    others = {}
+    for other in names:
+        if other == land:
+            continue
+        t_f = timed(fused_step(other), args.steps, args.warmup, torch)
+        others[other] = (t_f, prob.sig.read_status(compute))
 
     def copy_only_step(land_kind):
-        dst = [prob.a[c * prob.R:(c + 1) * prob.R] for c in range(prob.world)]
-
+        # the landing sequence of the fused step alone (an AG call with no units)
         def step():
             workloads.next_epoch(prob)
             for c in copies:
                 c.wait_stream(compute)
-            tlc.land(dst, prob.a_src, prob.R * prob.K * 2, prob.world, prob.rank, prob.sig,
-                     prob.epoch, land_kind, copies)
+            tlc.ag_gemm(**dict(call, n_tiles=0), a_src=prob.a_src, epoch=prob.epoch, land=land_kind,
+                        compute_stream=compute, copy_stream=copies)
             for c in copies:
                 compute.wait_stream(c)
         return step
 
     t_copy = timed(copy_only_step(land), args.steps, args.warmup, torch)
-    t_copy_other = timed(copy_only_step(other), args.steps, args.warmup, torch)
+    t_copy_others = {o: timed(copy_only_step(o), args.steps, args.warmup, torch) for o in others}
 
     # compute-only: the GEMM alone, every chunk in place, no flag checks (land
     # NONE, epoch 0), whole tiles, static schedule -- its fastest configuration
@@ -230,7 +242,7 @@ def run_ag(args, torch, tlc, si, workloads):
     torch.cuda.synchronize()
     comp_t = KernelTimer(torch, compute)
     ccall = dict(call, plan=comp.plan, n_tiles=comp.n_tiles, a=comp.a, sig=comp.sig, workspace=None,
-                 schedule=tlc.SCHED_STATIC)
+                 schedule=tlc.SCHED_STATIC, sub_chunks=0)
 
     def compute_only():
         comp_t(lambda: tlc.ag_gemm(**ccall, a_src=None, epoch=0, land=tlc.LAND_NONE,
@@ -240,13 +252,12 @@ def run_ag(args, torch, tlc, si, workloads):
     gemm_comp_ms = comp_t.mean_ms(args.warmup)
     torch.cuda.synchronize()
     achieved = flops / (gemm_comp_ms * 1e-3) / 1e12
-    names = {tlc.LAND_COPY_ENGINE: "copy_engine", tlc.LAND_CU: "cu"}
     extra = {
         "config": {"workload": wl.name, "M": prob.M, "N": prob.N, "K": prob.K, "world": prob.world,
                    "rank": prob.rank, "tile": [args.tile, args.tile, 64], "b_layout": args.layout,
                    "landing": args.land, "copy_streams": len(copies), "group_m": args.group_m,
-                   "n_units": prob.n_tiles, "split_k": split_k, "split_from": split_from,
-                   "schedule": args.schedule,
+                   "n_units": prob.n_tiles, "split_k": split_k, "split_from_chunk": split_from,
+                   "sub_chunks": sub, "schedule": args.schedule,
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -264,11 +275,12 @@ def run_ag(args, torch, tlc, si, workloads):
         "copy_gbs": round((prob.world - 1) * prob.R * prob.K * 2 / t_copy / 1e9, 1),
         "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,
-        "other_landing": {"landing": names[other], "value": round(flops / t_fused_other / 1e12, 2),
-                          "ms_per_step": round(t_fused_other * 1e3, 4),
-                          "copy_only_ms": round(t_copy_other * 1e3, 4),
-                          "overlap_efficiency": round(max(t_comp, t_copy_other) / t_fused_other, 4),
-                          "device_status": status_other},
+        "other_landings": {
+            names[o]: {"value": round(flops / t_f / 1e12, 2), "ms_per_step": round(t_f * 1e3, 4),
+                       "copy_only_ms": round(t_copy_others[o] * 1e3, 4),
+                       "overlap_efficiency": round(max(t_comp, t_copy_others[o]) / t_f, 4),
+                       "device_status": st}
+            for o, (t_f, st) in others.items()},
     }
     line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
     if not args.no_cpu_baseline:
@@ -281,7 +293,7 @@ def run_rs(args, torch, tlc, si, workloads, wid):
     dev = torch.device("cuda:0")
     inp = si.workload_inputs(wid, rank=args.rank)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
-    land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
+    land = {"copy_engine": tlc.LAND_COPY_ENGINE, "cu": tlc.LAND_CU, "memcpy": tlc.LAND_MEMCPY}[args.land]
     split_k = 0 if args.split_k is None else args.split_k
     split_from = 1 if args.split_from is None else args.split_from
     args.schedule = args.schedule or "static"
@@ -371,7 +383,7 @@ def run_moe(args, torch, tlc, si, workloads):
     dev = torch.device("cuda:0")
     inp = si.workload_inputs(4)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
-    land = tlc.LAND_COPY_ENGINE if args.land == "copy_engine" else tlc.LAND_CU
+    land = {"copy_engine": tlc.LAND_COPY_ENGINE, "cu": tlc.LAND_CU, "memcpy": tlc.LAND_MEMCPY}[args.land]
     schedule = tlc.SCHED_STATIC if args.schedule == "static" else tlc.SCHED_DYNAMIC
     prob = workloads.MoEProblem(inp.x_chunks, inp.logits, inp.w, args.rank, wl.topk, args.tile,
                                 args.tile, layout, device=dev)

@@ -84,8 +84,11 @@ enum { TLC_B_KN = 0, TLC_B_NK = 1 };
  *                  the chunk's flag (epoch in 1..TLC_EPOCH_MAX)
  *   CU          -- one copy kernel on the copy stream; its workgroups copy the
  *                  chunks in landing order and the last one to finish a chunk
- *                  publishes its flag with a release store                     */
-enum { TLC_LAND_NONE = 0, TLC_LAND_COPY_ENGINE = 1, TLC_LAND_CU = 2 };
+ *                  publishes its flag with a release store
+ *   MEMCPY      -- as COPY_ENGINE but with the default hipMemcpyDeviceToDevice
+ *                  kind, which the runtime carries out with its own copy kernels
+ *                  on CUs (epoch in 1..TLC_EPOCH_MAX)                          */
+enum { TLC_LAND_NONE = 0, TLC_LAND_COPY_ENGINE = 1, TLC_LAND_CU = 2, TLC_LAND_MEMCPY = 3 };
 
 #define TLC_MAX_WORLD 32
 
@@ -397,7 +400,7 @@ tlc_status tlc_ag_moe(const tlc_moe_args* args, void* compute_stream, void* cons
  * `bytes_per_chunk` bytes from src[c] to dst[c] and then raises
  * sig->flags[c] to epoch.  dst, src: host arrays of `world` device pointers,
  * 16-byte aligned; entries `rank` are ignored.  bytes_per_chunk % 16 == 0.
- * land: TLC_LAND_COPY_ENGINE or TLC_LAND_CU.  Used for copy-only timings. */
+ * land: TLC_LAND_COPY_ENGINE, TLC_LAND_CU or TLC_LAND_MEMCPY.  Used for copy-only timings. */
 tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_chunk,
                     int32_t world, int32_t rank, tlc_signals* sig, uint32_t epoch, int32_t land,
                     void* const* copy_streams, int32_t n_copy_streams);

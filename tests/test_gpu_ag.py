@@ -22,7 +22,7 @@ if torch.cuda.is_available():
 else:  # collected on CPU-only hosts, never run there
     from tile_level_communication_amd import tlc  # noqa: F401
 
-LANDS = {"none": 0, "copy_engine": 1, "cu": 2}
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3}
 
 SHAPES = [
     # name, W, R, K, N, tile
@@ -83,7 +83,7 @@ def test_ag_tile_order_does_not_change_bits():
                 absmax_bf16(inp.b), "order")
 
 
-@pytest.mark.parametrize("land", ["copy_engine", "cu"])
+@pytest.mark.parametrize("land", ["copy_engine", "cu", "memcpy"])
 def test_ag_fresh_data_every_call(land):
     """Landed data changes between calls (and the landing rows are poisoned
     before each call): a read of stale or not-yet-landed data fails."""
@@ -234,14 +234,15 @@ def test_ag_qwen3_ffn_up_full_size(rank):
     check_exact(prob.c.cpu().numpy(), og.ag_gemm(ii.a_chunks, ii.b), "cfg full integer")
 
 
-def test_ag_epoch_rewind_copy_engine():
+@pytest.mark.parametrize("sub", [1, 2])
+def test_ag_epoch_rewind_copy_engine(sub):
     """Copy-engine flags come from a table of TLC_EPOCH_MAX epochs: calls across
     the end of the table rewind the flags and stay correct."""
     W, R, K, N = 3, 128, 128, 256
     inp = si.ag_inputs(150, W, R, N, K)
-    prob = AGProblem(inp.a_chunks, inp.b, 2, 128, 128)
+    prob = AGProblem(inp.a_chunks, inp.b, 2, 128, 128, sub_chunks=sub)
     prob.epoch = tlc.EPOCH_MAX - 2
-    prob.sig.set(W, prob.epoch, prob.streams.compute)
+    prob.sig.set(W * sub, prob.epoch, prob.streams.compute)
     ref = og.ag_gemm(inp.a_chunks, inp.b)
     for it in range(4):
         log(f"[ag epoch rewind] call {it}, epoch before {prob.epoch}")

@@ -16,7 +16,7 @@ if torch.cuda.is_available():
     from tile_level_communication_amd import tlc
     from tile_level_communication_amd.workloads import MoEProblem
 
-LANDS = {"none": 0, "copy_engine": 1, "cu": 2}
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3}
 
 
 def _check_routing(prob, ref, order):

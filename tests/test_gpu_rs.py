@@ -16,7 +16,7 @@ if torch.cuda.is_available():
     from tile_level_communication_amd import tlc
     from tile_level_communication_amd.workloads import RSProblem
 
-LANDS = {"none": 0, "copy_engine": 1, "cu": 2}
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3}
 
 SHAPES = [
     ("w2_256x256x512_t128", 2, 128, 512, 256, 128),

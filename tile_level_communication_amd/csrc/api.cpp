@@ -66,7 +66,7 @@ tlc_status device_info(DeviceInfo* out) {
 }
 
 int reserve_for(int land) {
-  return land == TLC_LAND_COPY_ENGINE ? kReserveCUsCopyEngine
+  return (land == TLC_LAND_COPY_ENGINE || land == TLC_LAND_MEMCPY) ? kReserveCUsCopyEngine
                                       : (land == TLC_LAND_CU ? kReserveCUsLandCU : 0);
 }
 
@@ -104,17 +104,18 @@ tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, i
                            int world, int rank, int n_local, tlc_signals* sig, uint32_t epoch,
                            void* const* copy_streams, int n_copy_streams, const DeviceInfo& info) {
   if (land == TLC_LAND_NONE || world <= n_local) return TLC_OK;
-  if (land == TLC_LAND_COPY_ENGINE) {
+  if (land == TLC_LAND_COPY_ENGINE || land == TLC_LAND_MEMCPY) {
+    const hipMemcpyKind kind =
+        land == TLC_LAND_COPY_ENGINE ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
     for (int i = n_local; i < world; ++i) {
       const int c = (rank + i) % world;
       hipStream_t s = static_cast<hipStream_t>(copy_streams[(i - n_local) % n_copy_streams]);
-      tlc_status st = hip_check(hipMemcpyAsync(dst[c], src[c], static_cast<size_t>(bytes),
-                                               hipMemcpyDeviceToDeviceNoCU, s),
+      tlc_status st = hip_check(hipMemcpyAsync(dst[c], src[c], static_cast<size_t>(bytes), kind, s),
                                 "hipMemcpyAsync(landing)");
       if (st) return st;
       // the flag follows the data on the same copy engine queue
       st = hip_check(hipMemcpyAsync(&sig->flags[c], &sig->epoch_table[epoch - 1], sizeof(uint32_t),
-                                    hipMemcpyDeviceToDeviceNoCU, s),
+                                    kind, s),
                      "hipMemcpyAsync(flag)");
       if (st) return st;
     }
@@ -142,12 +143,13 @@ tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, i
 tlc_status check_land_args(int land, const void* const* src, const void* const* dst, int world,
                            int rank, int64_t bytes, const char* who, void* const* copy_streams,
                            int n_copy_streams, uint32_t epoch, int n_local = 1) {
-  if (land != TLC_LAND_NONE && land != TLC_LAND_COPY_ENGINE && land != TLC_LAND_CU)
+  if (land != TLC_LAND_NONE && land != TLC_LAND_COPY_ENGINE && land != TLC_LAND_CU &&
+      land != TLC_LAND_MEMCPY)
     return fail(TLC_ERR_INVALID_ARG, "%s: land %d unknown", who, land);
   if (land == TLC_LAND_NONE) return TLC_OK;
   if (!copy_streams || n_copy_streams < 1)
     return fail(TLC_ERR_INVALID_ARG, "%s: landing needs n_copy_streams >= 1 streams", who);
-  if (land == TLC_LAND_COPY_ENGINE && (epoch < 1 || epoch > TLC_EPOCH_MAX))
+  if ((land == TLC_LAND_COPY_ENGINE || land == TLC_LAND_MEMCPY) && (epoch < 1 || epoch > TLC_EPOCH_MAX))
     return fail(TLC_ERR_INVALID_ARG, "%s: copy-engine landing needs 1 <= epoch <= %d (got %u)", who,
                 TLC_EPOCH_MAX, epoch);
   if (!src || !dst) return fail(TLC_ERR_INVALID_ARG, "%s: landing needs source and destination arrays", who);

@@ -22,7 +22,7 @@ ERR_HIP, ERR_TIMEOUT, ERR_BAD_PLAN = -5, -6, -7
 MODE_AG, MODE_RS, MODE_MOE = 0, 1, 2
 ORDER_NATURAL, ORDER_RANK_OFFSET = 0, 1
 B_KN, B_NK = 0, 1
-LAND_NONE, LAND_COPY_ENGINE, LAND_CU = 0, 1, 2
+LAND_NONE, LAND_COPY_ENGINE, LAND_CU, LAND_MEMCPY = 0, 1, 2, 3
 SCHED_DYNAMIC, SCHED_STATIC = 0, 1
 MAX_WORLD = 32
 EPOCH_MAX = 4096

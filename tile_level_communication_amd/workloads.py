@@ -62,7 +62,7 @@ def next_epoch(prob) -> int:
         prob.streams.compute.synchronize()
         for c in prob.streams.copies:
             c.synchronize()
-        prob.sig.set(prob.world, 0, prob.streams.compute)
+        prob.sig.set(tlc.MAX_WORLD, 0, prob.streams.compute)  # sub-chunk flags included
         prob.epoch = 1
     return prob.epoch
 
@@ -127,7 +127,7 @@ class AGProblem:
         next_epoch(self)
         s = self.streams
         if land == tlc.LAND_NONE and preset_flags is not False:
-            self.sig.set(self.world, self.epoch, s.compute)
+            self.sig.set(self.world * max(self.sub_chunks, 1), self.epoch, s.compute)
         s.begin()
         tlc.ag_gemm(self.plan, self.n_tiles, self.M, self.N, self.K, self.world, self.rank, self.R,
                     self.bm, self.bn, self.a, self.a_src if land != tlc.LAND_NONE else None,
