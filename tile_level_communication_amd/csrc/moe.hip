@@ -18,9 +18,9 @@
 //                   expert, how many of the block's tokens chose it.
 //   scan_kernel     one wavefront: per expert, the prefix of those counts over
 //                   the blocks; counts, offsets and m-tile starts over experts.
-//   scatter_kernel  one wavefront per block: each (token, expert) pair's row =
-//                   offsets[e] + rows of e in earlier blocks + earlier lanes of
-//                   this block; row_token and slot.
+//   scatter_kernel  one wavefront per (block, 16 experts): each (token, expert)
+//                   pair's row = offsets[e] + rows of e in earlier blocks +
+//                   earlier lanes of this block; row_token and slot.
 //   pair_kernel     one wavefront per (expert, m-tile): readiness key and chunk
 //                   mask over the tile's rows.
 //   sort_kernel     one workgroup: stable counting sort of the (expert, m-tile)
@@ -144,29 +144,37 @@ __global__ __launch_bounds__(64) void scan_kernel(MoeDev d) {
   }
 }
 
+// One wavefront per (block of 64 arrival positions, group of 16 experts).
+constexpr int SCATTER_GROUP = 16;
+
 __global__ __launch_bounds__(64) void scatter_kernel(MoeDev d) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+  const int b = blockIdx.x, g0 = blockIdx.y * SCATTER_GROUP, lane = threadIdx.x;
   const int a = b * 64 + lane;
   const bool valid = a < d.T;
   const int t = valid ? arrival_token(d, a) : 0;
   const unsigned long long m = valid ? d.member[t] : 0ull;
-  // lane e holds the first row of expert e for this block
-  const int base = lane < d.E ? d.offsets[lane] + d.blk[static_cast<int64_t>(b) * d.E + lane] : 0;
+  // lane j < 16 holds the first row of expert g0 + j for this block
+  const int ej = g0 + lane;
+  const int base = (lane < SCATTER_GROUP && ej < d.E)
+                       ? d.offsets[ej] + d.blk[static_cast<int64_t>(b) * d.E + ej]
+                       : 0;
   int sel[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j)
     sel[j] = (valid && j < d.k) ? d.topk[static_cast<int64_t>(t) * d.k + j] : -1;
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int e = 0; e < d.E; ++e) {
-    const bool in = (m >> e) & 1ull;
+#pragma unroll
+  for (int j = 0; j < SCATTER_GROUP; ++j) {
+    const int e = g0 + j;
+    const bool in = e < d.E && ((m >> e) & 1ull);
     const unsigned long long bal = __ballot(in);
-    const int first = __shfl(base, e);
+    const int first = __shfl(base, j);
     if (in) {
       const int r = first + __popcll(bal & below);
       d.row_token[r] = t;
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (sel[j] == e) d.slot[static_cast<int64_t>(t) * d.k + j] = r;
+      for (int q = 0; q < 16; ++q)
+        if (sel[q] == e) d.slot[static_cast<int64_t>(t) * d.k + q] = r;
     }
   }
 }
@@ -281,7 +289,8 @@ tlc_status launch_moe_route(const MoeDev& d, void* stream) {
   hipLaunchKernelGGL(topk_kernel, dim3((d.T + 3) / 4), dim3(256), 0, s, d);
   hipLaunchKernelGGL(block_count_kernel, dim3(nb), dim3(64), 0, s, d);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64), 0, s, d);
-  hipLaunchKernelGGL(scatter_kernel, dim3(nb), dim3(64), 0, s, d);
+  hipLaunchKernelGGL(scatter_kernel, dim3(nb, (d.E + SCATTER_GROUP - 1) / SCATTER_GROUP), dim3(64),
+                     0, s, d);
   hipLaunchKernelGGL(pair_kernel, dim3((d.max_pairs + 3) / 4), dim3(256), 0, s, d);
   hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, s, d);
   const hipError_t e = hipGetLastError();
