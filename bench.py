@@ -8,8 +8,10 @@ whole path: the 7 peer chunks land on a side stream with hipMemcpyAsync (one
 device-to-device transfer per chunk, then a 4-byte transfer raising the chunk's
 flag), while the persistent tile-swizzled GEMM on the compute stream starts with
 the local chunk and consumes the others as their flags flip.  The same step with
-the transfers forced onto the SDMA engines and with the library's own copy
-kernel is reported beside it.  Inputs are seeded synthetic data resident in HBM.
+the transfers forced onto the SDMA engines, with the library's own copy kernel on
+reserved compute units, and with the co-located backend (the GEMM's own
+workgroups copy the chunks before computing) is reported beside it.  Inputs are
+seeded synthetic data resident in HBM.
 
 Other workloads (--workload rs | rs_long | moe) time GEMM-ReduceScatter (4096 x
 4096 x 2048, 4 chunks; 131072 x 5120 x 3200, 8 chunks) and AG-MoE (4096 tokens,
@@ -41,6 +43,7 @@ PEAK_HBM_GBS = 8000.0
 # plain-copy calibration factor 1.000.  Re-measure whenever that kernel changes.
 AG_COMPUTE_TRAFFIC_BYTES = (220280.2 + 102400.0) * 1024
 WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4}
+LANDINGS = {"memcpy": 3, "copy_engine": 1, "cu": 2, "colocated": 4}  # tlc.LAND_*
 
 
 def parse():
@@ -49,9 +52,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ag", choices=list(WORKLOAD_ID))
-    ap.add_argument("--land", default="memcpy", choices=["memcpy", "copy_engine", "cu"],
+    ap.add_argument("--land", default="memcpy", choices=list(LANDINGS),
                     help="memcpy: hipMemcpyAsync device-to-device on the side stream (default); "
-                         "copy_engine: the same forced onto the SDMA engines (NoCU); cu: our copy kernel")
+                         "copy_engine: the same forced onto the SDMA engines (NoCU); cu: our copy "
+                         "kernel on reserved CUs; colocated: the GEMM's own workgroups copy first")
+    ap.add_argument("--copy-wgs", type=int, default=0,
+                    help="colocated: workgroups that copy (0 = half the grid)")
     ap.add_argument("--layout", default="KN", choices=["KN", "NK"])
     ap.add_argument("--tile", type=int, default=256)
     ap.add_argument("--group-m", type=int, default=4)
@@ -71,9 +77,20 @@ def parse():
     return ap.parse_args()
 
 
+WARM_SECONDS = 0.5
+
+
 def timed(fn, steps, warmup, torch):
-    for _ in range(warmup):
+    # W untimed warm-up steps, continued until the GPU has been busy with this
+    # step for WARM_SECONDS: its clocks take that long to settle after an idle
+    # gap, and the first measurement of a process otherwise runs slow
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < WARM_SECONDS:
         fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -96,9 +113,20 @@ class KernelTimer:
         e1.record(self.stream)
         self.pairs.append((e0, e1))
 
-    def mean_ms(self, skip):
+    def mean_ms(self, last):
+        """Mean over the last `last` launches (the timed ones)."""
         import numpy as np
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs[skip:]]))
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs[-last:]]))
+
+
+def other_landings(flops, t_comp, others, t_copy_others):
+    """The same step with the other landing backends, for the JSON line."""
+    names = {v: k for k, v in LANDINGS.items()}
+    return {names[o]: {"value": round(flops / t_f / 1e12, 2), "ms_per_step": round(t_f * 1e3, 4),
+                       "copy_only_ms": round(t_copy_others[o] * 1e3, 4),
+                       "overlap_efficiency": round(max(t_comp, t_copy_others[o]) / t_f, 4),
+                       "device_status": st}
+            for o, (t_f, st) in others.items()}
 
 
 def cpu_baseline(kind, inp, budget_s, rank=0):
@@ -168,7 +196,7 @@ def run_ag(args, torch, tlc, si, workloads):
     dev = torch.device("cuda:0")
     inp = si.workload_inputs(2)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
-    land = {"copy_engine": tlc.LAND_COPY_ENGINE, "cu": tlc.LAND_CU, "memcpy": tlc.LAND_MEMCPY}[args.land]
+    land = LANDINGS[args.land]
     # fused plan: whole tiles; with the slow SDMA landing the last chunk's tiles
     # are cut in two along K, so that the tail after the last landing runs on
     # twice as many compute units
@@ -198,7 +226,8 @@ def run_ag(args, torch, tlc, si, workloads):
             for c in copies:
                 c.wait_stream(compute)
             run = lambda: tlc.ag_gemm(**call, a_src=prob.a_src, epoch=prob.epoch, land=land_kind,
-                                      compute_stream=compute, copy_stream=copies, grid=args.grid)
+                                      compute_stream=compute, copy_stream=copies, grid=args.grid,
+                                      copy_wgs=args.copy_wgs)
             timer(run) if timer else run()
             for c in copies:
                 compute.wait_stream(c)
@@ -206,17 +235,12 @@ def run_ag(args, torch, tlc, si, workloads):
 
     fused_t = KernelTimer(torch, compute)
     t_fused = timed(fused_step(land, fused_t), args.steps, args.warmup, torch)
-    gemm_fused_ms = fused_t.mean_ms(args.warmup)
+    gemm_fused_ms = fused_t.mean_ms(args.steps)
     status = prob.sig.read_status(compute)
 
     # the same step with the other landing backends (reported beside the headline)
-    names = {tlc.LAND_COPY_ENGINE: "copy_engine", tlc.LAND_CU: "cu", tlc.LAND_MEMCPY: "memcpy"}
-    others = {}
-    for other in names:
-        if other == land:
-            continue
-        t_f = timed(fused_step(other), args.steps, args.warmup, torch)
-        others[other] = (t_f, prob.sig.read_status(compute))
+    others = {o: (timed(fused_step(o), args.steps, args.warmup, torch), prob.sig.read_status(compute))
+              for o in LANDINGS.values() if o != land}
 
     def copy_only_step(land_kind):
         # the landing sequence of the fused step alone (an AG call with no units)
@@ -225,7 +249,7 @@ def run_ag(args, torch, tlc, si, workloads):
             for c in copies:
                 c.wait_stream(compute)
             tlc.ag_gemm(**dict(call, n_tiles=0), a_src=prob.a_src, epoch=prob.epoch, land=land_kind,
-                        compute_stream=compute, copy_stream=copies)
+                        compute_stream=compute, copy_stream=copies, copy_wgs=args.copy_wgs)
             for c in copies:
                 compute.wait_stream(c)
         return step
@@ -249,7 +273,7 @@ def run_ag(args, torch, tlc, si, workloads):
                                    compute_stream=compute, copy_stream=None, grid=0))
 
     t_comp = timed(compute_only, args.steps, args.warmup, torch)
-    gemm_comp_ms = comp_t.mean_ms(args.warmup)
+    gemm_comp_ms = comp_t.mean_ms(args.steps)
     torch.cuda.synchronize()
     achieved = flops / (gemm_comp_ms * 1e-3) / 1e12
     extra = {
@@ -275,12 +299,7 @@ def run_ag(args, torch, tlc, si, workloads):
         "copy_gbs": round((prob.world - 1) * prob.R * prob.K * 2 / t_copy / 1e9, 1),
         "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,
-        "other_landings": {
-            names[o]: {"value": round(flops / t_f / 1e12, 2), "ms_per_step": round(t_f * 1e3, 4),
-                       "copy_only_ms": round(t_copy_others[o] * 1e3, 4),
-                       "overlap_efficiency": round(max(t_comp, t_copy_others[o]) / t_f, 4),
-                       "device_status": st}
-            for o, (t_f, st) in others.items()},
+        "other_landings": other_landings(flops, t_comp, others, t_copy_others),
     }
     line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
     if not args.no_cpu_baseline:
@@ -293,7 +312,7 @@ def run_rs(args, torch, tlc, si, workloads, wid):
     dev = torch.device("cuda:0")
     inp = si.workload_inputs(wid, rank=args.rank)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
-    land = {"copy_engine": tlc.LAND_COPY_ENGINE, "cu": tlc.LAND_CU, "memcpy": tlc.LAND_MEMCPY}[args.land]
+    land = LANDINGS[args.land]
     split_k = 0 if args.split_k is None else args.split_k
     split_from = 1 if args.split_from is None else args.split_from
     args.schedule = args.schedule or "static"
@@ -310,16 +329,34 @@ def run_rs(args, torch, tlc, si, workloads, wid):
     torch.cuda.synchronize()
     steps, warm = args.steps, args.warmup
 
-    def fused():
-        workloads.next_epoch(prob)
-        for c in copies:
-            c.wait_stream(compute)
-        tlc.gemm_rs(*prob._args(), prob.remote_src, prob.landing, prob.out, prob.sig, prob.epoch,
-                    land, compute, copies, args.grid, **ws)
-        for c in copies:
-            compute.wait_stream(c)
+    def fused_step(land_kind):
+        def step():
+            workloads.next_epoch(prob)
+            for c in copies:
+                c.wait_stream(compute)
+            tlc.gemm_rs(*prob._args(), prob.remote_src, prob.landing, prob.out, prob.sig, prob.epoch,
+                        land_kind, compute, copies, args.grid, **ws)
+            for c in copies:
+                compute.wait_stream(c)
+        return step
 
-    t_fused = timed(fused, steps, warm, torch)
+    def copy_only_step(land_kind):
+        def step():
+            workloads.next_epoch(prob)
+            for c in copies:
+                c.wait_stream(compute)
+            tlc.land(prob.landing, prob.remote_src, prob.R * prob.N * 4, prob.world, prob.rank,
+                     prob.sig, prob.epoch, land_kind, copies)
+            for c in copies:
+                compute.wait_stream(c)
+        return step
+
+    t_fused = timed(fused_step(land), steps, warm, torch)
+    status = prob.sig.read_status(compute)
+    others = {o: (timed(fused_step(o), steps, warm, torch), prob.sig.read_status(compute))
+              for o in LANDINGS.values() if o != land}
+    t_copy = timed(copy_only_step(land), steps, warm, torch)
+    t_copy_others = {o: timed(copy_only_step(o), steps, warm, torch) for o in others}
     prob.place_all()
     prob.sig.set(prob.world, tlc.EPOCH_MAX, compute)
     torch.cuda.synchronize()
@@ -337,21 +374,10 @@ def run_rs(args, torch, tlc, si, workloads, wid):
                                     tlc.EPOCH_MAX, tlc.LAND_NONE, compute))
 
     timed(reduce_only, steps, warm, torch)
-    red_ms = red_t.mean_ms(warm)
+    red_ms = red_t.mean_ms(steps)
 
-    def copy_only():
-        workloads.next_epoch(prob)
-        for c in copies:
-            c.wait_stream(compute)
-        tlc.land(prob.landing, prob.remote_src, prob.R * prob.N * 4, prob.world, prob.rank, prob.sig,
-                 prob.epoch, land, copies)
-        for c in copies:
-            compute.wait_stream(c)
-
-    t_copy = timed(copy_only, steps, warm, torch)
     torch.cuda.synchronize()
-    status = prob.sig.read_status(compute)
-    gemm_ms = comp_t.mean_ms(warm) - red_ms
+    gemm_ms = comp_t.mean_ms(steps) - red_ms
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     red_gbs = prob.reduce_bytes / (red_ms * 1e-3) / 1e9
     extra = {
@@ -371,6 +397,7 @@ def run_rs(args, torch, tlc, si, workloads, wid):
         "copy_only_ms": round(t_copy * 1e3, 4),
         "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,
+        "other_landings": other_landings(flops, t_comp, others, t_copy_others),
     }
     line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
     if not args.no_cpu_baseline:
@@ -383,7 +410,7 @@ def run_moe(args, torch, tlc, si, workloads):
     dev = torch.device("cuda:0")
     inp = si.workload_inputs(4)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
-    land = {"copy_engine": tlc.LAND_COPY_ENGINE, "cu": tlc.LAND_CU, "memcpy": tlc.LAND_MEMCPY}[args.land]
+    land = LANDINGS[args.land]
     schedule = tlc.SCHED_STATIC if args.schedule == "static" else tlc.SCHED_DYNAMIC
     prob = workloads.MoEProblem(inp.x_chunks, inp.logits, inp.w, args.rank, wl.topk, args.tile,
                                 args.tile, layout, device=dev)
@@ -396,10 +423,16 @@ def run_moe(args, torch, tlc, si, workloads):
 
     # fused step: routing on the compute stream while the peers' tokens land,
     # then the readiness-sorted grouped GEMM consuming chunks as they arrive
-    t_fused = timed(lambda: prob.run(land, grid=args.grid), args.steps, args.warmup, torch)
-    status = prob.sig.read_status(compute)
+    def fused_step(land_kind):
+        return lambda: prob.run(land_kind, grid=args.grid, copy_wgs=args.copy_wgs)
 
+    t_fused = timed(fused_step(land), args.steps, args.warmup, torch)
+    status = prob.sig.read_status(compute)
+    others = {o: (timed(fused_step(o), args.steps, args.warmup, torch), prob.sig.read_status(compute))
+              for o in LANDINGS.values() if o != land}
     t_copy = timed(lambda: prob.land_only(land), args.steps, args.warmup, torch)
+    t_copy_others = {o: timed(lambda o=o: prob.land_only(o), args.steps, args.warmup, torch)
+                     for o in others}
 
     prob.place_all()
     torch.cuda.synchronize()
@@ -415,8 +448,8 @@ def run_moe(args, torch, tlc, si, workloads):
 
     t_comp = timed(compute_only, args.steps, args.warmup, torch)
     torch.cuda.synchronize()
-    gemm_ms = gemm_t.mean_ms(args.warmup)
-    route_ms = route_t.mean_ms(args.warmup)
+    gemm_ms = gemm_t.mean_ms(args.steps)
+    route_ms = route_t.mean_ms(args.steps)
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     extra = {
         "config": {"workload": wl.name, "tokens": prob.T, "experts": prob.E, "topk": prob.k,
@@ -434,6 +467,7 @@ def run_moe(args, torch, tlc, si, workloads):
         "copy_only_ms": round(t_copy * 1e3, 4),
         "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,
+        "other_landings": other_landings(flops, t_comp, others, t_copy_others),
     }
     return base_line(args, flops / t_fused / 1e12, t_fused, extra)
 

@@ -87,8 +87,24 @@ enum { TLC_B_KN = 0, TLC_B_NK = 1 };
  *                  publishes its flag with a release store
  *   MEMCPY      -- as COPY_ENGINE but with the default hipMemcpyDeviceToDevice
  *                  kind, which the runtime carries out with its own copy kernels
- *                  on CUs (epoch in 1..TLC_EPOCH_MAX)                          */
-enum { TLC_LAND_NONE = 0, TLC_LAND_COPY_ENGINE = 1, TLC_LAND_CU = 2, TLC_LAND_MEMCPY = 3 };
+ *                  on CUs (epoch in 1..TLC_EPOCH_MAX)
+ *   COLOCATED   -- no separate landing: the GEMM's own workgroups move the data
+ *                  (AutoOverlap §5.2, backend 5: load/store on the SMs that
+ *                  compute).  AG-GEMM / AG-MoE: before its first unit, each of
+ *                  the first copy_wgs workgroups copies an equal share of every
+ *                  peer chunk in landing order; the last workgroup to finish a
+ *                  chunk's shares raises its flag with a release store, and the
+ *                  GEMM's units wait on the flags as in the other modes.
+ *                  GEMM-RS: the reduce loads the peers' partials from
+ *                  remote_src itself (no landing buffers, no flags).  The copy
+ *                  streams are not used (they may be NULL / 0).            */
+enum {
+  TLC_LAND_NONE = 0,
+  TLC_LAND_COPY_ENGINE = 1,
+  TLC_LAND_CU = 2,
+  TLC_LAND_MEMCPY = 3,
+  TLC_LAND_COLOCATED = 4
+};
 
 #define TLC_MAX_WORLD 32
 
@@ -125,7 +141,7 @@ typedef struct {
  * engines).  flags[c] >= epoch  <=>  chunk c has landed for this call.
  * status[0] = 0 or a negative tlc_status, status[1] = plan index of the tile
  * that failed, status[2] = chunk it waited for.  land_count is internal to the
- * CU landing backend, work_next / work_done to the GEMM's dynamic work queue
+ * CU and co-located landings, work_next / work_done to the GEMM's dynamic work queue
  * (all zero between calls; the last workgroup of a launch resets them).
  * epoch_table[i] = i + 1, written once by tlc_signals_alloc.  One GEMM call
  * at a time per signals block. */
@@ -267,6 +283,9 @@ typedef struct {
    * rows_per_chunk / S rows, each raising its own flag (flags[c * S + j]); the
    * plan must be built with the same sub_chunks.  world * S <= 32. */
   int32_t sub_chunks;
+  /* TLC_LAND_COLOCATED only: workgroups that copy before computing
+   * (1..grid; 0 = half the grid, a multiple of 8). */
+  int32_t copy_wgs;
   /* Optional debug trace (NULL = off): device int64 array of n_tiles x 4,
    * entry t = {workgroup, wall-clock at wait start, at wait end, at tile end}
    * for the tile at plan index t; wall clock = the device's constant-rate
@@ -288,7 +307,8 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* args, void* compute_stream, void* cons
  * Requirements as tlc_ag_gemm plus N % 4 == 0.  plan: mode RS.
  *   remote_src / landing: host arrays of `world` device pointers (R x N f32);
  *   entries `rank` are ignored; remote_src may be NULL if land == NONE (then
- *   landing[s] must already hold the data and flags be >= epoch).
+ *   landing[s] must already hold the data and flags be >= epoch); landing may
+ *   be NULL if land == COLOCATED (the reduce reads remote_src directly).
  * The GEMM and then the reduce run on `compute`; the reduce waits in-kernel for
  * the remote partials' flags.  */
 typedef struct {
@@ -388,6 +408,7 @@ typedef struct {
   int32_t grid;
   int64_t timeout_ns;
   int32_t schedule; /* TLC_SCHED_* as in tlc_ag_args (MoE tiles are never split) */
+  int32_t copy_wgs; /* as in tlc_ag_args */
 } tlc_moe_args;
 
 tlc_status tlc_ag_moe(const tlc_moe_args* args, void* compute_stream, void* const* copy_streams,
@@ -400,7 +421,10 @@ tlc_status tlc_ag_moe(const tlc_moe_args* args, void* compute_stream, void* cons
  * `bytes_per_chunk` bytes from src[c] to dst[c] and then raises
  * sig->flags[c] to epoch.  dst, src: host arrays of `world` device pointers,
  * 16-byte aligned; entries `rank` are ignored.  bytes_per_chunk % 16 == 0.
- * land: TLC_LAND_COPY_ENGINE, TLC_LAND_CU or TLC_LAND_MEMCPY.  Used for copy-only timings. */
+ * land: TLC_LAND_COPY_ENGINE, TLC_LAND_CU, TLC_LAND_MEMCPY, or TLC_LAND_COLOCATED
+ * (the co-located copy work alone: the GEMM kernel with no units, its default
+ * number of copying workgroups, on copy_streams[0]).  Used for copy-only
+ * timings. */
 tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_chunk,
                     int32_t world, int32_t rank, tlc_signals* sig, uint32_t epoch, int32_t land,
                     void* const* copy_streams, int32_t n_copy_streams);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tlc.version() == 110
+    assert tlc.version() == 120
     assert tlc.status_string(tlc.ERR_TIMEOUT).startswith("timeout")
     assert tlc.status_string(0) == "ok"
 
@@ -71,6 +71,19 @@ def test_ag_gemm_argument_errors(over, want):
     s = tlc.lib().tlc_ag_gemm(C.byref(args), None, None, 0)
     assert s == want, tlc.last_error()
     assert tlc.last_error()
+
+
+def test_colocated_landing_argument_errors():
+    # the co-located landing raises flags from the kernel: epoch 0 would mean
+    # "already landed" and is refused; no copy streams are needed
+    src = (C.c_void_p * 2)(4096, 8192)
+    args = _ag_args(a=16, b=32, c=48, sig=64, land=tlc.LAND_COLOCATED, epoch=0,
+                    a_src=C.cast(src, C.POINTER(C.c_void_p)))
+    assert tlc.lib().tlc_ag_gemm(C.byref(args), None, None, 0) == tlc.ERR_INVALID_ARG
+    assert "epoch" in tlc.last_error()
+    d = (C.c_void_p * 2)(4096, 8192)
+    s = tlc.lib().tlc_land(d, src, 1024, 2, 0, C.c_void_p(64), 0, tlc.LAND_COLOCATED, None, 0)
+    assert s == tlc.ERR_INVALID_ARG and "epoch" in tlc.last_error()
 
 
 def test_plan_capacity_and_query():

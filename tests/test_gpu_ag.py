@@ -22,7 +22,7 @@ if torch.cuda.is_available():
 else:  # collected on CPU-only hosts, never run there
     from tile_level_communication_amd import tlc  # noqa: F401
 
-LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3}
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3, "colocated": 4}
 
 SHAPES = [
     # name, W, R, K, N, tile
@@ -83,7 +83,7 @@ def test_ag_tile_order_does_not_change_bits():
                 absmax_bf16(inp.b), "order")
 
 
-@pytest.mark.parametrize("land", ["copy_engine", "cu", "memcpy"])
+@pytest.mark.parametrize("land", ["copy_engine", "cu", "memcpy", "colocated"])
 def test_ag_fresh_data_every_call(land):
     """Landed data changes between calls (and the landing rows are poisoned
     before each call): a read of stale or not-yet-landed data fails."""
@@ -106,7 +106,7 @@ def test_ag_fresh_data_every_call(land):
 
 @pytest.mark.parametrize("sched", ["dynamic", "static"])
 @pytest.mark.parametrize("split", [(2, 0), (3, 1)], ids=["s2_from0", "s3_from1"])
-@pytest.mark.parametrize("land", ["copy_engine", "cu"])
+@pytest.mark.parametrize("land", ["copy_engine", "cu", "colocated"])
 def test_ag_split_parity(land, split, sched):
     """Tiles split along K (one K range per unit, fixup in split order), both
     schedules; K = 128 with three splits leaves one unit an empty K range."""
@@ -155,7 +155,7 @@ def test_ag_split_result_independent_of_schedule():
 
 
 @pytest.mark.parametrize("sub", [2, 4])
-@pytest.mark.parametrize("land", ["copy_engine", "cu"])
+@pytest.mark.parametrize("land", ["copy_engine", "cu", "colocated"])
 def test_ag_subchunk_parity(land, sub):
     """Each peer chunk lands as `sub` pieces with their own flags; tiles wait
     for exactly the pieces their rows read (straddling tiles included)."""
@@ -173,6 +173,64 @@ def test_ag_subchunk_parity(land, sub):
                     check_exact(c, ref, name)
                 else:
                     check_close(c, ref, K, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), name)
+
+
+def test_ag_colocated_copy_workgroups_and_grid():
+    """Co-located landing: the output bits do not depend on how many
+    workgroups copy or on the grid, and consecutive calls reuse the arrival
+    counters (they are back at zero after every chunk)."""
+    W, R, K, N = 4, 160, 256, 520
+    inp = si.ag_inputs(190, W, R, N, K)
+    outs = []
+    for schedule in (tlc.SCHED_DYNAMIC, tlc.SCHED_STATIC):
+        for grid, cw in ((0, 0), (1, 1), (3, 2), (16, 16), (16, 5), (24, 1)):
+            prob = AGProblem(inp.a_chunks, inp.b, 2, 128, 128, tlc.B_KN, schedule=schedule)
+            for call in range(2):
+                log(f"[ag coloc] schedule={schedule} grid={grid} copy_wgs={cw} call={call}")
+                prob.poison_remote()
+                prob.run(tlc.LAND_COLOCATED, grid=grid, copy_wgs=cw)
+                torch.cuda.synchronize()
+                assert prob.sig.read_status()[0] == 0
+                outs.append(prob.c.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    check_close(outs[0], og.ag_gemm(inp.a_chunks, inp.b), K, absmax_bf16(inp.a_chunks),
+                absmax_bf16(inp.b), "coloc")
+
+
+def test_ag_colocated_copy_only_and_errors():
+    """The copy work alone (no units) lands every chunk and raises its flag;
+    more copying workgroups than the grid is an argument error."""
+    W, R, K, N = 5, 96, 192, 136
+    inp = si.ag_inputs(191, W, R, N, K)
+    prob = AGProblem(inp.a_chunks, inp.b, 3, 128, 128, tlc.B_KN)
+    want = np.concatenate([c.view(np.int16) for c in inp.a_chunks])
+    for how in ("ag_gemm_no_tiles", "tlc_land"):
+        log(f"[ag coloc copy-only] {how}")
+        prob.poison_remote()
+        if how == "tlc_land":
+            prob.land_only(tlc.LAND_COLOCATED)
+        else:
+            n = prob.n_tiles
+            prob.n_tiles = 0
+            prob.run(tlc.LAND_COLOCATED, copy_wgs=3)
+            prob.n_tiles = n
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        got = prob.a.view(torch.int16).cpu().numpy()
+        assert np.array_equal(got, want)
+        # the flags reached this epoch: a GEMM that waits on them (no landing,
+        # 200 ms limit) finds every chunk ready
+        tlc.ag_gemm(prob.plan, prob.n_tiles, prob.M, prob.N, prob.K, W, 3, R, 128, 128, prob.a, None,
+                    prob.b, tlc.B_KN, prob.c, prob.sig, prob.epoch, tlc.LAND_NONE,
+                    prob.streams.compute, None, 0, 200_000_000)
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        check_close(prob.c.cpu().numpy(), og.ag_gemm(inp.a_chunks, inp.b), K,
+                    absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), how)
+    with pytest.raises(RuntimeError, match="copy_wgs"):
+        prob.run(tlc.LAND_COLOCATED, grid=4, copy_wgs=5)
+    torch.cuda.synchronize()
 
 
 def test_ag_timeout_reports_status():
@@ -223,6 +281,15 @@ def test_ag_qwen3_ffn_up_full_size(rank):
     assert prob.sig.read_status()[0] == 0
     got = prob.c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
     check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), "cfg full rows split")
+    # co-located landing: the GEMM's workgroups copy the chunks themselves
+    log(f"[ag full] {wl.name} rank={rank}: co-located landing, dynamic schedule")
+    prob = AGProblem(inp.a_chunks, inp.b, rank, 256, 256, tlc.B_KN)
+    prob.poison_remote()
+    prob.run(tlc.LAND_COLOCATED)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    got = prob.c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
+    check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), "cfg full rows coloc")
     # integer-valued inputs: the whole output bit for bit
     log(f"[ag full] {wl.name} rank={rank}: integer inputs, full compare")
     ii = si.workload_inputs(2, integer=True)

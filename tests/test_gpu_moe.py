@@ -16,7 +16,7 @@ if torch.cuda.is_available():
     from tile_level_communication_amd import tlc
     from tile_level_communication_amd.workloads import MoEProblem
 
-LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3}
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3, "colocated": 4}
 
 
 def _check_routing(prob, ref, order):
@@ -101,3 +101,12 @@ def test_moe_full_size(rank):
     y_ref = om.grouped_gemm(inp.x_chunks, inp.w, ref["offsets"], ref["row_token"])
     check_close(prob.y.cpu().numpy(), y_ref, wl.k, absmax_bf16(inp.x_chunks), absmax_bf16(inp.w),
                 "moe full")
+    log(f"[moe full] {wl.name} rank={rank}: co-located landing")
+    prob.poison_remote()
+    prob.y.fill_(float("nan"))
+    prob.run(tlc.LAND_COLOCATED)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    _check_routing(prob, ref, tlc.ORDER_RANK_OFFSET)
+    check_close(prob.y.cpu().numpy(), y_ref, wl.k, absmax_bf16(inp.x_chunks), absmax_bf16(inp.w),
+                "moe full coloc")

@@ -16,7 +16,7 @@ if torch.cuda.is_available():
     from tile_level_communication_amd import tlc
     from tile_level_communication_amd.workloads import RSProblem
 
-LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3}
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3, "colocated": 4}
 
 SHAPES = [
     ("w2_256x256x512_t128", 2, 128, 512, 256, 128),
@@ -125,6 +125,13 @@ def test_rs_ffn_down_128k_sampled(rank):
     rows = np.array([c * R + o for c in range(wl.world) for o in (0, R // 2, R - 1)])
     got = prob.partials[torch.from_numpy(rows).to(prob.out.device)].cpu().numpy()
     check_close(got, og.gemm_partial(inp.a, inp.b, rows), wl.k, am, bm, "partial rows")
+    # co-located: the reduce reads the peers' partials where they are
+    log(f"[rs 128k] rank={rank}: co-located landing")
+    prob.out.fill_(float("nan"))
+    prob.run(tlc.LAND_COLOCATED)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    check_close(prob.out[idx].cpu().numpy(), out_ref, wl.k, am, bm, "out rows coloc")
 
 
 @pytest.mark.parametrize("sched", ["dynamic", "static"])

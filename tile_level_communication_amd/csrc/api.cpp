@@ -103,7 +103,8 @@ tlc_status hip_check(hipError_t e, const char* what) {
 tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, int64_t bytes,
                            int world, int rank, int n_local, tlc_signals* sig, uint32_t epoch,
                            void* const* copy_streams, int n_copy_streams, const DeviceInfo& info) {
-  if (land == TLC_LAND_NONE || world <= n_local) return TLC_OK;
+  // the co-located landing is carried out by the GEMM kernel itself
+  if (land == TLC_LAND_NONE || land == TLC_LAND_COLOCATED || world <= n_local) return TLC_OK;
   if (land == TLC_LAND_COPY_ENGINE || land == TLC_LAND_MEMCPY) {
     const hipMemcpyKind kind =
         land == TLC_LAND_COPY_ENGINE ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
@@ -144,11 +145,14 @@ tlc_status check_land_args(int land, const void* const* src, const void* const* 
                            int rank, int64_t bytes, const char* who, void* const* copy_streams,
                            int n_copy_streams, uint32_t epoch, int n_local = 1) {
   if (land != TLC_LAND_NONE && land != TLC_LAND_COPY_ENGINE && land != TLC_LAND_CU &&
-      land != TLC_LAND_MEMCPY)
+      land != TLC_LAND_MEMCPY && land != TLC_LAND_COLOCATED)
     return fail(TLC_ERR_INVALID_ARG, "%s: land %d unknown", who, land);
   if (land == TLC_LAND_NONE) return TLC_OK;
-  if (!copy_streams || n_copy_streams < 1)
+  if (land == TLC_LAND_COLOCATED) {
+    if (epoch < 1) return fail(TLC_ERR_INVALID_ARG, "%s: co-located landing needs epoch >= 1", who);
+  } else if (!copy_streams || n_copy_streams < 1) {
     return fail(TLC_ERR_INVALID_ARG, "%s: landing needs n_copy_streams >= 1 streams", who);
+  }
   if ((land == TLC_LAND_COPY_ENGINE || land == TLC_LAND_MEMCPY) && (epoch < 1 || epoch > TLC_EPOCH_MAX))
     return fail(TLC_ERR_INVALID_ARG, "%s: copy-engine landing needs 1 <= epoch <= %d (got %u)", who,
                 TLC_EPOCH_MAX, epoch);
@@ -206,6 +210,30 @@ void set_schedule(GemmParams* p, int32_t schedule, void* ws, int64_t ws_bytes) {
   p->dynamic = schedule == TLC_SCHED_DYNAMIC;
   p->split_ws = static_cast<char*>(ws);
   p->split_bytes = ws ? ws_bytes : 0;
+}
+
+// Co-located landing: the chunks in landing order (rank+n_local, ... mod W)
+// and the number of workgroups that copy them (0 = half the grid, a multiple
+// of 8, at least 8 or the whole grid if smaller).
+tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src, int64_t bytes,
+                         int world, int rank, int n_local, int copy_wgs, int grid, const char* who) {
+  if (copy_wgs < 0 || copy_wgs > grid)
+    return fail(TLC_ERR_INVALID_ARG, "%s: copy_wgs %d outside 0..grid %d", who, copy_wgs, grid);
+  int cw = copy_wgs;
+  if (cw == 0) {
+    cw = grid / 2 / 8 * 8;
+    if (cw < 8) cw = grid < 8 ? grid : 8;
+  }
+  p->copy_wgs = world > n_local ? cw : 0;
+  p->copy_chunks = world - n_local;
+  p->copy_vec = bytes / 16;
+  for (int i = n_local; i < world; ++i) {
+    const int c = (rank + i) % world;
+    p->copy_src[i - n_local] = static_cast<const uint4*>(src[c]);
+    p->copy_dst[i - n_local] = static_cast<uint4*>(dst[c]);
+    p->copy_flag[i - n_local] = c;
+  }
+  return TLC_OK;
 }
 
 // Persistent grid: every CU left free (dynamic: no more workgroups than
@@ -277,13 +305,27 @@ tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_
                     void* const* copy_streams, int32_t n_copy_streams) {
   if (world < 1 || world > TLC_MAX_WORLD || rank < 0 || rank >= world || !sig || bytes_per_chunk < 0)
     return fail(TLC_ERR_INVALID_ARG, "tlc_land: bad world/rank/signals/size");
-  if (land == TLC_LAND_NONE) return fail(TLC_ERR_INVALID_ARG, "tlc_land: land must be COPY_ENGINE or CU");
+  if (land == TLC_LAND_NONE) return fail(TLC_ERR_INVALID_ARG, "tlc_land: land must not be NONE");
   tlc_status st = check_land_args(land, src, dst, world, rank, bytes_per_chunk, "tlc_land",
                                   copy_streams, n_copy_streams, epoch);
   if (st) return st;
   DeviceInfo info;
   st = device_info(&info);
   if (st) return st;
+  if (land == TLC_LAND_COLOCATED) {
+    if (world < 2) return ok();
+    // the GEMM kernel with no units: only its copying workgroups do work
+    GemmParams p;
+    memset(&p, 0, sizeof(p));
+    p.do_wait = 1;
+    p.sig = sig;
+    p.epoch = epoch;
+    st = set_colocated(&p, dst, src, bytes_per_chunk, world, rank, 1, 0, info.cus, "tlc_land");
+    if (st) return st;
+    st = launch_gemm(p, 256, 256, TLC_B_KN, KIND_DENSE, p.copy_wgs,
+                     copy_streams && n_copy_streams > 0 ? copy_streams[0] : nullptr);
+    return st ? st : ok();
+  }
   st = enqueue_landing(land, dst, src, bytes_per_chunk, world, rank, 1, sig, epoch, copy_streams,
                        n_copy_streams, info);
   return st ? st : ok();
@@ -330,7 +372,8 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   st = enqueue_landing(a->land, dst, src, chunk_bytes, Wf, rf, S, a->sig, a->epoch, copy_streams,
                        n_copy_streams, info);
   if (st) return st;
-  if (a->n_tiles == 0) return ok();
+  const bool coloc = a->land == TLC_LAND_COLOCATED && Wf > S;
+  if (a->n_tiles == 0 && !coloc) return ok();
 
   GemmParams p;
   memset(&p, 0, sizeof(p));
@@ -354,7 +397,15 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   p.trace = a->trace;
   set_schedule(&p, a->schedule, a->workspace, a->workspace_bytes);
   const int avail = info.cus - (p.do_wait ? reserve_for(a->land) : 0);
-  const int grid = pick_grid(a->grid, p.dynamic, a->n_tiles, avail);
+  // no units (copy-only run of the co-located landing): one workgroup per
+  // copying workgroup of a full grid
+  int grid = a->n_tiles > 0 ? pick_grid(a->grid, p.dynamic, a->n_tiles, avail)
+                            : (a->grid > 0 ? a->grid : avail);
+  if (coloc) {
+    st = set_colocated(&p, dst, src, chunk_bytes, Wf, rf, S, a->copy_wgs, grid, "tlc_ag_gemm");
+    if (st) return st;
+    if (a->n_tiles == 0) grid = p.copy_wgs;
+  }
   p.xcd_remap = grid % 8 == 0;
   st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
   return st ? st : ok();
@@ -371,19 +422,28 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
   if (st) return st;
   if (a->N % 4 != 0) return fail(TLC_ERR_UNSUPPORTED, "tlc_gemm_rs: N %% 4 != 0");
   if (!a->out || !aligned16(a->out)) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: out NULL or misaligned");
-  if (a->world > 1 && !a->landing) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: NULL landing array");
-  for (int s = 0; s < a->world; ++s) {
-    if (s == a->rank) continue;
-    if (!a->landing[s] || !aligned16(a->landing[s]))
-      return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: landing[%d] NULL or misaligned", s);
-  }
   const int64_t slice = static_cast<int64_t>(a->rows_per_chunk) * a->N;
   const int64_t slice_bytes = slice * 4;
-  int land = run_gemm ? a->land : TLC_LAND_NONE;
-  st = check_land_args(land, reinterpret_cast<const void* const*>(a->remote_src),
-                       reinterpret_cast<const void* const*>(a->landing), a->world, a->rank, slice_bytes,
-                       "tlc_gemm_rs", copy_streams, n_copy_streams, a->epoch);
-  if (st) return st;
+  const int land = run_gemm ? a->land : TLC_LAND_NONE;
+  // co-located: the reduce reads the peers' partials where they are
+  const bool coloc = land == TLC_LAND_COLOCATED;
+  const float* const* peer = coloc ? a->remote_src : a->landing;
+  if (a->world > 1 && !peer)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: NULL %s array", coloc ? "remote_src" : "landing");
+  for (int s = 0; s < a->world; ++s) {
+    if (s == a->rank) continue;
+    if (!peer[s] || !aligned16(peer[s]))
+      return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: %s[%d] NULL or misaligned",
+                  coloc ? "remote_src" : "landing", s);
+  }
+  if (coloc && a->epoch < 1)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: co-located landing needs epoch >= 1");
+  if (!coloc) {
+    st = check_land_args(land, reinterpret_cast<const void* const*>(a->remote_src),
+                         reinterpret_cast<const void* const*>(a->landing), a->world, a->rank,
+                         slice_bytes, "tlc_gemm_rs", copy_streams, n_copy_streams, a->epoch);
+    if (st) return st;
+  }
   DeviceInfo info;
   st = device_info(&info);
   if (st) return st;
@@ -422,11 +482,11 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
   ReduceParams r;
   memset(&r, 0, sizeof(r));
   for (int s = 0; s < a->world; ++s)
-    r.src[s] = s == a->rank ? a->partials + a->rank * slice : a->landing[s];
+    r.src[s] = s == a->rank ? a->partials + a->rank * slice : peer[s];
   r.out = a->out;
   r.n_vec4 = slice / 4;
   r.world = a->world;
-  r.wait_mask = ((a->world == 32) ? 0xFFFFFFFFu : ((1u << a->world) - 1u)) & ~(1u << a->rank);
+  r.wait_mask = coloc ? 0u : ((a->world == 32) ? 0xFFFFFFFFu : ((1u << a->world) - 1u)) & ~(1u << a->rank);
   r.sig = a->sig;
   r.epoch = a->epoch;
   r.timeout_ticks = ticks_for(a->timeout_ns, info);
@@ -582,6 +642,11 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
   const int avail = info.cus - (p.do_wait ? reserve_for(a->land) : 0);
   // The tile count is only known on the device: use every available CU.
   int grid = a->grid > 0 ? a->grid : (avail >= 8 ? avail / 8 * 8 : avail);
+  if (a->land == TLC_LAND_COLOCATED) {
+    st = set_colocated(&p, dst, a->x_src, chunk_bytes, a->world, a->rank, 1, a->copy_wgs, grid,
+                       "tlc_ag_moe");
+    if (st) return st;
+  }
   p.xcd_remap = grid % 8 == 0;
   st = launch_gemm(p, a->bm, a->bn, a->w_layout, KIND_MOE, grid, compute_stream);
   return st ? st : ok();
@@ -603,6 +668,6 @@ const char* tlc_status_string(tlc_status s) {
 
 const char* tlc_last_error(void) { return g_err; }
 
-int32_t tlc_version(void) { return 110; }
+int32_t tlc_version(void) { return 120; }
 
 }  // extern "C"

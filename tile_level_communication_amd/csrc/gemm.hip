@@ -498,6 +498,54 @@ struct Tile8w {
   }
 };
 
+// Co-located landing (AutoOverlap §5.2, backend 5: load/store transfers on the
+// SMs that compute, coordinated through global-memory signals).  Workgroup g <
+// copy_wgs copies the g-th of copy_wgs equal shares of every chunk, in landing
+// order, before its first unit; no wait precedes it, so the flags it raises
+// cannot depend on the units behind it.  Each thread keeps COPY_UNROLL 16-byte
+// loads in flight (non-temporal: the source is read once).  The stores are
+// device-coherent (sc1: written through past the XCD's L2), so after waiting
+// for them the workgroup counts itself in with a relaxed atomic and no L2
+// write-back; the last share of a chunk raises its flag with a release store.
+constexpr int COPY_UNROLL = 16;
+constexpr int CPOL_SC1 = 16;  // cache-policy bit of a device-coherent store
+typedef unsigned int copy_vec __attribute__((ext_vector_type(4)));
+
+__device__ void colocated_copy(const GemmParams& p) {
+  const int g = blockIdx.x, nt = blockDim.x;
+  const int64_t n = p.copy_vec;
+  const int64_t lo = n * g / p.copy_wgs, hi = n * (g + 1) / p.copy_wgs;
+  const int cnt = static_cast<int>(hi - lo);  // a chunk is < 2^32 bytes
+  for (int i = 0; i < p.copy_chunks; ++i) {
+    const copy_vec* src = reinterpret_cast<const copy_vec*>(p.copy_src[i]) + lo;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.copy_dst[i] + lo, static_cast<uint32_t>(cnt) * 16u);
+    for (int base = threadIdx.x; base < cnt; base += nt * COPY_UNROLL) {
+      copy_vec v[COPY_UNROLL];
+#pragma unroll
+      for (int u = 0; u < COPY_UNROLL; ++u) {
+        const int k = base + u * nt;
+        if (k < cnt) v[u] = __builtin_nontemporal_load(src + k);
+      }
+#pragma unroll
+      for (int u = 0; u < COPY_UNROLL; ++u) {
+        const int k = base + u * nt;
+        if (k < cnt) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, k * 16, 0, CPOL_SC1);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int c = p.copy_flag[i];
+      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->land_count[c], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == static_cast<uint32_t>(p.copy_wgs) - 1) {
+        __hip_atomic_store(&p.sig->land_count[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.sig->flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+  }
+}
+
 // Walks the plan: takes units (dynamic counter or static slots), validates
 // them, waits for their chunks, then `run_tile(unit)`.
 struct LoopShared {
@@ -509,6 +557,7 @@ struct LoopShared {
 template <int BM, int BN, int KIND, int WAIT, typename RunTile>
 __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile run_tile) {
   const int G = gridDim.x;
+  if (WAIT && static_cast<int>(blockIdx.x) < p.copy_wgs) colocated_copy(p);
   const int64_t n_tiles = KIND == KIND_MOE ? static_cast<int64_t>(*p.n_tiles_dev) : p.n_tiles;
   uint32_t seen = p.no_wait_mask;
   // The first unit of every workgroup is its slot (no counter traffic while all

@@ -47,6 +47,15 @@ struct GemmParams {
   int32_t dynamic;             // 1: units from the work counter in sig; 0: slot-strided
   char* split_ws;              // split tiles' blocks: 256-byte counter header + S partials
   int64_t split_bytes;         // bytes of split_ws
+  // Co-located landing: workgroups [0, copy_wgs) first copy their share of
+  // each of copy_chunks chunks (landing order) and count it in; the last share
+  // of chunk i raises flags[copy_flag[i]].
+  int32_t copy_wgs;
+  int32_t copy_chunks;
+  int64_t copy_vec;            // 16-byte units per chunk
+  const uint4* copy_src[TLC_MAX_WORLD];
+  uint4* copy_dst[TLC_MAX_WORLD];
+  int32_t copy_flag[TLC_MAX_WORLD];
 };
 
 // Bytes of one split tile's workspace block (counter header + split_k partials).

@@ -22,7 +22,7 @@ ERR_HIP, ERR_TIMEOUT, ERR_BAD_PLAN = -5, -6, -7
 MODE_AG, MODE_RS, MODE_MOE = 0, 1, 2
 ORDER_NATURAL, ORDER_RANK_OFFSET = 0, 1
 B_KN, B_NK = 0, 1
-LAND_NONE, LAND_COPY_ENGINE, LAND_CU, LAND_MEMCPY = 0, 1, 2, 3
+LAND_NONE, LAND_COPY_ENGINE, LAND_CU, LAND_MEMCPY, LAND_COLOCATED = 0, 1, 2, 3, 4
 SCHED_DYNAMIC, SCHED_STATIC = 0, 1
 MAX_WORLD = 32
 EPOCH_MAX = 4096
@@ -63,7 +63,7 @@ class AGArgs(C.Structure):
                 ("epoch", C.c_uint32), ("land", C.c_int32), ("grid", C.c_int32),
                 ("timeout_ns", C.c_int64), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_int64), ("schedule", C.c_int32), ("sub_chunks", C.c_int32),
-                ("trace", C.c_void_p)]
+                ("copy_wgs", C.c_int32), ("trace", C.c_void_p)]
 
 
 class RSArgs(C.Structure):
@@ -96,7 +96,7 @@ class MoEArgs(C.Structure):
                 ("x", C.c_void_p), ("x_src", C.POINTER(C.c_void_p)), ("w", C.c_void_p),
                 ("w_layout", C.c_int32), ("y", C.c_void_p), ("sig", C.c_void_p),
                 ("epoch", C.c_uint32), ("land", C.c_int32), ("grid", C.c_int32),
-                ("timeout_ns", C.c_int64), ("schedule", C.c_int32)]
+                ("timeout_ns", C.c_int64), ("schedule", C.c_int32), ("copy_wgs", C.c_int32)]
 
 
 _lib = None
@@ -273,7 +273,7 @@ def signals_alloc() -> Signals:
 
 def ag_gemm(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, a_src, b, b_layout, c,
             sig: Signals, epoch, land, compute_stream=None, copy_stream=None, grid=0, timeout_ns=0,
-            trace=None, workspace=None, schedule=SCHED_DYNAMIC, sub_chunks=0):
+            trace=None, workspace=None, schedule=SCHED_DYNAMIC, sub_chunks=0, copy_wgs=0):
     """tlc_ag_gemm.  a_src: list of `world` device tensors (entry `rank` unused) or None.
     copy_stream: one stream or a list of streams for the landing.  workspace: a
     zero-filled device tensor for split plans (or None)."""
@@ -281,7 +281,7 @@ def ag_gemm(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, a_sr
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = AGArgs(_ptr(plan), n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, _ptr(a), src,
                   _ptr(b), b_layout, _ptr(c), sig.ptr, epoch, land, grid, timeout_ns,
-                  _ptr(workspace), ws_bytes, schedule, sub_chunks, _ptr(trace))
+                  _ptr(workspace), ws_bytes, schedule, sub_chunks, copy_wgs, _ptr(trace))
     cs, n = _streams(copy_stream)
     _check(lib().tlc_ag_gemm(C.byref(args), _stream(compute_stream), cs, n), "tlc_ag_gemm")
 
@@ -339,11 +339,11 @@ def moe_route(logits, tokens_per_chunk, world, rank, experts, topk, N, bm, bn, o
 
 def ag_moe(plan, n_tiles_dev, plan_cap, row_token, tokens_per_chunk, world, rank, experts, topk, H,
            N, bm, bn, x, x_src, w, w_layout, y, sig: Signals, epoch, land, compute_stream=None,
-           copy_stream=None, grid=0, timeout_ns=0, schedule=SCHED_DYNAMIC):
+           copy_stream=None, grid=0, timeout_ns=0, schedule=SCHED_DYNAMIC, copy_wgs=0):
     src = _ptr_array(x_src, world) if x_src is not None else None
     args = MoEArgs(_ptr(plan), _ptr(n_tiles_dev), plan_cap, _ptr(row_token), tokens_per_chunk,
                    world, rank, experts, topk, H, N, bm, bn, _ptr(x), src, _ptr(w), w_layout,
-                   _ptr(y), sig.ptr, epoch, land, grid, timeout_ns, schedule)
+                   _ptr(y), sig.ptr, epoch, land, grid, timeout_ns, schedule, copy_wgs)
     cs, n = _streams(copy_stream)
     _check(lib().tlc_ag_moe(C.byref(args), _stream(compute_stream), cs, n), "tlc_ag_moe")
 

@@ -120,7 +120,8 @@ class AGProblem:
             if c != self.rank:
                 self.a[c * self.R:(c + 1) * self.R].fill_(float("nan"))
 
-    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, preset_flags=None, trace=None):
+    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, preset_flags=None, trace=None,
+            copy_wgs=0):
         """Enqueue one AG-GEMM.  With land == LAND_NONE the flags are raised to the
         new epoch first (chunks must already be in place) unless preset_flags is
         False."""
@@ -132,7 +133,8 @@ class AGProblem:
         tlc.ag_gemm(self.plan, self.n_tiles, self.M, self.N, self.K, self.world, self.rank, self.R,
                     self.bm, self.bn, self.a, self.a_src if land != tlc.LAND_NONE else None,
                     self.b, self.b_layout, self.c, self.sig, self.epoch, land, s.compute, s.copy,
-                    grid, timeout_ns, trace, self.workspace, self.schedule, self.sub_chunks)
+                    grid, timeout_ns, trace, self.workspace, self.schedule, self.sub_chunks,
+                    copy_wgs)
         s.end()
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
@@ -281,7 +283,7 @@ class MoEProblem:
                       self.row_token, self.slot, self.plan, self.plan_cap, self.n_tiles_dev,
                       self.workspace, s.compute)
 
-    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, do_route=True):
+    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, do_route=True, copy_wgs=0):
         next_epoch(self)
         s = self.streams
         if land == tlc.LAND_NONE:
@@ -292,7 +294,8 @@ class MoEProblem:
         tlc.ag_moe(self.plan, self.n_tiles_dev, self.plan_cap, self.row_token, self.Tc, self.world,
                    self.rank, self.E, self.k, self.H, self.N, self.bm, self.bn, self.x,
                    self.x_src if land != tlc.LAND_NONE else None, self.w, self.b_layout, self.y,
-                   self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns)
+                   self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns,
+                   copy_wgs=copy_wgs)
         s.end()
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
