@@ -18,6 +18,13 @@ values up to rounding order because it only reorders tiles and transfers
   order).  On one GPU only the local partial P_r is computed; the other ranks'
   slices for rank r arrive as inputs ("remote partials").
 
+* GEMM-AllReduce (DITRON §4, the tensor-parallel kernels GEMM-AllReduce next
+  to AG-GEMM and GEMM-RS; §5.1 reports it separately): every rank ends with the
+  whole sum C = sum_s P_s.  Taken here as the reduce-scatter above followed by
+  an all-gather of the reduced slices: rows of chunk r are rank r's own reduce,
+  rows of chunk c != r are the slice rank c reduced ("gathered" inputs on one
+  GPU).
+
 Inputs are bf16 bit patterns (uint16) and fp32 arrays from ``seeded_inputs``;
 bf16 -> float64 widening is exact.
 """
@@ -82,3 +89,15 @@ def gemm_rs_rows(a_local, b_kn, remote: dict, world: int, rank: int, local_rows)
     p = gemm_partial(a_local, b_kn, rank * R + local_rows)
     sub = {s: np.asarray(v)[local_rows] for s, v in remote.items()}
     return p, reduce_slice(p, sub, world, rank)
+
+
+def gemm_ar(a_local, b_kn, remote: dict, gathered: dict, world: int, rank: int):
+    """(P, C): the local partial (M x N) and the all-reduced product C (M x N),
+    whose row chunk `rank` is this rank's reduced slice and whose row chunk c
+    (c != rank) is gathered[c], the slice rank c reduced."""
+    p, out = gemm_rs(a_local, b_kn, remote, world, rank)
+    R = p.shape[0] // world
+    c = np.empty_like(p)
+    for ch in range(world):
+        c[ch * R:(ch + 1) * R] = out if ch == rank else np.asarray(gathered[ch], dtype=np.float64)
+    return p, c

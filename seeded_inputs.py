@@ -31,6 +31,7 @@ T_A = 0        # activations: A chunks (AG), local A (RS), tokens X (MoE)
 T_B = 1        # weights: B (AG/RS), stacked expert weights (MoE)
 T_REMOTE = 2   # fp32 partial sums of the emulated peer ranks (RS)
 T_LOGITS = 3   # fp32 router logits (MoE)
+T_GATHERED = 4  # fp32 reduced slices of the emulated peer ranks (GEMM-AllReduce)
 
 
 def rng_for(*key: int) -> np.random.Generator:
@@ -135,6 +136,14 @@ class RSInputs:
 
 
 @dataclass
+class ARInputs:
+    a: np.ndarray             # M x K bf16 bits (local K shard)
+    b: np.ndarray             # K x N bf16 bits
+    remote: dict              # s -> R x N fp32, for every s != rank (partials for rank's rows)
+    gathered: dict            # c -> R x N fp32, for every c != rank (rank c's reduced slice)
+
+
+@dataclass
 class MoEInputs:
     x_chunks: list            # W arrays, each Tc x H bf16 bits
     logits: np.ndarray        # T x E fp32
@@ -168,6 +177,21 @@ def rs_inputs(wl_id: int, world: int, rank: int, rows: int, n: int, k: int, a_st
         remote = {s: np.zeros((rows, n), np.float32) for s in remote}
     assert a.shape == (m, k)
     return RSInputs(a, b, remote)
+
+
+def ar_inputs(wl_id: int, world: int, rank: int, rows: int, n: int, k: int, a_std=1.0,
+              b_std=1.0, remote_std=1.0, integer: bool = False) -> ARInputs:
+    """GEMM-RS inputs plus the reduced slices the other ranks produce: each is a
+    sum of `world` partials, so it is drawn with std remote_std * sqrt(world)
+    (integer case: uniform integers in [-256, 256])."""
+    rs = rs_inputs(wl_id, world, rank, rows, n, k, a_std, b_std, remote_std, integer)
+    if integer:
+        gathered = {c: int_f32((rows, n), (wl_id, T_GATHERED, c), -256, 256)
+                    for c in range(world) if c != rank}
+    else:
+        gathered = {c: normal_f32((rows, n), (wl_id, T_GATHERED, c), remote_std * math.sqrt(world))
+                    for c in range(world) if c != rank}
+    return ARInputs(rs.a, rs.b, rs.remote, gathered)
 
 
 def moe_inputs(wl_id: int, world: int, tokens: int, hidden: int, n: int, experts: int,

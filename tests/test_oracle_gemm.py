@@ -127,3 +127,47 @@ def test_gemm_rs_rows_matches_full():
     ps, outs = og.gemm_rs_rows(inp.a, inp.b, inp.remote, world, rank, sel)
     np.testing.assert_array_equal(ps, p[rank * rows + np.array(sel)])
     np.testing.assert_array_equal(outs, out[sel])
+
+
+@pytest.mark.parametrize("world,rank", [(4, 1), (3, 2), (2, 0)])
+def test_gemm_ar_integer_exact(world, rank):
+    rows, k, n = 3, 8, 5
+    inp = si.ar_inputs(908, world, rank, rows, n, k, integer=True)
+    p, c = og.gemm_ar(inp.a, inp.b, inp.remote, inp.gathered, world, rank)
+    a = si.bf16_bits_to_f32(inp.a).astype(np.int64)
+    b = si.bf16_bits_to_f32(inp.b).astype(np.int64)
+    for ch in range(world):
+        for i in range(rows):
+            for j in range(n):
+                if ch != rank:
+                    assert c[ch * rows + i, j] == inp.gathered[ch][i, j]
+                    continue
+                want = sum(int(inp.remote[s][i, j]) for s in range(world) if s != rank)
+                want += sum(int(a[rank * rows + i, kk]) * int(b[kk, j]) for kk in range(k))
+                assert c[ch * rows + i, j] == want
+
+
+def test_gemm_ar_consistent_shards_give_unsharded_product():
+    """W ranks each hold a K shard (A_s, B_s).  With every peer input built
+    from those shards by brute force, every rank's all-reduced C is the
+    unsharded product [A_0 .. A_{W-1}] @ [B_0; ..; B_{W-1}] (K concatenated),
+    computed here by one integer matrix product."""
+    world, rows, n, ks = 3, 4, 6, 5
+    M = world * rows
+    shards = [si.rs_inputs(909 + s, world, 0, rows, n, ks, integer=True) for s in range(world)]
+    A = [si.bf16_bits_to_f32(sh.a).astype(np.int64) for sh in shards]
+    B = [si.bf16_bits_to_f32(sh.b).astype(np.int64) for sh in shards]
+
+    def partial(s, i, j):  # brute force P_s[i, j]
+        return sum(int(A[s][i, kk]) * int(B[s][kk, j]) for kk in range(ks))
+
+    full = np.concatenate(A, axis=1) @ np.concatenate(B, axis=0)
+    for rank in range(world):
+        remote = {s: np.array([[partial(s, rank * rows + i, j) for j in range(n)] for i in range(rows)],
+                              np.float32) for s in range(world) if s != rank}
+        gathered = {c: np.array([[sum(partial(s, c * rows + i, j) for s in range(world))
+                                  for j in range(n)] for i in range(rows)], np.float32)
+                    for c in range(world) if c != rank}
+        _, c = og.gemm_ar(shards[rank].a, shards[rank].b, remote, gathered, world, rank)
+        assert c.shape == (M, n)
+        np.testing.assert_array_equal(c, full.astype(np.float64))
