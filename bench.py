@@ -42,7 +42,7 @@ PEAK_HBM_GBS = 8000.0
 # recorded in profiles/gemm_kernel_8w_ag_ffn_up_8192x3200x5120.md, scaled by the
 # plain-copy calibration factor 1.000.  Re-measure whenever that kernel changes.
 AG_COMPUTE_TRAFFIC_BYTES = (220280.2 + 102400.0) * 1024
-WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4}
+WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4, "ar": 1}
 LANDINGS = {"memcpy": 3, "copy_engine": 1, "cu": 2, "colocated": 4}  # tlc.LAND_*
 
 
@@ -307,20 +307,40 @@ def run_ag(args, torch, tlc, si, workloads):
     return line
 
 
-def run_rs(args, torch, tlc, si, workloads, wid):
+def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
+    """GEMM-RS; with ar=True GEMM-AllReduce on the same shape (the reduce-scatter
+    plus the all-gather of the peers' reduced slices into the M x N output)."""
     wl = si.WORKLOADS[wid]
     dev = torch.device("cuda:0")
-    inp = si.workload_inputs(wid, rank=args.rank)
+    if ar:
+        inp = si.ar_inputs(wid, wl.world, args.rank, wl.rows_per_chunk, wl.n, wl.k, wl.a_std,
+                           wl.b_std, wl.remote_std)
+    else:
+        inp = si.workload_inputs(wid, rank=args.rank)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
     land = LANDINGS[args.land]
     split_k = 0 if args.split_k is None else args.split_k
     split_from = 1 if args.split_from is None else args.split_from
     args.schedule = args.schedule or "static"
     schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
-    prob = workloads.RSProblem(inp.a, inp.b, inp.remote, wl.world, args.rank, args.tile, args.tile,
-                               layout, group_m=args.group_m, device=dev, split_k=split_k,
-                               split_from=split_from, schedule=schedule)
+    if ar:
+        prob = workloads.ARProblem(inp.a, inp.b, inp.remote, inp.gathered, wl.world, args.rank,
+                                   args.tile, args.tile, layout, group_m=args.group_m, device=dev,
+                                   split_k=split_k, split_from=split_from, schedule=schedule)
+    else:
+        prob = workloads.RSProblem(inp.a, inp.b, inp.remote, wl.world, args.rank, args.tile,
+                                   args.tile, layout, group_m=args.group_m, device=dev,
+                                   split_k=split_k, split_from=split_from, schedule=schedule)
     ws = dict(workspace=prob.workspace, schedule=schedule)
+    c_chunks = ([prob.c[c * prob.R:(c + 1) * prob.R] for c in range(prob.world)] if ar else None)
+
+    def call(land_kind, remote, landing, gathered, epoch, stream_list):
+        if ar:
+            tlc.gemm_ar(*prob._args(), remote, landing, gathered, prob.c, prob.sig, epoch,
+                        land_kind, compute, stream_list, args.grid, copy_wgs=args.copy_wgs, **ws)
+        else:
+            tlc.gemm_rs(*prob._args(), remote, landing, prob.out, prob.sig, epoch, land_kind,
+                        compute, stream_list, args.grid, **ws)
     compute = torch.cuda.Stream(device=dev)
     copies = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.copy_streams))]
     prob.streams.compute = compute
@@ -334,8 +354,8 @@ def run_rs(args, torch, tlc, si, workloads, wid):
             workloads.next_epoch(prob)
             for c in copies:
                 c.wait_stream(compute)
-            tlc.gemm_rs(*prob._args(), prob.remote_src, prob.landing, prob.out, prob.sig, prob.epoch,
-                        land_kind, compute, copies, args.grid, **ws)
+            call(land_kind, prob.remote_src, prob.landing, getattr(prob, "gathered_src", None),
+                 prob.epoch, copies)
             for c in copies:
                 compute.wait_stream(c)
         return step
@@ -345,8 +365,14 @@ def run_rs(args, torch, tlc, si, workloads, wid):
             workloads.next_epoch(prob)
             for c in copies:
                 c.wait_stream(compute)
-            tlc.land(prob.landing, prob.remote_src, prob.R * prob.N * 4, prob.world, prob.rank,
-                     prob.sig, prob.epoch, land_kind, copies)
+            # co-located: the reduce reads the partials in place, so only the
+            # all-gather (GEMM-AllReduce) moves data
+            if not (ar and land_kind == tlc.LAND_COLOCATED):
+                tlc.land(prob.landing, prob.remote_src, prob.R * prob.N * 4, prob.world, prob.rank,
+                         prob.sig, prob.epoch, land_kind, copies)
+            if ar:
+                tlc.land(c_chunks, prob.gathered_src, prob.R * prob.N * 4, prob.world, prob.rank,
+                         prob.sig, prob.epoch, land_kind, copies)
             for c in copies:
                 compute.wait_stream(c)
         return step
@@ -363,8 +389,7 @@ def run_rs(args, torch, tlc, si, workloads, wid):
     comp_t = KernelTimer(torch, compute)
 
     def compute_only():
-        comp_t(lambda: tlc.gemm_rs(*prob._args(), None, prob.landing, prob.out, prob.sig,
-                                   tlc.EPOCH_MAX, tlc.LAND_NONE, compute, None, args.grid, **ws))
+        comp_t(lambda: call(tlc.LAND_NONE, None, prob.landing, None, tlc.EPOCH_MAX, None))
 
     t_comp = timed(compute_only, steps, warm, torch)
     red_t = KernelTimer(torch, compute)
@@ -381,7 +406,8 @@ def run_rs(args, torch, tlc, si, workloads, wid):
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     red_gbs = prob.reduce_bytes / (red_ms * 1e-3) / 1e9
     extra = {
-        "config": {"workload": wl.name, "M": prob.M, "N": prob.N, "K": prob.K, "world": prob.world,
+        "config": {"workload": wl.name.replace("rs_", "ar_", 1) if ar else wl.name, "M": prob.M,
+                   "N": prob.N, "K": prob.K, "world": prob.world,
                    "rank": prob.rank, "tile": [args.tile, args.tile, 64], "b_layout": args.layout,
                    "landing": args.land, "copy_streams": len(copies), "n_units": prob.n_tiles,
                    "split_k": split_k, "split_from": split_from, "schedule": args.schedule,
@@ -489,7 +515,8 @@ def main():
     elif args.workload == "moe":
         line = run_moe(args, torch, tlc, si, workloads)
     else:
-        line = run_rs(args, torch, tlc, si, workloads, WORKLOAD_ID[args.workload])
+        line = run_rs(args, torch, tlc, si, workloads, WORKLOAD_ID[args.workload],
+                      ar=args.workload == "ar")
     print(json.dumps(line), flush=True)
 
 

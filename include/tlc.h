@@ -341,6 +341,37 @@ tlc_status tlc_gemm_rs(const tlc_rs_args* args, void* compute_stream, void* cons
  * nor the landing is run: landing[s] must hold the data, flags >= epoch). */
 tlc_status tlc_rs_reduce(const tlc_rs_args* args, void* compute_stream);
 
+/* --------------------------------------------------- GEMM-AllReduce ------ */
+
+/* GEMM then all-reduce, one rank's share (DITRON §4: GEMM-AllReduce is one of
+ * the tensor-parallel overlap kernels next to AG-GEMM and GEMM-RS), taken as
+ * tlc_gemm_rs followed by an all-gather of the reduced slices:
+ *   P = A @ B in scatter order (rs.plan: mode RS), as tlc_gemm_rs;
+ *   C[rows of chunk rank] = sum over s in ascending s of S_s (tlc_gemm_rs's out);
+ *   C[rows of chunk c], c != rank = gathered_src[c], the slice rank c reduced.
+ * rs: the GEMM-RS arguments; rs.out is ignored (the reduce writes C's row
+ *     chunk `rank`).
+ * gathered_src: host array of `world` device pointers (R x N f32, 16-byte
+ *     aligned); entry `rank` is ignored; may be NULL if rs.land == NONE (then C's
+ *     other row chunks must already hold the slices).
+ * c: device f32 M x N, ldc = N.
+ * Requirements: those of tlc_gemm_rs, and 2 * world <= 32.  The peers' slices
+ * land after the remote partials on the same copy streams and raise
+ * flags[world + c].  With TLC_LAND_COLOCATED the reduce reads the remote
+ * partials in place and the GEMM's first copy_wgs workgroups copy the slices
+ * into C before their first unit.  Nothing inside the call waits for the
+ * slices' flags: C is complete once the compute stream and the copy streams
+ * have finished. */
+typedef struct {
+  tlc_rs_args rs;
+  const float* const* gathered_src;
+  float* c;
+  int32_t copy_wgs; /* as in tlc_ag_args */
+} tlc_ar_args;
+
+tlc_status tlc_gemm_ar(const tlc_ar_args* args, void* compute_stream, void* const* copy_streams,
+                       int32_t n_copy_streams);
+
 /* ------------------------------------------------------------ AG-MoE ------ */
 
 /* Routing for AG-MoE, on the device (DITRON §3.1 device level: chunk sizes
@@ -431,7 +462,7 @@ tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_
 
 const char* tlc_status_string(tlc_status s);
 const char* tlc_last_error(void);
-/* Library version, e.g. 110 = 0.1.10. */
+/* Library version, e.g. 130 = 0.1.30. */
 int32_t tlc_version(void);
 
 #ifdef __cplusplus

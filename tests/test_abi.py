@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tlc.version() == 120
+    assert tlc.version() == 130
     assert tlc.status_string(tlc.ERR_TIMEOUT).startswith("timeout")
     assert tlc.status_string(0) == "ok"
 
@@ -84,6 +84,25 @@ def test_colocated_landing_argument_errors():
     d = (C.c_void_p * 2)(4096, 8192)
     s = tlc.lib().tlc_land(d, src, 1024, 2, 0, C.c_void_p(64), 0, tlc.LAND_COLOCATED, None, 0)
     assert s == tlc.ERR_INVALID_ARG and "epoch" in tlc.last_error()
+
+
+def test_gemm_ar_argument_errors():
+    rs = tlc.RSArgs(plan=None, n_tiles=0, M=256, N=256, K=512, world=2, rank=0, rows_per_chunk=128,
+                    bm=128, bn=128, a=16, b=32, b_layout=tlc.B_KN, partials=48, sig=64, epoch=1,
+                    land=tlc.LAND_NONE)
+    for over, want in [(dict(world=17, M=17 * 128), "2 * world"), (dict(), "c NULL")]:
+        r = tlc.RSArgs.from_buffer_copy(rs)
+        for k, v in over.items():
+            setattr(r, k, v)
+        args = tlc.ARArgs(r, None, None, 0)
+        assert tlc.lib().tlc_gemm_ar(C.byref(args), None, None, 0) == tlc.ERR_INVALID_ARG
+        assert want in tlc.last_error(), tlc.last_error()
+    # landing without the peers' reduced slices
+    r = tlc.RSArgs.from_buffer_copy(rs)
+    r.land = tlc.LAND_MEMCPY
+    args = tlc.ARArgs(r, None, 128, 0)
+    assert tlc.lib().tlc_gemm_ar(C.byref(args), None, None, 0) == tlc.ERR_INVALID_ARG
+    assert "gathered_src" in tlc.last_error()
 
 
 def test_plan_capacity_and_query():

@@ -102,7 +102,8 @@ tlc_status hip_check(hipError_t e, const char* what) {
 // are already in place) and raise each chunk's flag to `epoch` after its bytes.
 tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, int64_t bytes,
                            int world, int rank, int n_local, tlc_signals* sig, uint32_t epoch,
-                           void* const* copy_streams, int n_copy_streams, const DeviceInfo& info) {
+                           void* const* copy_streams, int n_copy_streams, const DeviceInfo& info,
+                           int flag_base = 0) {
   // the co-located landing is carried out by the GEMM kernel itself
   if (land == TLC_LAND_NONE || land == TLC_LAND_COLOCATED || world <= n_local) return TLC_OK;
   if (land == TLC_LAND_COPY_ENGINE || land == TLC_LAND_MEMCPY) {
@@ -115,8 +116,8 @@ tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, i
                                 "hipMemcpyAsync(landing)");
       if (st) return st;
       // the flag follows the data on the same copy engine queue
-      st = hip_check(hipMemcpyAsync(&sig->flags[c], &sig->epoch_table[epoch - 1], sizeof(uint32_t),
-                                    kind, s),
+      st = hip_check(hipMemcpyAsync(&sig->flags[flag_base + c], &sig->epoch_table[epoch - 1],
+                                    sizeof(uint32_t), kind, s),
                      "hipMemcpyAsync(flag)");
       if (st) return st;
     }
@@ -134,6 +135,7 @@ tlc_status enqueue_landing(int land, void* const* dst, const void* const* src, i
   p.vec_per_chunk = bytes / 16;
   p.sig = sig;
   p.epoch = epoch;
+  p.flag_base = flag_base;
   // one 1024-thread workgroup per CU the GEMM leaves free (a CU that holds a
   // landing workgroup cannot also hold a GEMM workgroup: those take all of a
   // CU's registers)
@@ -216,7 +218,8 @@ void set_schedule(GemmParams* p, int32_t schedule, void* ws, int64_t ws_bytes) {
 // and the number of workgroups that copy them (0 = half the grid, a multiple
 // of 8, at least 8 or the whole grid if smaller).
 tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src, int64_t bytes,
-                         int world, int rank, int n_local, int copy_wgs, int grid, const char* who) {
+                         int world, int rank, int n_local, int copy_wgs, int grid, const char* who,
+                         int flag_base = 0) {
   if (copy_wgs < 0 || copy_wgs > grid)
     return fail(TLC_ERR_INVALID_ARG, "%s: copy_wgs %d outside 0..grid %d", who, copy_wgs, grid);
   int cw = copy_wgs;
@@ -231,7 +234,7 @@ tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src
     const int c = (rank + i) % world;
     p->copy_src[i - n_local] = static_cast<const uint4*>(src[c]);
     p->copy_dst[i - n_local] = static_cast<uint4*>(dst[c]);
-    p->copy_flag[i - n_local] = c;
+    p->copy_flag[i - n_local] = flag_base + c;
   }
   return TLC_OK;
 }
@@ -411,8 +414,16 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   return st ? st : ok();
 }
 
+// The all-gather half of GEMM-AllReduce: the peers' reduced slices, landed
+// into the output's other row chunks after the remote partials.
+struct GatherPart {
+  void* dst[TLC_MAX_WORLD];
+  const void* src[TLC_MAX_WORLD];
+  int32_t copy_wgs;
+};
+
 static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* const* copy_streams,
-                            int n_copy_streams, bool run_gemm) {
+                            int n_copy_streams, bool run_gemm, const GatherPart* g = nullptr) {
   if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: NULL args");
   tlc_status st = check_dense("tlc_gemm_rs", a->M, a->N, a->K, a->world, a->rank, a->rows_per_chunk,
                               a->bm, a->bn, a->b_layout, a->plan, a->n_tiles, a->a, a->b,
@@ -444,6 +455,11 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
                          slice_bytes, "tlc_gemm_rs", copy_streams, n_copy_streams, a->epoch);
     if (st) return st;
   }
+  if (g) {
+    st = check_land_args(land, g->src, g->dst, a->world, a->rank, slice_bytes, "tlc_gemm_ar",
+                         copy_streams, n_copy_streams, a->epoch);
+    if (st) return st;
+  }
   DeviceInfo info;
   st = device_info(&info);
   if (st) return st;
@@ -452,8 +468,17 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
                        reinterpret_cast<const void* const*>(a->remote_src), slice_bytes, a->world,
                        a->rank, 1, a->sig, a->epoch, copy_streams, n_copy_streams, info);
   if (st) return st;
+  // the reduced slices of the peers raise flags[world + c]
+  if (g) {
+    st = enqueue_landing(land, g->dst, g->src, slice_bytes, a->world, a->rank, 1, a->sig, a->epoch,
+                         copy_streams, n_copy_streams, info, a->world);
+    if (st) return st;
+  }
+  // co-located all-gather: the GEMM's first workgroups copy the slices before
+  // their first unit (the waiting kernel variant, with no chunk ever waited for)
+  const bool coloc_gather = g && coloc && a->world > 1;
 
-  if (run_gemm && a->n_tiles > 0) {
+  if (run_gemm && (a->n_tiles > 0 || coloc_gather)) {
     GemmParams p;
     memset(&p, 0, sizeof(p));
     p.plan = a->plan;
@@ -473,7 +498,17 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
     p.timeout_ticks = ticks_for(a->timeout_ns, info);
     set_schedule(&p, a->schedule, a->workspace, a->workspace_bytes);
     // the GEMM does not wait, but the landing running beside it may need CUs
-    const int grid = pick_grid(a->grid, p.dynamic, a->n_tiles, info.cus - reserve_for(land));
+    const int avail = info.cus - reserve_for(land);
+    int grid = a->n_tiles > 0 ? pick_grid(a->grid, p.dynamic, a->n_tiles, avail)
+                              : (a->grid > 0 ? a->grid : avail);
+    if (coloc_gather) {
+      p.do_wait = 1;
+      p.no_wait_mask = 0xFFFFFFFFu;
+      st = set_colocated(&p, const_cast<void* const*>(g->dst), g->src, slice_bytes, a->world,
+                         a->rank, 1, g->copy_wgs, grid, "tlc_gemm_ar", a->world);
+      if (st) return st;
+      if (a->n_tiles == 0) grid = p.copy_wgs;
+    }
     p.xcd_remap = grid % 8 == 0;
     st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
     if (st) return st;
@@ -504,6 +539,32 @@ tlc_status tlc_gemm_rs(const tlc_rs_args* a, void* compute_stream, void* const* 
 
 tlc_status tlc_rs_reduce(const tlc_rs_args* a, void* compute_stream) {
   return rs_common(a, compute_stream, nullptr, 0, false);
+}
+
+tlc_status tlc_gemm_ar(const tlc_ar_args* a, void* compute_stream, void* const* copy_streams,
+                       int32_t n_copy_streams) {
+  if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_ar: NULL args");
+  const tlc_rs_args& r = a->rs;
+  if (r.world < 1 || 2 * r.world > TLC_MAX_WORLD || r.rank < 0 || r.rank >= r.world)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_ar: world %d (2 * world <= %d), rank %d", r.world,
+                TLC_MAX_WORLD, r.rank);
+  if (r.rows_per_chunk < 1 || r.N < 1)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_ar: sizes must be >= 1");
+  if (!a->c || !aligned16(a->c)) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_ar: c NULL or misaligned");
+  if (r.land != TLC_LAND_NONE && r.world > 1 && !a->gathered_src)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_ar: landing needs gathered_src");
+  const int64_t slice = static_cast<int64_t>(r.rows_per_chunk) * r.N;
+  tlc_rs_args rr = r;
+  rr.out = a->c + r.rank * slice;
+  GatherPart g;
+  memset(&g, 0, sizeof(g));
+  for (int c = 0; c < r.world; ++c) {
+    g.dst[c] = a->c + c * slice;
+    g.src[c] = (a->gathered_src && c != r.rank) ? a->gathered_src[c] : nullptr;
+  }
+  g.copy_wgs = a->copy_wgs;
+  return rs_common(&rr, compute_stream, copy_streams, n_copy_streams, true,
+                   r.land == TLC_LAND_NONE ? nullptr : &g);
 }
 
 int64_t tlc_moe_plan_capacity(int32_t T, int32_t topk, int32_t experts, int32_t N, int32_t bm, int32_t bn) {
@@ -668,6 +729,6 @@ const char* tlc_status_string(tlc_status s) {
 
 const char* tlc_last_error(void) { return g_err; }
 
-int32_t tlc_version(void) { return 120; }
+int32_t tlc_version(void) { return 130; }
 
 }  // extern "C"

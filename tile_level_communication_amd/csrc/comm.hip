@@ -81,12 +81,13 @@ __global__ __launch_bounds__(LAND_THREADS) void land_kernel(LandParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
+      const int f = p.flag_base + c;
       __atomic_thread_fence(__ATOMIC_RELEASE);
-      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->land_count[c], 1u, __ATOMIC_ACQ_REL,
+      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->land_count[f], 1u, __ATOMIC_ACQ_REL,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (prev == gridDim.x - 1) {
-        __hip_atomic_store(&p.sig->land_count[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.sig->flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&p.sig->land_count[f], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.sig->flags[f], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
   }

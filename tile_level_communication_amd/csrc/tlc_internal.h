@@ -87,6 +87,7 @@ struct LandParams {
   int64_t vec_per_chunk;  // 16-byte units per chunk
   tlc_signals* sig;
   uint32_t epoch;
+  int32_t flag_base;      // chunk c raises flags[flag_base + c]
 };
 tlc_status launch_land_cu(const LandParams& p, int grid, void* stream);
 

@@ -31,7 +31,7 @@ EXPORTS = [
     "tlc_chunk_plan", "tlc_signals_alloc", "tlc_signals_free", "tlc_signals_set",
     "tlc_signals_clear_status", "tlc_read_status", "tlc_ag_gemm", "tlc_gemm_rs", "tlc_rs_reduce",
     "tlc_moe_plan_capacity", "tlc_moe_workspace_bytes", "tlc_moe_route", "tlc_ag_moe", "tlc_land",
-    "tlc_status_string", "tlc_last_error", "tlc_version", "tlc_split_workspace_bytes",
+    "tlc_status_string", "tlc_last_error", "tlc_version", "tlc_split_workspace_bytes", "tlc_gemm_ar",
 ]
 
 
@@ -76,6 +76,11 @@ class RSArgs(C.Structure):
                 ("epoch", C.c_uint32), ("land", C.c_int32), ("grid", C.c_int32),
                 ("timeout_ns", C.c_int64), ("workspace", C.c_void_p),
                 ("workspace_bytes", C.c_int64), ("schedule", C.c_int32)]
+
+
+class ARArgs(C.Structure):
+    _fields_ = [("rs", RSArgs), ("gathered_src", C.POINTER(C.c_void_p)), ("c", C.c_void_p),
+                ("copy_wgs", C.c_int32)]
 
 
 class MoERouteArgs(C.Structure):
@@ -129,6 +134,8 @@ def lib() -> C.CDLL:
         L.tlc_ag_gemm.restype = st
         L.tlc_gemm_rs.argtypes = [C.POINTER(RSArgs), vp, C.POINTER(vp), C.c_int32]
         L.tlc_gemm_rs.restype = st
+        L.tlc_gemm_ar.argtypes = [C.POINTER(ARArgs), vp, C.POINTER(vp), C.c_int32]
+        L.tlc_gemm_ar.restype = st
         L.tlc_rs_reduce.argtypes = [C.POINTER(RSArgs), vp]
         L.tlc_rs_reduce.restype = st
         L.tlc_moe_plan_capacity.argtypes = [C.c_int32] * 6
@@ -306,6 +313,21 @@ def gemm_rs(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b
                     workspace, schedule)
     cs, n = _streams(copy_stream)
     _check(lib().tlc_gemm_rs(C.byref(args), _stream(compute_stream), cs, n), "tlc_gemm_rs")
+
+
+def gemm_ar(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout, partials,
+            remote_src, landing, gathered_src, c, sig: Signals, epoch, land, compute_stream=None,
+            copy_stream=None, grid=0, timeout_ns=0, workspace=None, schedule=SCHED_DYNAMIC,
+            copy_wgs=0):
+    """tlc_gemm_ar.  remote_src, landing, gathered_src: lists of `world` device tensors (entry
+    `rank` unused); c: the M x N output."""
+    rs = _rs_args(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout,
+                  partials, remote_src, landing, None, sig, epoch, land, grid, timeout_ns,
+                  workspace, schedule)
+    g = _ptr_array(gathered_src, world) if gathered_src is not None else None
+    args = ARArgs(rs, g, _ptr(c), copy_wgs)
+    cs, n = _streams(copy_stream)
+    _check(lib().tlc_gemm_ar(C.byref(args), _stream(compute_stream), cs, n), "tlc_gemm_ar")
 
 
 def rs_reduce(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout, partials,

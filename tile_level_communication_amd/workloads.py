@@ -227,6 +227,44 @@ class RSProblem:
         s.end()
 
 
+class ARProblem(RSProblem):
+    """GEMM-AllReduce: the GEMM-RS problem plus the peers' reduced slices, which
+    land into the other row chunks of the M x N output `c`."""
+
+    def __init__(self, a, b_kn, remote: dict, gathered: dict, world, rank, bm=256, bn=256,
+                 b_layout=tlc.B_KN, order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda",
+                 split_k=0, split_from=0, schedule=tlc.SCHED_DYNAMIC):
+        super().__init__(a, b_kn, remote, world, rank, bm, bn, b_layout, order, group_m, device,
+                         split_k, split_from, schedule)
+        self.gathered_src = [None] * world
+        for c in range(world):
+            if c != rank:
+                self.gathered_src[c] = to_f32(gathered[c], self.device)
+        self.c = torch.empty((self.M, self.N), dtype=torch.float32, device=self.device)
+
+    def place_all(self):
+        super().place_all()
+        for c in range(self.world):
+            if c != self.rank:
+                self.c[c * self.R:(c + 1) * self.R].copy_(self.gathered_src[c])
+
+    def poison_remote(self):
+        super().poison_remote()
+        self.c.fill_(float("nan"))
+
+    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, copy_wgs=0):
+        next_epoch(self)
+        s = self.streams
+        if land == tlc.LAND_NONE:
+            self.sig.set(self.world, self.epoch, s.compute)
+        s.begin()
+        tlc.gemm_ar(*self._args(), self.remote_src if land != tlc.LAND_NONE else None, self.landing,
+                    self.gathered_src if land != tlc.LAND_NONE else None, self.c, self.sig,
+                    self.epoch, land, s.compute, s.copy, grid, timeout_ns, self.workspace,
+                    self.schedule, copy_wgs)
+        s.end()
+
+
 class MoEProblem:
     def __init__(self, x_chunks, logits, w_ekn, rank, topk, bm=256, bn=256, b_layout=tlc.B_KN,
                  order=tlc.ORDER_RANK_OFFSET, device="cuda"):
