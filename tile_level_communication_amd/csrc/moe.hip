@@ -12,8 +12,10 @@
 // rank+2, ... (position a = p(c) * Tc + token offset), in blocks of 64.
 //
 //   topk_kernel     one wavefront per token, one expert per lane (E <= 64):
-//                   k rounds of a butterfly arg-max (ties -> lower expert),
-//                   softmax over the k winners, a 64-bit membership mask.
+//                   k rounds of a wavefront maximum of order-preserving keys
+//                   and a ballot for the lowest expert holding it (ties ->
+//                   lower expert), softmax over the k winners, a 64-bit
+//                   membership mask.
 //   block_count     one wavefront per block of 64 arrival positions: for each
 //                   expert, how many of the block's tokens chose it.
 //   scan_kernel     one wavefront: per expert, the prefix of those counts over
@@ -34,38 +36,50 @@ namespace tlc {
 
 namespace {
 
-__device__ inline bool better(float va, int ia, bool oka, float vb, int ib, bool okb) {
-  if (oka != okb) return oka;
-  if (va != vb) return va > vb;
-  return ia < ib;
+// Order-preserving map of a float to an unsigned key (-0 counts as +0, as in
+// a value comparison); 0 is below every finite float's key.
+__device__ inline uint32_t ordered_key(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(256) void topk_kernel(MoeDev d) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= d.T) return;
+__device__ inline float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Maximum over the wavefront, the same in every lane: quad swaps, half-row and
+// row mirrors (DPP), then the four rows' maxima through scalar registers.
+__device__ inline uint32_t wave_max(uint32_t x) {
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x),
+                                                               0xB1, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x),
+                                                               0x4E, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x),
+                                                               0x141, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x),
+                                                               0x140, 0xF, 0xF, false)));
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Routing of token t by one wavefront (lane = expert): k rounds of the
+// largest remaining logit (wave maximum of the ordered keys) and the lowest
+// expert holding it (first set bit of the ballot), then the softmax over the k
+// winners in lane 0.  Returns the membership mask (the same in every lane).
+__device__ inline unsigned long long route_token(const MoeDev& d, int t, int lane) {
   const bool mine = lane < d.E;
-  const float v = mine ? d.logits[static_cast<int64_t>(t) * d.E + lane] : 0.0f;
+  const uint32_t key = mine ? ordered_key(d.logits[static_cast<int64_t>(t) * d.E + lane]) : 0u;
   bool taken = !mine;
   float win_v[16];
   int win_i[16];
   unsigned long long member = 0;
   for (int j = 0; j < d.k; ++j) {
-    float bv = v;
-    int bi = lane;
-    bool bok = !taken;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      const bool ook = __shfl_xor(static_cast<int>(bok), off) != 0;
-      if (better(ov, oi, ook, bv, bi, bok)) {
-        bv = ov;
-        bi = oi;
-        bok = ook;
-      }
-    }
-    win_v[j] = bv;
+    const uint32_t kk = taken ? 0u : key;
+    const uint32_t mx = wave_max(kk);
+    int bi = __ffsll(static_cast<unsigned long long>(__ballot(kk == mx))) - 1;
+    bi = bi < 0 ? 0 : bi;  // a lane always holds the maximum; keeps the mask shift defined
+    win_v[j] = key_value(mx);
     win_i[j] = bi;
     member |= 1ull << bi;
     if (lane == bi) taken = true;
@@ -84,6 +98,7 @@ __global__ __launch_bounds__(256) void topk_kernel(MoeDev d) {
     }
     d.member[t] = member;
   }
+  return member;
 }
 
 // Token at arrival position a (0 <= a < T).
@@ -91,6 +106,11 @@ __device__ inline int arrival_token(const MoeDev& d, int a) {
   const int pos = a / d.Tc;
   const int c = (d.rank + pos) % d.world;
   return c * d.Tc + (a - pos * d.Tc);
+}
+
+__global__ __launch_bounds__(256) void topk_kernel(MoeDev d) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t < d.T) route_token(d, t, threadIdx.x & 63);
 }
 
 __global__ __launch_bounds__(64) void block_count_kernel(MoeDev d) {
@@ -179,11 +199,9 @@ __global__ __launch_bounds__(64) void scatter_kernel(MoeDev d) {
   }
 }
 
-__global__ __launch_bounds__(256) void pair_kernel(MoeDev d) {
-  const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int P = d.pstart[d.E];
-  if (q >= P) return;
+// Pair q = (expert e, m-tile mt) by one wavefront: the readiness key (latest
+// consume position of the chunks its rows come from) and the chunk mask.
+__device__ inline void pair_one(const MoeDev& d, int q, int lane) {
   int lo = 0, hi = d.E - 1;  // expert e with pstart[e] <= q < pstart[e+1]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -209,6 +227,11 @@ __global__ __launch_bounds__(256) void pair_kernel(MoeDev d) {
     d.pair_key[q] = d.order == TLC_ORDER_NATURAL ? 0 : key;
     d.pair_mask[q] = mask;
   }
+}
+
+__global__ __launch_bounds__(256) void pair_kernel(MoeDev d) {
+  const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (q < d.pstart[d.E]) pair_one(d, q, threadIdx.x & 63);
 }
 
 __global__ __launch_bounds__(1024) void sort_kernel(MoeDev d) {
