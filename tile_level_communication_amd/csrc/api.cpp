@@ -526,7 +526,7 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
   r.epoch = a->epoch;
   r.timeout_ticks = ticks_for(a->timeout_ns, info);
   int rgrid = info.cus * 4;
-  const int64_t need = (r.n_vec4 + 255) / 256;
+  const int64_t need = (r.n_vec4 + 1023) / 1024;  // 256 threads x 4 float4 per pass
   if (need < rgrid) rgrid = static_cast<int>(need > 0 ? need : 1);
   st = launch_reduce(r, rgrid, compute_stream);
   return st ? st : ok();

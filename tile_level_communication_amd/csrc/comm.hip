@@ -22,6 +22,9 @@
 namespace tlc {
 namespace {
 
+constexpr int RED_UNROLL = 4;
+typedef float red_vec __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
   __shared__ int s_abort;
   if (p.wait_mask) {
@@ -29,18 +32,33 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
     __syncthreads();
     if (s_abort) return;
   }
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < p.n_vec4;
-       i += stride) {
-    float4 acc = reinterpret_cast<const float4*>(p.src[0])[i];
-    for (int s = 1; s < p.world; ++s) {
-      const float4 v = reinterpret_cast<const float4*>(p.src[s])[i];
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+  // RED_UNROLL elements per thread per pass, all W sources loaded before the
+  // sums, so that W * RED_UNROLL 16-byte loads are in flight; the partials are
+  // read once (non-temporal).  The sum runs in ascending source rank.
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x * RED_UNROLL;
+  for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x * RED_UNROLL + threadIdx.x;
+       i0 < p.n_vec4; i0 += stride) {
+    red_vec acc[RED_UNROLL];
+#pragma unroll
+    for (int u = 0; u < RED_UNROLL; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * blockDim.x;
+      if (i < p.n_vec4) acc[u] = __builtin_nontemporal_load(reinterpret_cast<const red_vec*>(p.src[0]) + i);
     }
-    reinterpret_cast<float4*>(p.out)[i] = acc;
+    for (int s = 1; s < p.world; ++s) {
+      red_vec v[RED_UNROLL];
+#pragma unroll
+      for (int u = 0; u < RED_UNROLL; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * blockDim.x;
+        if (i < p.n_vec4) v[u] = __builtin_nontemporal_load(reinterpret_cast<const red_vec*>(p.src[s]) + i);
+      }
+#pragma unroll
+      for (int u = 0; u < RED_UNROLL; ++u) acc[u] += v[u];
+    }
+#pragma unroll
+    for (int u = 0; u < RED_UNROLL; ++u) {
+      const int64_t i = i0 + static_cast<int64_t>(u) * blockDim.x;
+      if (i < p.n_vec4) reinterpret_cast<red_vec*>(p.out)[i] = acc[u];
+    }
   }
 }
 
