@@ -37,11 +37,25 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-# HBM bytes of one compute-only AG-GEMM launch (gemm_kernel_8w<KN, dense, no-wait>,
-# whole tiles, static schedule) from the rocprofv3 FETCH_SIZE and WRITE_SIZE passes
-# recorded in profiles/gemm_kernel_8w_ag_ffn_up_8192x3200x5120.md, scaled by the
-# plain-copy calibration factor 1.000.  Re-measure whenever that kernel changes.
-AG_COMPUTE_TRAFFIC_BYTES = (220280.2 + 102400.0) * 1024
+# Memory traffic per launch of each workload's dominant kernels (256 x 256 tiles,
+# K x N weight), from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (KiB per
+# dispatch) recorded under profiles/, each scaled by what the same counter reads
+# for the plain copy kernel land_kernel of known size: FETCH_SIZE x 2.000 (it
+# reads half the bytes the copy loads), WRITE_SIZE x 1.000.  Re-measure
+# whenever one of these kernels changes.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE)
+    "ag": {"gemm": (220286.0, 102400.0)},
+    "moe": {"gemm": (271901.3, 98327.2)},
+    "rs": {"gemm": (59104.9, 65536.0), "reduce": (32788.5, 16384.0)},
+    "ar": {"gemm": (59104.9, 65536.0), "reduce": (32788.5, 16384.0)},
+    "rs_long": {"gemm": (3498860.5, 2621440.0), "reduce": (1310765.8, 327680.0)},
+}
+
+
+def traffic_bytes(workload, kernel):
+    f, w = TRAFFIC_KIB[workload][kernel]
+    return round((f * FETCH_SCALE + w * WRITE_SCALE) * 1024)
 WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4, "ar": 1}
 LANDINGS = {"memcpy": 3, "copy_engine": 1, "cu": 2, "colocated": 4}  # tlc.LAND_*
 
@@ -74,6 +88,8 @@ def parse():
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--warm-seconds", type=float, default=0.5,
+                    help="minimum busy time of each leg's warm-up (after the W warm-up steps)")
     return ap.parse_args()
 
 
@@ -285,9 +301,9 @@ def run_ag(args, torch, tlc, si, workloads):
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": (round(AG_COMPUTE_TRAFFIC_BYTES) if args.tile == 256
+                     "traffic": (traffic_bytes("ag", "gemm") if args.tile == 256
                                  and args.layout == "KN" else None),
-                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE)",
+                     "traffic_unit": "bytes per launch past the L2 (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes": prob.M * prob.K * 2 + prob.K * prob.N * 2 + prob.M * prob.N * 4,
                      "kernel": "gemm_kernel_8w<KN,dense,no-wait>: compute-only launch, whole tiles, "
                                "static schedule, every chunk resident"},
@@ -414,9 +430,15 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "kernel": "gemm_kernel_8w (scatter order, no waits)"},
+                     "traffic": (traffic_bytes(args.workload, "gemm") if args.tile == 256
+                                 and args.layout == "KN" else None),
+                     "traffic_unit": "bytes per launch past the L2 (calibrated FETCH_SIZE + WRITE_SIZE)",
+                     "algorithmic_bytes": prob.M * prob.K * 2 + prob.K * prob.N * 2 + prob.M * prob.N * 4,
+                     "kernel": "gemm_kernel_8w (scatter order, no waits)"},
         "reduce_roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(red_gbs / PEAK_HBM_GBS, 4),
+                            "traffic": traffic_bytes(args.workload, "reduce"),
+                            "algorithmic_bytes": prob.reduce_bytes,
                             "kernel": "reduce_kernel", "ms": round(red_ms, 4)},
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
@@ -485,7 +507,11 @@ def run_moe(args, torch, tlc, si, workloads):
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": (traffic_bytes("moe", "gemm") if args.tile == 256
+                                 and args.layout == "KN" else None),
+                     "traffic_unit": "bytes per launch past the L2 (calibrated FETCH_SIZE + WRITE_SIZE)",
+                     "algorithmic_bytes": prob.T * prob.H * 2 + prob.E * prob.H * prob.N * 2
+                     + prob.T * prob.k * prob.N * 4,
                      "kernel": "gemm_kernel_8w<KN,moe,no-wait>: grouped GEMM, every chunk resident"},
         "route_ms": round(route_ms, 4),
         "compute_only_ms": round(t_comp * 1e3, 4),
@@ -499,7 +525,9 @@ def run_moe(args, torch, tlc, si, workloads):
 
 
 def main():
+    global WARM_SECONDS
     args = parse()
+    WARM_SECONDS = args.warm_seconds
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the method (the other ranks are emulated on "
               "the same GPU); runs on more than one GPU are not supported.", file=sys.stderr)
