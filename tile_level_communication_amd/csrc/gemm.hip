@@ -328,10 +328,31 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
                                            0x00020000);
 }
 
-// 16 bytes per lane from global memory straight into LDS at base + 16 * lane.
-__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, TLC_LDS void* lds, uint32_t voff,
+// Buffer descriptor as four wave-uniform words (base, 0 stride, byte size,
+// format flags) for the LDS-writing loads below.
+typedef unsigned int rsrc_words __attribute__((ext_vector_type(4)));
+__device__ inline rsrc_words rsrc_raw(const void* base, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  rsrc_words d;
+  d.x = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  d.y = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)) & 0xFFFFu;
+  d.z = __builtin_amdgcn_readfirstlane(bytes);
+  d.w = 0x00020000u;
+  return d;
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (the LDS base goes in M0).  Written as an instruction rather than the
+// compiler builtin: the compiler cannot tell which LDS stage such a load
+// writes, and would otherwise wait for every outstanding one before each LDS
+// read of the other stage.  Completion is awaited explicitly (vmcnt) before
+// the workgroup barrier that precedes any read of the stage.
+__device__ inline void load_lds16(rsrc_words r, const TLC_LDS void* lds, uint32_t voff,
                                   uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
 }
 
 template <int B_NK, int KIND>
@@ -348,12 +369,12 @@ struct Tile8w {
 
     // ---- global sources of the 4 A blocks and 4 B blocks (1 KB each) this
     // wave fills per stage; rows outside the tile are clamped into it ----
-    __amdgpu_buffer_rsrc_t ra;
+    rsrc_words ra;
     uint32_t a_off[4];
     if (KIND == KIND_MOE) {
-      ra = make_rsrc(p.a, static_cast<uint32_t>(p.a_rows) * lda2);
+      ra = rsrc_raw(p.a, static_cast<uint32_t>(p.a_rows) * lda2);
     } else {
-      ra = make_rsrc(p.a + static_cast<int64_t>(tl.m0) * p.lda, static_cast<uint32_t>(tl.m_rows) * lda2);
+      ra = rsrc_raw(p.a + static_cast<int64_t>(tl.m0) * p.lda, static_cast<uint32_t>(tl.m_rows) * lda2);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -365,10 +386,10 @@ struct Tile8w {
       a_off[q] = src_row * lda2 + kc * 16;
     }
     const uint16_t* bexp = p.b + (KIND == KIND_MOE ? tl.expert * p.b_expert_stride : 0);
-    __amdgpu_buffer_rsrc_t rb;
+    rsrc_words rb;
     uint32_t b_off[4];
     if constexpr (B_NK) {
-      rb = make_rsrc(bexp + static_cast<int64_t>(tl.n0) * p.ldb, static_cast<uint32_t>(tl.n_cols) * ldb2);
+      rb = rsrc_raw(bexp + static_cast<int64_t>(tl.n0) * p.ldb, static_cast<uint32_t>(tl.n_cols) * ldb2);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         int row = (wave * 4 + q) * 8 + (lane >> 3);
@@ -377,7 +398,7 @@ struct Tile8w {
         b_off[q] = row * ldb2 + kc * 16;
       }
     } else {
-      rb = make_rsrc(bexp + tl.n0, static_cast<uint32_t>(p.K) * ldb2);
+      rb = rsrc_raw(bexp + tl.n0, static_cast<uint32_t>(p.K) * ldb2);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int k = (wave * 4 + q) * 2 + (lane >> 5);
@@ -390,10 +411,10 @@ struct Tile8w {
     auto issue = [&](int kt, TLC_LDS u32x4* As, TLC_LDS u32x4* Bs) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        load_lds16(ra, (TLC_LDS void*)(As + (wave * 4 + q) * 64), a_off[q], kt * 128u);
+        load_lds16(ra, (const TLC_LDS void*)(As + (wave * 4 + q) * 64), a_off[q], kt * 128u);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        load_lds16(rb, (TLC_LDS void*)(Bs + (wave * 4 + q) * 64), b_off[q], kt * b_step);
+        load_lds16(rb, (const TLC_LDS void*)(Bs + (wave * 4 + q) * 64), b_off[q], kt * b_step);
     };
 
     f32x16 acc[FM][FN];
@@ -437,43 +458,59 @@ struct Tile8w {
         }
       }
     };
-    // One BK = 64 stage: fragments for step ks+1 are requested before the
-    // MFMAs of step ks are issued (the scheduling barriers keep that order).
-    auto compute = [&](const TLC_LDS u32x4* As, const TLC_LDS u32x4* Bs) {
-      fread(As, Bs, 0, 0);
+    auto mfmas = [&](int sl) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int sl = ks & 1;
-        if (ks < 3) fread(As, Bs, ks + 1, sl ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
     };
-    // LDS-writing buffer loads are tracked by vmcnt: wait for this wave's, then
-    // the barrier covers the other waves'.
-    auto stage_done = [&]() {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    };
-
+    // One BK = 64 step on stage (Ac, Bc), whose first fragments are already in
+    // registers: the fragments of sub-step ks+1 are requested before the MFMAs
+    // of sub-step ks (the scheduling barriers keep that order).  Before the
+    // last sub-step's MFMAs -- their fragments are in registers -- the wave
+    // waits for its LDS reads and its loads of the next stage, and the
+    // workgroup barrier makes the next stage whole and this one free; under
+    // those MFMAs go the next stage's first fragment reads and the loads of
+    // the step after next into this stage.
     int kt0, kt1;
     unit_k_range(tl.split, p.K / 64, &kt0, &kt1);
-    if (kt0 < kt1) issue(kt0, A0, B0);
-    stage_done();
-    for (int kt = kt0; kt < kt1; kt += 2) {
-      if (kt + 1 < kt1) issue(kt + 1, A1, B1);
-      compute(A0, B0);
-      stage_done();
-      if (kt + 1 < kt1) {
-        if (kt + 2 < kt1) issue(kt + 2, A0, B0);
-        compute(A1, B1);
-        stage_done();
+    const int nk = kt1 - kt0;
+    auto step = [&](int i, const TLC_LDS u32x4* Ac, const TLC_LDS u32x4* Bc, TLC_LDS u32x4* Aw,
+                    TLC_LDS u32x4* Bw, const TLC_LDS u32x4* An, const TLC_LDS u32x4* Bn) {
+#pragma unroll
+      for (int ks = 0; ks < 3; ++ks) {
+        fread(Ac, Bc, ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(ks & 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < nk) fread(An, Bn, 0, 0);
+      if (i + 2 < nk) issue(kt0 + i + 2, Aw, Bw);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (nk > 0) {
+      issue(kt0, A0, B0);
+      if (nk > 1) {
+        issue(kt0 + 1, A1, B1);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0's eight loads done
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+      fread(A0, B0, 0, 0);
+      for (int i = 0; i < nk; i += 2) {
+        step(i, A0, B0, A0, B0, A1, B1);
+        if (i + 1 < nk) step(i + 1, A1, B1, A1, B1, A0, B0);
+      }
+    } else {
+      __syncthreads();
     }
     if (!split_epilogue<NT>(p, tl, acc, s_flag)) return;
 
