@@ -363,7 +363,12 @@ struct Tile8w {
   __device__ static void run(const GemmParams& p, const tlc_tile& tl, TLC_LDS u32x4* A0,
                              TLC_LDS u32x4* A1, TLC_LDS u32x4* B0, TLC_LDS u32x4* B1,
                              int* s_flag) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the thread index is made opaque per tile, so that the lane-dependent
+    // offsets below are formed per tile instead of being kept (and spilled)
+    // across the whole persistent loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const uint32_t lda2 = static_cast<uint32_t>(p.lda) * 2, ldb2 = static_cast<uint32_t>(p.ldb) * 2;
 
