@@ -283,8 +283,11 @@ typedef struct {
    * rows_per_chunk / S rows, each raising its own flag (flags[c * S + j]); the
    * plan must be built with the same sub_chunks.  world * S <= 32. */
   int32_t sub_chunks;
-  /* TLC_LAND_COLOCATED only: workgroups that copy before computing
-   * (1..grid; 0 = half the grid, a multiple of 8). */
+  /* TLC_LAND_COLOCATED only: workgroups that copy before computing (1..grid;
+   * 0 = those the last round of units leaves idle, grid rounds minus the unit
+   * count rounded down to a multiple of 8, or the whole grid when that is
+   * under 32; for AG-MoE, whose unit count is known only on the device, a
+   * quarter of the grid).  They take the last units of the first round. */
   int32_t copy_wgs;
   /* Optional debug trace (NULL = off): device int64 array of n_tiles x 4,
    * entry t = {workgroup, wall-clock at wait start, at wait end, at tile end}

@@ -215,17 +215,26 @@ void set_schedule(GemmParams* p, int32_t schedule, void* ws, int64_t ws_bytes) {
 }
 
 // Co-located landing: the chunks in landing order (rank+n_local, ... mod W)
-// and the number of workgroups that copy them (0 = half the grid, a multiple
-// of 8, at least 8 or the whole grid if smaller).
+// and the number of workgroups that copy them.  Default: the workgroups that
+// the last round of units leaves idle anyway (rounds * grid - n_units, a
+// multiple of 8); when that is under 32 the copy is on the critical path
+// whoever does it, and every workgroup takes a share; a quarter of the grid
+// when the unit count is only known on the device (n_units < 0).
 tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src, int64_t bytes,
                          int world, int rank, int n_local, int copy_wgs, int grid, const char* who,
-                         int flag_base = 0) {
+                         int flag_base = 0, int64_t n_units = -1) {
   if (copy_wgs < 0 || copy_wgs > grid)
     return fail(TLC_ERR_INVALID_ARG, "%s: copy_wgs %d outside 0..grid %d", who, copy_wgs, grid);
   int cw = copy_wgs;
   if (cw == 0) {
-    cw = grid / 2 / 8 * 8;
-    if (cw < 8) cw = grid < 8 ? grid : 8;
+    if (n_units >= 0) {
+      const int64_t rounds = (n_units + grid - 1) / grid;
+      cw = static_cast<int>((rounds * grid - n_units) / 8 * 8);
+      if (cw < 32) cw = grid;
+    } else {
+      cw = grid / 4 / 8 * 8;
+      if (cw < 8) cw = grid < 8 ? grid : 8;
+    }
   }
   p->copy_wgs = world > n_local ? cw : 0;
   p->copy_chunks = world - n_local;
@@ -405,7 +414,8 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   int grid = a->n_tiles > 0 ? pick_grid(a->grid, p.dynamic, a->n_tiles, avail)
                             : (a->grid > 0 ? a->grid : avail);
   if (coloc) {
-    st = set_colocated(&p, dst, src, chunk_bytes, Wf, rf, S, a->copy_wgs, grid, "tlc_ag_gemm");
+    st = set_colocated(&p, dst, src, chunk_bytes, Wf, rf, S, a->copy_wgs, grid, "tlc_ag_gemm", 0,
+                       a->n_tiles);
     if (st) return st;
     if (a->n_tiles == 0) grid = p.copy_wgs;
   }
@@ -505,7 +515,7 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
       p.do_wait = 1;
       p.no_wait_mask = 0xFFFFFFFFu;
       st = set_colocated(&p, const_cast<void* const*>(g->dst), g->src, slice_bytes, a->world,
-                         a->rank, 1, g->copy_wgs, grid, "tlc_gemm_ar", a->world);
+                         a->rank, 1, g->copy_wgs, grid, "tlc_gemm_ar", a->world, a->n_tiles);
       if (st) return st;
       if (a->n_tiles == 0) grid = p.copy_wgs;
     }

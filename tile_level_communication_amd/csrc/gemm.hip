@@ -604,8 +604,19 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
   uint32_t seen = p.no_wait_mask;
   // The first unit of every workgroup is its slot (no counter traffic while all
   // workgroups start at once); the dynamic schedule then hands out units
-  // G, G+1, ... from the counter as workgroups become free.
-  int64_t t = p.xcd_remap ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  // G, G+1, ... from the counter as workgroups become free.  Slots are spread
+  // so that each XCD takes a contiguous run of the plan.  With co-located
+  // copying, the copying workgroups -- busy first -- take the last slots of
+  // the round, the units of the latest chunks, and the others the rest.
+  const int g = blockIdx.x;
+  int64_t t;
+  const int cw = WAIT ? p.copy_wgs : 0;
+  if (cw > 0 && cw < G) {
+    const int Gr = G - cw, r = g - cw;
+    t = g < cw ? Gr + g : ((p.xcd_remap && Gr % 8 == 0 && cw % 8 == 0) ? (r & 7) * (Gr >> 3) + (r >> 3) : r);
+  } else {
+    t = p.xcd_remap ? (g & 7) * (G >> 3) + (g >> 3) : g;
+  }
   for (int it = 1; t < n_tiles; ++it) {
     const tlc_tile tl = p.plan[t];
     const uint32_t S = tl.split & 0xFFu;
