@@ -101,3 +101,24 @@ def gemm_ar(a_local, b_kn, remote: dict, gathered: dict, world: int, rank: int):
     for ch in range(world):
         c[ch * R:(ch + 1) * R] = out if ch == rank else np.asarray(gathered[ch], dtype=np.float64)
     return p, c
+
+
+def blocked_gemm_f32(a_rows, b_kn, units, K_split=None):
+    """The blocked fp32 GEMM: C (fp32) assembled tile by tile in the given unit
+    order (m0, n0, m_rows, n_cols, ...), each tile accumulating its products in
+    fp32 over k = 0, 1, ..., K-1 in increasing order (DITRON §3.1, core-level
+    tiles; the tile order is the only thing the swizzle changes).  a_rows: M x K
+    bf16 bits (the gathered rows), b_kn: K x N bf16 bits.  Slow (one fp32
+    rank-1 update per k): for small shapes only."""
+    a = bf16_to_f64(a_rows).astype(np.float32)
+    b = bf16_to_f64(b_kn).astype(np.float32)
+    M, K = a.shape
+    N = b.shape[1]
+    c = np.full((M, N), np.nan, dtype=np.float32)
+    for u in units:
+        m0, n0, mr, nc = u[0], u[1], u[2], u[3]
+        acc = np.zeros((mr, nc), dtype=np.float32)
+        for k in range(K):
+            acc += a[m0:m0 + mr, k:k + 1] * b[k:k + 1, n0:n0 + nc]
+        c[m0:m0 + mr, n0:n0 + nc] = acc
+    return c

@@ -171,3 +171,47 @@ def test_gemm_ar_consistent_shards_give_unsharded_product():
         _, c = og.gemm_ar(shards[rank].a, shards[rank].b, remote, gathered, world, rank)
         assert c.shape == (M, n)
         np.testing.assert_array_equal(c, full.astype(np.float64))
+
+
+def test_blocked_f32_tile_order_never_changes_the_result():
+    """The blocked fp32 GEMM gives the same bits in every tile order -- the
+    communication-aware orders of every rank, the natural order, reversed and
+    shuffled orders -- covers C exactly once, and stays within the stated
+    tolerance of the float64 definition."""
+    from oracle import plan as op
+    W, R, K, N = 3, 40, 48, 56
+    inp = si.ag_inputs(911, W, R, N, K)
+    a_rows = np.concatenate(inp.a_chunks)
+    ref64 = og.ag_gemm(inp.a_chunks, inp.b)
+    base, _ = op.chunk_plan(op.AG, W, 0, W * R, N, R, 32, 32, op.ORDER_NATURAL, 1)
+    first = og.blocked_gemm_f32(a_rows, inp.b, base)
+    assert not np.isnan(first).any()
+    rng = np.random.default_rng(5)
+    orders = [list(reversed(base)), [base[i] for i in rng.permutation(len(base))]]
+    for rank in range(W):
+        for mode in (op.AG, op.RS):
+            orders.append(op.chunk_plan(mode, W, rank, W * R, N, R, 32, 32, op.ORDER_RANK_OFFSET, 2)[0])
+    for units in orders:
+        got = og.blocked_gemm_f32(a_rows, inp.b, units)
+        assert np.array_equal(got.view(np.uint32), first.view(np.uint32))
+    amax = float(np.abs(si.bf16_bits_to_f32(a_rows)).max())
+    bmax = float(np.abs(si.bf16_bits_to_f32(inp.b)).max())
+    err = np.abs(first.astype(np.float64) - ref64)
+    assert err.max() <= 2e-3 * np.sqrt(K) * amax * bmax
+    assert np.linalg.norm(first - ref64) / np.linalg.norm(ref64) <= 1e-3
+
+
+def test_blocked_f32_integer_inputs_exact():
+    """Integer-valued inputs make every fp32 partial sum exact: the blocked
+    fp32 GEMM then equals the integer brute force."""
+    from oracle import plan as op
+    W, R, K, N = 2, 9, 12, 10
+    inp = si.ag_inputs(912, W, R, N, K, integer=True)
+    a_rows = np.concatenate(inp.a_chunks)
+    units, _ = op.chunk_plan(op.AG, W, 1, W * R, N, R, 8, 8, op.ORDER_RANK_OFFSET, 1)
+    got = og.blocked_gemm_f32(a_rows, inp.b, units)
+    a = si.bf16_bits_to_f32(a_rows).astype(np.int64)
+    b = si.bf16_bits_to_f32(inp.b).astype(np.int64)
+    for i in range(W * R):
+        for j in range(N):
+            assert got[i, j] == sum(int(a[i, k]) * int(b[k, j]) for k in range(K))
