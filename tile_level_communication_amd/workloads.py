@@ -267,8 +267,9 @@ class ARProblem(RSProblem):
 
 class MoEProblem:
     def __init__(self, x_chunks, logits, w_ekn, rank, topk, bm=256, bn=256, b_layout=tlc.B_KN,
-                 order=tlc.ORDER_RANK_OFFSET, device="cuda"):
+                 order=tlc.ORDER_RANK_OFFSET, device="cuda", schedule=tlc.SCHED_DYNAMIC):
         self.device = torch.device(device)
+        self.schedule = schedule
         dev = self.device
         self.world = len(x_chunks)
         self.rank = rank
@@ -333,7 +334,7 @@ class MoEProblem:
                    self.rank, self.E, self.k, self.H, self.N, self.bm, self.bn, self.x,
                    self.x_src if land != tlc.LAND_NONE else None, self.w, self.b_layout, self.y,
                    self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns,
-                   copy_wgs=copy_wgs)
+                   schedule=self.schedule, copy_wgs=copy_wgs)
         s.end()
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
