@@ -161,6 +161,10 @@ tlc_status check_land_args(int land, const void* const* src, const void* const* 
   if (!src || !dst) return fail(TLC_ERR_INVALID_ARG, "%s: landing needs source and destination arrays", who);
   if (bytes % 16 != 0) return fail(TLC_ERR_MISALIGNED, "%s: chunk bytes %lld not a multiple of 16", who,
                                    static_cast<long long>(bytes));
+  // the CU and co-located copies address a chunk with 32-bit buffer offsets
+  if ((land == TLC_LAND_CU || land == TLC_LAND_COLOCATED) && bytes >= (1LL << 32))
+    return fail(TLC_ERR_UNSUPPORTED, "%s: chunk of %lld bytes (the CU copies take < 4 GiB)", who,
+                static_cast<long long>(bytes));
   for (int c = 0; c < world; ++c) {
     if ((c - rank + world) % world < n_local) continue;
     if (!src[c] || !dst[c]) return fail(TLC_ERR_INVALID_ARG, "%s: chunk %d pointer is NULL", who, c);

@@ -65,11 +65,24 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceParams p) {
 // Each workgroup copies blocks of LAND_THREADS * LAND_UNROLL 16-byte units of a
 // chunk: every thread first loads LAND_UNROLL units (consecutive threads read
 // consecutive units), then stores them, so each CU keeps 128 KB of reads in
-// flight.  The source is read once (non-temporal loads); the destination is
-// stored normally, since the GEMM reads it next.
+// flight.  The source is read once (non-temporal loads).  The stores are
+// device-coherent (sc1: written through past the XCD's L2), so after waiting
+// for them a workgroup counts itself in with a relaxed atomic and no L2
+// write-back; the last arrival raises the chunk's flag with a release store.
 constexpr int LAND_THREADS = 1024;
 constexpr int LAND_UNROLL = 8;
+constexpr int LAND_CPOL_SC1 = 16;  // cache-policy bit of a device-coherent store
 typedef unsigned int land_vec __attribute__((ext_vector_type(4)));
+
+__device__ inline __amdgpu_buffer_rsrc_t land_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0),
+                                           static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
+                                           0x00020000);
+}
 
 __global__ __launch_bounds__(LAND_THREADS) void land_kernel(LandParams p) {
   const int64_t block = static_cast<int64_t>(LAND_THREADS) * LAND_UNROLL;
@@ -77,8 +90,8 @@ __global__ __launch_bounds__(LAND_THREADS) void land_kernel(LandParams p) {
   for (int i = 0; i < p.n_chunks; ++i) {
     const int c = p.order[i];
     const land_vec* src = reinterpret_cast<const land_vec*>(p.src[c]);
-    land_vec* dst = reinterpret_cast<land_vec*>(p.dst[c]);
-    const int64_t n = p.vec_per_chunk;
+    const int64_t n = p.vec_per_chunk;  // a chunk is < 2^32 bytes
+    const __amdgpu_buffer_rsrc_t rd = land_rsrc(p.dst[c], static_cast<uint32_t>(n * 16));
     for (int64_t base = static_cast<int64_t>(blockIdx.x) * block + threadIdx.x; base < n;
          base += stride) {
       land_vec v[LAND_UNROLL];
@@ -90,18 +103,15 @@ __global__ __launch_bounds__(LAND_THREADS) void land_kernel(LandParams p) {
 #pragma unroll
       for (int u = 0; u < LAND_UNROLL; ++u) {
         const int64_t k = base + static_cast<int64_t>(u) * LAND_THREADS;
-        if (k < n) dst[k] = v[u];
+        if (k < n)
+          __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, static_cast<int>(k * 16), 0, LAND_CPOL_SC1);
       }
     }
-    // every wave's stores have reached the cache; one thread then releases
-    // them device-wide (a release writes back the whole L2 once, instead of
-    // once per wave) and counts the workgroup in
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
       const int f = p.flag_base + c;
-      __atomic_thread_fence(__ATOMIC_RELEASE);
-      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->land_count[f], 1u, __ATOMIC_ACQ_REL,
+      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->land_count[f], 1u, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
       if (prev == gridDim.x - 1) {
         __hip_atomic_store(&p.sig->land_count[f], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
