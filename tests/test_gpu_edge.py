@@ -1,0 +1,86 @@
+"""Degenerate cases on the GPU through the C ABI, against the oracle: one
+rank (nothing to land, every landing mode), and a single tile smaller than the
+tile shape."""
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as si
+from oracle import gemm as og
+from oracle import moe as om
+from tests.parity import absmax_bf16, check_close, check_exact, log
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tile_level_communication_amd import tlc
+    from tile_level_communication_amd.workloads import AGProblem, ARProblem, MoEProblem, RSProblem
+else:  # collected on CPU-only hosts, never run there
+    from tile_level_communication_amd import tlc  # noqa: F401
+
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3, "colocated": 4}
+
+
+@pytest.mark.parametrize("land", list(LANDS))
+def test_single_rank_every_path(land):
+    """world = 1: AG-GEMM is a plain GEMM, GEMM-RS's reduce is the local slice,
+    GEMM-AR's output is the local product, AG-MoE routes the local tokens."""
+    L = LANDS[land]
+    R, K, N = 200, 128, 136
+    inp = si.ag_inputs(500, 1, R, N, K, integer=True)
+    log(f"[edge] W=1 AG land={land}")
+    prob = AGProblem(inp.a_chunks, inp.b, 0, 128, 128, tlc.B_KN)
+    prob.place_all()
+    prob.run(L)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    check_exact(prob.c.cpu().numpy(), og.ag_gemm(inp.a_chunks, inp.b), "W=1 AG")
+
+    rs = si.rs_inputs(501, 1, 0, R, N, K, integer=True)
+    p_ref, out_ref = og.gemm_rs(rs.a, rs.b, rs.remote, 1, 0)
+    log(f"[edge] W=1 RS land={land}")
+    prob = RSProblem(rs.a, rs.b, rs.remote, 1, 0, 128, 128, tlc.B_KN)
+    prob.run(L)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    check_exact(prob.partials.cpu().numpy(), p_ref, "W=1 RS partials")
+    check_exact(prob.out.cpu().numpy(), out_ref, "W=1 RS out")
+
+    ar = si.ar_inputs(502, 1, 0, R, N, K, integer=True)
+    p_ref, c_ref = og.gemm_ar(ar.a, ar.b, ar.remote, ar.gathered, 1, 0)
+    log(f"[edge] W=1 AR land={land}")
+    prob = ARProblem(ar.a, ar.b, ar.remote, ar.gathered, 1, 0, 128, 128, tlc.B_KN)
+    prob.run(L)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    check_exact(prob.c.cpu().numpy(), c_ref, "W=1 AR")
+
+    mi = si.moe_inputs(503, 1, 48, 64, 72, 8, integer=True)
+    ref = om.route(mi.logits, 2, 1, 0, 48)
+    log(f"[edge] W=1 MoE land={land}")
+    prob = MoEProblem(mi.x_chunks, mi.logits, mi.w, 0, 2, 128, 128, tlc.B_KN)
+    prob.place_all()
+    prob.run(L)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    assert np.array_equal(prob.row_token.cpu().numpy(), ref["row_token"])
+    y_ref = om.grouped_gemm(mi.x_chunks, mi.w, ref["offsets"], ref["row_token"])
+    check_exact(prob.y.cpu().numpy(), y_ref, "W=1 MoE")
+
+
+@pytest.mark.parametrize("tile", [128, 256])
+@pytest.mark.parametrize("land", ["memcpy", "colocated"])
+def test_one_small_tile(tile, land):
+    """A whole problem smaller than one tile (8 x 8 output, K = 64): both edges
+    masked, two ranks of 4 rows each."""
+    W, R, K, N = 2, 4, 64, 8
+    inp = si.ag_inputs(504, W, R, N, K)
+    for rank in range(W):
+        log(f"[edge] tiny AG tile={tile} land={land} rank={rank}")
+        prob = AGProblem(inp.a_chunks, inp.b, rank, tile, tile, tlc.B_KN)
+        prob.poison_remote()
+        prob.run(LANDS[land])
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        check_close(prob.c.cpu().numpy(), og.ag_gemm(inp.a_chunks, inp.b), K, absmax_bf16(inp.a_chunks),
+                    absmax_bf16(inp.b), "tiny")
