@@ -136,3 +136,20 @@ def test_ar_4096_full_size(rank):
         _, p, c = _run(inp, wl.world, rank, 256, tlc.B_KN, LANDS[land])
         check_close(p, p_ref, wl.k, am, bm, "partials")
         check_close(c, c_ref, wl.k, am, bm, "all-reduced")
+
+
+@pytest.mark.parametrize("land", ["memcpy", "colocated"])
+@pytest.mark.parametrize("sched", ["dynamic", "static"])
+def test_ar_split_parity(land, sched):
+    """GEMM-AllReduce with tiles split along K (partial slots, in-order fixup):
+    integer inputs bit for bit, with the all-gather landed or co-located."""
+    schedule = tlc.SCHED_DYNAMIC if sched == "dynamic" else tlc.SCHED_STATIC
+    for (name, W, R, K, N, tile) in SHAPES:
+        rank = W - 1
+        log(f"[ar split] {name} land={land} sched={sched}")
+        inp = si.ar_inputs(440 + W, W, rank, R, N, K, integer=True)
+        p_ref, c_ref = og.gemm_ar(inp.a, inp.b, inp.remote, inp.gathered, W, rank)
+        _, p, c = _run(inp, W, rank, tile, tlc.B_KN, LANDS[land], split_k=3, split_from=0,
+                       schedule=schedule)
+        check_exact(p, p_ref, name + " partials")
+        check_exact(c, c_ref, name + " all-reduced")
