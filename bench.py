@@ -416,6 +416,20 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
 
     timed(reduce_only, steps, warm, torch)
     red_ms = red_t.mean_ms(steps)
+    # the same with the 256 MB MALL flushed before each launch (a 512 MiB
+    # fill in between): the reduce's sources then come from HBM
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    red_f = KernelTimer(torch, compute)
+
+    def reduce_flushed():
+        with torch.cuda.stream(compute):
+            flush.fill_(1)
+        red_f(lambda: tlc.rs_reduce(*prob._args(), None, prob.landing, prob.out, prob.sig,
+                                    tlc.EPOCH_MAX, tlc.LAND_NONE, compute))
+
+    timed(reduce_flushed, steps, warm, torch)
+    red_flushed_ms = red_f.mean_ms(steps)
+    del flush
 
     torch.cuda.synchronize()
     gemm_ms = comp_t.mean_ms(steps) - red_ms
@@ -439,7 +453,9 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
                             "unit": "GB/s", "frac": round(red_gbs / PEAK_HBM_GBS, 4),
                             "traffic": traffic_bytes(args.workload, "reduce"),
                             "algorithmic_bytes": prob.reduce_bytes,
-                            "kernel": "reduce_kernel", "ms": round(red_ms, 4)},
+                            "kernel": "reduce_kernel", "ms": round(red_ms, 4),
+                            "ms_mall_flushed": round(red_flushed_ms, 4),
+                            "achieved_mall_flushed": round(prob.reduce_bytes / (red_flushed_ms * 1e-3) / 1e9, 1)},
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
         "copy_only_ms": round(t_copy * 1e3, 4),
