@@ -254,6 +254,27 @@ def run_ag(args, torch, tlc, si, workloads):
     gemm_fused_ms = fused_t.mean_ms(args.steps)
     status = prob.sig.read_status(compute)
 
+    # one more fused step with per-unit trace stamps: time the workgroups spent
+    # spinning on chunk flags (the exposed part of the landing inside the GEMM)
+    trace = torch.zeros((prob.n_tiles, 4), dtype=torch.int64, device=dev)
+    workloads.next_epoch(prob)
+    for c in copies:
+        c.wait_stream(compute)
+    tlc.ag_gemm(**call, a_src=prob.a_src, epoch=prob.epoch, land=land, compute_stream=compute,
+                copy_stream=copies, grid=args.grid, trace=trace, copy_wgs=args.copy_wgs)
+    for c in copies:
+        compute.wait_stream(c)
+    torch.cuda.synchronize()
+    tr = trace.cpu().numpy()
+    khz = max(tlc.wall_clock_khz(), 1)
+    wait_us = (tr[:, 2] - tr[:, 1]) * 1e3 / khz
+    span_us = float(tr[:, 3].max() - tr[:, 1].min()) * 1e3 / khz
+    n_wg = len(set(tr[:, 0].tolist()))
+    spin = {"wait_us_total": round(float(wait_us.sum()), 1),
+            "units_that_waited": int((wait_us > 1.0).sum()),
+            "wait_fraction_of_workgroup_time": round(float(wait_us.sum()) / (n_wg * span_us), 4),
+            "kernel_span_us": round(span_us, 1)}
+
     # the same step with the other landing backends (reported beside the headline)
     others = {o: (timed(fused_step(o), args.steps, args.warmup, torch), prob.sig.read_status(compute))
               for o in LANDINGS.values() if o != land}
@@ -312,6 +333,8 @@ def run_ag(args, torch, tlc, si, workloads):
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
         "gemm_kernel_ms": {"fused": round(gemm_fused_ms, 4), "compute_only": round(gemm_comp_ms, 4)},
         "copy_only_ms": round(t_copy * 1e3, 4),
+        "exposed_copy_ms": round((t_fused - t_comp) * 1e3, 4),
+        "flag_spin": spin,
         "copy_gbs": round((prob.world - 1) * prob.R * prob.K * 2 / t_copy / 1e9, 1),
         "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,

@@ -463,6 +463,11 @@ tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_
                     int32_t world, int32_t rank, tlc_signals* sig, uint32_t epoch, int32_t land,
                     void* const* copy_streams, int32_t n_copy_streams);
 
+/* Rate in kHz of the device clock that timeouts and the debug traces count in
+ * (hipDeviceAttributeWallClockRate of the current device); 0 if it cannot be
+ * queried. */
+int64_t tlc_wall_clock_khz(void);
+
 const char* tlc_status_string(tlc_status s);
 const char* tlc_last_error(void);
 /* Library version, e.g. 130 = 0.1.30. */

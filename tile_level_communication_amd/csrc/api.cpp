@@ -727,6 +727,12 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
   return st ? st : ok();
 }
 
+int64_t tlc_wall_clock_khz(void) {
+  DeviceInfo info;
+  if (device_info(&info)) return 0;
+  return info.wall_khz;
+}
+
 const char* tlc_status_string(tlc_status s) {
   switch (s) {
     case TLC_OK: return "ok";

@@ -32,6 +32,7 @@ EXPORTS = [
     "tlc_signals_clear_status", "tlc_read_status", "tlc_ag_gemm", "tlc_gemm_rs", "tlc_rs_reduce",
     "tlc_moe_plan_capacity", "tlc_moe_workspace_bytes", "tlc_moe_route", "tlc_ag_moe", "tlc_land",
     "tlc_status_string", "tlc_last_error", "tlc_version", "tlc_split_workspace_bytes", "tlc_gemm_ar",
+    "tlc_wall_clock_khz",
 ]
 
 
@@ -153,6 +154,8 @@ def lib() -> C.CDLL:
         L.tlc_status_string.restype = C.c_char_p
         L.tlc_last_error.argtypes = []
         L.tlc_last_error.restype = C.c_char_p
+        L.tlc_wall_clock_khz.argtypes = []
+        L.tlc_wall_clock_khz.restype = C.c_int64
         L.tlc_version.argtypes = []
         L.tlc_version.restype = C.c_int32
         L.tlc_split_workspace_bytes.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32]
@@ -167,6 +170,11 @@ def status_string(s: int) -> str:
 
 def last_error() -> str:
     return lib().tlc_last_error().decode()
+
+
+def wall_clock_khz() -> int:
+    """Rate of the device clock the traces count in (kHz)."""
+    return int(lib().tlc_wall_clock_khz())
 
 
 def version() -> int:
