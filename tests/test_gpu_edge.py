@@ -84,3 +84,25 @@ def test_one_small_tile(tile, land):
         assert prob.sig.read_status()[0] == 0
         check_close(prob.c.cpu().numpy(), og.ag_gemm(inp.a_chunks, inp.b), K, absmax_bf16(inp.a_chunks),
                     absmax_bf16(inp.b), "tiny")
+
+
+@pytest.mark.parametrize("layout", ["KN", "NK"])
+def test_ragged_last_m_tile_row_blocks(layout):
+    """The 256 x 256 core skips the fragment reads and MFMAs of the 32-row
+    blocks past a tile's last row (each wavefront owns four blocks; a
+    wavefront with none only loads): every remainder from 1 row to a full
+    tile, whole and K-split units, bit-exact against the oracle."""
+    bl = tlc.B_KN if layout == "KN" else tlc.B_NK
+    K, N = 192, 264
+    for r in (1, 31, 32, 33, 96, 127, 128, 129, 160, 224, 255, 256):
+        M = 256 + r
+        inp = si.ag_inputs(505, 1, M, N, K, integer=True)
+        ref = og.ag_gemm(inp.a_chunks, inp.b)
+        for split in (0, 3):
+            log(f"[edge] ragged M={M} layout={layout} split_k={split}")
+            prob = AGProblem(inp.a_chunks, inp.b, 0, 256, 256, bl, split_k=split, split_from=0)
+            prob.place_all()
+            prob.run(tlc.LAND_NONE)
+            torch.cuda.synchronize()
+            assert prob.sig.read_status()[0] == 0
+            check_exact(prob.c.cpu().numpy(), ref, f"ragged M={M} split_k={split}")

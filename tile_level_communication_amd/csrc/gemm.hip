@@ -31,6 +31,8 @@
 //  * 128 x 128 (small problems): 4 wavefronts, register-staged loads.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_sync.h"
 #include "tlc_internal.h"
 
@@ -430,46 +432,17 @@ struct Tile8w {
     const int h = lane >> 5;
     const int s_lane = swz(lane & 31);
     bf16x8 fa[2][FM], fb[2][FN];
-    auto fread = [&](const TLC_LDS u32x4* As, const TLC_LDS u32x4* Bs, int ks, int slot) {
-      const int phys = (ks * 2 + h) ^ s_lane;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[slot][i] = __builtin_bit_cast(
-            bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)As +
-                                            (wm * WM + i * 32 + (lane & 31)) * 128 + phys * 16));
-      if constexpr (B_NK) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          fb[slot][j] = __builtin_bit_cast(
-              bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)Bs +
-                                              (wn * WN + j * 32 + (lane & 31)) * 128 + phys * 16));
-      } else {
-        // Lane l needs B[k = 16 ks + 8 (l / 32) + t][n] for t = 0..7 (n = l % 32 of the block):
-        // two transposing reads, each giving 4 consecutive k of one column.
-        const int g = lane >> 4, i16 = lane & 15;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          v4i16 hv[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int k = ks * 16 + 8 * (g >> 1) + 4 * hh + (i16 >> 2);
-            const int n = wn * WN + j * 32 + 16 * (g & 1) + 4 * (i16 & 3);
-            const int pc = (n >> 3) ^ (2 * (k & 15));
-            hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (TLC_LDS v4i16*)((const TLC_LDS char*)Bs + k * 512 + pc * 16 + (n & 7) * 2));
-          }
-          const v8i16 v = {hv[0][0], hv[0][1], hv[0][2], hv[0][3], hv[1][0], hv[1][1], hv[1][2], hv[1][3]};
-          fb[slot][j] = __builtin_bit_cast(bf16x8, v);
-        }
-      }
-    };
-    auto mfmas = [&](int sl) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
-    };
+    // Rows of the unit this wave computes: 32-row blocks i < fm_act hold rows
+    // below m_rows.  In a tile with fewer rows (the ragged last m-tile of an
+    // expert, or of M) a wave skips the fragment reads and MFMAs of its empty
+    // blocks -- a wave with no rows only loads and meets the barriers -- in a
+    // second copy of the K loop, so the loop of a full tile is unchanged.  The
+    // stored rows' results do not change.
+    int kt0, kt1;
+    unit_k_range(tl.split, p.K / 64, &kt0, &kt1);
+    const int nk = kt1 - kt0;
+    const int rows_left = tl.m_rows - __builtin_amdgcn_readfirstlane(wm) * WM;
+    const int fm_act = rows_left <= 0 ? 0 : (rows_left >= FM * 32 ? FM : (rows_left + 31) >> 5);
     // One BK = 64 step on stage (Ac, Bc), whose first fragments are already in
     // registers: the fragments of sub-step ks+1 are requested before the MFMAs
     // of sub-step ks (the scheduling barriers keep that order).  Before the
@@ -478,45 +451,94 @@ struct Tile8w {
     // workgroup barrier makes the next stage whole and this one free; under
     // those MFMAs go the next stage's first fragment reads and the loads of
     // the step after next into this stage.
-    int kt0, kt1;
-    unit_k_range(tl.split, p.K / 64, &kt0, &kt1);
-    const int nk = kt1 - kt0;
-    auto step = [&](int i, const TLC_LDS u32x4* Ac, const TLC_LDS u32x4* Bc, TLC_LDS u32x4* Aw,
-                    TLC_LDS u32x4* Bw, const TLC_LDS u32x4* An, const TLC_LDS u32x4* Bn) {
+    auto kloop = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      auto fread = [&](const TLC_LDS u32x4* As, const TLC_LDS u32x4* Bs, int ks, int slot) {
+        const int phys = (ks * 2 + h) ^ s_lane;
 #pragma unroll
-      for (int ks = 0; ks < 3; ++ks) {
-        fread(Ac, Bc, ks + 1, (ks + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(ks & 1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < nk) fread(An, Bn, 0, 0);
-      if (i + 2 < nk) issue(kt0 + i + 2, Aw, Bw);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(1);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    if (nk > 0) {
-      issue(kt0, A0, B0);
-      if (nk > 1) {
-        issue(kt0 + 1, A1, B1);
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0's eight loads done
-      } else {
+        for (int i = 0; i < FM; ++i) {
+          if (!FULL && i >= fm_act) continue;
+          fa[slot][i] = __builtin_bit_cast(
+              bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)As +
+                                              (wm * WM + i * 32 + (lane & 31)) * 128 + phys * 16));
+        }
+        if (!FULL && fm_act == 0) return;
+        if constexpr (B_NK) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            fb[slot][j] = __builtin_bit_cast(
+                bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)Bs +
+                                                (wn * WN + j * 32 + (lane & 31)) * 128 + phys * 16));
+        } else {
+          // Lane l needs B[k = 16 ks + 8 (l / 32) + t][n] for t = 0..7 (n = l % 32 of the block):
+          // two transposing reads, each giving 4 consecutive k of one column.
+          const int g = lane >> 4, i16 = lane & 15;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            v4i16 hv[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int k = ks * 16 + 8 * (g >> 1) + 4 * hh + (i16 >> 2);
+              const int n = wn * WN + j * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+              const int pc = (n >> 3) ^ (2 * (k & 15));
+              hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (TLC_LDS v4i16*)((const TLC_LDS char*)Bs + k * 512 + pc * 16 + (n & 7) * 2));
+            }
+            const v8i16 v = {hv[0][0], hv[0][1], hv[0][2], hv[0][3], hv[1][0], hv[1][1], hv[1][2], hv[1][3]};
+            fb[slot][j] = __builtin_bit_cast(bf16x8, v);
+          }
+        }
+      };
+      auto mfmas = [&](int sl) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          if (!FULL && i >= fm_act) continue;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
+        }
+      };
+      auto step = [&](int i, const TLC_LDS u32x4* Ac, const TLC_LDS u32x4* Bc, TLC_LDS u32x4* Aw,
+                      TLC_LDS u32x4* Bw, const TLC_LDS u32x4* An, const TLC_LDS u32x4* Bn) {
+#pragma unroll
+        for (int ks = 0; ks < 3; ++ks) {
+          fread(Ac, Bc, ks + 1, (ks + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          mfmas(ks & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < nk) fread(An, Bn, 0, 0);
+        if (i + 2 < nk) issue(kt0 + i + 2, Aw, Bw);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(1);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      if (nk > 0) {
+        issue(kt0, A0, B0);
+        if (nk > 1) {
+          issue(kt0 + 1, A1, B1);
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0's eight loads done
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        fread(A0, B0, 0, 0);
+        for (int i = 0; i < nk; i += 2) {
+          step(i, A0, B0, A0, B0, A1, B1);
+          if (i + 1 < nk) step(i + 1, A1, B1, A1, B1, A0, B0);
+        }
+      } else {
+        __syncthreads();
       }
-      __syncthreads();
-      fread(A0, B0, 0, 0);
-      for (int i = 0; i < nk; i += 2) {
-        step(i, A0, B0, A0, B0, A1, B1);
-        if (i + 1 < nk) step(i + 1, A1, B1, A1, B1, A0, B0);
-      }
-    } else {
-      __syncthreads();
-    }
+    };
+    if (fm_act == FM)
+      kloop(std::true_type{});
+    else
+      kloop(std::false_type{});
     if (!split_epilogue<NT>(p, tl, acc, s_flag)) return;
 
     // ---- epilogue: fp32 to C, one 32-bit lane offset plus per-element
