@@ -45,11 +45,11 @@ PEAK_HBM_GBS = 8000.0
 # whenever one of these kernels changes.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE)
-    "ag": {"gemm": (221984.9, 105728.0)},
-    "moe": {"gemm": (269312.1, 104159.2)},
-    "rs": {"gemm": (60176.9, 67584.0), "reduce": (32792.1, 16384.0)},
-    "ar": {"gemm": (60176.9, 67584.0), "reduce": (32792.1, 16384.0)},
-    "rs_long": {"gemm": (3578312.8, 2703360.0), "reduce": (1310765.5, 327680.0)},
+    "ag": {"gemm": (220330.4, 107392.0)},
+    "moe": {"gemm": (265525.8, 104136.0)},
+    "rs": {"gemm": (59170.7, 68608.0), "reduce": (32795.4, 16384.0)},
+    "ar": {"gemm": (59170.7, 68608.0), "reduce": (32795.4, 16384.0)},
+    "rs_long": {"gemm": (3557317.4, 2744320.0), "reduce": (1310751.4, 327680.0)},
 }
 
 
