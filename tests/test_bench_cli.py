@@ -1,0 +1,39 @@
+"""Host-side parts of bench.py: the one-GPU guard and the traffic arithmetic
+(no GPU is touched)."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv],
+                           capture_output=True, text=True, timeout=120,
+                           env={**os.environ, **env})
+        assert r.returncode == 2, r
+        assert "more than one GPU" in r.stderr
+        assert r.stdout == ""
+
+
+def test_traffic_bytes_scale_fetch_and_write():
+    # FETCH_SIZE counts half the loaded bytes (scaled by 2), WRITE_SIZE all of them
+    assert bench.FETCH_SCALE == 2.0 and bench.WRITE_SCALE == 1.0
+    for wl, kernels in bench.TRAFFIC_KIB.items():
+        for k, (f, w) in kernels.items():
+            assert bench.traffic_bytes(wl, k) == round((2 * f + w) * 1024)
+    # the reduce moves exactly its algorithmic bytes: W + 1 slices of R x N fp32
+    assert abs(bench.traffic_bytes("rs_long", "reduce") - 9 * 16384 * 5120 * 4) < 1e-4 * 9 * 16384 * 5120 * 4
+    assert abs(bench.traffic_bytes("rs", "reduce") - 5 * 1024 * 4096 * 4) < 1e-3 * 5 * 1024 * 4096 * 4
+
+
+def test_workload_ids_name_the_configs():
+    import seeded_inputs as si
+    want = {"ag": "ag_qwen3_32b_ffn_up_w8_8192x3200x5120", "rs": "rs_w4_4096x4096x2048",
+            "ar": "rs_w4_4096x4096x2048", "rs_long": "rs_ffn_down_128k_w8_131072x5120x3200",
+            "moe": "ag_moe_w8_t4096_e64_top8_h2048_n768"}
+    assert {k: si.WORKLOADS[v].name for k, v in bench.WORKLOAD_ID.items()} == want
