@@ -135,9 +135,10 @@ class KernelTimer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs[-last:]]))
 
 
-def other_landings(flops, t_comp, others, t_copy_others):
+def other_landings(flops, t_comp, others, t_copy_others, extra_names=None):
     """The same step with the other landing backends, for the JSON line."""
     names = {v: k for k, v in LANDINGS.items()}
+    names.update(extra_names or {})
     return {names[o]: {"value": round(flops / t_f / 1e12, 2), "ms_per_step": round(t_f * 1e3, 4),
                        "copy_only_ms": round(t_copy_others[o] * 1e3, 4),
                        "overlap_efficiency": round(max(t_comp, t_copy_others[o]) / t_f, 4),
@@ -519,8 +520,11 @@ def run_moe(args, torch, tlc, si, workloads):
 
     t_fused = timed(fused_step(land), args.steps, args.warmup, torch)
     status = prob.sig.read_status(compute)
+    # besides the four backends of tlc_ag_moe: the chunks landed by the routing's
+    # top-k kernel (copy-only timed as the same load/store copy alone)
+    route_name = {workloads.LAND_WITH_ROUTE: "colocated_route"}
     others = {o: (timed(fused_step(o), args.steps, args.warmup, torch), prob.sig.read_status(compute))
-              for o in LANDINGS.values() if o != land}
+              for o in [*LANDINGS.values(), workloads.LAND_WITH_ROUTE] if o != land}
     t_copy = timed(lambda: prob.land_only(land), args.steps, args.warmup, torch)
     t_copy_others = {o: timed(lambda o=o: prob.land_only(o), args.steps, args.warmup, torch)
                      for o in others}
@@ -562,7 +566,7 @@ def run_moe(args, torch, tlc, si, workloads):
         "copy_only_ms": round(t_copy * 1e3, 4),
         "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,
-        "other_landings": other_landings(flops, t_comp, others, t_copy_others),
+        "other_landings": other_landings(flops, t_comp, others, t_copy_others, route_name),
     }
     return base_line(args, flops / t_fused / 1e12, t_fused, extra)
 

@@ -395,7 +395,20 @@ tlc_status tlc_gemm_ar(const tlc_ar_args* args, void* compute_stream, void* cons
  * Limits: E <= 64 (one expert per lane of a wavefront), k <= E, k <= 16,
  * T <= 2^20, bm in {128, 256}.  plan_cap >= tlc_moe_plan_capacity(...).
  * All arrays are device memory; `workspace` is device memory of at least
- * tlc_moe_workspace_bytes(T, k, E, bm) bytes (contents need not be initialised). */
+ * tlc_moe_workspace_bytes(T, k, E, bm) bytes (contents need not be initialised).
+ *
+ * Optional co-located landing of the peers' token chunks (x_src != NULL): the
+ * top-k kernel's first workgroups also copy chunk c (c != rank, tokens_per_chunk
+ * x H bf16) from x_src[c] into rows [c Tc, (c+1) Tc) of x with load/store
+ * instructions, a fixed number of workgroups per chunk, and the last of them
+ * raises sig->flags[c] to `epoch` (AutoOverlap §5.2, backend 5, here beside
+ * the routing rather than inside the GEMM).  The transfer then overlaps the
+ * routing, which waits for nothing; the grouped GEMM that follows consumes the
+ * chunks with land = TLC_LAND_NONE and the same epoch (tlc_ag_moe waits for
+ * the raised flags).  x: device T x H bf16, 16-byte aligned; x_src: host array
+ * of `world` device pointers, 16-byte aligned (entry `rank` unused); H >= 8,
+ * H % 8 == 0, tokens_per_chunk * H * 2 < 2^32; sig non-NULL; epoch >= 1.  The
+ * other landing fields are ignored when x_src is NULL. */
 typedef struct {
   const float* logits; /* device f32 T x E */
   int32_t tokens_per_chunk, world, rank, experts, topk;
@@ -410,6 +423,11 @@ typedef struct {
   int64_t plan_cap;
   int32_t* n_tiles_dev;
   void* workspace;
+  void* x;                  /* co-located landing: gathered tokens (device) */
+  const void* const* x_src; /* co-located landing: peers' chunks, or NULL */
+  int32_t H;
+  tlc_signals* sig;
+  uint32_t epoch;
 } tlc_moe_route_args;
 
 int64_t tlc_moe_plan_capacity(int32_t T, int32_t topk, int32_t experts, int32_t N, int32_t bm,
@@ -421,7 +439,10 @@ tlc_status tlc_moe_route(const tlc_moe_route_args* args, void* stream);
  * for the expert e whose row segment holds i.  X is the gathered token matrix
  * (T x H, chunk c = rows [c Tc, (c+1) Tc)); chunks land as in tlc_ag_gemm.
  * w: device bf16, E stacked matrices, layout w_layout (KN: E x H x N; NK:
- * E x N x H).  Tiles come from tlc_moe_route (plan, n_tiles_dev).
+ * E x N x H).  Tiles come from tlc_moe_route (plan, n_tiles_dev).  With
+ * land = TLC_LAND_NONE and epoch >= 1 nothing is landed here but the tiles
+ * still wait for their chunks' flags: chunks landed by tlc_moe_route's
+ * co-located landing (or by the caller), with that epoch.
  * Requirements: H % 64 == 0, N % 8 == 0, 16-byte aligned pointers. */
 typedef struct {
   const tlc_tile* plan;
@@ -470,7 +491,7 @@ int64_t tlc_wall_clock_khz(void);
 
 const char* tlc_status_string(tlc_status s);
 const char* tlc_last_error(void);
-/* Library version, e.g. 130 = 0.1.30. */
+/* Library version, e.g. 131 = 0.1.31. */
 int32_t tlc_version(void);
 
 #ifdef __cplusplus

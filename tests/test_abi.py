@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tlc.version() == 130
+    assert tlc.version() == 131
     assert tlc.status_string(tlc.ERR_TIMEOUT).startswith("timeout")
     assert tlc.status_string(0) == "ok"
 
@@ -103,6 +103,34 @@ def test_gemm_ar_argument_errors():
     args = tlc.ARArgs(r, None, 128, 0)
     assert tlc.lib().tlc_gemm_ar(C.byref(args), None, None, 0) == tlc.ERR_INVALID_ARG
     assert "gathered_src" in tlc.last_error()
+
+
+def test_moe_route_landing_argument_errors():
+    """The routing's co-located landing is validated on the host before anything
+    is enqueued (no GPU is touched: every case fails its checks)."""
+    T, E, k, N = 64, 8, 2, 128
+    cap = tlc.moe_plan_capacity(T, k, E, N, 128, 128)
+
+    def args(**over):
+        base = dict(logits=16, tokens_per_chunk=32, world=2, rank=0, experts=E, topk=k, N=N, bm=128,
+                    bn=128, order=1, topk_idx=16, gates=16, counts=16, offsets=16, row_token=16,
+                    slot=16, plan=16, plan_cap=cap, n_tiles_dev=16, workspace=4096, x=None,
+                    x_src=None, H=64, sig=None, epoch=1)
+        base.update(over)
+        return tlc.MoERouteArgs(**base)
+
+    src = (C.c_void_p * 2)(8192, 16384)
+    srcp = C.cast(src, C.POINTER(C.c_void_p))
+    for over, want, text in [
+        (dict(x_src=srcp), tlc.ERR_INVALID_ARG, "needs x and sig"),
+        (dict(x_src=srcp, x=4096), tlc.ERR_INVALID_ARG, "needs x and sig"),
+        (dict(x_src=srcp, x=4096, sig=64, H=60), tlc.ERR_UNSUPPORTED, "H % 8"),
+        (dict(x_src=srcp, x=4096, sig=64, epoch=0), tlc.ERR_INVALID_ARG, "epoch"),
+        (dict(x_src=srcp, x=4104, sig=64), tlc.ERR_MISALIGNED, "16-byte"),
+    ]:
+        a = args(**over)
+        assert tlc.lib().tlc_moe_route(C.byref(a), None) == want, (over, tlc.last_error())
+        assert text in tlc.last_error(), tlc.last_error()
 
 
 def test_plan_capacity_and_query():

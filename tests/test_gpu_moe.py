@@ -14,9 +14,12 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     from tile_level_communication_amd import tlc
-    from tile_level_communication_amd.workloads import MoEProblem
+    from tile_level_communication_amd.workloads import LAND_WITH_ROUTE, MoEProblem
+else:  # collected on CPU-only hosts, never run there
+    LAND_WITH_ROUTE = -1
 
-LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3, "colocated": 4}
+# "route": the routing's top-k kernel lands the chunks, the GEMM waits for the flags
+LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3, "colocated": 4, "route": LAND_WITH_ROUTE}
 
 
 def _check_routing(prob, ref, order):
@@ -110,3 +113,41 @@ def test_moe_full_size(rank):
     _check_routing(prob, ref, tlc.ORDER_RANK_OFFSET)
     check_close(prob.y.cpu().numpy(), y_ref, wl.k, absmax_bf16(inp.x_chunks), absmax_bf16(inp.w),
                 "moe full coloc")
+    log(f"[moe full] {wl.name} rank={rank}: landing beside the routing")
+    prob.poison_remote()
+    prob.y.fill_(float("nan"))
+    prob.run(LAND_WITH_ROUTE)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    _check_routing(prob, ref, tlc.ORDER_RANK_OFFSET)
+    check_close(prob.y.cpu().numpy(), y_ref, wl.k, absmax_bf16(inp.x_chunks), absmax_bf16(inp.w),
+                "moe full route landing")
+
+
+@pytest.mark.parametrize("land", ["route", "colocated", "memcpy"])
+def test_moe_fresh_data_each_call(land):
+    """Three calls on one problem, the peers' tokens changed and the landed rows
+    poisoned before each: every call must see its own call's data (flags of an
+    earlier epoch do not count)."""
+    W, Tc, H, N, E, k = 4, 48, 128, 256, 16, 4
+    inp = si.moe_inputs(330, W, Tc, H, N, E, integer=True)
+    rank = 1
+    ref = om.route(inp.logits, k, W, rank, Tc)
+    prob = MoEProblem(inp.x_chunks, inp.logits, inp.w, rank, k, 128, 128)
+    rng = np.random.default_rng(331)
+    for call in range(3):
+        log(f"[moe fresh] land={land} call={call}")
+        # new integer tokens for the peers (bf16 bit patterns, as the inputs are)
+        x_chunks = [x if c == rank else
+                    si.f32_to_bf16_bits(rng.integers(-4, 5, size=(Tc, H)).astype(np.float32))
+                    for c, x in enumerate(inp.x_chunks)]
+        for c in range(W):
+            if c != rank:
+                prob.x_src[c].copy_(torch.from_numpy(x_chunks[c].view(np.int16)).view(torch.bfloat16))
+        prob.poison_remote()
+        prob.y.fill_(float("nan"))
+        prob.run(LANDS[land])
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        y_ref = om.grouped_gemm(x_chunks, inp.w, ref["offsets"], ref["row_token"])
+        check_exact(prob.y.cpu().numpy(), y_ref, f"fresh {land} call {call}")

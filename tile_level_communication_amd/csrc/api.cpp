@@ -224,6 +224,20 @@ void set_schedule(GemmParams* p, int32_t schedule, void* ws, int64_t ws_bytes) {
 // multiple of 8); when that is under 32 the copy is on the critical path
 // whoever does it, and every workgroup takes a share; a quarter of the grid
 // when the unit count is only known on the device (n_units < 0).
+// The peers' chunks in landing order (rank+n_local, ... mod world; the n_local
+// chunks from `rank` on are already in place), chunk c raising flags[flag_base + c].
+void fill_copy_chunks(CopyPlan* cp, void* const* dst, const void* const* src, int64_t bytes,
+                      int world, int rank, int n_local, int flag_base) {
+  cp->chunks = world - n_local;
+  cp->vec = bytes / 16;
+  for (int i = n_local; i < world; ++i) {
+    const int c = (rank + i) % world;
+    cp->src[i - n_local] = static_cast<const uint4*>(src[c]);
+    cp->dst[i - n_local] = static_cast<uint4*>(dst[c]);
+    cp->flag[i - n_local] = flag_base + c;
+  }
+}
+
 tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src, int64_t bytes,
                          int world, int rank, int n_local, int copy_wgs, int grid, const char* who,
                          int flag_base = 0, int64_t n_units = -1) {
@@ -240,15 +254,8 @@ tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src
       if (cw < 8) cw = grid < 8 ? grid : 8;
     }
   }
-  p->copy_wgs = world > n_local ? cw : 0;
-  p->copy_chunks = world - n_local;
-  p->copy_vec = bytes / 16;
-  for (int i = n_local; i < world; ++i) {
-    const int c = (rank + i) % world;
-    p->copy_src[i - n_local] = static_cast<const uint4*>(src[c]);
-    p->copy_dst[i - n_local] = static_cast<uint4*>(dst[c]);
-    p->copy_flag[i - n_local] = flag_base + c;
-  }
+  p->copy.wgs = world > n_local ? cw : 0;
+  fill_copy_chunks(&p->copy, dst, src, bytes, world, rank, n_local, flag_base);
   return TLC_OK;
 }
 
@@ -338,7 +345,7 @@ tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_
     p.epoch = epoch;
     st = set_colocated(&p, dst, src, bytes_per_chunk, world, rank, 1, 0, info.cus, "tlc_land");
     if (st) return st;
-    st = launch_gemm(p, 256, 256, TLC_B_KN, KIND_DENSE, p.copy_wgs,
+    st = launch_gemm(p, 256, 256, TLC_B_KN, KIND_DENSE, p.copy.wgs,
                      copy_streams && n_copy_streams > 0 ? copy_streams[0] : nullptr);
     return st ? st : ok();
   }
@@ -421,7 +428,7 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
     st = set_colocated(&p, dst, src, chunk_bytes, Wf, rf, S, a->copy_wgs, grid, "tlc_ag_gemm", 0,
                        a->n_tiles);
     if (st) return st;
-    if (a->n_tiles == 0) grid = p.copy_wgs;
+    if (a->n_tiles == 0) grid = p.copy.wgs;
   }
   p.xcd_remap = grid % 8 == 0;
   st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
@@ -521,7 +528,7 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
       st = set_colocated(&p, const_cast<void* const*>(g->dst), g->src, slice_bytes, a->world,
                          a->rank, 1, g->copy_wgs, grid, "tlc_gemm_ar", a->world, a->n_tiles);
       if (st) return st;
-      if (a->n_tiles == 0) grid = p.copy_wgs;
+      if (a->n_tiles == 0) grid = p.copy.wgs;
     }
     p.xcd_remap = grid % 8 == 0;
     st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
@@ -617,8 +624,34 @@ tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
                 static_cast<long long>(cap));
   if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0)
     return fail(TLC_ERR_MISALIGNED, "tlc_moe_route: workspace not 256-byte aligned");
+  // optional co-located landing of the token chunks by the top-k kernel
+  void* dst[TLC_MAX_WORLD];
+  int64_t chunk_bytes = 0;
+  if (a->x_src) {
+    if (!a->x || !a->sig)
+      return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: co-located landing needs x and sig");
+    if (a->H < 8 || a->H % 8 != 0)
+      return fail(TLC_ERR_UNSUPPORTED, "tlc_moe_route: co-located landing needs H %% 8 == 0 (H %d)", a->H);
+    chunk_bytes = static_cast<int64_t>(a->tokens_per_chunk) * a->H * 2;
+    for (int c = 0; c < a->world; ++c) dst[c] = static_cast<char*>(a->x) + c * chunk_bytes;
+    const tlc_status st = check_land_args(TLC_LAND_COLOCATED, a->x_src, dst, a->world, a->rank,
+                                          chunk_bytes, "tlc_moe_route", nullptr, 0, a->epoch);
+    if (st) return st;
+  }
   MoeDev d;
   memset(&d, 0, sizeof(d));
+  if (a->x_src && a->world > 1) {
+    fill_copy_chunks(&d.copy, dst, a->x_src, chunk_bytes, a->world, a->rank, 1, 0);
+    // about 64 KB per copying workgroup; the top-k kernel (one workgroup per
+    // four tokens) is launched with at least that many workgroups
+    const int64_t per = (chunk_bytes + 65535) / 65536;
+    if (per * d.copy.chunks > (1 << 30))
+      return fail(TLC_ERR_UNSUPPORTED, "tlc_moe_route: co-located landing of %lld-byte chunks",
+                  static_cast<long long>(chunk_bytes));
+    d.copy.wgs = static_cast<int32_t>(per * d.copy.chunks);
+    d.sig = a->sig;
+    d.epoch = a->epoch;
+  }
   d.logits = a->logits;
   d.T = static_cast<int32_t>(T);
   d.E = a->experts;
@@ -749,6 +782,6 @@ const char* tlc_status_string(tlc_status s) {
 
 const char* tlc_last_error(void) { return g_err; }
 
-int32_t tlc_version(void) { return 130; }
+int32_t tlc_version(void) { return 131; }
 
 }  // extern "C"

@@ -33,6 +33,7 @@
 
 #include <type_traits>
 
+#include "colocated_copy.h"
 #include "device_sync.h"
 #include "tlc_internal.h"
 
@@ -318,18 +319,6 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 #define TLC_LDS __attribute__((address_space(3)))
 
-// Buffer resource with wave-uniform fields (readfirstlane), so that the
-// compiler keeps it in scalar registers.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t v = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0),
-                                           static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
-                                           0x00020000);
-}
-
 // Buffer descriptor as four wave-uniform words (base, 0 stride, byte size,
 // format flags) for the LDS-writing loads below.
 typedef unsigned int rsrc_words __attribute__((ext_vector_type(4)));
@@ -562,54 +551,6 @@ struct Tile8w {
   }
 };
 
-// Co-located landing (AutoOverlap §5.2, backend 5: load/store transfers on the
-// SMs that compute, coordinated through global-memory signals).  Workgroup g <
-// copy_wgs copies the g-th of copy_wgs equal shares of every chunk, in landing
-// order, before its first unit; no wait precedes it, so the flags it raises
-// cannot depend on the units behind it.  Each thread keeps COPY_UNROLL 16-byte
-// loads in flight (non-temporal: the source is read once).  The stores are
-// device-coherent (sc1: written through past the XCD's L2), so after waiting
-// for them the workgroup counts itself in with a relaxed atomic and no L2
-// write-back; the last share of a chunk raises its flag with a release store.
-constexpr int COPY_UNROLL = 16;
-constexpr int CPOL_SC1 = 16;  // cache-policy bit of a device-coherent store
-typedef unsigned int copy_vec __attribute__((ext_vector_type(4)));
-
-__device__ void colocated_copy(const GemmParams& p) {
-  const int g = blockIdx.x, nt = blockDim.x;
-  const int64_t n = p.copy_vec;
-  const int64_t lo = n * g / p.copy_wgs, hi = n * (g + 1) / p.copy_wgs;
-  const int cnt = static_cast<int>(hi - lo);  // a chunk is < 2^32 bytes
-  for (int i = 0; i < p.copy_chunks; ++i) {
-    const copy_vec* src = reinterpret_cast<const copy_vec*>(p.copy_src[i]) + lo;
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.copy_dst[i] + lo, static_cast<uint32_t>(cnt) * 16u);
-    for (int base = threadIdx.x; base < cnt; base += nt * COPY_UNROLL) {
-      copy_vec v[COPY_UNROLL];
-#pragma unroll
-      for (int u = 0; u < COPY_UNROLL; ++u) {
-        const int k = base + u * nt;
-        if (k < cnt) v[u] = __builtin_nontemporal_load(src + k);
-      }
-#pragma unroll
-      for (int u = 0; u < COPY_UNROLL; ++u) {
-        const int k = base + u * nt;
-        if (k < cnt) __builtin_amdgcn_raw_buffer_store_b128(v[u], rd, k * 16, 0, CPOL_SC1);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int c = p.copy_flag[i];
-      const uint32_t prev = __hip_atomic_fetch_add(&p.sig->land_count[c], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == static_cast<uint32_t>(p.copy_wgs) - 1) {
-        __hip_atomic_store(&p.sig->land_count[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.sig->flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-      }
-    }
-  }
-}
-
 // Walks the plan: takes units (dynamic counter or static slots), validates
 // them, waits for their chunks, then `run_tile(unit)`.
 struct LoopShared {
@@ -621,7 +562,10 @@ struct LoopShared {
 template <int BM, int BN, int KIND, int WAIT, typename RunTile>
 __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile run_tile) {
   const int G = gridDim.x;
-  if (WAIT && static_cast<int>(blockIdx.x) < p.copy_wgs) colocated_copy(p);
+  // co-located landing: the first copy.wgs workgroups copy every chunk's
+  // share before their first unit; no wait precedes the copy, so the flags it
+  // raises cannot depend on the units behind it
+  if (WAIT && static_cast<int>(blockIdx.x) < p.copy.wgs) copy_in_landing_order(p.copy, p.sig, p.epoch);
   const int64_t n_tiles = KIND == KIND_MOE ? static_cast<int64_t>(*p.n_tiles_dev) : p.n_tiles;
   uint32_t seen = p.no_wait_mask;
   // The first unit of every workgroup is its slot (no counter traffic while all
@@ -632,7 +576,7 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
   // the round, the units of the latest chunks, and the others the rest.
   const int g = blockIdx.x;
   int64_t t;
-  const int cw = WAIT ? p.copy_wgs : 0;
+  const int cw = WAIT ? p.copy.wgs : 0;
   if (cw > 0 && cw < G) {
     const int Gr = G - cw, r = g - cw;
     t = g < cw ? Gr + g : ((p.xcd_remap && Gr % 8 == 0 && cw % 8 == 0) ? (r & 7) * (Gr >> 3) + (r >> 3) : r);

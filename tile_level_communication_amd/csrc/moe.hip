@@ -11,7 +11,9 @@
 // Tokens are visited in arrival order: the local chunk first, then rank+1,
 // rank+2, ... (position a = p(c) * Tc + token offset), in blocks of 64.
 //
-//   topk_kernel     one wavefront per token, one expert per lane (E <= 64):
+//   topk_kernel     (optionally, its first workgroups also land the peers'
+//                   token chunks: the co-located landing beside the routing)
+//                   one wavefront per token, one expert per lane (E <= 64):
 //                   k rounds of a wavefront maximum of order-preserving keys
 //                   and a ballot for the lowest expert holding it (ties ->
 //                   lower expert), softmax over the k winners, a 64-bit
@@ -30,6 +32,7 @@
 //                   batches of pairs), expanded over the n-tiles.
 #include <hip/hip_runtime.h>
 
+#include "colocated_copy.h"
 #include "tlc_internal.h"
 
 namespace tlc {
@@ -109,6 +112,9 @@ __device__ inline int arrival_token(const MoeDev& d, int a) {
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(MoeDev d) {
+  // co-located landing of the token chunks (d.copy.wgs = 0: none); the
+  // routing waits for nothing, so the copy overlaps it
+  if (static_cast<int>(blockIdx.x) < d.copy.wgs) copy_by_chunk(d.copy, d.sig, d.epoch);
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t < d.T) route_token(d, t, threadIdx.x & 63);
 }
@@ -309,7 +315,9 @@ int64_t moe_max_pairs(int32_t T, int32_t topk, int32_t experts, int32_t bm) {
 tlc_status launch_moe_route(const MoeDev& d, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nb = (d.T + 63) / 64;
-  hipLaunchKernelGGL(topk_kernel, dim3((d.T + 3) / 4), dim3(256), 0, s, d);
+  const int topk_grid = (d.T + 3) / 4;
+  hipLaunchKernelGGL(topk_kernel, dim3(topk_grid > d.copy.wgs ? topk_grid : d.copy.wgs), dim3(256), 0,
+                     s, d);
   hipLaunchKernelGGL(block_count_kernel, dim3(nb), dim3(64), 0, s, d);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64), 0, s, d);
   hipLaunchKernelGGL(scatter_kernel, dim3(nb, (d.E + SCATTER_GROUP - 1) / SCATTER_GROUP), dim3(64),

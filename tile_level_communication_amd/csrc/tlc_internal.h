@@ -24,6 +24,19 @@ struct DeviceInfo {
 };
 tlc_status device_info(DeviceInfo* out);
 
+// Co-located landing: the first `wgs` workgroups of a launch copy the peers'
+// chunks (landing order i = 0 .. chunks-1, chunk i from src[i] to dst[i]) with
+// load/store instructions and count themselves in; the last share of chunk i
+// raises flags[flag[i]] to the epoch.
+struct CopyPlan {
+  int32_t wgs;
+  int32_t chunks;
+  int64_t vec;  // 16-byte units per chunk
+  const uint4* src[TLC_MAX_WORLD];
+  uint4* dst[TLC_MAX_WORLD];
+  int32_t flag[TLC_MAX_WORLD];
+};
+
 // Parameters of the tiled GEMM kernels (one struct for all modes).
 struct GemmParams {
   const tlc_tile* plan;
@@ -47,15 +60,9 @@ struct GemmParams {
   int32_t dynamic;             // 1: units from the work counter in sig; 0: slot-strided
   char* split_ws;              // split tiles' blocks: 256-byte counter header + S partials
   int64_t split_bytes;         // bytes of split_ws
-  // Co-located landing: workgroups [0, copy_wgs) first copy their share of
-  // each of copy_chunks chunks (landing order) and count it in; the last share
-  // of chunk i raises flags[copy_flag[i]].
-  int32_t copy_wgs;
-  int32_t copy_chunks;
-  int64_t copy_vec;            // 16-byte units per chunk
-  const uint4* copy_src[TLC_MAX_WORLD];
-  uint4* copy_dst[TLC_MAX_WORLD];
-  int32_t copy_flag[TLC_MAX_WORLD];
+  // Co-located landing: workgroups [0, copy.wgs) each copy a share of every
+  // chunk, in landing order, before their first unit.
+  CopyPlan copy;
 };
 
 // Bytes of one split tile's workspace block (counter header + split_k partials).
@@ -110,6 +117,11 @@ struct MoeDev {
   int32_t* pair_key;           // workspace: max_pairs
   uint32_t* pair_mask;         // workspace: max_pairs
   int32_t* blk;                // workspace: ceil(T/64) x E block counts, then their prefixes
+  // Optional landing of the peers' token chunks by the top-k kernel's first
+  // copy.wgs workgroups (copy.wgs = 0: none), flags raised to `epoch` in sig.
+  CopyPlan copy;
+  tlc_signals* sig;
+  uint32_t epoch;
 };
 
 int64_t moe_max_pairs(int32_t T, int32_t topk, int32_t experts, int32_t bm);

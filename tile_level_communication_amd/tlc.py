@@ -91,7 +91,8 @@ class MoERouteArgs(C.Structure):
                 ("topk_idx", C.c_void_p), ("gates", C.c_void_p), ("counts", C.c_void_p),
                 ("offsets", C.c_void_p), ("row_token", C.c_void_p), ("slot", C.c_void_p),
                 ("plan", C.c_void_p), ("plan_cap", C.c_int64), ("n_tiles_dev", C.c_void_p),
-                ("workspace", C.c_void_p)]
+                ("workspace", C.c_void_p), ("x", C.c_void_p), ("x_src", C.POINTER(C.c_void_p)),
+                ("H", C.c_int32), ("sig", C.c_void_p), ("epoch", C.c_uint32)]
 
 
 class MoEArgs(C.Structure):
@@ -359,11 +360,17 @@ def moe_workspace_bytes(T, topk, experts, bm) -> int:
 
 def moe_route(logits, tokens_per_chunk, world, rank, experts, topk, N, bm, bn, order, topk_idx,
               gates, counts, offsets, row_token, slot, plan, plan_cap, n_tiles_dev, workspace,
-              stream=None):
+              stream=None, x=None, x_src=None, H=0, sig: "Signals" = None, epoch=0):
+    """tlc_moe_route.  With x_src (list of `world` device tensors, entry `rank`
+    unused) the top-k kernel also lands the peers' token chunks into x and
+    raises their flags in sig to epoch (the co-located landing beside the
+    routing)."""
+    src = _ptr_array(x_src, world) if x_src is not None else None
     args = MoERouteArgs(_ptr(logits), tokens_per_chunk, world, rank, experts, topk, N, bm, bn,
                         order, _ptr(topk_idx), _ptr(gates), _ptr(counts), _ptr(offsets),
                         _ptr(row_token), _ptr(slot), _ptr(plan), plan_cap, _ptr(n_tiles_dev),
-                        _ptr(workspace))
+                        _ptr(workspace), _ptr(x) if x is not None else None, src, H,
+                        sig.ptr if sig is not None else None, epoch)
     _check(lib().tlc_moe_route(C.byref(args), _stream(stream)), "tlc_moe_route")
 
 

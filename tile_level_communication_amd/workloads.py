@@ -43,14 +43,31 @@ class Streams:
     def copy(self):
         return self.copies
 
-    def begin(self):
-        # the landing may only overwrite buffers once earlier work is done
+    def begin(self, land=None):
+        """The landing may only overwrite buffers once earlier work is done.
+        A step whose landing runs on the compute stream (co-located, or none)
+        leaves the copy streams alone."""
+        if land is not None and not uses_copy_streams(land):
+            return
         for c in self.copies:
             c.wait_stream(self.compute)
 
-    def end(self):
+    def end(self, land=None):
+        if land is not None and not uses_copy_streams(land):
+            return
         for c in self.copies:
             self.compute.wait_stream(c)
+
+
+def uses_copy_streams(land) -> bool:
+    """Whether a fused step with this landing enqueues work on the copy streams."""
+    return land in (tlc.LAND_COPY_ENGINE, tlc.LAND_CU, tlc.LAND_MEMCPY)
+
+
+# MoE landing mode of the Python layer: the chunks are landed by the routing's
+# top-k kernel (tlc_moe_route with x_src), and tlc_ag_moe runs with
+# TLC_LAND_NONE and the same epoch, waiting for their flags.
+LAND_WITH_ROUTE = -1
 
 
 def next_epoch(prob) -> int:
@@ -129,13 +146,13 @@ class AGProblem:
         s = self.streams
         if land == tlc.LAND_NONE and preset_flags is not False:
             self.sig.set(self.world * max(self.sub_chunks, 1), self.epoch, s.compute)
-        s.begin()
+        s.begin(land)
         tlc.ag_gemm(self.plan, self.n_tiles, self.M, self.N, self.K, self.world, self.rank, self.R,
                     self.bm, self.bn, self.a, self.a_src if land != tlc.LAND_NONE else None,
                     self.b, self.b_layout, self.c, self.sig, self.epoch, land, s.compute, s.copy,
                     grid, timeout_ns, trace, self.workspace, self.schedule, self.sub_chunks,
                     copy_wgs)
-        s.end()
+        s.end(land)
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
         next_epoch(self)
@@ -205,11 +222,11 @@ class RSProblem:
         s = self.streams
         if land == tlc.LAND_NONE:
             self.sig.set(self.world, self.epoch, s.compute)
-        s.begin()
+        s.begin(land)
         tlc.gemm_rs(*self._args(), self.remote_src if land != tlc.LAND_NONE else None, self.landing,
                     self.out, self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns,
                     self.workspace, self.schedule)
-        s.end()
+        s.end(land)
 
     def reduce_only(self, timeout_ns=0):
         next_epoch(self)
@@ -257,12 +274,12 @@ class ARProblem(RSProblem):
         s = self.streams
         if land == tlc.LAND_NONE:
             self.sig.set(self.world, self.epoch, s.compute)
-        s.begin()
+        s.begin(land)
         tlc.gemm_ar(*self._args(), self.remote_src if land != tlc.LAND_NONE else None, self.landing,
                     self.gathered_src if land != tlc.LAND_NONE else None, self.c, self.sig,
                     self.epoch, land, s.compute, s.copy, grid, timeout_ns, self.workspace,
                     self.schedule, copy_wgs)
-        s.end()
+        s.end(land)
 
 
 class MoEProblem:
@@ -315,33 +332,44 @@ class MoEProblem:
             if c != self.rank:
                 self.x[c * self.Tc:(c + 1) * self.Tc].fill_(float("nan"))
 
-    def route(self):
+    def route(self, land_chunks=False):
+        """Routing on the compute stream; with land_chunks the top-k kernel also
+        lands the peers' token chunks (co-located landing beside the routing)
+        and raises their flags to the current epoch."""
         s = self.streams
         tlc.moe_route(self.logits, self.Tc, self.world, self.rank, self.E, self.k, self.N, self.bm,
                       self.bn, self.order, self.topk_idx, self.gates, self.counts, self.offsets,
                       self.row_token, self.slot, self.plan, self.plan_cap, self.n_tiles_dev,
-                      self.workspace, s.compute)
+                      self.workspace, s.compute, x=self.x if land_chunks else None,
+                      x_src=self.x_src if land_chunks else None, H=self.H,
+                      sig=self.sig if land_chunks else None, epoch=self.epoch)
 
     def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, do_route=True, copy_wgs=0):
+        """One step: routing, then the grouped GEMM consuming the chunks as they
+        land.  land: a TLC_LAND_* backend of tlc_ag_moe, or LAND_WITH_ROUTE (the
+        routing's top-k kernel lands the chunks; the GEMM waits for their flags)."""
         next_epoch(self)
         s = self.streams
+        with_route = land == LAND_WITH_ROUTE
         if land == tlc.LAND_NONE:
             self.sig.set(self.world, self.epoch, s.compute)
-        s.begin()
-        if do_route:
-            self.route()
+        s.begin(land)
+        if do_route or with_route:
+            self.route(land_chunks=with_route)
+        gemm_land = tlc.LAND_NONE if with_route else land
         tlc.ag_moe(self.plan, self.n_tiles_dev, self.plan_cap, self.row_token, self.Tc, self.world,
                    self.rank, self.E, self.k, self.H, self.N, self.bm, self.bn, self.x,
-                   self.x_src if land != tlc.LAND_NONE else None, self.w, self.b_layout, self.y,
-                   self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns,
+                   self.x_src if gemm_land != tlc.LAND_NONE else None, self.w, self.b_layout, self.y,
+                   self.sig, self.epoch, gemm_land, s.compute, s.copy, grid, timeout_ns,
                    schedule=self.schedule, copy_wgs=copy_wgs)
-        s.end()
+        s.end(land)
 
     def land_only(self, land=tlc.LAND_COPY_ENGINE):
         next_epoch(self)
         s = self.streams
         s.begin()
         dst = [self.x[c * self.Tc:(c + 1) * self.Tc] for c in range(self.world)]
+        # the routing's landing is timed as the same load/store copy alone
         tlc.land(dst, self.x_src, self.Tc * self.H * 2, self.world, self.rank, self.sig, self.epoch,
-                 land, s.copy)
+                 tlc.LAND_COLOCATED if land == LAND_WITH_ROUTE else land, s.copy)
         s.end()
