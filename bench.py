@@ -219,7 +219,9 @@ def run_ag(args, torch, tlc, si, workloads):
     # twice as many compute units
     split_k = (2 if land == tlc.LAND_COPY_ENGINE else 0) if args.split_k is None else args.split_k
     split_from = 7 if args.split_from is None else args.split_from
-    args.schedule = args.schedule or "dynamic"
+    # static slots: 1.3 % faster than the dynamic counter for the memcpy landing
+    # and 0.7 % for the co-located one (one process each, two runs)
+    args.schedule = args.schedule or "static"
     schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
     sub = 1 if args.sub_chunks is None else args.sub_chunks
     prob = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
