@@ -272,24 +272,28 @@ def test_ag_qwen3_ffn_up_full_size(rank):
     got = c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
     ref = og.ag_gemm_rows(inp.a_chunks, inp.b, rows)
     check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), "cfg full rows")
-    # the late chunks split along K (the bench's schedule)
-    log(f"[ag full] {wl.name} rank={rank}: split 4 from key 1, dynamic schedule")
-    prob = AGProblem(inp.a_chunks, inp.b, rank, 256, 256, tlc.B_KN, split_k=4, split_from=1)
-    prob.poison_remote()
-    prob.run(tlc.LAND_COPY_ENGINE)
-    torch.cuda.synchronize()
-    assert prob.sig.read_status()[0] == 0
-    got = prob.c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
-    check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), "cfg full rows split")
-    # co-located landing: the GEMM's workgroups copy the chunks themselves
-    log(f"[ag full] {wl.name} rank={rank}: co-located landing, dynamic schedule")
-    prob = AGProblem(inp.a_chunks, inp.b, rank, 256, 256, tlc.B_KN)
-    prob.poison_remote()
-    prob.run(tlc.LAND_COLOCATED)
-    torch.cuda.synchronize()
-    assert prob.sig.read_status()[0] == 0
-    got = prob.c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
-    check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), "cfg full rows coloc")
+    legs = [
+        # the bench's headline launch: memcpy landing, whole tiles, static slots
+        ("memcpy landing, static schedule", tlc.LAND_MEMCPY, dict(schedule=tlc.SCHED_STATIC)),
+        ("co-located landing, static schedule", tlc.LAND_COLOCATED, dict(schedule=tlc.SCHED_STATIC)),
+        ("co-located landing, dynamic schedule", tlc.LAND_COLOCATED, {}),
+        # the bench's SDMA plan: the last chunk's tiles split in two along K
+        ("SDMA landing, split 2 from key 7", tlc.LAND_COPY_ENGINE,
+         dict(split_k=2, split_from=7, schedule=tlc.SCHED_STATIC)),
+        ("SDMA landing, split 4 from key 1, dynamic schedule", tlc.LAND_COPY_ENGINE,
+         dict(split_k=4, split_from=1)),
+    ]
+    for what, land, kw in legs:
+        log(f"[ag full] {wl.name} rank={rank}: {what}")
+        prob = AGProblem(inp.a_chunks, inp.b, rank, 256, 256, tlc.B_KN, **kw)
+        prob.poison_remote()
+        prob.c.fill_(float("nan"))
+        prob.run(land)
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        got = prob.c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
+        check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), f"cfg full rows, {what}")
+        assert not torch.isnan(prob.c).any().item(), what
     # integer-valued inputs: the whole output bit for bit
     log(f"[ag full] {wl.name} rank={rank}: integer inputs, full compare")
     ii = si.workload_inputs(2, integer=True)
