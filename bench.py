@@ -47,9 +47,9 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE)
     "ag": {"gemm": (220330.4, 107392.0)},
     "moe": {"gemm": (265525.8, 104136.0)},
-    "rs": {"gemm": (59170.7, 68608.0), "reduce": (32795.4, 16384.0)},
-    "ar": {"gemm": (59170.7, 68608.0), "reduce": (32795.4, 16384.0)},
-    "rs_long": {"gemm": (3557317.4, 2744320.0), "reduce": (1310751.4, 327680.0)},
+    "rs": {"gemm": (59170.7, 68608.0), "reduce": (32791.6, 16415.5)},
+    "ar": {"gemm": (59170.7, 68608.0), "reduce": (32791.6, 16415.5)},
+    "rs_long": {"gemm": (3557317.4, 2744320.0), "reduce": (1310750.8, 327680.0)},
 }
 
 
