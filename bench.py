@@ -501,11 +501,22 @@ def run_moe(args, torch, tlc, si, workloads):
     inp = si.workload_inputs(4)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
     land = LANDINGS[args.land]
-    # static slots keep each XCD on a contiguous run of the expert-major plan
-    # (its weights and token rows stay in that XCD's L2): 3 % faster than the
-    # dynamic counter here
-    args.schedule = args.schedule or "static"
-    schedule = tlc.SCHED_STATIC if args.schedule == "static" else tlc.SCHED_DYNAMIC
+    # Schedule per landing unless one is given: with the full grid (co-located
+    # landings) static slots keep each XCD on a contiguous run of the
+    # expert-major plan (its weights and token rows stay in that XCD's L2), 3 %
+    # faster than the dynamic counter; with 32 CUs left to the side-stream
+    # landing, ~486 units no longer fit two static rounds of 224 and the
+    # dynamic counter balances them (0.5-1 % faster for the memcpy landing,
+    # 1-2 % for the CU landing).
+    forced = {"static": tlc.SCHED_STATIC, "dynamic": tlc.SCHED_DYNAMIC}.get(args.schedule)
+
+    def schedule_for(land_kind):
+        if forced is not None:
+            return forced
+        return tlc.SCHED_DYNAMIC if workloads.uses_copy_streams(land_kind) else tlc.SCHED_STATIC
+
+    schedule = schedule_for(land)
+    args.schedule = args.schedule or ("dynamic" if schedule == tlc.SCHED_DYNAMIC else "static")
     prob = workloads.MoEProblem(inp.x_chunks, inp.logits, inp.w, args.rank, wl.topk, args.tile,
                                 args.tile, layout, device=dev, schedule=schedule)
     compute = torch.cuda.Stream(device=dev)
@@ -518,7 +529,10 @@ def run_moe(args, torch, tlc, si, workloads):
     # fused step: routing on the compute stream while the peers' tokens land,
     # then the readiness-sorted grouped GEMM consuming chunks as they arrive
     def fused_step(land_kind):
-        return lambda: prob.run(land_kind, grid=args.grid, copy_wgs=args.copy_wgs)
+        def step():
+            prob.schedule = schedule_for(land_kind)
+            prob.run(land_kind, grid=args.grid, copy_wgs=args.copy_wgs)
+        return step
 
     t_fused = timed(fused_step(land), args.steps, args.warmup, torch)
     status = prob.sig.read_status(compute)
@@ -541,7 +555,8 @@ def run_moe(args, torch, tlc, si, workloads):
         gemm_t(lambda: tlc.ag_moe(prob.plan, prob.n_tiles_dev, prob.plan_cap, prob.row_token, prob.Tc,
                                   prob.world, prob.rank, prob.E, prob.k, prob.H, prob.N, prob.bm,
                                   prob.bn, prob.x, None, prob.w, prob.b_layout, prob.y, prob.sig, 0,
-                                  tlc.LAND_NONE, compute, None, args.grid, schedule=schedule))
+                                  tlc.LAND_NONE, compute, None, args.grid,
+                                  schedule=schedule_for(tlc.LAND_NONE)))
 
     t_comp = timed(compute_only, args.steps, args.warmup, torch)
     torch.cuda.synchronize()
