@@ -36,6 +36,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_SCLK_MHZ = 2400.0  # the clock the published MFMA peak is quoted at
 PEAK_HBM_GBS = 8000.0
 # Memory traffic per launch of each workload's dominant kernels (256 x 256 tiles,
 # K x N weight), from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (KiB per
@@ -259,7 +260,7 @@ def run_ag(args, torch, tlc, si, workloads):
 
     # one more fused step with per-unit trace stamps: time the workgroups spent
     # spinning on chunk flags (the exposed part of the landing inside the GEMM)
-    trace = torch.zeros((prob.n_tiles, 4), dtype=torch.int64, device=dev)
+    trace = torch.zeros((prob.n_tiles, 6), dtype=torch.int64, device=dev)
     workloads.next_epoch(prob)
     for c in copies:
         c.wait_stream(compute)
@@ -314,8 +315,18 @@ def run_ag(args, torch, tlc, si, workloads):
 
     t_comp = timed(compute_only, args.steps, args.warmup, torch)
     gemm_comp_ms = comp_t.mean_ms(args.steps)
+    # one more compute-only launch with trace stamps, right after the timed
+    # ones (clocks settled): the shader clock the workgroups ran at, from
+    # their cycle counters against the constant-rate clock, and the MFMA peak
+    # at that clock
+    ctrace = torch.zeros((comp.n_tiles, 6), dtype=torch.int64, device=dev)
+    tlc.ag_gemm(**ccall, a_src=None, epoch=0, land=tlc.LAND_NONE, compute_stream=compute,
+                copy_stream=None, grid=0, trace=ctrace)
     torch.cuda.synchronize()
+    ct = ctrace.cpu().numpy()
+    sclk_mhz = float((ct[:, 5] - ct[:, 4]).sum()) / max(float((ct[:, 3] - ct[:, 2]).sum()), 1.0) * khz / 1e3
     achieved = flops / (gemm_comp_ms * 1e-3) / 1e12
+    peak_at_sclk = PEAK_BF16_TFLOPS * sclk_mhz / PEAK_SCLK_MHZ
     extra = {
         "config": {"workload": wl.name, "M": prob.M, "N": prob.N, "K": prob.K, "world": prob.world,
                    "rank": prob.rank, "tile": [args.tile, args.tile, 64], "b_layout": args.layout,
@@ -330,7 +341,10 @@ def run_ag(args, torch, tlc, si, workloads):
                      "traffic_unit": "bytes per launch past the L2 (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes": prob.M * prob.K * 2 + prob.K * prob.N * 2 + prob.M * prob.N * 4,
                      "kernel": "gemm_kernel_8w<KN,dense,no-wait>: compute-only launch, whole tiles, "
-                               "static schedule, every chunk resident"},
+                               "static schedule, every chunk resident",
+                     "sclk_mhz_measured": round(sclk_mhz, 1),
+                     "peak_at_measured_sclk": round(peak_at_sclk, 1),
+                     "frac_at_measured_sclk": round(achieved / peak_at_sclk, 4)},
         "pct_peak": round(100 * flops / t_fused / 1e12 / PEAK_BF16_TFLOPS, 2),
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),

@@ -289,11 +289,13 @@ typedef struct {
    * under 32; for AG-MoE, whose unit count is known only on the device, a
    * quarter of the grid).  They take the last units of the first round. */
   int32_t copy_wgs;
-  /* Optional debug trace (NULL = off): device int64 array of n_tiles x 4,
-   * entry t = {workgroup, wall-clock at wait start, at wait end, at tile end}
-   * for the tile at plan index t; wall clock = the device's constant-rate
-   * counter (hipDeviceAttributeWallClockRate).  Entries of tiles not run keep
-   * their previous contents. */
+  /* Optional debug trace (NULL = off): device int64 array of n_tiles x 6,
+   * entry t = {workgroup, wall clock at wait start, at wait end, at unit end,
+   * shader clock at wait end, at unit end} for the unit at plan index t; wall
+   * clock = the device's constant-rate counter (hipDeviceAttributeWallClockRate),
+   * shader clock = the compute unit's cycle counter (its ratio to the wall
+   * clock gives the clock frequency the unit ran at).  Entries of units not run
+   * keep their previous contents. */
   int64_t* trace;
 } tlc_ag_args;
 
@@ -491,7 +493,7 @@ int64_t tlc_wall_clock_khz(void);
 
 const char* tlc_status_string(tlc_status s);
 const char* tlc_last_error(void);
-/* Library version, e.g. 131 = 0.1.31. */
+/* Library version, e.g. 132 = 0.1.32. */
 int32_t tlc_version(void);
 
 #ifdef __cplusplus

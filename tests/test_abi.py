@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert tlc.version() == 131
+    assert tlc.version() == 132
     assert tlc.status_string(tlc.ERR_TIMEOUT).startswith("timeout")
     assert tlc.status_string(0) == "ok"
 

@@ -782,6 +782,6 @@ const char* tlc_status_string(tlc_status s) {
 
 const char* tlc_last_error(void) { return g_err; }
 
-int32_t tlc_version(void) { return 131; }
+int32_t tlc_version(void) { return 132; }
 
 }  // extern "C"
