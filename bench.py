@@ -46,11 +46,11 @@ PEAK_HBM_GBS = 8000.0
 # whenever one of these kernels changes.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE)
-    "ag": {"gemm": (220330.4, 107392.0)},
-    "moe": {"gemm": (265525.8, 104136.0)},
-    "rs": {"gemm": (59170.7, 68608.0), "reduce": (32791.6, 16415.5)},
-    "ar": {"gemm": (59170.7, 68608.0), "reduce": (32791.6, 16415.5)},
-    "rs_long": {"gemm": (3557317.4, 2744320.0), "reduce": (1310750.8, 327680.0)},
+    "ag": {"gemm": (220333.7, 103236.9)},
+    "moe": {"gemm": (266866.2, 99328.0)},
+    "rs": {"gemm": (59154.6, 66252.8), "reduce": (32795.8, 16423.9)},
+    "ar": {"gemm": (59154.6, 66252.8), "reduce": (32795.8, 16423.9)},
+    "rs_long": {"gemm": (3556843.1, 2622387.2), "reduce": (1310750.4, 327680.1)},
 }
 
 

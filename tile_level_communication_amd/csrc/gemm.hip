@@ -599,8 +599,9 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
       if (threadIdx.x == 0) report(p.sig, TLC_ERR_BAD_PLAN, t);
       break;
     }
-    int64_t t_wait0 = 0, t_wait1 = 0, c_start = 0;
-    if (p.trace && threadIdx.x == 0) t_wait0 = static_cast<int64_t>(wall_clock64());
+    // trace stamps go to memory as they are taken, so that nothing is kept
+    // in registers across the unit
+    if (p.trace && threadIdx.x == 0) p.trace[6 * t + 1] = static_cast<int64_t>(wall_clock64());
     if (WAIT) {
       const uint32_t need = tl.chunk_mask & ~seen;
       if (need) {
@@ -615,17 +616,15 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
       sh->next[it & 1] = G + static_cast<int64_t>(__hip_atomic_fetch_add(
                                  &p.sig->work_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     if (p.trace && threadIdx.x == 0) {
-      t_wait1 = static_cast<int64_t>(wall_clock64());
-      c_start = static_cast<int64_t>(__builtin_amdgcn_s_memtime());
+      int64_t* e = p.trace + 6 * t;
+      e[2] = static_cast<int64_t>(wall_clock64());
+      e[4] = static_cast<int64_t>(__builtin_amdgcn_s_memtime());
     }
     run_tile(tl, &sh->split_last);  // has workgroup barriers: next[] is visible after it
     if (p.trace && threadIdx.x == 0) {
       int64_t* e = p.trace + 6 * t;
       e[0] = blockIdx.x;
-      e[1] = t_wait0;
-      e[2] = t_wait1;
       e[3] = static_cast<int64_t>(wall_clock64());
-      e[4] = c_start;
       e[5] = static_cast<int64_t>(__builtin_amdgcn_s_memtime());
     }
     t = p.dynamic ? sh->next[it & 1] : t + G;
