@@ -323,3 +323,27 @@ def test_ag_epoch_rewind_copy_engine(sub):
         assert prob.sig.read_status()[0] == 0
         check_close(prob.c.cpu().numpy(), ref, K, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), f"call{it}")
     assert prob.epoch == 2
+
+
+def test_ag_trace_stamps():
+    """The optional unit trace: one entry of six per unit -- workgroup, constant-
+    rate stamps at wait start, wait end and unit end, shader-cycle stamps at wait
+    end and unit end -- consistent with each other, and a clock in a plausible
+    range; results unchanged."""
+    W, R, K, N = 4, 256, 512, 512
+    inp = si.ag_inputs(140, W, R, N, K)
+    prob = AGProblem(inp.a_chunks, inp.b, 1, 256, 256, tlc.B_KN, schedule=tlc.SCHED_STATIC)
+    prob.poison_remote()
+    trace = torch.full((prob.n_tiles, 6), -1, dtype=torch.int64, device=prob.c.device)
+    log("[ag trace]")
+    prob.run(tlc.LAND_COLOCATED, trace=trace)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    check_close(prob.c.cpu().numpy(), og.ag_gemm(inp.a_chunks, inp.b), K, absmax_bf16(inp.a_chunks),
+                absmax_bf16(inp.b), "traced")
+    tr = trace.cpu().numpy()
+    assert (tr[:, 0] >= 0).all() and (tr[:, 0] < 256).all()
+    assert (tr[:, 1] <= tr[:, 2]).all() and (tr[:, 2] < tr[:, 3]).all()
+    assert (tr[:, 4] < tr[:, 5]).all()
+    mhz = (tr[:, 5] - tr[:, 4]).sum() / (tr[:, 3] - tr[:, 2]).sum() * tlc.wall_clock_khz() / 1e3
+    assert 300 < mhz < 3000, mhz
