@@ -140,7 +140,9 @@ def other_landings(flops, t_comp, others, t_copy_others, extra_names=None):
     """The same step with the other landing backends, for the JSON line."""
     names = {v: k for k, v in LANDINGS.items()}
     names.update(extra_names or {})
-    return {names[o]: {"value": round(flops / t_f / 1e12, 2), "ms_per_step": round(t_f * 1e3, 4),
+    # a device-side failure (a flag wait that timed out) voids the leg's timing
+    return {names[o]: {"value": round(flops / t_f / 1e12, 2) if st[0] == 0 else None,
+                       "ms_per_step": round(t_f * 1e3, 4),
                        "copy_only_ms": round(t_copy_others[o] * 1e3, 4),
                        "overlap_efficiency": round(max(t_comp, t_copy_others[o]) / t_f, 4),
                        "device_status": st}
@@ -270,14 +272,19 @@ def run_ag(args, torch, tlc, si, workloads):
         compute.wait_stream(c)
     torch.cuda.synchronize()
     tr = trace.cpu().numpy()
-    khz = max(tlc.wall_clock_khz(), 1)
-    wait_us = (tr[:, 2] - tr[:, 1]) * 1e3 / khz
-    span_us = float(tr[:, 3].max() - tr[:, 1].min()) * 1e3 / khz
-    n_wg = len(set(tr[:, 0].tolist()))
-    spin = {"wait_us_total": round(float(wait_us.sum()), 1),
-            "units_that_waited": int((wait_us > 1.0).sum()),
-            "wait_fraction_of_workgroup_time": round(float(wait_us.sum()) / (n_wg * span_us), 4),
-            "kernel_span_us": round(span_us, 1)}
+    trace_status = prob.sig.read_status(compute)
+    if trace_status[0] != 0 or (tr[:, 1:4] == 0).any():
+        # units that stopped early carry no stamps: nothing to report
+        spin = {"error": f"traced step ended with device status {trace_status}"}
+    else:
+        khz = max(tlc.wall_clock_khz(), 1)
+        wait_us = (tr[:, 2] - tr[:, 1]) * 1e3 / khz
+        span_us = float(tr[:, 3].max() - tr[:, 1].min()) * 1e3 / khz
+        n_wg = len(set(tr[:, 0].tolist()))
+        spin = {"wait_us_total": round(float(wait_us.sum()), 1),
+                "units_that_waited": int((wait_us > 1.0).sum()),
+                "wait_fraction_of_workgroup_time": round(float(wait_us.sum()) / (n_wg * span_us), 4),
+                "kernel_span_us": round(span_us, 1)}
 
     # the same step with the other landing backends (reported beside the headline)
     others = {o: (timed(fused_step(o), args.steps, args.warmup, torch), prob.sig.read_status(compute))
@@ -623,7 +630,18 @@ def main():
     else:
         line = run_rs(args, torch, tlc, si, workloads, WORKLOAD_ID[args.workload],
                       ar=args.workload == "ar")
+    void_on_device_error(line, tlc)
     print(json.dumps(line), flush=True)
+
+
+def void_on_device_error(line, tlc):
+    """A flag wait that timed out on the device (status[0] != 0) means units were
+    skipped: the headline steps measured incomplete work, so no value is given."""
+    st = line.get("device_status") or [0]
+    if st[0] != 0:
+        line["value"] = None
+        line["error"] = (f"device status {st}: {tlc.status_string(st[0])}; "
+                         "the timed fused steps did not complete their work")
 
 
 if __name__ == "__main__":

@@ -38,3 +38,20 @@ def test_workload_ids_name_the_configs():
             "ar": "rs_w4_4096x4096x2048", "rs_long": "rs_ffn_down_128k_w8_131072x5120x3200",
             "moe": "ag_moe_w8_t4096_e64_top8_h2048_n768"}
     assert {k: si.WORKLOADS[v].name for k, v in bench.WORKLOAD_ID.items()} == want
+
+
+def test_device_timeout_voids_the_values():
+    """A fused step whose flag wait timed out on the device skipped units: its
+    throughput is not reported, for the headline or for another landing."""
+    from tile_level_communication_amd import tlc
+    line = {"value": 900.0, "device_status": [tlc.ERR_TIMEOUT, 190, 3, 0]}
+    bench.void_on_device_error(line, tlc)
+    assert line["value"] is None and "timeout" in line["error"]
+    ok = {"value": 900.0, "device_status": [0, 0, 0, 0]}
+    bench.void_on_device_error(ok, tlc)
+    assert ok == {"value": 900.0, "device_status": [0, 0, 0, 0]}
+    others = bench.other_landings(1e12, 1e-3, {tlc.LAND_CU: (2e-3, [tlc.ERR_TIMEOUT, 1, 2, 0]),
+                                               tlc.LAND_COLOCATED: (1e-3, [0, 0, 0, 0])},
+                                  {tlc.LAND_CU: 1e-3, tlc.LAND_COLOCATED: 0.5e-3})
+    assert others["cu"]["value"] is None
+    assert others["colocated"]["value"] == 1000.0 and others["colocated"]["overlap_efficiency"] == 1.0
