@@ -136,6 +136,27 @@ class KernelTimer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.pairs[-last:]]))
 
 
+def flushed_ms(step, compute, steps, warmup, torch, dev):
+    """Mean time of `step` (which orders its side streams after `compute` and
+    joins them back) with the 256 MB MALL flushed before each one by a 512 MiB
+    fill on `compute`: HIP events on `compute` after the fill and after the
+    join, so the fill is not timed and the step's sources come from HBM."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    pairs = []
+    for _ in range(warmup + steps):
+        with torch.cuda.stream(compute):
+            flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(compute)
+        step()
+        e1.record(compute)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    del flush
+    return sum(a.elapsed_time(b) for a, b in pairs[warmup:]) / steps
+
+
 def other_landings(flops, t_comp, others, t_copy_others, extra_names=None):
     """The same step with the other landing backends, for the JSON line."""
     names = {v: k for k, v in LANDINGS.items()}
@@ -303,6 +324,7 @@ def run_ag(args, torch, tlc, si, workloads):
         return step
 
     t_copy = timed(copy_only_step(land), args.steps, args.warmup, torch)
+    copy_flushed_ms = flushed_ms(copy_only_step(land), compute, args.steps, args.warmup, torch, dev)
     t_copy_others = {o: timed(copy_only_step(o), args.steps, args.warmup, torch) for o in others}
 
     # compute-only: the GEMM alone, every chunk in place, no flag checks (land
@@ -357,6 +379,7 @@ def run_ag(args, torch, tlc, si, workloads):
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
         "gemm_kernel_ms": {"fused": round(gemm_fused_ms, 4), "compute_only": round(gemm_comp_ms, 4)},
         "copy_only_ms": round(t_copy * 1e3, 4),
+        "copy_only_ms_mall_flushed": round(copy_flushed_ms, 4),
         "exposed_copy_ms": round((t_fused - t_comp) * 1e3, 4),
         "flag_spin": spin,
         "copy_gbs": round((prob.world - 1) * prob.R * prob.K * 2 / t_copy / 1e9, 1),
@@ -445,6 +468,7 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
     others = {o: (timed(fused_step(o), steps, warm, torch), prob.sig.read_status(compute))
               for o in LANDINGS.values() if o != land}
     t_copy = timed(copy_only_step(land), steps, warm, torch)
+    copy_flushed_ms = flushed_ms(copy_only_step(land), compute, steps, warm, torch, dev)
     t_copy_others = {o: timed(copy_only_step(o), steps, warm, torch) for o in others}
     prob.place_all()
     prob.sig.set(prob.world, tlc.EPOCH_MAX, compute)
@@ -506,6 +530,7 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
         "copy_only_ms": round(t_copy * 1e3, 4),
+        "copy_only_ms_mall_flushed": round(copy_flushed_ms, 4),
         "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
         "device_status": status,
         "other_landings": other_landings(flops, t_comp, others, t_copy_others),
