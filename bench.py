@@ -294,11 +294,11 @@ def run_ag(args, torch, tlc, si, workloads):
     torch.cuda.synchronize()
     tr = trace.cpu().numpy()
     trace_status = prob.sig.read_status(compute)
+    khz = max(tlc.wall_clock_khz(), 1)
     if trace_status[0] != 0 or (tr[:, 1:4] == 0).any():
         # units that stopped early carry no stamps: nothing to report
         spin = {"error": f"traced step ended with device status {trace_status}"}
     else:
-        khz = max(tlc.wall_clock_khz(), 1)
         wait_us = (tr[:, 2] - tr[:, 1]) * 1e3 / khz
         span_us = float(tr[:, 3].max() - tr[:, 1].min()) * 1e3 / khz
         n_wg = len(set(tr[:, 0].tolist()))
