@@ -95,6 +95,8 @@ enum { TLC_B_KN = 0, TLC_B_NK = 1 };
  *                  peer chunk in landing order; the last workgroup to finish a
  *                  chunk's shares raises its flag with a release store, and the
  *                  GEMM's units wait on the flags as in the other modes.
+ *                  A share of 2 GiB or more (chunk bytes / copy_wgs) returns
+ *                  TLC_ERR_UNSUPPORTED.
  *                  GEMM-RS: the reduce loads the peers' partials from
  *                  remote_src itself (no landing buffers, no flags).  The copy
  *                  streams are not used (they may be NULL / 0).            */

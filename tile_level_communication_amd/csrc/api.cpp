@@ -256,6 +256,10 @@ tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src
   }
   p->copy.wgs = world > n_local ? cw : 0;
   fill_copy_chunks(&p->copy, dst, src, bytes, world, rank, n_local, flag_base);
+  // a workgroup's share is addressed with 32-bit byte offsets
+  if (p->copy.wgs > 0 && (p->copy.vec + p->copy.wgs - 1) / p->copy.wgs >= (int64_t{1} << 27))
+    return fail(TLC_ERR_UNSUPPORTED, "%s: co-located share of a %lld-byte chunk over %d workgroups "
+                "exceeds 2 GiB", who, static_cast<long long>(bytes), p->copy.wgs);
   return TLC_OK;
 }
 

@@ -31,7 +31,7 @@ __device__ inline __amdgpu_buffer_rsrc_t copy_rsrc(const void* base, uint32_t by
                                            0x00020000);
 }
 
-// Copies units [lo, hi) of chunk i (hi - lo < 2^28), waits for the stores and
+// Copies units [lo, hi) of chunk i (hi - lo < 2^27: 32-bit offsets), waits for the stores and
 // counts the workgroup in; `arrivals` shares complete the chunk.
 __device__ inline void copy_share(const CopyPlan& cp, int i, int64_t lo, int64_t hi, uint32_t arrivals,
                                   tlc_signals* sig, uint32_t epoch) {
