@@ -170,7 +170,7 @@ def other_landings(flops, t_comp, others, t_copy_others, extra_names=None):
             for o, (t_f, st) in others.items()}
 
 
-def cpu_baseline(kind, inp, budget_s, rank=0):
+def cpu_baseline(kind, inp, budget_s, rank=0, topk=0):
     """The float64 oracle on a bounded sample of the workload (whole row blocks
     of the output, as many as fit in about `budget_s` seconds)."""
     import numpy as np
@@ -194,6 +194,24 @@ def cpu_baseline(kind, inp, budget_s, rank=0):
             if time.perf_counter() - t0 >= budget_s:
                 break
         what = f"{blocks} row chunks of {R}x{N} (K={K}) of C"
+    elif kind == "moe":  # the routing once, then blocks of grouped-GEMM rows
+        from oracle import moe as om
+        k = topk
+        r = om.route(inp.logits, k, len(inp.x_chunks), rank, inp.x_chunks[0].shape[0])
+        H, N = inp.w.shape[1], inp.w.shape[2]
+        n_rows = int(r["offsets"][-1])
+        rows = 1024
+        while True:
+            start = (blocks * rows) % n_rows
+            idx = np.arange(start, min(start + rows, n_rows))
+            om.grouped_gemm(inp.x_chunks, inp.w, r["offsets"], r["row_token"], idx)
+            flops += 2.0 * len(idx) * N * H
+            blocks += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        what = (f"routing of {inp.logits.shape[0]} tokens (top-{k} of {inp.logits.shape[1]}), then "
+                f"{blocks} blocks of up to {rows} grouped-GEMM rows (H={H}, N={N}); the routing's "
+                "time is counted, its work is not")
     else:  # rs: rows of the local slice (partial GEMM + reduce)
         K, N = inp.b.shape
         W = len(inp.remote) + 1
@@ -631,7 +649,10 @@ def run_moe(args, torch, tlc, si, workloads):
         "device_status": status,
         "other_landings": other_landings(flops, t_comp, others, t_copy_others, route_name),
     }
-    return base_line(args, flops / t_fused / 1e12, t_fused, extra)
+    line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline("moe", inp, args.cpu_seconds, args.rank, wl.topk)
+    return line
 
 
 def main():

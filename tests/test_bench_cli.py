@@ -55,3 +55,10 @@ def test_device_timeout_voids_the_values():
                                   {tlc.LAND_CU: 1e-3, tlc.LAND_COLOCATED: 0.5e-3})
     assert others["cu"]["value"] is None
     assert others["colocated"]["value"] == 1000.0 and others["colocated"]["overlap_efficiency"] == 1.0
+
+
+def test_cpu_baseline_moe_reports_the_oracle_sample():
+    import seeded_inputs as si
+    r = bench.cpu_baseline("moe", si.workload_inputs(4), 0.05, 0, si.WORKLOADS[4].topk)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0 and r["cores"] >= 1
+    assert "top-8 of 64" in r["sample"] and "H=2048, N=768" in r["sample"]
