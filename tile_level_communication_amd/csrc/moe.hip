@@ -20,8 +20,9 @@
 //                   membership mask.
 //   block_count     one wavefront per block of 64 arrival positions: for each
 //                   expert, how many of the block's tokens chose it.
-//   scan_kernel     one wavefront: per expert, the prefix of those counts over
-//                   the blocks; counts, offsets and m-tile starts over experts.
+//   scan_kernel     sixteen wavefronts over runs of blocks: per expert, the
+//                   prefix of those counts over the blocks; counts, offsets and
+//                   m-tile starts over experts.
 //   scatter_kernel  one wavefront per (block, 16 experts): each (token, expert)
 //                   pair's row = offsets[e] + rows of e in earlier blocks +
 //                   earlier lanes of this block; row_token and slot.
@@ -131,22 +132,48 @@ __global__ __launch_bounds__(64) void block_count_kernel(MoeDev d) {
   if (lane < d.E) d.blk[static_cast<int64_t>(b) * d.E + lane] = mine;
 }
 
-__global__ __launch_bounds__(64) void scan_kernel(MoeDev d) {
-  const int e = threadIdx.x;
+// Sixteen wavefronts: wavefront w takes a contiguous run of blocks, lane =
+// expert.  Its per-expert total goes through LDS; each wavefront then rewrites
+// its blocks with the exclusive prefix (the totals of the runs before it plus
+// its own running sum), and wavefront 0 forms counts, offsets and m-tile starts.
+constexpr int SCAN_WAVES = 16;
+
+__global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(MoeDev d) {
+  __shared__ int part[SCAN_WAVES][64];
+  const int e = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int NB = (d.T + 63) / 64;
-  int run = 0;
-  // per expert (lane), exclusive prefix of the block counts, 16 blocks per batch
-  for (int b0 = 0; b0 < NB; b0 += 16) {
-    int v[16];
+  const int per = (NB + SCAN_WAVES - 1) / SCAN_WAVES;
+  const int b_lo = min(NB, w * per), b_hi = min(NB, b_lo + per);
+  const bool lane_ok = e < d.E;
+  int v[16];
+  int tot = 0;
+  for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      v[i] = (e < d.E && b0 + i < NB) ? d.blk[static_cast<int64_t>(b0 + i) * d.E + e] : 0;
+      v[i] = (lane_ok && b0 + i < b_hi) ? d.blk[static_cast<int64_t>(b0 + i) * d.E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tot += v[i];
+  }
+  part[w][e] = tot;
+  __syncthreads();
+  int run = 0;
+  for (int u = 0; u < w; ++u) run += part[u][e];
+  // a run of at most 16 blocks is still in v[]; longer runs are read again
+  for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
+    if (per > 16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = (lane_ok && b0 + i < b_hi) ? d.blk[static_cast<int64_t>(b0 + i) * d.E + e] : 0;
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (e < d.E && b0 + i < NB) d.blk[static_cast<int64_t>(b0 + i) * d.E + e] = run;
+      if (lane_ok && b0 + i < b_hi) d.blk[static_cast<int64_t>(b0 + i) * d.E + e] = run;
       run += v[i];
     }
   }
+  if (w != 0) return;
+  run = 0;
+  for (int u = 0; u < SCAN_WAVES; ++u) run += part[u][e];
   const int cnt = e < d.E ? run : 0;
   const int tiles = (cnt + d.bm - 1) / d.bm;
   // exclusive scans over the experts (lanes)
@@ -319,7 +346,7 @@ tlc_status launch_moe_route(const MoeDev& d, void* stream) {
   hipLaunchKernelGGL(topk_kernel, dim3(topk_grid > d.copy.wgs ? topk_grid : d.copy.wgs), dim3(256), 0,
                      s, d);
   hipLaunchKernelGGL(block_count_kernel, dim3(nb), dim3(64), 0, s, d);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64), 0, s, d);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64 * SCAN_WAVES), 0, s, d);
   hipLaunchKernelGGL(scatter_kernel, dim3(nb, (d.E + SCATTER_GROUP - 1) / SCATTER_GROUP), dim3(64),
                      0, s, d);
   hipLaunchKernelGGL(pair_kernel, dim3((d.max_pairs + 3) / 4), dim3(256), 0, s, d);
