@@ -12,8 +12,8 @@ tile-level communication:
 
 * ``oracle.plan``  -- tile execution order of the communication-aware tile
   scheduler (DITRON paper notes, §3.2 "distributed swizzling"; Triton-Distributed
-  talk, sections on swizzling and on non-perfect tiling; AutoOverlap §5.2 and
-  §5.4 with Fig. 6; Syncopate wiki, core method 5 "tile order follows chunk
+  talk, sections on swizzling and on non-perfect tiling; AutoOverlap §5.2
+  (dependency resolution) and §5.4 with Fig. 6; Syncopate wiki, core method 5 "tile order follows chunk
   arrival").
 * ``oracle.gemm``  -- AllGather-GEMM C = concat_c(A_c) @ B and GEMM-ReduceScatter
   out_r = sum_s P_s[rows of r] (DITRON §2/§4.1 workload definitions; talk,

@@ -3,7 +3,8 @@
 Plain definitions in float64; the swizzled, overlapped method reaches the same
 values up to rounding order because it only reorders tiles and transfers
 (AutoOverlap §6.2/§7.2: the tile-order knobs keep semantics unchanged; DITRON
-§4.4: adapted kernels are bitwise equal to the native ones).
+paper notes, the §4.3 text on training deployment: adapted kernels are
+bitwise equal to the native ones).
 
 * AllGather-GEMM (DITRON §2 and §4.1, AG-GEMM workload; talk, swizzling
   section): every rank r holds one row chunk A_r of the activations; after the
@@ -103,7 +104,7 @@ def gemm_ar(a_local, b_kn, remote: dict, gathered: dict, world: int, rank: int):
     return p, c
 
 
-def blocked_gemm_f32(a_rows, b_kn, units, K_split=None):
+def blocked_gemm_f32(a_rows, b_kn, units):
     """The blocked fp32 GEMM: C (fp32) assembled tile by tile in the given unit
     order (m0, n0, m_rows, n_cols, ...), each tile accumulating its products in
     fp32 over k = 0, 1, ..., K-1 in increasing order (DITRON §3.1, core-level

@@ -26,17 +26,15 @@ chunks instead of the kernel's natural wave order:
 * AG-MoE: tiles of the grouped GEMM are ordered by how late their rows' data
   arrives (fewest dependencies first).  Talk, section "MoE dynamic sorting".
 
-* K-split units (not from the pages; a scheduling device of this library):
-  when requested, every tile whose key is at least ``split_from`` is replaced
-  by ``split_k`` adjacent units, one per K range, so that the work depending on
-  the last chunks can be spread over all compute units.  The units of one tile
-  carry split = S | s << 8 | f << 16, f = ordinal of the split tile in plan
-  order.
+* Sub-chunks (AutoOverlap §6.1 inter-chunk tuning of the split factor, and
+  Fig. 11(b)): each rank's chunk may arrive as S pieces, each with its own
+  ready flag, so the order is the one of world*S smaller chunks.
 
-A unit is the tuple (m0, n0, m_rows, n_cols, expert, chunk_mask, key, split)
+A tile is the tuple (m0, n0, m_rows, n_cols, expert, chunk_mask, key, 0)
 with ``chunk_mask`` = bit c set for every chunk c whose rows the tile reads
 (gather and MoE) or writes (scatter); ``key`` = wait position / send position /
-readiness used as the primary sort key; ``split`` = 0 for a whole tile.
+readiness used as the primary sort key.  The last field is always 0 here: the
+pages keep whole tiles.
 """
 from __future__ import annotations
 
@@ -84,16 +82,15 @@ def landing_order(world: int, rank: int, n_local: int = 1):
 
 def chunk_plan(mode: int, world: int, rank: int, M: int, N: int, rows_per_chunk: int,
                bm: int, bn: int, order: int = ORDER_RANK_OFFSET, group_m: int = 1,
-               split_k: int = 0, split_from: int = 0, sub_chunks: int = 0):
-    """Unit list in execution order for a dense gather (AG) or scatter (RS) GEMM.
+               sub_chunks: int = 0):
+    """Tile list in execution order for a dense gather (AG) or scatter (RS) GEMM.
 
     Sort key: (key, mt // group_m, nt, mt), where key = max consume_pos over the
     touched chunks (AG), min send_pos over the touched chunks (RS), or 0 when the
     natural (un-swizzled) order is requested.  Python's sort is stable and the
-    key is total, so the order is unique.  With split_k >= 2, each tile whose
-    key >= split_from then becomes split_k adjacent units (split index 0 first).
+    key is total, so the order is unique.
 
-    Sub-chunks (gather mode, DITRON §4.3 / Fig. 11 chunk split factor): each
+    Sub-chunks (gather mode, AutoOverlap §6.1 / Fig. 11(b) split factor): each
     rank's chunk arrives as S pieces of R/S rows with their own flags, so chunks,
     positions and masks are those of world*S pieces, rank*S being the first local
     one; the S local pieces are the rank's own (never landed).
@@ -119,26 +116,7 @@ def chunk_plan(mode: int, world: int, rank: int, M: int, N: int, rows_per_chunk:
             key = min(send_pos(c, world, rank) for c in cs)
         tiles.append(((key, mt // group_m, nt, mt), (m0, n0, mr, nc, -1, mask, key, 0)))
     tiles.sort(key=lambda kv: kv[0])
-    units = []
-    n_split = 0
-    for _, t in tiles:
-        key = t[6]
-        if split_k >= 2 and key >= split_from:
-            for s in range(split_k):
-                units.append(t[:7] + (split_k | (s << 8) | (n_split << 16),))
-            n_split += 1
-        else:
-            units.append(t)
-    return units, landing_order(world, rank, n_local)
-
-
-def split_k_range(split: int, K: int, bk: int = 64):
-    """K range [k0, k1) of a unit: the 64-wide steps [s*KT//S, (s+1)*KT//S)."""
-    if split == 0:
-        return 0, K
-    S, s = split & 0xFF, (split >> 8) & 0xFF
-    kt = K // bk
-    return (s * kt // S) * bk, ((s + 1) * kt // S) * bk
+    return [t for _, t in tiles], landing_order(world, rank, n_local)
 
 
 def moe_plan(counts, offsets, row_token, tokens_per_chunk: int, world: int, rank: int,

@@ -25,8 +25,7 @@ def _cases():
 def test_golden_orders(case):
     tiles, landing = op.chunk_plan(case["mode"], case["world"], case["rank"], case["M"], case["N"],
                                    case["R"], case["bm"], case["bn"], case["order"], case["group_m"],
-                                    case.get("split_k", 0), case.get("split_from", 0),
-                                    case.get("sub_chunks", 0))
+                                   case.get("sub_chunks", 0))
     assert [list(t) for t in tiles] == case["tiles"]
     assert landing == case["landing"]
 
@@ -104,50 +103,6 @@ def test_moe_plan_brute_force():
         for nt, (n0, nc) in enumerate([(0, 2), (2, 1)]):
             want.append([m0, n0, mr, nc, e, mask, key, 0])
     assert [list(t) for t in tiles] == want
-
-
-@pytest.mark.parametrize("K,S,want", [
-    (320, 2, [(0, 128), (128, 320)]),
-    (320, 3, [(0, 64), (64, 192), (192, 320)]),
-    (320, 5, [(0, 64), (64, 128), (128, 192), (192, 256), (256, 320)]),
-    (5120, 4, [(0, 1280), (1280, 2560), (2560, 3840), (3840, 5120)]),
-])
-def test_split_k_ranges_hand_values(K, S, want):
-    got = [op.split_k_range(S | (s << 8), K) for s in range(S)]
-    assert got == want
-    assert op.split_k_range(0, K) == (0, K)
-
-
-@pytest.mark.parametrize("mode", [op.AG, op.RS])
-@pytest.mark.parametrize("S,split_from", [(2, 0), (3, 1), (4, 2), (7, 3)])
-def test_split_units_brute(mode, S, split_from):
-    """Split units: the unsplit plan with each tile of key >= split_from
-    replaced in place by S adjacent units whose K ranges partition [0, K),
-    split-tile ordinals numbered 0, 1, ... in plan order."""
-    world, rank, R, N, bm, bn, K = 4, 1, 6, 10, 4, 4, 7 * 64
-    M = world * R
-    base, _ = op.chunk_plan(mode, world, rank, M, N, R, bm, bn)
-    units, _ = op.chunk_plan(mode, world, rank, M, N, R, bm, bn, split_k=S, split_from=split_from)
-    i = 0
-    f = 0
-    for t in base:
-        if t[6] >= split_from:
-            group = units[i:i + S]
-            assert [u[:7] for u in group] == [t[:7]] * S
-            assert [u[7] & 0xFF for u in group] == [S] * S
-            assert [(u[7] >> 8) & 0xFF for u in group] == list(range(S))
-            assert [u[7] >> 16 for u in group] == [f] * S
-            covered = []
-            for u in group:
-                k0, k1 = op.split_k_range(u[7], K)
-                covered.extend(range(k0, k1))
-            assert covered == list(range(K))
-            i += S
-            f += 1
-        else:
-            assert units[i] == t
-            i += 1
-    assert i == len(units)
 
 
 @pytest.mark.parametrize("S", [2, 4])
