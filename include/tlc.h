@@ -89,7 +89,7 @@ enum { TLC_B_KN = 0, TLC_B_NK = 1 };
  *                  kind, which the runtime carries out with its own copy kernels
  *                  on CUs (epoch in 1..TLC_EPOCH_MAX)
  *   COLOCATED   -- no separate landing: the GEMM's own workgroups move the data
- *                  (AutoOverlap §5.2, backend 5: load/store on the SMs that
+ *                  (AutoOverlap §5.3, backend 5: load/store on the SMs that
  *                  compute).  AG-GEMM / AG-MoE: before its first unit, each of
  *                  the first copy_wgs workgroups copies an equal share of every
  *                  peer chunk in landing order; the last workgroup to finish a
@@ -145,14 +145,23 @@ typedef struct {
  * that failed, status[2] = chunk it waited for.  land_count is internal to the
  * CU and co-located landings, work_next / work_done to the GEMM's dynamic work queue
  * (all zero between calls; the last workgroup of a launch resets them).
+ * Scatter mode with sends (tlc_rs_args.send_dst): dest_done[c] counts the
+ * output elements of destination slice P[c] stored so far in this call (zero
+ * between calls: the store that completes the slice rewinds it), and
+ * dest_ready[c] >= epoch  <=>  P[c] is complete for this call (the GEMM's
+ * per-destination notification; Triton-Distributed talk, GEMM-ReduceScatter
+ * example: the GEMM notifies, the consumer waits).
  * epoch_table[i] = i + 1, written once by tlc_signals_alloc.  One GEMM call
- * at a time per signals block. */
+ * at a time per signals block.  After a device error (status[0] != 0)
+ * tlc_signals_clear_status also rewinds dest_done. */
 typedef struct {
   uint32_t flags[TLC_MAX_WORLD];
   uint32_t land_count[TLC_MAX_WORLD];
   int32_t status[4];
   uint32_t work_next, work_done;
-  uint32_t reserved[58];
+  uint32_t dest_done[TLC_MAX_WORLD];
+  uint32_t dest_ready[TLC_MAX_WORLD];
+  uint32_t reserved[122];
   uint32_t epoch_table[TLC_EPOCH_MAX];
 } tlc_signals;
 
@@ -190,7 +199,7 @@ typedef struct {
  *   can spread over every compute unit.
  *   Sub-chunks (gather mode, S = sub_chunks >= 2, R % S == 0, world * S <= 32):
  *   every rank's chunk lands as S pieces of R/S rows, each with its own flag
- *   (DITRON §4.3 and Fig. 11 chunk split factor).  The plan is then the one of
+ *   (AutoOverlap §6.1 and Fig. 11(b): the split factor of a chunk).  The plan is then the one of
  *   world * S chunks of R/S rows with rank * S as the local one: chunk_mask
  *   and key refer to sub-chunks c' = row / (R/S), consumed at position
  *   (c' - rank * S) mod (world * S).
@@ -221,12 +230,21 @@ tlc_status tlc_signals_alloc(tlc_signals** out);
 tlc_status tlc_signals_free(tlc_signals* sig);
 /* Enqueue on `stream`: flags[0..world-1] = value (a one-workgroup kernel; no
  * memset, so it may be captured in a graph).  Used to mark every chunk as
- * landed for compute-only runs, or to rewind the flags to 0. */
+ * landed for compute-only runs (not from the pages: epochs are this library's
+ * way of never resetting a flag). */
 tlc_status tlc_signals_set(tlc_signals* sig, int32_t world, uint32_t value, void* stream);
-/* Enqueue on `stream`: status[0..3] = 0. */
+/* Enqueue on `stream`: every flags[] and dest_ready[] entry = 0, so that the
+ * epochs can restart at 1 (after TLC_EPOCH_MAX in copy-engine mode; not from
+ * the pages). */
+tlc_status tlc_signals_rewind(tlc_signals* sig, void* stream);
+/* Enqueue on `stream`: status[0..3] = 0 and dest_done[0..31] = 0. */
 tlc_status tlc_signals_clear_status(tlc_signals* sig, void* stream);
 /* Synchronize `stream`, then copy status[0..3] to the host array out[4]. */
 tlc_status tlc_read_status(const tlc_signals* sig, void* stream, int32_t* out);
+/* Synchronize `stream`, then copy the whole block to the host struct *out
+ * (not from the pages: an aid for tests and debugging, e.g. to check that
+ * every counter is back at zero after a call). */
+tlc_status tlc_read_signals(const tlc_signals* sig, void* stream, tlc_signals* out);
 
 /* ---------------------------------------------------------- AG-GEMM ------- */
 
@@ -256,6 +274,10 @@ tlc_status tlc_read_status(const tlc_signals* sig, void* stream, int32_t* out);
  *          workspace_bytes is reported as BAD_PLAN.
  * Streams: the GEMM runs on `compute_stream`, the landing on the copy streams.
  * grid: persistent workgroups (0 = every compute unit the landing leaves free).
+ *   With a COPY_ENGINE, CU or MEMCPY landing a grid above (compute units - 32)
+ *   is refused with INVALID_ARG: the landing's kernels (the CU copy kernel, or
+ *   the runtime's kernels for the copies and the 4-byte flag transfers) need
+ *   CUs that no GEMM workgroup holds while those workgroups wait on flags.
  * schedule: TLC_SCHED_DYNAMIC -- workgroups take the next unit in plan order
  *   from a counter in `sig` as they become free (units that wait for a late
  *   chunk then do not hold back the ones behind them); TLC_SCHED_STATIC --
@@ -317,7 +339,29 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* args, void* compute_stream, void* cons
  *   landing[s] must already hold the data and flags be >= epoch); landing may
  *   be NULL if land == COLOCATED (the reduce reads remote_src directly).
  * The GEMM and then the reduce run on `compute`; the reduce waits in-kernel for
- * the remote partials' flags.  */
+ * the remote partials' flags.
+ * Sends (send_dst != NULL; DITRON §3.2 scatter mode, the partial results are
+ * sent to the other ranks while the rest is computed; talk, GEMM-ReduceScatter
+ * example, a producer GEMM that notifies per tile and a consumer that waits on
+ * a second stream): the GEMM stores P with device-coherent stores and, for
+ * every destination c != rank, counts the elements of P[c] it has stored; the
+ * store that completes P[c] raises sig->dest_ready[c] to epoch.  On
+ * send_stream, for c in send order (rank+1, rank+2, ..., rank-1 mod W), the
+ * slice is then copied to send_dst[c] (the emulated peer's receive buffer,
+ * R x N f32, 16-byte aligned; entry rank ignored) as soon as it is complete:
+ *   send_land = TLC_LAND_MEMCPY or TLC_LAND_COPY_ENGINE: a one-wavefront gate
+ *     kernel waits (bounded by timeout_ns; reports TIMEOUT) for dest_ready[c],
+ *     then hipMemcpyAsync(send_dst[c], P[c]) of that kind;
+ *   send_land = TLC_LAND_CU: one copy kernel whose workgroups wait for each
+ *     slice in send order and copy it with load/store instructions.
+ * Requirements for sends: R * N < 2^32, R * N * 4 < 2^32 for TLC_LAND_CU,
+ * the GEMM leaves the CUs of a copy-stream landing free (grid limit below),
+ * and the caller orders send_stream after earlier readers of send_dst and
+ * later readers after it.  The GEMM is always enqueued before the gates.
+ * Grid: a caller grid greater than (compute units - 32) is refused with
+ * INVALID_ARG whenever a copy-stream landing (COPY_ENGINE, CU, MEMCPY) or a
+ * send runs beside the GEMM: the landing's and the sends' kernels need CUs no
+ * GEMM workgroup holds. */
 typedef struct {
   const tlc_tile* plan;
   int64_t n_tiles;
@@ -339,6 +383,9 @@ typedef struct {
   void* workspace;         /* as in tlc_ag_args */
   int64_t workspace_bytes;
   int32_t schedule;
+  float* const* send_dst;  /* host array of `world` device pointers, or NULL: no sends */
+  int32_t send_land;       /* TLC_LAND_MEMCPY, TLC_LAND_COPY_ENGINE or TLC_LAND_CU */
+  void* send_stream;       /* stream of the sends (NULL = the default stream) */
 } tlc_rs_args;
 
 tlc_status tlc_gemm_rs(const tlc_rs_args* args, void* compute_stream, void* const* copy_streams,
@@ -405,7 +452,7 @@ tlc_status tlc_gemm_ar(const tlc_ar_args* args, void* compute_stream, void* cons
  * top-k kernel's first workgroups also copy chunk c (c != rank, tokens_per_chunk
  * x H bf16) from x_src[c] into rows [c Tc, (c+1) Tc) of x with load/store
  * instructions, a fixed number of workgroups per chunk, and the last of them
- * raises sig->flags[c] to `epoch` (AutoOverlap §5.2, backend 5, here beside
+ * raises sig->flags[c] to `epoch` (AutoOverlap §5.3, backend 5, here beside
  * the routing rather than inside the GEMM).  The transfer then overlaps the
  * routing, which waits for nothing; the grouped GEMM that follows consumes the
  * chunks with land = TLC_LAND_NONE and the same epoch (tlc_ag_moe waits for

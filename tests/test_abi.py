@@ -167,3 +167,96 @@ def test_moe_sizes():
     assert tlc.moe_plan_capacity(4096, 8, 64, 768, 256, 256) == (4096 * 8 // 256 + 64) * 3
     assert tlc.moe_workspace_bytes(4096, 8, 64, 256) >= 4096 * 8 + 65 * 4 + 2 * 192 * 4
     assert tlc.moe_plan_capacity(0, 8, 64, 768, 256, 256) == 0
+
+
+def test_signals_block_layout():
+    # 256 words of flags, counters and status, then the epoch table
+    assert C.sizeof(tlc.SignalsBlock) == (256 + tlc.EPOCH_MAX) * 4
+    assert tlc.SignalsBlock.dest_done.offset == 70 * 4
+    assert tlc.SignalsBlock.dest_ready.offset == 102 * 4
+    assert tlc.SignalsBlock.epoch_table.offset == 256 * 4
+    assert tlc.lib().tlc_signals_rewind(None, None) == tlc.ERR_INVALID_ARG
+    assert tlc.lib().tlc_read_signals(None, None, None) == tlc.ERR_INVALID_ARG
+
+
+def _src2():
+    src = (C.c_void_p * 2)(4096, 8192)
+    return C.cast(src, C.POINTER(C.c_void_p)), src
+
+
+@pytest.mark.parametrize("land", [tlc.LAND_MEMCPY, tlc.LAND_COPY_ENGINE, tlc.LAND_CU])
+def test_ag_grid_that_leaves_no_cus_for_the_landing_is_refused(land):
+    """A copy-stream landing needs 32 CUs that no GEMM workgroup holds: a caller
+    grid above 256 - 32 is refused on the host, before any device call."""
+    srcp, keep = _src2()
+    streams = (C.c_void_p * 1)(None)
+    args = _ag_args(a=16, b=32, c=48, sig=64, land=land, a_src=srcp, grid=225)
+    assert tlc.lib().tlc_ag_gemm(C.byref(args), None, streams, 1) == tlc.ERR_INVALID_ARG
+    assert "compute units free" in tlc.last_error(), tlc.last_error()
+    # the largest grid the host allows passes this check (and only then needs the device)
+    args = _ag_args(a=16, b=32, c=48, sig=64, land=land, a_src=srcp, grid=224)
+    s = tlc.lib().tlc_ag_gemm(C.byref(args), None, streams, 1)
+    assert s != tlc.ERR_INVALID_ARG or "compute units free" not in tlc.last_error()
+    # the co-located landing runs inside the GEMM and reserves nothing
+    args = _ag_args(a=16, b=32, c=48, sig=64, land=tlc.LAND_COLOCATED, a_src=srcp, grid=256)
+    s = tlc.lib().tlc_ag_gemm(C.byref(args), None, None, 0)
+    assert "compute units free" not in tlc.last_error()
+    args = _ag_args(a=16, b=32, c=48, sig=64, grid=-1)
+    assert tlc.lib().tlc_ag_gemm(C.byref(args), None, None, 0) == tlc.ERR_INVALID_ARG
+
+
+def _rs_args(**over):
+    base = dict(plan=16, n_tiles=4, M=256, N=256, K=512, world=2, rank=0, rows_per_chunk=128,
+                bm=128, bn=128, a=16, b=32, b_layout=tlc.B_KN, partials=48, out=4096, sig=64,
+                epoch=1, land=tlc.LAND_NONE)
+    base.update(over)
+    return tlc.RSArgs(**base)
+
+
+def test_gemm_rs_send_and_grid_argument_errors():
+    landing = (C.c_void_p * 2)(None, 8192)
+    lp = C.cast(landing, C.POINTER(C.c_void_p))
+    dst = (C.c_void_p * 2)(None, 12288)
+    dp = C.cast(dst, C.POINTER(C.c_void_p))
+    bad_dst = (C.c_void_p * 2)(None, 12290)
+    streams = (C.c_void_p * 1)(None)
+    for over, want, text in [
+        (dict(send_dst=dp, send_land=9), tlc.ERR_INVALID_ARG, "send_land"),
+        (dict(send_dst=dp, send_land=tlc.LAND_COLOCATED), tlc.ERR_INVALID_ARG, "send_land"),
+        (dict(send_dst=C.cast(bad_dst, C.POINTER(C.c_void_p)), send_land=tlc.LAND_MEMCPY),
+         tlc.ERR_INVALID_ARG, "send_dst[1]"),
+        (dict(send_dst=dp, send_land=tlc.LAND_CU, n_tiles=0), tlc.ERR_INVALID_ARG, "CU sends"),
+        (dict(send_dst=dp, send_land=tlc.LAND_MEMCPY, grid=225), tlc.ERR_INVALID_ARG,
+         "compute units free"),
+        (dict(land=tlc.LAND_MEMCPY, remote_src=lp, grid=240), tlc.ERR_INVALID_ARG,
+         "compute units free"),
+    ]:
+        args = _rs_args(landing=lp, **over)
+        s = tlc.lib().tlc_gemm_rs(C.byref(args), None, streams, 1)
+        assert s == want, (over, tlc.last_error())
+        assert text in tlc.last_error(), tlc.last_error()
+    # GEMM-AllReduce takes no sends
+    r = _rs_args(landing=lp, send_dst=dp, send_land=tlc.LAND_MEMCPY)
+    args = tlc.ARArgs(r, None, 128, 0)
+    assert tlc.lib().tlc_gemm_ar(C.byref(args), None, None, 0) == tlc.ERR_INVALID_ARG
+    assert "send_dst" in tlc.last_error()
+
+
+def test_ag_moe_grid_and_topk_errors():
+    srcp, keep = _src2()
+    streams = (C.c_void_p * 1)(None)
+
+    def args(**over):
+        base = dict(plan=16, n_tiles_dev=16, plan_cap=100, row_token=16, tokens_per_chunk=32,
+                    world=2, rank=0, experts=8, topk=2, H=64, N=128, bm=128, bn=128, x=4096,
+                    x_src=srcp, w=8192, w_layout=tlc.B_KN, y=12288, sig=64, epoch=1,
+                    land=tlc.LAND_MEMCPY, grid=0)
+        base.update(over)
+        return tlc.MoEArgs(**base)
+
+    for over, want, text in [(dict(grid=230), tlc.ERR_INVALID_ARG, "compute units free"),
+                             (dict(topk=9), tlc.ERR_UNSUPPORTED, "topk"),
+                             (dict(plan_cap=-1), tlc.ERR_INVALID_ARG, "plan_cap")]:
+        a = args(**over)
+        assert tlc.lib().tlc_ag_moe(C.byref(a), None, streams, 1) == want, (over, tlc.last_error())
+        assert text in tlc.last_error(), tlc.last_error()

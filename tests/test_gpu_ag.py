@@ -3,8 +3,9 @@
 Small shapes span several tiles with ragged edges and a tile that straddles two
 chunks; every rank; both weight layouts; all three landing modes.  Integer-
 valued inputs are compared bit for bit.  The full Qwen3-32B-like FFN-up shape
-(8 chunks of 1024 x 5120, weight 5120 x 3200) is checked on sampled rows with
-normal inputs and in full with integer inputs.
+(8 chunks of 1024 x 5120, weight 5120 x 3200) is compared element by element
+over its whole output, for every landing and schedule the bench runs, with
+normal inputs and with integer inputs.
 """
 import numpy as np
 import pytest
@@ -254,55 +255,58 @@ def test_ag_timeout_reports_status():
 
 @pytest.mark.parametrize("rank", [0, 7])
 def test_ag_qwen3_ffn_up_full_size(rank):
+    """The whole 8192 x 3200 output of every landing and schedule the bench runs,
+    element by element against the float64 oracle (a misrouted tile anywhere
+    fails), and with integer inputs bit for bit."""
     wl = si.WORKLOADS[2]
-    log(f"[ag full] {wl.name} rank={rank}: generating inputs")
+    log(f"[ag full] {wl.name} rank={rank}: generating inputs and the oracle")
     inp = si.workload_inputs(2)
-    prob = AGProblem(inp.a_chunks, inp.b, rank, 256, 256, tlc.B_KN)
-    prob.poison_remote()
-    log(f"[ag full] {wl.name} rank={rank}: run (copy engine landing)")
-    prob.run(tlc.LAND_COPY_ENGINE)
-    torch.cuda.synchronize()
-    assert prob.sig.read_status()[0] == 0
-    c = prob.c
-    rng = np.random.default_rng(rank)
-    rows = np.unique(np.concatenate([
-        [0, 1, 255, 256, 1023, 1024, 4095, 4096, 8191],
-        [ch * 1024 + o for ch in range(8) for o in (0, 511, 1023)],
-        rng.integers(0, 8192, 40)]))
-    got = c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
-    ref = og.ag_gemm_rows(inp.a_chunks, inp.b, rows)
-    check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), "cfg full rows")
+    ref = og.ag_gemm(inp.a_chunks, inp.b)
+    am, bm = absmax_bf16(inp.a_chunks), absmax_bf16(inp.b)
     legs = [
+        ("SDMA landing, dynamic schedule", tlc.LAND_COPY_ENGINE, {}),
         # the bench's headline launch: memcpy landing, whole tiles, static slots
         ("memcpy landing, static schedule", tlc.LAND_MEMCPY, dict(schedule=tlc.SCHED_STATIC)),
+        ("CU landing, static schedule", tlc.LAND_CU, dict(schedule=tlc.SCHED_STATIC)),
         ("co-located landing, static schedule", tlc.LAND_COLOCATED, dict(schedule=tlc.SCHED_STATIC)),
         ("co-located landing, dynamic schedule", tlc.LAND_COLOCATED, {}),
+        ("natural order, memcpy landing", tlc.LAND_MEMCPY,
+         dict(schedule=tlc.SCHED_STATIC, order=tlc.ORDER_NATURAL)),
         # the bench's SDMA plan: the last chunk's tiles split in two along K
         ("SDMA landing, split 2 from key 7", tlc.LAND_COPY_ENGINE,
          dict(split_k=2, split_from=7, schedule=tlc.SCHED_STATIC)),
         ("SDMA landing, split 4 from key 1, dynamic schedule", tlc.LAND_COPY_ENGINE,
          dict(split_k=4, split_from=1)),
+        ("compute only (every chunk in place)", tlc.LAND_NONE, dict(schedule=tlc.SCHED_STATIC)),
     ]
     for what, land, kw in legs:
         log(f"[ag full] {wl.name} rank={rank}: {what}")
         prob = AGProblem(inp.a_chunks, inp.b, rank, 256, 256, tlc.B_KN, **kw)
-        prob.poison_remote()
+        if land == tlc.LAND_NONE:
+            prob.place_all()
+        else:
+            prob.poison_remote()
         prob.c.fill_(float("nan"))
         prob.run(land)
         torch.cuda.synchronize()
-        assert prob.sig.read_status()[0] == 0
-        got = prob.c[torch.from_numpy(rows).to(c.device)].cpu().numpy()
-        check_close(got, ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b), f"cfg full rows, {what}")
-        assert not torch.isnan(prob.c).any().item(), what
+        assert prob.sig.read_status()[0] == 0, what
+        check_close(prob.c.cpu().numpy(), ref, wl.k, am, bm, f"cfg full, {what}")
+        del prob
     # integer-valued inputs: the whole output bit for bit
     log(f"[ag full] {wl.name} rank={rank}: integer inputs, full compare")
     ii = si.workload_inputs(2, integer=True)
-    prob = AGProblem(ii.a_chunks, ii.b, rank, 256, 256, tlc.B_KN, split_k=4, split_from=2)
-    prob.poison_remote()
-    prob.run(tlc.LAND_CU)
-    torch.cuda.synchronize()
-    assert prob.sig.read_status()[0] == 0
-    check_exact(prob.c.cpu().numpy(), og.ag_gemm(ii.a_chunks, ii.b), "cfg full integer")
+    iref = og.ag_gemm(ii.a_chunks, ii.b)
+    for what, land, kw in [("CU landing, split 4 from key 2", tlc.LAND_CU, dict(split_k=4, split_from=2)),
+                           ("memcpy landing, static schedule", tlc.LAND_MEMCPY,
+                            dict(schedule=tlc.SCHED_STATIC))]:
+        log(f"[ag full] {wl.name} rank={rank}: integer inputs, {what}")
+        prob = AGProblem(ii.a_chunks, ii.b, rank, 256, 256, tlc.B_KN, **kw)
+        prob.poison_remote()
+        prob.run(land)
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        check_exact(prob.c.cpu().numpy(), iref, f"cfg full integer, {what}")
+        del prob
 
 
 @pytest.mark.parametrize("sub", [1, 2])

@@ -106,3 +106,50 @@ def test_ragged_last_m_tile_row_blocks(layout):
             torch.cuda.synchronize()
             assert prob.sig.read_status()[0] == 0
             check_exact(prob.c.cpu().numpy(), ref, f"ragged M={M} split_k={split}")
+
+
+def test_bad_plan_reported_on_the_device():
+    """A plan entry outside the output is caught by the GEMM before it touches
+    any operand: status BAD_PLAN with the entry's plan index, every workgroup
+    ends normally, and after clearing the status the same problem runs clean."""
+    W, R, K, N = 2, 128, 128, 256
+    inp = si.ag_inputs(160, W, R, N, K, integer=True)
+    prob = AGProblem(inp.a_chunks, inp.b, 0, 128, 128, tlc.B_KN, schedule=tlc.SCHED_STATIC)
+    prob.place_all()
+    good = prob.plan.clone()
+    bad_idx = 2
+    for field, value in [(0, prob.M), (2, 129), (3, 12), (1, N)]:  # m0, m_rows, n_cols, n0
+        plan = good.clone()
+        plan[bad_idx, field] = value
+        prob.plan = plan
+        log(f"[edge] bad plan field {field} = {value}")
+        prob.run(tlc.LAND_NONE)
+        st = prob.sig.read_status(prob.streams.compute)
+        assert st[0] == tlc.ERR_BAD_PLAN and st[1] == bad_idx, (field, st)
+        prob.sig.clear_status(prob.streams.compute)
+    prob.plan = good
+    prob.run(tlc.LAND_NONE)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    check_exact(prob.c.cpu().numpy(), og.ag_gemm(inp.a_chunks, inp.b), "after bad plans")
+
+
+def test_moe_tile_count_beyond_plan_capacity_reported():
+    """The grouped GEMM reads its unit count from the device; a count above the
+    plan capacity it was given is reported as BAD_PLAN and no unit runs."""
+    mi = si.moe_inputs(504, 2, 64, 64, 128, 8, integer=True)
+    prob = MoEProblem(mi.x_chunks, mi.logits, mi.w, 0, 2, 128, 128, tlc.B_KN)
+    prob.place_all()
+    log("[edge] MoE unit count beyond the plan capacity")
+    prob.route()
+    torch.cuda.synchronize()
+    n = int(prob.n_tiles_dev.item())
+    assert n > 1
+    prob.y.fill_(7.0)
+    tlc.ag_moe(prob.plan, prob.n_tiles_dev, n - 1, prob.row_token, prob.Tc, prob.world, prob.rank,
+               prob.E, prob.k, prob.H, prob.N, prob.bm, prob.bn, prob.x, None, prob.w,
+               prob.b_layout, prob.y, prob.sig, 0, tlc.LAND_NONE, prob.streams.compute, None, 0)
+    st = prob.sig.read_status(prob.streams.compute)
+    assert st[0] == tlc.ERR_BAD_PLAN and st[1] == n, st
+    assert bool((prob.y == 7.0).all().item())
+    prob.sig.clear_status(prob.streams.compute)

@@ -25,6 +25,13 @@ bool g_info_ok[64] = {};
 // until the wait timed out, even when the landing kernel was dispatched first.
 constexpr int kReserveCUsLandCU = 32;
 constexpr int kReserveCUsCopyEngine = 32;
+// The compute units of the largest gfx950 part: a caller grid is checked
+// against it on the host before any device query, then against the device's
+// own count.
+constexpr int kMaxCUs = 256;
+// Workgroups of the CU send kernel (scatter mode): they hold their CUs while
+// they wait for the slices, so they stay within the reserved ones.
+constexpr int kSendCUWorkgroups = 16;
 constexpr int64_t kDefaultTimeoutNs = 2000000000LL;
 }  // namespace
 
@@ -263,6 +270,21 @@ tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src
   return TLC_OK;
 }
 
+// A caller grid must leave the reserved CUs free whenever kernels on other
+// streams (a copy-stream landing, the scatter mode's sends) need them while
+// the GEMM runs: checked against the largest part before any device call,
+// and against the device's own count once it is known (cus > 0).
+tlc_status check_grid(int grid, int reserve, int cus, const char* who) {
+  if (grid < 0) return fail(TLC_ERR_INVALID_ARG, "%s: grid %d < 0", who, grid);
+  if (reserve <= 0 || grid == 0) return TLC_OK;
+  const int limit = (cus > 0 ? cus : kMaxCUs) - reserve;
+  if (grid > limit)
+    return fail(TLC_ERR_INVALID_ARG,
+                "%s: grid %d leaves fewer than %d compute units free for the landing or send "
+                "kernels (at most %d workgroups)", who, grid, reserve, limit);
+  return TLC_OK;
+}
+
 // Persistent grid: every CU left free (dynamic: no more workgroups than
 // units), or the evenly spread static default.
 int pick_grid(int requested, int dynamic, int64_t n_units, int avail) {
@@ -313,6 +335,12 @@ tlc_status tlc_signals_set(tlc_signals* sig, int32_t world, uint32_t value, void
   return st ? st : ok();
 }
 
+tlc_status tlc_signals_rewind(tlc_signals* sig, void* stream) {
+  if (!sig) return fail(TLC_ERR_INVALID_ARG, "tlc_signals_rewind: NULL");
+  tlc_status st = launch_signals_rewind(sig, stream);
+  return st ? st : ok();
+}
+
 tlc_status tlc_signals_clear_status(tlc_signals* sig, void* stream) {
   if (!sig) return fail(TLC_ERR_INVALID_ARG, "tlc_signals_clear_status: NULL");
   tlc_status st = launch_status_clear(sig, stream);
@@ -324,6 +352,14 @@ tlc_status tlc_read_status(const tlc_signals* sig, void* stream, int32_t* out) {
   tlc_status st = hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
   if (st) return st;
   st = hip_check(hipMemcpy(out, sig->status, 4 * sizeof(int32_t), hipMemcpyDeviceToHost), "hipMemcpy(status)");
+  return st ? st : ok();
+}
+
+tlc_status tlc_read_signals(const tlc_signals* sig, void* stream, tlc_signals* out) {
+  if (!sig || !out) return fail(TLC_ERR_INVALID_ARG, "tlc_read_signals: NULL");
+  tlc_status st = hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
+  if (st) return st;
+  st = hip_check(hipMemcpy(out, sig, sizeof(tlc_signals), hipMemcpyDeviceToHost), "hipMemcpy(signals)");
   return st ? st : ok();
 }
 
@@ -389,8 +425,12 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   st = check_land_args(a->land, src, dst, Wf, rf, chunk_bytes, "tlc_ag_gemm", copy_streams,
                        n_copy_streams, a->epoch, S);
   if (st) return st;
+  st = check_grid(a->grid, Wf > S ? reserve_for(a->land) : 0, 0, "tlc_ag_gemm");
+  if (st) return st;
   DeviceInfo info;
   st = device_info(&info);
+  if (st) return st;
+  st = check_grid(a->grid, Wf > S ? reserve_for(a->land) : 0, info.cus, "tlc_ag_gemm");
   if (st) return st;
 
   // The producer is always enqueued before the consumer: two streams may share
@@ -447,6 +487,44 @@ struct GatherPart {
   int32_t copy_wgs;
 };
 
+// The outgoing slices P[c], c != rank, in send order (rank+1, ..., rank-1 mod
+// W), each once the GEMM has raised its ready flag.  With no tiles in the
+// plan nothing would raise the flags: the slices are then sent as they are.
+static tlc_status enqueue_sends(const tlc_rs_args* a, int64_t slice, const DeviceInfo& info) {
+  const int64_t ticks = ticks_for(a->timeout_ns, info);
+  hipStream_t s = static_cast<hipStream_t>(a->send_stream);
+  if (a->send_land == TLC_LAND_CU) {
+    SendParams sp;
+    memset(&sp, 0, sizeof(sp));
+    for (int i = 1; i < a->world; ++i) {
+      const int c = (a->rank + i) % a->world;
+      sp.order[i - 1] = c;
+      sp.src[c] = reinterpret_cast<const uint4*>(a->partials + c * slice);
+      sp.dst[c] = reinterpret_cast<uint4*>(a->send_dst[c]);
+    }
+    sp.n = a->world - 1;
+    sp.vec_per_slice = slice / 4;
+    sp.sig = a->sig;
+    sp.epoch = a->epoch;
+    sp.timeout_ticks = ticks;
+    return launch_send_cu(sp, kSendCUWorkgroups, s);
+  }
+  const hipMemcpyKind kind =
+      a->send_land == TLC_LAND_COPY_ENGINE ? hipMemcpyDeviceToDeviceNoCU : hipMemcpyDeviceToDevice;
+  for (int i = 1; i < a->world; ++i) {
+    const int c = (a->rank + i) % a->world;
+    if (a->n_tiles > 0) {
+      tlc_status st = launch_send_gate(a->sig, c, a->epoch, ticks, s);
+      if (st) return st;
+    }
+    tlc_status st = hip_check(hipMemcpyAsync(a->send_dst[c], a->partials + c * slice,
+                                             static_cast<size_t>(slice) * 4, kind, s),
+                              "hipMemcpyAsync(send)");
+    if (st) return st;
+  }
+  return TLC_OK;
+}
+
 static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* const* copy_streams,
                             int n_copy_streams, bool run_gemm, const GatherPart* g = nullptr) {
   if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: NULL args");
@@ -485,9 +563,39 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
                          copy_streams, n_copy_streams, a->epoch);
     if (st) return st;
   }
+  // sends of the partial slices to their owners (scatter mode's outgoing half)
+  const bool sends = run_gemm && a->send_dst && a->world > 1;
+  if (run_gemm && a->send_dst) {
+    if (a->send_land != TLC_LAND_MEMCPY && a->send_land != TLC_LAND_COPY_ENGINE &&
+        a->send_land != TLC_LAND_CU)
+      return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: send_land %d (MEMCPY, COPY_ENGINE or CU)",
+                  a->send_land);
+    if (slice >= (int64_t{1} << 32))
+      return fail(TLC_ERR_UNSUPPORTED, "tlc_gemm_rs: sends need rows_per_chunk * N < 2^32");
+    if (a->send_land == TLC_LAND_CU && slice_bytes >= (int64_t{1} << 32))
+      return fail(TLC_ERR_UNSUPPORTED, "tlc_gemm_rs: CU sends need slices of < 4 GiB");
+    if (a->send_land == TLC_LAND_CU && a->n_tiles == 0)
+      return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: CU sends need a plan with tiles");
+    for (int c = 0; c < a->world; ++c) {
+      if (c == a->rank) continue;
+      if (!a->send_dst[c] || !aligned16(a->send_dst[c]))
+        return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: send_dst[%d] NULL or misaligned", c);
+    }
+  }
+  // CUs the landing and the sends need beside the GEMM
+  int reserve = reserve_for(land);
+  if (sends && reserve < kReserveCUsCopyEngine) reserve = kReserveCUsCopyEngine;
+  if (run_gemm) {
+    st = check_grid(a->grid, reserve, 0, "tlc_gemm_rs");
+    if (st) return st;
+  }
   DeviceInfo info;
   st = device_info(&info);
   if (st) return st;
+  if (run_gemm) {
+    st = check_grid(a->grid, reserve, info.cus, "tlc_gemm_rs");
+    if (st) return st;
+  }
 
   st = enqueue_landing(land, reinterpret_cast<void* const*>(a->landing),
                        reinterpret_cast<const void* const*>(a->remote_src), slice_bytes, a->world,
@@ -522,8 +630,13 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
     p.epoch = a->epoch;
     p.timeout_ticks = ticks_for(a->timeout_ns, info);
     set_schedule(&p, a->schedule, a->workspace, a->workspace_bytes);
-    // the GEMM does not wait, but the landing running beside it may need CUs
-    const int avail = info.cus - reserve_for(land);
+    if (sends) {
+      p.rows_per_chunk = a->rows_per_chunk;
+      p.notify_mask = ((a->world == 32) ? 0xFFFFFFFFu : ((1u << a->world) - 1u)) & ~(1u << a->rank);
+      p.dest_total = static_cast<uint32_t>(slice);
+    }
+    // the GEMM does not wait, but the landing and the sends beside it may need CUs
+    const int avail = info.cus - reserve;
     int grid = a->n_tiles > 0 ? pick_grid(a->grid, p.dynamic, a->n_tiles, avail)
                               : (a->grid > 0 ? a->grid : avail);
     if (coloc_gather) {
@@ -535,7 +648,14 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
       if (a->n_tiles == 0) grid = p.copy.wgs;
     }
     p.xcd_remap = grid % 8 == 0;
-    st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
+    st = launch_gemm(p, a->bm, a->bn, a->b_layout, sends ? KIND_RS_NOTIFY : KIND_DENSE, grid,
+                     compute_stream);
+    if (st) return st;
+  }
+  // The sends are enqueued after the GEMM that raises their flags, so that a
+  // hardware queue shared by the two streams never holds a gate ahead of it.
+  if (sends) {
+    st = enqueue_sends(a, slice, info);
     if (st) return st;
   }
 
@@ -576,6 +696,7 @@ tlc_status tlc_gemm_ar(const tlc_ar_args* a, void* compute_stream, void* const* 
   if (r.rows_per_chunk < 1 || r.N < 1)
     return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_ar: sizes must be >= 1");
   if (!a->c || !aligned16(a->c)) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_ar: c NULL or misaligned");
+  if (r.send_dst) return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_ar: send_dst must be NULL");
   if (r.land != TLC_LAND_NONE && r.world > 1 && !a->gathered_src)
     return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_ar: landing needs gathered_src");
   const int64_t slice = static_cast<int64_t>(r.rows_per_chunk) * r.N;
@@ -710,6 +831,9 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
     return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: w_layout");
   const int64_t T = static_cast<int64_t>(a->world) * a->tokens_per_chunk;
   if (T * a->H >= (1LL << 31)) return fail(TLC_ERR_UNSUPPORTED, "tlc_ag_moe: T*H >= 2^31");
+  if (a->topk > a->experts || T * a->topk >= (1LL << 31))
+    return fail(TLC_ERR_UNSUPPORTED, "tlc_ag_moe: topk %d (<= experts), T*topk < 2^31", a->topk);
+  if (a->plan_cap < 0) return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: plan_cap < 0");
   if (!a->plan || !a->n_tiles_dev || !a->row_token || !a->x || !a->w || !a->y || !a->sig)
     return fail(TLC_ERR_INVALID_ARG, "tlc_ag_moe: NULL array");
   if (!aligned16(a->x) || !aligned16(a->w) || !aligned16(a->y))
@@ -721,8 +845,13 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
   tlc_status st = check_land_args(a->land, a->x_src, dst, a->world, a->rank, chunk_bytes, "tlc_ag_moe",
                                   copy_streams, n_copy_streams, a->epoch);
   if (st) return st;
+  const int moe_reserve = a->world > 1 ? reserve_for(a->land) : 0;
+  st = check_grid(a->grid, moe_reserve, 0, "tlc_ag_moe");
+  if (st) return st;
   DeviceInfo info;
   st = device_info(&info);
+  if (st) return st;
+  st = check_grid(a->grid, moe_reserve, info.cus, "tlc_ag_moe");
   if (st) return st;
   st = enqueue_landing(a->land, dst, a->x_src, chunk_bytes, a->world, a->rank, 1, a->sig, a->epoch,
                        copy_streams, n_copy_streams, info);

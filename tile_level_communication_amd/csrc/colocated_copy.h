@@ -1,4 +1,4 @@
-// Co-located landing (AutoOverlap §5.2, backend 5: transfers by load/store
+// Co-located landing (AutoOverlap §5.3, backend 5: transfers by load/store
 // instructions on the SMs that compute, coordinated through global-memory
 // signals), shared by the GEMM kernels and the AG-MoE top-k kernel.
 //

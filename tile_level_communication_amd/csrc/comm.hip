@@ -14,6 +14,14 @@
 // signalled through global memory): workgroups copy the chunks in landing
 // order; each workgroup publishes its part of a chunk with a release fence and
 // an arrival count, and the last arrival raises the chunk's flag.
+//
+// Sends of the scatter mode (DITRON §3.2 scatter mode; Triton-Distributed
+// talk, GEMM-ReduceScatter example: the GEMM notifies per tile, a consumer on
+// another stream waits and moves the data): the GEMM raises dest_ready[c] once
+// every element of the destination slice P[c] is stored.  Either a
+// one-wavefront gate waits for that flag in front of a runtime copy of the
+// slice, or a copy kernel's workgroups wait for each slice in send order and
+// copy it themselves.
 #include <hip/hip_runtime.h>
 
 #include "device_sync.h"
@@ -123,14 +131,67 @@ __global__ __launch_bounds__(LAND_THREADS) void land_kernel(LandParams p) {
   }
 }
 
+// Holds the stream until the GEMM has stored every element of slice c.  The
+// wait is bounded; after a timeout or another kernel's failure (status[0]
+// nonzero) it returns at once and the copy that follows moves stale data.
+__global__ __launch_bounds__(64) void send_gate_kernel(tlc_signals* sig, int c, uint32_t epoch,
+                                                       int64_t timeout_ticks) {
+  if (threadIdx.x == 0) (void)wait_flags(sig, sig->dest_ready, 1u << c, epoch, timeout_ticks, -1);
+}
+
+// Every workgroup waits for slice order[i] to be complete, then copies its
+// share of it (grid-stride over 16-byte units, LAND_UNROLL loads in flight
+// per thread), slice after slice in send order.
+__global__ __launch_bounds__(LAND_THREADS) void send_kernel(SendParams p) {
+  __shared__ int s_abort;
+  const int64_t block = static_cast<int64_t>(LAND_THREADS) * LAND_UNROLL;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * block;
+  for (int i = 0; i < p.n; ++i) {
+    const int c = p.order[i];
+    if (threadIdx.x == 0) s_abort = wait_flags(p.sig, p.sig->dest_ready, 1u << c, p.epoch, p.timeout_ticks, -1);
+    __syncthreads();
+    if (s_abort) return;
+    const land_vec* src = reinterpret_cast<const land_vec*>(p.src[c]);
+    land_vec* dst = reinterpret_cast<land_vec*>(p.dst[c]);
+    const int64_t n = p.vec_per_slice;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * block + threadIdx.x; base < n;
+         base += stride) {
+      land_vec v[LAND_UNROLL];
+#pragma unroll
+      for (int u = 0; u < LAND_UNROLL; ++u) {
+        const int64_t k = base + static_cast<int64_t>(u) * LAND_THREADS;
+        if (k < n) v[u] = __builtin_nontemporal_load(src + k);
+      }
+#pragma unroll
+      for (int u = 0; u < LAND_UNROLL; ++u) {
+        const int64_t k = base + static_cast<int64_t>(u) * LAND_THREADS;
+        if (k < n) __builtin_nontemporal_store(v[u], dst + k);
+      }
+    }
+    // the next wait's flag load must not pass this workgroup's reads of s_abort
+    __syncthreads();
+  }
+}
+
 __global__ void signals_set_kernel(tlc_signals* sig, int world, uint32_t value) {
   const int c = threadIdx.x;
   if (c < world) __hip_atomic_store(&sig->flags[c], value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// Every flag and ready flag back to 0, before the epochs restart at 1.
+__global__ void signals_rewind_kernel(tlc_signals* sig) {
+  const int c = threadIdx.x;
+  if (c < TLC_MAX_WORLD) {
+    __hip_atomic_store(&sig->dest_ready[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(&sig->flags[c], 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 __global__ void status_clear_kernel(tlc_signals* sig) {
   const int i = threadIdx.x;
   if (i < 4) __hip_atomic_store(&sig->status[i], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (i < TLC_MAX_WORLD)
+    __hip_atomic_store(&sig->dest_done[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 tlc_status check_launch(const char* what) {
@@ -151,10 +212,27 @@ tlc_status launch_land_cu(const LandParams& p, int grid, void* stream) {
   return check_launch("land");
 }
 
+tlc_status launch_send_gate(tlc_signals* sig, int c, uint32_t epoch, int64_t timeout_ticks,
+                            void* stream) {
+  hipLaunchKernelGGL(send_gate_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), sig, c,
+                     epoch, timeout_ticks);
+  return check_launch("send_gate");
+}
+
+tlc_status launch_send_cu(const SendParams& p, int grid, void* stream) {
+  hipLaunchKernelGGL(send_kernel, dim3(grid), dim3(LAND_THREADS), 0, static_cast<hipStream_t>(stream), p);
+  return check_launch("send");
+}
+
 tlc_status launch_signals_set(tlc_signals* sig, int world, uint32_t value, void* stream) {
   hipLaunchKernelGGL(signals_set_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), sig,
                      world, value);
   return check_launch("signals_set");
+}
+
+tlc_status launch_signals_rewind(tlc_signals* sig, void* stream) {
+  hipLaunchKernelGGL(signals_rewind_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), sig);
+  return check_launch("signals_rewind");
 }
 
 tlc_status launch_status_clear(tlc_signals* sig, void* stream) {

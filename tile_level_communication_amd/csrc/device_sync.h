@@ -10,16 +10,18 @@
 
 namespace tlc {
 
-// Waits until flags[c] >= epoch for every bit c of `need` (one thread only).
-// Returns 0 when all are ready (after an acquire fence at system scope, so the
-// copy engine's and other kernels' writes of those chunks are visible), 1 if
-// the call was aborted (another workgroup failed, or this wait timed out).
-__device__ inline int wait_chunks(tlc_signals* sig, uint32_t need, uint32_t epoch, int64_t timeout_ticks,
-                           int64_t tile_index) {
+// Waits until flag[c] >= epoch for every bit c of `need` (one thread only),
+// flag being one of the flag arrays of `sig` (chunk flags, or the scatter
+// mode's per-destination ready flags).  Returns 0 when all are ready (after
+// an acquire fence at system scope, so the copy engine's and other kernels'
+// writes are visible), 1 if the call was aborted (another workgroup failed,
+// or this wait timed out).
+__device__ inline int wait_flags(tlc_signals* sig, const uint32_t* flag, uint32_t need, uint32_t epoch,
+                                 int64_t timeout_ticks, int64_t tile_index) {
   const uint64_t start = wall_clock64();
   while (need) {
     const int c = __builtin_ctz(need);
-    const uint32_t v = __hip_atomic_load(&sig->flags[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint32_t v = __hip_atomic_load(&flag[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     if (static_cast<int32_t>(v - epoch) >= 0) {
       need &= need - 1;
       continue;
@@ -41,6 +43,12 @@ __device__ inline int wait_chunks(tlc_signals* sig, uint32_t need, uint32_t epoc
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
   return 0;
+}
+
+// The chunk flags: flags[c] >= epoch  <=>  chunk c has landed.
+__device__ inline int wait_chunks(tlc_signals* sig, uint32_t need, uint32_t epoch, int64_t timeout_ticks,
+                                  int64_t tile_index) {
+  return wait_flags(sig, sig->flags, need, epoch, timeout_ticks, tile_index);
 }
 
 __device__ inline void report(tlc_signals* sig, int32_t code, int64_t tile_index) {

@@ -152,6 +152,47 @@ __device__ inline bool split_epilogue(const GemmParams& p, const tlc_tile& tl,
   return true;
 }
 
+// One element of C.  Scatter mode with sends: a device-coherent store (written
+// through past this XCD's L2), so that the slice is complete in memory when
+// the notification below is raised and a copy on another engine or XCD reads
+// it whole.
+template <int KIND>
+__device__ inline void store_c(float* dst, float v) {
+  if constexpr (KIND == KIND_RS_NOTIFY)
+    __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *dst = v;
+}
+
+// Per-destination notification after a tile is stored (scatter mode with
+// sends): once every wave's stores have completed, one thread adds the
+// tile's element count in each destination slice it wrote; the addition that
+// completes a slice (R * N elements) rewinds the count and raises the slice's
+// ready flag with a release store.
+template <int KIND>
+__device__ inline void notify_dests(const GemmParams& p, const tlc_tile& tl) {
+  if constexpr (KIND != KIND_RS_NOTIFY) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  uint32_t m = tl.chunk_mask & p.notify_mask;
+  const int64_t R = p.rows_per_chunk;
+  while (m) {
+    const int c = __builtin_ctz(m);
+    m &= m - 1;
+    const int64_t lo = tl.m0 > c * R ? tl.m0 : c * R;
+    const int64_t hi = tl.m0 + tl.m_rows < (c + 1) * R ? tl.m0 + tl.m_rows : (c + 1) * R;
+    if (hi <= lo) continue;
+    const uint32_t add = static_cast<uint32_t>((hi - lo) * tl.n_cols);
+    const uint32_t prev =
+        __hip_atomic_fetch_add(&p.sig->dest_done[c], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev + add == p.dest_total) {
+      __hip_atomic_store(&p.sig->dest_done[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.sig->dest_ready[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+}
+
 template <int BM, int BN, int B_NK, int KIND>
 struct Tile {
   static constexpr int WM = BM / 2, WN = BN / 2;  // per-wave sub-tile
@@ -306,9 +347,11 @@ struct Tile {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int row = wm * WM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          if (row < tl.m_rows && col < tl.n_cols) cbase[static_cast<int64_t>(row) * p.ldc + col] = acc[i][j][e];
+          if (row < tl.m_rows && col < tl.n_cols)
+            store_c<KIND>(cbase + static_cast<int64_t>(row) * p.ldc + col, acc[i][j][e]);
         }
       }
+    notify_dests<KIND>(p, tl);
   }
 };
 
@@ -546,8 +589,9 @@ struct Tile8w {
           const int rr = i * 32 + 8 * (e >> 2) + (e & 3);
           const int cc = j * 32;
           if (full || (lrow + rr < tl.m_rows && lcol + cc < tl.n_cols))
-            cbase[lane_off + rr * static_cast<int>(p.ldc) + cc] = acc[i][j][e];
+            store_c<KIND>(cbase + lane_off + rr * static_cast<int>(p.ldc) + cc, acc[i][j][e]);
         }
+    notify_dests<KIND>(p, tl);
   }
 };
 
@@ -566,7 +610,18 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
   // share before their first unit; no wait precedes the copy, so the flags it
   // raises cannot depend on the units behind it
   if (WAIT && static_cast<int>(blockIdx.x) < p.copy.wgs) copy_in_landing_order(p.copy, p.sig, p.epoch);
-  const int64_t n_tiles = KIND == KIND_MOE ? static_cast<int64_t>(*p.n_tiles_dev) : p.n_tiles;
+  // MoE: the unit count the routing wrote on the device, bounded by the plan's
+  // capacity (a count beyond it is reported and nothing is run)
+  int64_t n_tiles = p.n_tiles;
+  if (KIND == KIND_MOE) {
+    const int64_t nd = *p.n_tiles_dev;
+    if (nd < 0 || nd > p.n_tiles) {
+      if (threadIdx.x == 0) report(p.sig, TLC_ERR_BAD_PLAN, nd);
+      n_tiles = 0;
+    } else {
+      n_tiles = nd;
+    }
+  }
   uint32_t seen = p.no_wait_mask;
   // The first unit of every workgroup is its slot (no counter traffic while all
   // workgroups start at once); the dynamic schedule then hands out units
@@ -689,6 +744,15 @@ tlc_status launch_one(const GemmParams& p, int grid, void* stream) {
 
 template <int BM, int BN>
 tlc_status launch_shape(const GemmParams& p, int b_layout, int kind, int grid, void* stream) {
+  if (kind == KIND_RS_NOTIFY) {
+    // the scatter-mode GEMM never waits for chunks
+    if (p.do_wait) return fail(TLC_ERR_UNSUPPORTED, "notifying GEMM with chunk waits");
+    if (b_layout == TLC_B_NK) launch_kernel<BM, BN, 1, KIND_RS_NOTIFY, 0>(p, grid, stream);
+    else launch_kernel<BM, BN, 0, KIND_RS_NOTIFY, 0>(p, grid, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TLC_ERR_HIP, "gemm launch: %s", hipGetErrorString(e));
+    return ok();
+  }
   if (kind == KIND_MOE)
     return b_layout == TLC_B_NK ? launch_one<BM, BN, 1, KIND_MOE>(p, grid, stream)
                                 : launch_one<BM, BN, 0, KIND_MOE>(p, grid, stream);

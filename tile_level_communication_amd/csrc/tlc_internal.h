@@ -63,12 +63,19 @@ struct GemmParams {
   // Co-located landing: workgroups [0, copy.wgs) each copy a share of every
   // chunk, in landing order, before their first unit.
   CopyPlan copy;
+  // Scatter mode with sends (KIND_RS_NOTIFY): stores are device-coherent and
+  // every stored tile counts its elements into sig->dest_done[c] for each
+  // destination c in notify_mask it writes; the store completing dest_total
+  // elements rewinds the count and raises sig->dest_ready[c] to epoch.
+  int32_t rows_per_chunk;
+  uint32_t notify_mask;
+  uint32_t dest_total;
 };
 
 // Bytes of one split tile's workspace block (counter header + split_k partials).
 int64_t split_block_bytes(int32_t split_k, int32_t bm, int32_t bn);
 
-enum GemmKind { KIND_DENSE = 0, KIND_MOE = 1 };
+enum GemmKind { KIND_DENSE = 0, KIND_MOE = 1, KIND_RS_NOTIFY = 2 };
 
 // Launch the persistent tiled GEMM: bm x bn in {256x256, 128x128}.
 tlc_status launch_gemm(const GemmParams& p, int bm, int bn, int b_layout, int kind, int grid,
@@ -98,8 +105,27 @@ struct LandParams {
 };
 tlc_status launch_land_cu(const LandParams& p, int grid, void* stream);
 
+// Sends of the scatter mode: the slices order[0..n) of the partial product,
+// each once sig->dest_ready[c] has reached epoch.
+struct SendParams {
+  const uint4* src[TLC_MAX_WORLD];
+  uint4* dst[TLC_MAX_WORLD];
+  int32_t order[TLC_MAX_WORLD];
+  int32_t n;
+  int64_t vec_per_slice;  // 16-byte units per slice (< 2^28)
+  tlc_signals* sig;
+  uint32_t epoch;
+  int64_t timeout_ticks;
+};
+// One wavefront that waits (bounded) for sig->dest_ready[c] >= epoch.
+tlc_status launch_send_gate(tlc_signals* sig, int c, uint32_t epoch, int64_t timeout_ticks,
+                            void* stream);
+// Copy kernel: its workgroups wait for each slice in order, then copy it.
+tlc_status launch_send_cu(const SendParams& p, int grid, void* stream);
+
 tlc_status launch_signals_set(tlc_signals* sig, int world, uint32_t value, void* stream);
 tlc_status launch_status_clear(tlc_signals* sig, void* stream);
+tlc_status launch_signals_rewind(tlc_signals* sig, void* stream);
 
 struct MoeDev {
   const float* logits;

@@ -32,7 +32,7 @@ EXPORTS = [
     "tlc_signals_clear_status", "tlc_read_status", "tlc_ag_gemm", "tlc_gemm_rs", "tlc_rs_reduce",
     "tlc_moe_plan_capacity", "tlc_moe_workspace_bytes", "tlc_moe_route", "tlc_ag_moe", "tlc_land",
     "tlc_status_string", "tlc_last_error", "tlc_version", "tlc_split_workspace_bytes", "tlc_gemm_ar",
-    "tlc_wall_clock_khz",
+    "tlc_wall_clock_khz", "tlc_read_signals", "tlc_signals_rewind",
 ]
 
 
@@ -76,7 +76,17 @@ class RSArgs(C.Structure):
                 ("landing", C.POINTER(C.c_void_p)), ("out", C.c_void_p), ("sig", C.c_void_p),
                 ("epoch", C.c_uint32), ("land", C.c_int32), ("grid", C.c_int32),
                 ("timeout_ns", C.c_int64), ("workspace", C.c_void_p),
-                ("workspace_bytes", C.c_int64), ("schedule", C.c_int32)]
+                ("workspace_bytes", C.c_int64), ("schedule", C.c_int32),
+                ("send_dst", C.POINTER(C.c_void_p)), ("send_land", C.c_int32),
+                ("send_stream", C.c_void_p)]
+
+
+class SignalsBlock(C.Structure):
+    """Host image of tlc_signals."""
+    _fields_ = [("flags", C.c_uint32 * 32), ("land_count", C.c_uint32 * 32), ("status", C.c_int32 * 4),
+                ("work_next", C.c_uint32), ("work_done", C.c_uint32), ("dest_done", C.c_uint32 * 32),
+                ("dest_ready", C.c_uint32 * 32), ("reserved", C.c_uint32 * 122),
+                ("epoch_table", C.c_uint32 * 4096)]
 
 
 class ARArgs(C.Structure):
@@ -128,10 +138,14 @@ def lib() -> C.CDLL:
         L.tlc_signals_free.restype = st
         L.tlc_signals_set.argtypes = [vp, C.c_int32, C.c_uint32, vp]
         L.tlc_signals_set.restype = st
+        L.tlc_signals_rewind.argtypes = [vp, vp]
+        L.tlc_signals_rewind.restype = st
         L.tlc_signals_clear_status.argtypes = [vp, vp]
         L.tlc_signals_clear_status.restype = st
         L.tlc_read_status.argtypes = [vp, vp, C.POINTER(C.c_int32)]
         L.tlc_read_status.restype = st
+        L.tlc_read_signals.argtypes = [vp, vp, C.POINTER(SignalsBlock)]
+        L.tlc_read_signals.restype = st
         L.tlc_ag_gemm.argtypes = [C.POINTER(AGArgs), vp, C.POINTER(vp), C.c_int32]
         L.tlc_ag_gemm.restype = st
         L.tlc_gemm_rs.argtypes = [C.POINTER(RSArgs), vp, C.POINTER(vp), C.c_int32]
@@ -261,6 +275,9 @@ class Signals:
     def set(self, world: int, value: int, stream=None):
         _check(lib().tlc_signals_set(self.ptr, world, value, _stream(stream)), "tlc_signals_set")
 
+    def rewind(self, stream=None):
+        _check(lib().tlc_signals_rewind(self.ptr, _stream(stream)), "tlc_signals_rewind")
+
     def clear_status(self, stream=None):
         _check(lib().tlc_signals_clear_status(self.ptr, _stream(stream)), "tlc_signals_clear_status")
 
@@ -268,6 +285,12 @@ class Signals:
         out = (C.c_int32 * 4)()
         _check(lib().tlc_read_status(self.ptr, _stream(stream), out), "tlc_read_status")
         return [int(v) for v in out]
+
+    def read_block(self, stream=None) -> SignalsBlock:
+        """tlc_read_signals: the whole block, copied to the host after `stream`."""
+        out = SignalsBlock()
+        _check(lib().tlc_read_signals(self.ptr, _stream(stream), C.byref(out)), "tlc_read_signals")
+        return out
 
     def free(self):
         if self.ptr:
@@ -304,22 +327,27 @@ def ag_gemm(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, a_sr
 
 def _rs_args(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout, partials,
              remote_src, landing, out, sig, epoch, land, grid, timeout_ns, workspace=None,
-             schedule=SCHED_DYNAMIC):
+             schedule=SCHED_DYNAMIC, send_dst=None, send_land=LAND_MEMCPY, send_stream=None):
     src = _ptr_array(remote_src, world) if remote_src is not None else None
     lnd = _ptr_array(landing, world) if landing is not None else None
+    snd = _ptr_array(send_dst, world) if send_dst is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return RSArgs(_ptr(plan), n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, _ptr(a),
                   _ptr(b), b_layout, _ptr(partials), src, lnd, _ptr(out), sig.ptr, epoch, land,
-                  grid, timeout_ns, _ptr(workspace), ws_bytes, schedule)
+                  grid, timeout_ns, _ptr(workspace), ws_bytes, schedule, snd, send_land,
+                  _stream(send_stream))
 
 
 def gemm_rs(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout, partials,
             remote_src, landing, out, sig: Signals, epoch, land, compute_stream=None,
-            copy_stream=None, grid=0, timeout_ns=0, workspace=None, schedule=SCHED_DYNAMIC):
-    """tlc_gemm_rs.  remote_src, landing: lists of `world` device tensors (entry `rank` unused)."""
+            copy_stream=None, grid=0, timeout_ns=0, workspace=None, schedule=SCHED_DYNAMIC,
+            send_dst=None, send_land=LAND_MEMCPY, send_stream=None):
+    """tlc_gemm_rs.  remote_src, landing: lists of `world` device tensors (entry `rank` unused).
+    send_dst: list of `world` device tensors (R x N f32, entry `rank` unused) receiving the
+    partial slices P[c] once each is complete, on send_stream; None = no sends."""
     args = _rs_args(plan, n_tiles, M, N, K, world, rank, rows_per_chunk, bm, bn, a, b, b_layout,
                     partials, remote_src, landing, out, sig, epoch, land, grid, timeout_ns,
-                    workspace, schedule)
+                    workspace, schedule, send_dst, send_land, send_stream)
     cs, n = _streams(copy_stream)
     _check(lib().tlc_gemm_rs(C.byref(args), _stream(compute_stream), cs, n), "tlc_gemm_rs")
 

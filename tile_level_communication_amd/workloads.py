@@ -79,7 +79,7 @@ def next_epoch(prob) -> int:
         prob.streams.compute.synchronize()
         for c in prob.streams.copies:
             c.synchronize()
-        prob.sig.set(tlc.MAX_WORLD, 0, prob.streams.compute)  # sub-chunk flags included
+        prob.sig.rewind(prob.streams.compute)  # sub-chunk and ready flags included
         prob.epoch = 1
     return prob.epoch
 
@@ -167,7 +167,7 @@ class AGProblem:
 class RSProblem:
     def __init__(self, a, b_kn, remote: dict, world, rank, bm=256, bn=256, b_layout=tlc.B_KN,
                  order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda", split_k=0, split_from=0,
-                 schedule=tlc.SCHED_DYNAMIC):
+                 schedule=tlc.SCHED_DYNAMIC, sends=False):
         self.device = torch.device(device)
         self.world, self.rank = world, rank
         self.M, self.K = a.shape
@@ -194,6 +194,14 @@ class RSProblem:
         self.sig = tlc.Signals()
         self.epoch = 0
         self.streams = Streams(self.device)
+        # the emulated peers' receive buffers for this rank's partial slices
+        self.send_dst = None
+        self.send_stream = None
+        if sends:
+            self.send_dst = [None if c == rank else
+                             torch.empty((self.R, self.N), dtype=torch.float32, device=self.device)
+                             for c in range(world)]
+            self.send_stream = torch.cuda.Stream(device=self.device)
 
     @property
     def flops(self) -> float:
@@ -217,16 +225,24 @@ class RSProblem:
         return (self.plan, self.n_tiles, self.M, self.N, self.K, self.world, self.rank, self.R,
                 self.bm, self.bn, self.a, self.b, self.b_layout, self.partials)
 
-    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0):
+    def run(self, land=tlc.LAND_COPY_ENGINE, grid=0, timeout_ns=0, send_land=None):
+        """Enqueue one GEMM-RS; with send_land (and a problem built with sends)
+        the partial slices are also sent to send_dst on send_stream."""
         next_epoch(self)
         s = self.streams
         if land == tlc.LAND_NONE:
             self.sig.set(self.world, self.epoch, s.compute)
         s.begin(land)
+        send = send_land is not None and self.send_dst is not None
+        if send:
+            self.send_stream.wait_stream(s.compute)
         tlc.gemm_rs(*self._args(), self.remote_src if land != tlc.LAND_NONE else None, self.landing,
                     self.out, self.sig, self.epoch, land, s.compute, s.copy, grid, timeout_ns,
-                    self.workspace, self.schedule)
+                    self.workspace, self.schedule, self.send_dst if send else None,
+                    send_land if send else tlc.LAND_MEMCPY, self.send_stream if send else None)
         s.end(land)
+        if send:
+            s.compute.wait_stream(self.send_stream)
 
     def reduce_only(self, timeout_ns=0):
         next_epoch(self)
