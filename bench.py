@@ -1,8 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the chunk-swizzled overlap path on one MI355X.
 
-Default workload (--workload ag): the Qwen3-32B-like FFN-up AllGather-GEMM --
-8 chunks of 1024 x 5120 bf16 activations gathered into A (8192 x 5120), weight
+Default line (--workload ag): the Qwen3-32B-like FFN-up AllGather-GEMM -- 8
+chunks of 1024 x 5120 bf16 activations gathered into A (8192 x 5120), weight
 shard B 5120 x 3200 bf16 (K x N), C = A @ B in fp32.  One step = one pass of the
 whole path: the 7 peer chunks land on a side stream with hipMemcpyAsync (one
 device-to-device transfer per chunk, then a 4-byte transfer raising the chunk's
@@ -10,24 +10,28 @@ flag), while the persistent tile-swizzled GEMM on the compute stream starts with
 the local chunk and consumes the others as their flags flip.  The same step with
 the transfers forced onto the SDMA engines, with the library's own copy kernel on
 reserved compute units, and with the co-located backend (the GEMM's own
-workgroups copy the chunks before computing) is reported beside it.  Inputs are
-seeded synthetic data resident in HBM.
+workgroups copy the chunks before computing) is reported beside it.
 
-Other workloads (--workload rs | rs_long | moe) time GEMM-ReduceScatter (4096 x
-4096 x 2048, 4 chunks; 131072 x 5120 x 3200, 8 chunks) and AG-MoE (4096 tokens,
-64 experts, top-8) the same way; the default line is the AG-GEMM one.
+The same line carries the other half of the metric, GEMM-ReduceScatter, as the
+sub-object "gemm_rs": the long-context FFN-down shape (A 131072 x 3200, B 3200 x
+5120, 8 row chunks of 16384), scatter-order GEMM, the 7 remote partials landed
+by hipMemcpyAsync and reduced into the local 16384 x 5120 slice, and the sends
+of this rank's 7 partial slices to their owners gated on the GEMM's
+per-destination ready flags (send tail in scatter and in natural order).
 
-The JSON line carries: fused TFLOP/s (value), compute-only and copy-only times,
-overlap efficiency eta = max(compute-only, copy-only) / fused, the roofline of
-the dominant kernel (the persistent GEMM with every chunk resident, timed with
-HIP events on its stream; bf16 MFMA peak 2.5 PFLOP/s), and the CPU oracle timed
-on a bounded sample (cpu_baseline).
+Other workloads (--workload rs | rs_long | ar | moe) print their own line.  Every
+leg clears the status word (and the split workspace) first and reads it after:
+a leg whose flag waits failed on the device reports no derived figure.
+
+Inputs are seeded synthetic data resident in HBM when the timed region starts.
+The CPU oracle is timed on a bounded sample of the same workload (cpu_baseline).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -41,27 +45,32 @@ PEAK_HBM_GBS = 8000.0
 # Memory traffic per launch of each workload's dominant kernels (256 x 256 tiles,
 # K x N weight), from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (KiB per
 # dispatch) recorded under profiles/, each scaled by what the same counter reads
-# for the plain copy kernel land_kernel of known size: FETCH_SIZE x 2.000 (it
-# reads half the bytes the copy loads), WRITE_SIZE x 1.000.  Re-measure
-# whenever one of these kernels changes.
+# for a plain copy kernel of known size: FETCH_SIZE x FETCH_SCALE, WRITE_SIZE x
+# WRITE_SCALE.  None where the kernel changed since the counters were taken.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
-TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE)
-    "ag": {"gemm": (220333.7, 103236.9)},
+TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE) or None
+    "ag": {"gemm": None},
     "moe": {"gemm": (266866.2, 99328.0)},
-    "rs": {"gemm": (59154.6, 66252.8), "reduce": (32795.8, 16423.9)},
-    "ar": {"gemm": (59154.6, 66252.8), "reduce": (32795.8, 16423.9)},
-    "rs_long": {"gemm": (3556843.1, 2622387.2), "reduce": (1310750.4, 327680.1)},
+    "rs": {"gemm": None, "reduce": (32795.8, 16423.9)},
+    "ar": {"gemm": None, "reduce": (32795.8, 16423.9)},
+    "rs_long": {"gemm": None, "reduce": (1310750.4, 327680.1)},
 }
 
 
 def traffic_bytes(workload, kernel):
-    f, w = TRAFFIC_KIB[workload][kernel]
+    t = TRAFFIC_KIB[workload][kernel]
+    if t is None:
+        return None
+    f, w = t
     return round((f * FETCH_SCALE + w * WRITE_SCALE) * 1024)
+
+
 WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4, "ar": 1}
 LANDINGS = {"memcpy": 3, "copy_engine": 1, "cu": 2, "colocated": 4}  # tlc.LAND_*
+ORDERS = {"natural": 0, "rank_offset": 1}  # tlc.ORDER_*
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -71,27 +80,35 @@ def parse():
                     help="memcpy: hipMemcpyAsync device-to-device on the side stream (default); "
                          "copy_engine: the same forced onto the SDMA engines (NoCU); cu: our copy "
                          "kernel on reserved CUs; colocated: the GEMM's own workgroups copy first")
+    ap.add_argument("--order", default="rank_offset", choices=list(ORDERS),
+                    help="tile order: rank_offset (the chunk-following swizzle) or natural "
+                         "(every rank walks the tiles from tile 0)")
+    ap.add_argument("--legs", default="all", choices=["all", "headline"],
+                    help="headline: only the named landing, its copy-only and the compute-only "
+                         "step (for sweeps); all: every landing backend beside it")
+    ap.add_argument("--no-rs", action="store_true",
+                    help="ag: leave the GEMM-RS sub-object out of the line")
     ap.add_argument("--copy-wgs", type=int, default=0,
-                    help="colocated: workgroups that copy (0 = half the grid)")
+                    help="colocated: workgroups that copy (0 = the library's default)")
     ap.add_argument("--layout", default="KN", choices=["KN", "NK"])
     ap.add_argument("--tile", type=int, default=256)
     ap.add_argument("--group-m", type=int, default=4)
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--copy-streams", type=int, default=1)
     ap.add_argument("--split-k", type=int, default=None,
-                    help="K ranges per split tile (default: 4 for ag, none otherwise)")
+                    help="K ranges per split tile (default: 2 with the SDMA landing, none otherwise)")
     ap.add_argument("--split-from", type=int, default=None,
-                    help="first key (chunk position) whose tiles are split (default 1)")
+                    help="first key (chunk position) whose tiles are split (default 7)")
     ap.add_argument("--sub-chunks", type=int, default=None,
                     help="ag: land every peer chunk as S pieces with their own flags (default 1)")
     ap.add_argument("--schedule", default=None, choices=["dynamic", "static"],
-                    help="work distribution (default: dynamic for ag, static for moe, rs and ar)")
+                    help="work distribution (default: static for ag, rs and ar; per landing for moe)")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--warm-seconds", type=float, default=0.5,
                     help="minimum busy time of each leg's warm-up (after the W warm-up steps)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 WARM_SECONDS = 0.5
@@ -114,6 +131,19 @@ def timed(fn, steps, warmup, torch):
         fn()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
+
+
+def run_leg(prob, fn, steps, warmup, torch, stream):
+    """One leg: status word (and split workspace) cleared first, the step timed,
+    the status read after.  Returns (seconds per step, status[4])."""
+    prob.sig.clear_status(stream)
+    ws = getattr(prob, "workspace", None)
+    if ws is not None:
+        with torch.cuda.stream(stream):
+            ws.zero_()
+    torch.cuda.synchronize()
+    t = timed(fn, steps, warmup, torch)
+    return t, prob.sig.read_status(stream)
 
 
 class KernelTimer:
@@ -157,29 +187,43 @@ def flushed_ms(step, compute, steps, warmup, torch, dev):
     return sum(a.elapsed_time(b) for a, b in pairs[warmup:]) / steps
 
 
+def leg_summary(flops, t_fused, t_comp, t_copy, status):
+    """Figures of one fused leg; a leg whose status word is nonzero skipped work,
+    so none of its derived figures is given."""
+    ok = status[0] == 0
+    out = {"value": round(flops / t_fused / 1e12, 2) if ok else None,
+           "ms_per_step": round(t_fused * 1e3, 4) if ok else None,
+           "copy_only_ms": round(t_copy * 1e3, 4) if t_copy is not None else None,
+           "overlap_efficiency": (round(max(t_comp, t_copy or 0.0) / t_fused, 4) if ok else None),
+           "pct_peak": round(100 * flops / t_fused / 1e12 / PEAK_BF16_TFLOPS, 2) if ok else None,
+           "device_status": status}
+    if not ok:
+        out["error"] = f"device status {status}: the leg's steps did not complete their work"
+    return out
+
+
 def other_landings(flops, t_comp, others, t_copy_others, extra_names=None):
     """The same step with the other landing backends, for the JSON line."""
     names = {v: k for k, v in LANDINGS.items()}
     names.update(extra_names or {})
-    # a device-side failure (a flag wait that timed out) voids the leg's timing
-    return {names[o]: {"value": round(flops / t_f / 1e12, 2) if st[0] == 0 else None,
-                       "ms_per_step": round(t_f * 1e3, 4),
-                       "copy_only_ms": round(t_copy_others[o] * 1e3, 4),
-                       "overlap_efficiency": round(max(t_comp, t_copy_others[o]) / t_f, 4),
-                       "device_status": st}
+    return {names[o]: leg_summary(flops, t_f, t_comp, t_copy_others.get(o), st)
             for o, (t_f, st) in others.items()}
 
 
-def cpu_baseline(kind, inp, budget_s, rank=0, topk=0):
-    """The float64 oracle on a bounded sample of the workload (whole row blocks
-    of the output, as many as fit in about `budget_s` seconds)."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def _oracle_sample(kind, inp, budget_s, rank, topk):
     import numpy as np
     from oracle import gemm as og
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
     flops = 0.0
     blocks = 0
     t0 = time.perf_counter()
@@ -196,8 +240,7 @@ def cpu_baseline(kind, inp, budget_s, rank=0, topk=0):
         what = f"{blocks} row chunks of {R}x{N} (K={K}) of C"
     elif kind == "moe":  # the routing once, then blocks of grouped-GEMM rows
         from oracle import moe as om
-        k = topk
-        r = om.route(inp.logits, k, len(inp.x_chunks), rank, inp.x_chunks[0].shape[0])
+        r = om.route(inp.logits, topk, len(inp.x_chunks), rank, inp.x_chunks[0].shape[0])
         H, N = inp.w.shape[1], inp.w.shape[2]
         n_rows = int(r["offsets"][-1])
         rows = 1024
@@ -209,9 +252,9 @@ def cpu_baseline(kind, inp, budget_s, rank=0, topk=0):
             blocks += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
-        what = (f"routing of {inp.logits.shape[0]} tokens (top-{k} of {inp.logits.shape[1]}), then "
-                f"{blocks} blocks of up to {rows} grouped-GEMM rows (H={H}, N={N}); the routing's "
-                "time is counted, its work is not")
+        what = (f"routing of {inp.logits.shape[0]} tokens (top-{topk} of {inp.logits.shape[1]}), "
+                f"then {blocks} blocks of up to {rows} grouped-GEMM rows (H={H}, N={N}); the "
+                "routing's time is counted, its work is not")
     else:  # rs: rows of the local slice (partial GEMM + reduce)
         K, N = inp.b.shape
         W = len(inp.remote) + 1
@@ -226,15 +269,35 @@ def cpu_baseline(kind, inp, budget_s, rank=0, topk=0):
                 break
         what = f"{blocks} blocks of {rows} rows of the reduced slice (K={K}, N={N})"
     dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "sample": f"{what}, float64, {dt:.1f} s"}
+    return flops / dt / 1e12, what, dt
+
+
+def cpu_baseline(kind, inp, budget_s, rank=0, topk=0):
+    """The float64 oracle on a bounded sample of the workload (whole row blocks
+    of the output, as many as fit in about `budget_s` seconds), with the BLAS
+    thread pool as the host sets it and again with one thread."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: no one-thread run
+        threadpool_limits = None
+        threads = os.cpu_count() or 1
+    value, what, dt = _oracle_sample(kind, inp, budget_s, rank, topk)
+    out = {"value": round(value, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{what}, float64, {dt:.1f} s",
+           "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            v1, what1, dt1 = _oracle_sample(kind, inp, budget_s / 2, rank, topk)
+        out["one_thread"] = {"value": round(v1, 6), "cores": 1, "sample": f"{what1}, float64, {dt1:.1f} s"}
+    return out
 
 
 def base_line(args, value, t_fused, extra):
     line = {
         "metric": "AG-GEMM / GEMM-RS TFLOP/s @1 GPU (fused landing + chunk-swizzled GEMM), "
                   "% bf16 MFMA peak, overlap efficiency",
-        "value": round(value, 2),
+        "value": round(value, 2) if value is not None else None,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -256,18 +319,19 @@ def run_ag(args, torch, tlc, si, workloads):
     inp = si.workload_inputs(2)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
     land = LANDINGS[args.land]
+    order = ORDERS[args.order]
     # fused plan: whole tiles; with the slow SDMA landing the last chunk's tiles
     # are cut in two along K, so that the tail after the last landing runs on
     # twice as many compute units
     split_k = (2 if land == tlc.LAND_COPY_ENGINE else 0) if args.split_k is None else args.split_k
     split_from = 7 if args.split_from is None else args.split_from
-    # static slots: 1.3 % faster than the dynamic counter for the memcpy landing
-    # and 0.7 % for the co-located one (one process each, two runs)
+    # static slots: faster than the dynamic counter for the memcpy and the
+    # co-located landings (one process each, two runs)
     args.schedule = args.schedule or "static"
     schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
     sub = 1 if args.sub_chunks is None else args.sub_chunks
     prob = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
-                               group_m=args.group_m, device=dev, split_k=split_k,
+                               order=order, group_m=args.group_m, device=dev, split_k=split_k,
                                split_from=split_from * sub + (sub - 1), schedule=schedule,
                                sub_chunks=sub)
     compute = torch.cuda.Stream(device=dev)
@@ -295,13 +359,13 @@ def run_ag(args, torch, tlc, si, workloads):
         return step
 
     fused_t = KernelTimer(torch, compute)
-    t_fused = timed(fused_step(land, fused_t), args.steps, args.warmup, torch)
+    t_fused, status = run_leg(prob, fused_step(land, fused_t), args.steps, args.warmup, torch, compute)
     gemm_fused_ms = fused_t.mean_ms(args.steps)
-    status = prob.sig.read_status(compute)
 
     # one more fused step with per-unit trace stamps: time the workgroups spent
     # spinning on chunk flags (the exposed part of the landing inside the GEMM)
     trace = torch.zeros((prob.n_tiles, 6), dtype=torch.int64, device=dev)
+    prob.sig.clear_status(compute)
     workloads.next_epoch(prob)
     for c in copies:
         c.wait_stream(compute)
@@ -326,8 +390,9 @@ def run_ag(args, torch, tlc, si, workloads):
                 "kernel_span_us": round(span_us, 1)}
 
     # the same step with the other landing backends (reported beside the headline)
-    others = {o: (timed(fused_step(o), args.steps, args.warmup, torch), prob.sig.read_status(compute))
-              for o in LANDINGS.values() if o != land}
+    other_kinds = [o for o in LANDINGS.values() if o != land] if args.legs == "all" else []
+    others = {o: run_leg(prob, fused_step(o), args.steps, args.warmup, torch, compute)
+              for o in other_kinds}
 
     def copy_only_step(land_kind):
         # the landing sequence of the fused step alone (an AG call with no units)
@@ -341,14 +406,17 @@ def run_ag(args, torch, tlc, si, workloads):
                 compute.wait_stream(c)
         return step
 
-    t_copy = timed(copy_only_step(land), args.steps, args.warmup, torch)
-    copy_flushed_ms = flushed_ms(copy_only_step(land), compute, args.steps, args.warmup, torch, dev)
-    t_copy_others = {o: timed(copy_only_step(o), args.steps, args.warmup, torch) for o in others}
+    t_copy, copy_status = run_leg(prob, copy_only_step(land), args.steps, args.warmup, torch, compute)
+    copy_flushed_ms = (flushed_ms(copy_only_step(land), compute, args.steps, args.warmup, torch, dev)
+                       if args.legs == "all" else None)
+    t_copy_others = {o: run_leg(prob, copy_only_step(o), args.steps, args.warmup, torch, compute)[0]
+                     for o in others}
 
     # compute-only: the GEMM alone, every chunk in place, no flag checks (land
     # NONE, epoch 0), whole tiles, static schedule -- its fastest configuration
     comp = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
-                               group_m=args.group_m, device=dev, schedule=tlc.SCHED_STATIC)
+                               order=order, group_m=args.group_m, device=dev,
+                               schedule=tlc.SCHED_STATIC)
     comp.place_all()
     comp.c = prob.c
     torch.cuda.synchronize()
@@ -360,7 +428,7 @@ def run_ag(args, torch, tlc, si, workloads):
         comp_t(lambda: tlc.ag_gemm(**ccall, a_src=None, epoch=0, land=tlc.LAND_NONE,
                                    compute_stream=compute, copy_stream=None, grid=0))
 
-    t_comp = timed(compute_only, args.steps, args.warmup, torch)
+    t_comp, comp_status = run_leg(comp, compute_only, args.steps, args.warmup, torch, compute)
     gemm_comp_ms = comp_t.mean_ms(args.steps)
     # one more compute-only launch with trace stamps, right after the timed
     # ones (clocks settled): the shader clock the workgroups ran at, from
@@ -374,12 +442,13 @@ def run_ag(args, torch, tlc, si, workloads):
     sclk_mhz = float((ct[:, 5] - ct[:, 4]).sum()) / max(float((ct[:, 3] - ct[:, 2]).sum()), 1.0) * khz / 1e3
     achieved = flops / (gemm_comp_ms * 1e-3) / 1e12
     peak_at_sclk = PEAK_BF16_TFLOPS * sclk_mhz / PEAK_SCLK_MHZ
+    head = leg_summary(flops, t_fused, t_comp, t_copy, status)
     extra = {
         "config": {"workload": wl.name, "M": prob.M, "N": prob.N, "K": prob.K, "world": prob.world,
-                   "rank": prob.rank, "tile": [args.tile, args.tile, 64], "b_layout": args.layout,
-                   "landing": args.land, "copy_streams": len(copies), "group_m": args.group_m,
-                   "n_units": prob.n_tiles, "split_k": split_k, "split_from_chunk": split_from,
-                   "sub_chunks": sub, "schedule": args.schedule,
+                   "rank": prob.rank, "order": args.order, "tile": [args.tile, args.tile, 64],
+                   "b_layout": args.layout, "landing": args.land, "copy_streams": len(copies),
+                   "group_m": args.group_m, "n_units": prob.n_tiles, "split_k": split_k,
+                   "split_from_chunk": split_from, "sub_chunks": sub, "schedule": args.schedule,
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -387,33 +456,36 @@ def run_ag(args, torch, tlc, si, workloads):
                                  and args.layout == "KN" else None),
                      "traffic_unit": "bytes per launch past the L2 (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes": prob.M * prob.K * 2 + prob.K * prob.N * 2 + prob.M * prob.N * 4,
-                     "kernel": "gemm_kernel_8w<KN,dense,no-wait>: compute-only launch, whole tiles, "
+                     "kernel": "gemm_kernel_4w<KN,dense,no-wait>: compute-only launch, whole tiles, "
                                "static schedule, every chunk resident",
                      "sclk_mhz_measured": round(sclk_mhz, 1),
                      "peak_at_measured_sclk": round(peak_at_sclk, 1),
-                     "frac_at_measured_sclk": round(achieved / peak_at_sclk, 4)},
-        "pct_peak": round(100 * flops / t_fused / 1e12 / PEAK_BF16_TFLOPS, 2),
+                     "frac_at_measured_sclk": round(achieved / peak_at_sclk, 4),
+                     "device_status": comp_status},
+        "pct_peak": head["pct_peak"],
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
         "gemm_kernel_ms": {"fused": round(gemm_fused_ms, 4), "compute_only": round(gemm_comp_ms, 4)},
         "copy_only_ms": round(t_copy * 1e3, 4),
-        "copy_only_ms_mall_flushed": round(copy_flushed_ms, 4),
-        "exposed_copy_ms": round((t_fused - t_comp) * 1e3, 4),
+        "copy_only_ms_mall_flushed": round(copy_flushed_ms, 4) if copy_flushed_ms is not None else None,
+        "copy_only_status": copy_status,
+        "exposed_copy_ms": round((t_fused - t_comp) * 1e3, 4) if status[0] == 0 else None,
         "flag_spin": spin,
         "copy_gbs": round((prob.world - 1) * prob.R * prob.K * 2 / t_copy / 1e9, 1),
-        "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
+        "overlap_efficiency": head["overlap_efficiency"],
         "device_status": status,
         "other_landings": other_landings(flops, t_comp, others, t_copy_others),
     }
-    line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
+    line = base_line(args, head["value"], t_fused, extra)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline("ag", inp, args.cpu_seconds)
     return line
 
 
-def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
+def run_rs(args, torch, tlc, si, workloads, wid, ar=False, sub_object=False):
     """GEMM-RS; with ar=True GEMM-AllReduce on the same shape (the reduce-scatter
-    plus the all-gather of the peers' reduced slices into the M x N output)."""
+    plus the all-gather of the peers' reduced slices into the M x N output).
+    sub_object: the figures for the AG line's "gemm_rs" entry."""
     wl = si.WORKLOADS[wid]
     dev = torch.device("cuda:0")
     if ar:
@@ -423,32 +495,40 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
         inp = si.workload_inputs(wid, rank=args.rank)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
     land = LANDINGS[args.land]
-    split_k = 0 if args.split_k is None else args.split_k
+    order = ORDERS[args.order]
+    split_k = 0 if (args.split_k is None or sub_object) else args.split_k
     split_from = 1 if args.split_from is None else args.split_from
-    args.schedule = args.schedule or "static"
-    schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
+    schedule_name = "static" if sub_object else (args.schedule or "static")
+    schedule = tlc.SCHED_DYNAMIC if schedule_name == "dynamic" else tlc.SCHED_STATIC
     if ar:
         prob = workloads.ARProblem(inp.a, inp.b, inp.remote, inp.gathered, wl.world, args.rank,
-                                   args.tile, args.tile, layout, group_m=args.group_m, device=dev,
-                                   split_k=split_k, split_from=split_from, schedule=schedule)
+                                   args.tile, args.tile, layout, order=order, group_m=args.group_m,
+                                   device=dev, split_k=split_k, split_from=split_from,
+                                   schedule=schedule)
     else:
         prob = workloads.RSProblem(inp.a, inp.b, inp.remote, wl.world, args.rank, args.tile,
-                                   args.tile, layout, group_m=args.group_m, device=dev,
-                                   split_k=split_k, split_from=split_from, schedule=schedule)
+                                   args.tile, layout, order=order, group_m=args.group_m, device=dev,
+                                   split_k=split_k, split_from=split_from, schedule=schedule,
+                                   sends=True)
     ws = dict(workspace=prob.workspace, schedule=schedule)
     c_chunks = ([prob.c[c * prob.R:(c + 1) * prob.R] for c in range(prob.world)] if ar else None)
-
-    def call(land_kind, remote, landing, gathered, epoch, stream_list):
-        if ar:
-            tlc.gemm_ar(*prob._args(), remote, landing, gathered, prob.c, prob.sig, epoch,
-                        land_kind, compute, stream_list, args.grid, copy_wgs=args.copy_wgs, **ws)
-        else:
-            tlc.gemm_rs(*prob._args(), remote, landing, prob.out, prob.sig, epoch, land_kind,
-                        compute, stream_list, args.grid, **ws)
     compute = torch.cuda.Stream(device=dev)
     copies = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.copy_streams))]
     prob.streams.compute = compute
     prob.streams.copies = copies
+    grid = 0 if sub_object else args.grid
+
+    def call(land_kind, remote, landing, gathered, epoch, stream_list, sends=None):
+        if ar:
+            tlc.gemm_ar(*prob._args(), remote, landing, gathered, prob.c, prob.sig, epoch,
+                        land_kind, compute, stream_list, grid, copy_wgs=args.copy_wgs, **ws)
+        else:
+            tlc.gemm_rs(*prob._args(), remote, landing, prob.out, prob.sig, epoch, land_kind,
+                        compute, stream_list, grid, **ws,
+                        send_dst=prob.send_dst if sends is not None else None,
+                        send_land=sends if sends is not None else tlc.LAND_MEMCPY,
+                        send_stream=prob.send_stream if sends is not None else None)
+
     flops = prob.flops
     torch.cuda.synchronize()
     steps, warm = args.steps, args.warmup
@@ -481,13 +561,74 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
                 compute.wait_stream(c)
         return step
 
-    t_fused = timed(fused_step(land), steps, warm, torch)
-    status = prob.sig.read_status(compute)
-    others = {o: (timed(fused_step(o), steps, warm, torch), prob.sig.read_status(compute))
-              for o in LANDINGS.values() if o != land}
-    t_copy = timed(copy_only_step(land), steps, warm, torch)
-    copy_flushed_ms = flushed_ms(copy_only_step(land), compute, steps, warm, torch, dev)
-    t_copy_others = {o: timed(copy_only_step(o), steps, warm, torch) for o in others}
+    t_fused, status = run_leg(prob, fused_step(land), steps, warm, torch, compute)
+    other_kinds = ([o for o in LANDINGS.values() if o != land]
+                   if (args.legs == "all" and not sub_object) else [])
+    others = {o: run_leg(prob, fused_step(o), steps, warm, torch, compute) for o in other_kinds}
+    t_copy, copy_status = run_leg(prob, copy_only_step(land), steps, warm, torch, compute)
+    copy_flushed_ms = (flushed_ms(copy_only_step(land), compute, steps, warm, torch, dev)
+                       if args.legs == "all" else None)
+    t_copy_others = {o: run_leg(prob, copy_only_step(o), steps, warm, torch, compute)[0]
+                     for o in others}
+
+    # sends of this rank's partial slices to their owners, gated on the GEMM's
+    # per-destination ready flags, in the problem's order and in natural order:
+    # when the last send completes against when the GEMM alone ends
+    sends = None
+    if not ar and prob.world > 1:
+        plans = {args.order: (prob.plan, prob.n_tiles)}
+        other = "natural" if args.order == "rank_offset" else "rank_offset"
+        t_o, _ = tlc.chunk_plan(tlc.MODE_RS, prob.world, prob.rank, prob.M, prob.N, prob.R,
+                                args.tile, args.tile, ORDERS[other], args.group_m, split_k,
+                                split_from)
+        plans[other] = (torch.from_numpy(t_o).to(dev), int(t_o.shape[0]))
+        sends = {}
+        for name, (plan, n_tiles) in plans.items():
+            prob.plan, prob.n_tiles = plan, n_tiles
+            rec = []
+
+            def send_step(rec=rec):
+                workloads.next_epoch(prob)
+                for c in copies:
+                    c.wait_stream(compute)
+                prob.send_stream.wait_stream(compute)
+                e0, ec, es = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record(compute)
+                call(land, prob.remote_src, prob.landing, None, prob.epoch, copies, sends=tlc.LAND_MEMCPY)
+                ec.record(compute)
+                es.record(prob.send_stream)
+                rec.append((e0, ec, es))
+                for c in copies:
+                    compute.wait_stream(c)
+                compute.wait_stream(prob.send_stream)
+
+            t_send, st_send = run_leg(prob, send_step, steps, warm, torch, compute)
+            # the GEMM alone in this order (no landing, no sends), less the reduce
+            prob.place_all()
+            prob.sig.set(prob.world, tlc.EPOCH_MAX, compute)
+            gt = KernelTimer(torch, compute)
+            rt = KernelTimer(torch, compute)
+            for _ in range(warm + steps):
+                gt(lambda: call(tlc.LAND_NONE, None, prob.landing, None, tlc.EPOCH_MAX, None))
+                rt(lambda: tlc.rs_reduce(*prob._args(), None, prob.landing, prob.out, prob.sig,
+                                         tlc.EPOCH_MAX, tlc.LAND_NONE, compute))
+            torch.cuda.synchronize()
+            gemm_ms = gt.mean_ms(steps) - rt.mean_ms(steps)
+            prob.sig.rewind(compute)
+            prob.epoch = 0
+            torch.cuda.synchronize()
+            import numpy as np
+            sends_done = float(np.median([a.elapsed_time(c) for a, _, c in rec[-steps:]]))
+            comp_done = float(np.median([a.elapsed_time(b) for a, b, _ in rec[-steps:]]))
+            ok = st_send[0] == 0
+            sends[name] = {"step_ms": round(t_send * 1e3, 4) if ok else None,
+                           "sends_done_ms": round(sends_done, 4) if ok else None,
+                           "gemm_and_reduce_done_ms": round(comp_done, 4) if ok else None,
+                           "gemm_alone_ms": round(gemm_ms, 4),
+                           "send_tail_ms": round(sends_done - gemm_ms, 4) if ok else None,
+                           "device_status": st_send}
+        prob.plan, prob.n_tiles = plans[args.order]
+
     prob.place_all()
     prob.sig.set(prob.world, tlc.EPOCH_MAX, compute)
     torch.cuda.synchronize()
@@ -496,7 +637,8 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
     def compute_only():
         comp_t(lambda: call(tlc.LAND_NONE, None, prob.landing, None, tlc.EPOCH_MAX, None))
 
-    t_comp = timed(compute_only, steps, warm, torch)
+    t_comp, comp_status = run_leg(prob, compute_only, steps, warm, torch, compute)
+    prob.sig.set(prob.world, tlc.EPOCH_MAX, compute)
     red_t = KernelTimer(torch, compute)
 
     def reduce_only():
@@ -519,41 +661,55 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False):
     timed(reduce_flushed, steps, warm, torch)
     red_flushed_ms = red_f.mean_ms(steps)
     del flush
+    reduce_status = prob.sig.read_status(compute)
 
     torch.cuda.synchronize()
     gemm_ms = comp_t.mean_ms(steps) - red_ms
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12
     red_gbs = prob.reduce_bytes / (red_ms * 1e-3) / 1e9
+    head = leg_summary(flops, t_fused, t_comp, t_copy, status)
+    name = wl.name.replace("rs_", "ar_", 1) if ar else wl.name
     extra = {
-        "config": {"workload": wl.name.replace("rs_", "ar_", 1) if ar else wl.name, "M": prob.M,
-                   "N": prob.N, "K": prob.K, "world": prob.world,
-                   "rank": prob.rank, "tile": [args.tile, args.tile, 64], "b_layout": args.layout,
-                   "landing": args.land, "copy_streams": len(copies), "n_units": prob.n_tiles,
-                   "split_k": split_k, "split_from": split_from, "schedule": args.schedule,
+        "config": {"workload": name, "M": prob.M, "N": prob.N, "K": prob.K, "world": prob.world,
+                   "rank": prob.rank, "order": args.order, "tile": [args.tile, args.tile, 64],
+                   "b_layout": args.layout, "landing": args.land, "copy_streams": len(copies),
+                   "n_units": prob.n_tiles, "split_k": split_k, "split_from": split_from,
+                   "schedule": schedule_name,
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": (traffic_bytes(args.workload, "gemm") if args.tile == 256
-                                 and args.layout == "KN" else None),
+                     "traffic": (traffic_bytes("rs_long" if wid == 3 else ("ar" if ar else "rs"), "gemm")
+                                 if args.tile == 256 and args.layout == "KN" else None),
                      "traffic_unit": "bytes per launch past the L2 (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes": prob.M * prob.K * 2 + prob.K * prob.N * 2 + prob.M * prob.N * 4,
-                     "kernel": "gemm_kernel_8w (scatter order, no waits)"},
+                     "kernel": "gemm_kernel_4w (scatter order, no waits)",
+                     "device_status": comp_status},
         "reduce_roofline": {"bound": "hbm", "achieved": round(red_gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(red_gbs / PEAK_HBM_GBS, 4),
-                            "traffic": traffic_bytes(args.workload, "reduce"),
+                            "traffic": traffic_bytes("rs_long" if wid == 3 else "rs", "reduce"),
                             "algorithmic_bytes": prob.reduce_bytes,
                             "kernel": "reduce_kernel", "ms": round(red_ms, 4),
                             "ms_mall_flushed": round(red_flushed_ms, 4),
-                            "achieved_mall_flushed": round(prob.reduce_bytes / (red_flushed_ms * 1e-3) / 1e9, 1)},
+                            "achieved_mall_flushed": round(prob.reduce_bytes / (red_flushed_ms * 1e-3) / 1e9, 1),
+                            "device_status": reduce_status},
+        "pct_peak": head["pct_peak"],
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
         "copy_only_ms": round(t_copy * 1e3, 4),
-        "copy_only_ms_mall_flushed": round(copy_flushed_ms, 4),
-        "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
+        "copy_only_ms_mall_flushed": round(copy_flushed_ms, 4) if copy_flushed_ms is not None else None,
+        "copy_only_status": copy_status,
+        "overlap_efficiency": head["overlap_efficiency"],
         "device_status": status,
-        "other_landings": other_landings(flops, t_comp, others, t_copy_others),
     }
-    line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
+    if sends is not None:
+        extra["sends"] = sends
+    if other_kinds:
+        extra["other_landings"] = other_landings(flops, t_comp, others, t_copy_others)
+    if sub_object:
+        return {"metric": "GEMM-RS TFLOP/s (fused landing + scatter-order GEMM + reduce)",
+                "value": head["value"], "unit": "TFLOP/s", "ms_per_step": head["ms_per_step"],
+                "steps": steps, "warmup": warm, **extra}
+    line = base_line(args, head["value"], t_fused, extra)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline("rs", inp, args.cpu_seconds, args.rank)
     return line
@@ -565,6 +721,7 @@ def run_moe(args, torch, tlc, si, workloads):
     inp = si.workload_inputs(4)
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
     land = LANDINGS[args.land]
+    order = ORDERS[args.order]
     # Schedule per landing unless one is given: with the full grid (co-located
     # landings) static slots keep each XCD on a contiguous run of the
     # expert-major plan (its weights and token rows stay in that XCD's L2), 3 %
@@ -582,7 +739,7 @@ def run_moe(args, torch, tlc, si, workloads):
     schedule = schedule_for(land)
     args.schedule = args.schedule or ("dynamic" if schedule == tlc.SCHED_DYNAMIC else "static")
     prob = workloads.MoEProblem(inp.x_chunks, inp.logits, inp.w, args.rank, wl.topk, args.tile,
-                                args.tile, layout, device=dev, schedule=schedule)
+                                args.tile, layout, order=order, device=dev, schedule=schedule)
     compute = torch.cuda.Stream(device=dev)
     copies = [torch.cuda.Stream(device=dev) for _ in range(max(1, args.copy_streams))]
     prob.streams.compute = compute
@@ -598,15 +755,18 @@ def run_moe(args, torch, tlc, si, workloads):
             prob.run(land_kind, grid=args.grid, copy_wgs=args.copy_wgs)
         return step
 
-    t_fused = timed(fused_step(land), args.steps, args.warmup, torch)
-    status = prob.sig.read_status(compute)
+    t_fused, status = run_leg(prob, fused_step(land), args.steps, args.warmup, torch, compute)
     # besides the four backends of tlc_ag_moe: the chunks landed by the routing's
     # top-k kernel (copy-only timed as the same load/store copy alone)
     route_name = {workloads.LAND_WITH_ROUTE: "colocated_route"}
-    others = {o: (timed(fused_step(o), args.steps, args.warmup, torch), prob.sig.read_status(compute))
-              for o in [*LANDINGS.values(), workloads.LAND_WITH_ROUTE] if o != land}
-    t_copy = timed(lambda: prob.land_only(land), args.steps, args.warmup, torch)
-    t_copy_others = {o: timed(lambda o=o: prob.land_only(o), args.steps, args.warmup, torch)
+    other_kinds = ([o for o in [*LANDINGS.values(), workloads.LAND_WITH_ROUTE] if o != land]
+                   if args.legs == "all" else [])
+    others = {o: run_leg(prob, fused_step(o), args.steps, args.warmup, torch, compute)
+              for o in other_kinds}
+    t_copy, copy_status = run_leg(prob, lambda: prob.land_only(land), args.steps, args.warmup, torch,
+                                  compute)
+    t_copy_others = {o: run_leg(prob, lambda o=o: prob.land_only(o), args.steps, args.warmup, torch,
+                                compute)[0]
                      for o in others}
 
     prob.place_all()
@@ -622,15 +782,16 @@ def run_moe(args, torch, tlc, si, workloads):
                                   tlc.LAND_NONE, compute, None, args.grid,
                                   schedule=schedule_for(tlc.LAND_NONE)))
 
-    t_comp = timed(compute_only, args.steps, args.warmup, torch)
+    t_comp, comp_status = run_leg(prob, compute_only, args.steps, args.warmup, torch, compute)
     torch.cuda.synchronize()
     gemm_ms = gemm_t.mean_ms(args.steps)
     route_ms = route_t.mean_ms(args.steps)
     achieved = flops / (gemm_ms * 1e-3) / 1e12
+    head = leg_summary(flops, t_fused, t_comp, t_copy, status)
     extra = {
         "config": {"workload": wl.name, "tokens": prob.T, "experts": prob.E, "topk": prob.k,
                    "H": prob.H, "N": prob.N, "world": prob.world, "rank": prob.rank,
-                   "landing": args.land, "tile": [args.tile, args.tile, 64],
+                   "order": args.order, "landing": args.land, "tile": [args.tile, args.tile, 64],
                    "n_tiles": int(prob.n_tiles_dev.item()), "schedule": args.schedule,
                    "parallelism": "one GPU's share; peer ranks emulated by side-stream landings"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -640,16 +801,19 @@ def run_moe(args, torch, tlc, si, workloads):
                      "traffic_unit": "bytes per launch past the L2 (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes": prob.T * prob.H * 2 + prob.E * prob.H * prob.N * 2
                      + prob.T * prob.k * prob.N * 4,
-                     "kernel": "gemm_kernel_8w<KN,moe,no-wait>: grouped GEMM, every chunk resident"},
+                     "kernel": "gemm_kernel_8w<KN,moe,no-wait>: grouped GEMM, every chunk resident",
+                     "device_status": comp_status},
         "route_ms": round(route_ms, 4),
+        "pct_peak": head["pct_peak"],
         "compute_only_ms": round(t_comp * 1e3, 4),
         "compute_only_tflops": round(flops / t_comp / 1e12, 2),
         "copy_only_ms": round(t_copy * 1e3, 4),
-        "overlap_efficiency": round(max(t_comp, t_copy) / t_fused, 4),
+        "copy_only_status": copy_status,
+        "overlap_efficiency": head["overlap_efficiency"],
         "device_status": status,
         "other_landings": other_landings(flops, t_comp, others, t_copy_others, route_name),
     }
-    line = base_line(args, flops / t_fused / 1e12, t_fused, extra)
+    line = base_line(args, head["value"], t_fused, extra)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline("moe", inp, args.cpu_seconds, args.rank, wl.topk)
     return line
@@ -671,6 +835,11 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "ag":
         line = run_ag(args, torch, tlc, si, workloads)
+        if not args.no_rs:
+            # the GEMM-RS half of the metric: the long-context FFN-down shape
+            # with the landing and order of the headline
+            line["gemm_rs"] = run_rs(args, torch, tlc, si, workloads, WORKLOAD_ID["rs_long"],
+                                     sub_object=True)
     elif args.workload == "moe":
         line = run_moe(args, torch, tlc, si, workloads)
     else:
@@ -682,10 +851,13 @@ def main():
 
 def void_on_device_error(line, tlc):
     """A flag wait that timed out on the device (status[0] != 0) means units were
-    skipped: the headline steps measured incomplete work, so no value is given."""
+    skipped: the headline steps measured incomplete work, so no figure derived
+    from them is given."""
     st = line.get("device_status") or [0]
     if st[0] != 0:
-        line["value"] = None
+        for k in ("value", "pct_peak", "overlap_efficiency", "exposed_copy_ms"):
+            if k in line:
+                line[k] = None
         line["error"] = (f"device status {st}: {tlc.status_string(st[0])}; "
                          "the timed fused steps did not complete their work")
 

@@ -24,7 +24,11 @@ def test_traffic_bytes_scale_fetch_and_write():
     # FETCH_SIZE counts half the loaded bytes (scaled by 2), WRITE_SIZE all of them
     assert bench.FETCH_SCALE == 2.0 and bench.WRITE_SCALE == 1.0
     for wl, kernels in bench.TRAFFIC_KIB.items():
-        for k, (f, w) in kernels.items():
+        for k, t in kernels.items():
+            if t is None:  # the kernel changed since its counters were taken
+                assert bench.traffic_bytes(wl, k) is None
+                continue
+            f, w = t
             assert bench.traffic_bytes(wl, k) == round((2 * f + w) * 1024)
     # the reduce moves its algorithmic bytes, W + 1 slices of R x N fp32, up to
     # the counters' noise
@@ -54,7 +58,24 @@ def test_device_timeout_voids_the_values():
                                                tlc.LAND_COLOCATED: (1e-3, [0, 0, 0, 0])},
                                   {tlc.LAND_CU: 1e-3, tlc.LAND_COLOCATED: 0.5e-3})
     assert others["cu"]["value"] is None
+    # a failed leg gives none of its derived figures, and names its status
+    for k in ("ms_per_step", "overlap_efficiency", "pct_peak"):
+        assert others["cu"][k] is None
+    assert "device status" in others["cu"]["error"]
     assert others["colocated"]["value"] == 1000.0 and others["colocated"]["overlap_efficiency"] == 1.0
+    assert others["colocated"]["pct_peak"] == 40.0 and "error" not in others["colocated"]
+    # the headline fields of a failed line go too
+    line = {"value": 900.0, "pct_peak": 36.0, "overlap_efficiency": 0.8, "exposed_copy_ms": 0.05,
+            "device_status": [tlc.ERR_TIMEOUT, 1, 2, 0]}
+    bench.void_on_device_error(line, tlc)
+    assert all(line[k] is None for k in ("value", "pct_peak", "overlap_efficiency", "exposed_copy_ms"))
+
+
+def test_order_and_legs_options():
+    a = bench.parse(["--order", "natural", "--rank", "3", "--legs", "headline", "--no-rs"])
+    assert bench.ORDERS[a.order] == 0 and a.rank == 3 and a.legs == "headline" and a.no_rs
+    a = bench.parse([])
+    assert a.order == "rank_offset" and a.legs == "all" and not a.no_rs and a.land == "memcpy"
 
 
 def test_cpu_baseline_moe_reports_the_oracle_sample():
@@ -62,3 +83,6 @@ def test_cpu_baseline_moe_reports_the_oracle_sample():
     r = bench.cpu_baseline("moe", si.workload_inputs(4), 0.05, 0, si.WORKLOADS[4].topk)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0 and r["cores"] >= 1
     assert "top-8 of 64" in r["sample"] and "H=2048, N=768" in r["sample"]
+    # the host it ran on, and the same oracle on one thread
+    assert r["nproc"] == os.cpu_count() and r["cpu_model"]
+    assert r["one_thread"]["cores"] == 1 and r["one_thread"]["value"] > 0

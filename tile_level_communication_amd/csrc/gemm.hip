@@ -18,16 +18,22 @@
 // low-level signal wait with scope, memory semantics and expected value;
 // AutoOverlap §5.2: only the tiles that consume a chunk wait for it).
 //
-// Two tile cores:
-//  * 256 x 256 (the default): 8 wavefronts (2 x 4), 128 x 64 per wavefront,
-//    two per SIMD so that one wave's MFMAs cover the other's LDS reads.
-//    Operands go global -> LDS with buffer loads that write LDS directly (no
-//    register staging), BK = 64, two stages of 64 KB.  A rows (and N x K
-//    weight rows) are 64 bf16 = eight 16-byte chunks per LDS row, chunk c of
-//    row r stored at c ^ ((r >> 1) & 7): the 16 lanes that one LDS cycle
-//    serves read 16 different bank groups.  A K x N weight is kept K-major in
-//    LDS (512-byte rows, chunk c of row k at c ^ 2(k & 15)) and transposed on
-//    the way to the registers with ds_read_b64_tr_b16.
+// Tile cores:
+//  * 256 x 256, 4 wavefronts (2 x 2), 128 x 128 per wavefront, one per SIMD,
+//    accumulators in the accumulation registers (whole-matrix GEMMs).  Its
+//    K loop for whole tiles fixes the place of every instruction: fragment
+//    reads and loads are threaded one by one between the MFMAs, since no
+//    second wavefront on the SIMD fills the gaps.
+//  * 256 x 256, 8 wavefronts (2 x 4), 128 x 64 per wavefront, two per SIMD
+//    so that one wave's MFMAs cover the other's LDS reads (grouped MoE GEMM,
+//    whose ragged tiles it runs as fast as whole ones).
+//  Both: operands go global -> LDS with buffer loads that write LDS directly
+//  (no register staging), BK = 64, two stages of 64 KB.  A rows (and N x K
+//  weight rows) are 64 bf16 = eight 16-byte chunks per LDS row, chunk c of
+//  row r stored at c ^ ((r >> 1) & 7): the 16 lanes that one LDS cycle
+//  serves read 16 different bank groups.  A K x N weight is kept K-major in
+//  LDS (512-byte rows, chunk c of row k at c ^ 2(k & 15)) and transposed on
+//  the way to the registers with ds_read_b64_tr_b16.
 //  * 128 x 128 (small problems): 4 wavefronts, register-staged loads.
 #include <hip/hip_runtime.h>
 
@@ -58,6 +64,17 @@ __device__ inline void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
       const uint32_t lo = in[2 * j][w], hi = in[2 * j + 1][w];
       out[nn][j] = (nn & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
     }
+  }
+}
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): loop
+// bodies whose indices are compile-time constants, so that register arrays
+// indexed by them stay in registers.
+template <int N, int I = 0, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
   }
 }
 
@@ -191,6 +208,35 @@ __device__ inline void notify_dests(const GemmParams& p, const tlc_tile& tl) {
       __hip_atomic_store(&p.sig->dest_ready[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
+}
+
+// Epilogue of the 256 x 256 cores: the wave's fp32 accumulators to C, edge
+// tiles masked.  Element e of block (i, j) belongs to row i*32 + 8*(e/4) +
+// 4*(lane/32) + e%4 and column j*32 + lane%32 of the wave's sub-tile.  The
+// row offset is advanced row by row in one register (opaque to the compiler,
+// so that it does not form all 4*FM row offsets ahead and keep them), and
+// the column block is the store's immediate offset.
+template <int KIND, int WM, int WN, int FM, int FN>
+__device__ inline void store_tile(const GemmParams& p, const tlc_tile& tl, f32x16 (&acc)[FM][FN],
+                                  int wm, int wn, int lane) {
+  const int ldc = static_cast<int>(p.ldc);
+  float* cbase = p.c + static_cast<int64_t>(tl.m0) * p.ldc + tl.n0;
+  const bool full = tl.m_rows == 256 && tl.n_cols == 256;
+  const int lrow = wm * WM + 4 * (lane >> 5), lcol = wn * WN + (lane & 31);
+  int off = lrow * ldc + lcol;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int rr = i * 32 + 8 * (e >> 2) + (e & 3);
+      asm volatile("" : "+v"(off));
+      float* row = cbase + off;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        if (full || (lrow + rr < tl.m_rows && lcol + j * 32 < tl.n_cols))
+          store_c<KIND>(row + j * 32, acc[i][j][e]);
+      off += ((e & 3) == 3 ? 5 : 1) * ldc;
+    }
 }
 
 template <int BM, int BN, int B_NK, int KIND>
@@ -375,6 +421,22 @@ __device__ inline rsrc_words rsrc_raw(const void* base, uint32_t bytes) {
   return d;
 }
 
+// 16 bytes per lane from global memory straight into LDS at m0 + 16 * lane.
+// Every scalar operand goes through readfirstlane: under register pressure the
+// compiler may hold a uniform value in a vector register, and the instruction
+// takes scalar registers only (and no literal offset).
+__device__ inline void load_lds16_m0(rsrc_words r, uint32_t m0, uint32_t voff, uint32_t soff) {
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  const uint32_t ms = __builtin_amdgcn_readfirstlane(m0);
+  rsrc_words rs;
+  rs.x = __builtin_amdgcn_readfirstlane(r.x);
+  rs.y = __builtin_amdgcn_readfirstlane(r.y);
+  rs.z = __builtin_amdgcn_readfirstlane(r.z);
+  rs.w = __builtin_amdgcn_readfirstlane(r.w);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(ms), "v"(voff), "s"(rs), "s"(so) : "memory", "m0");
+}
+
 // 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
 // (the LDS base goes in M0).  Written as an instruction rather than the
 // compiler builtin: the compiler cannot tell which LDS stage such a load
@@ -385,8 +447,7 @@ __device__ inline void load_lds16(rsrc_words r, const TLC_LDS void* lds, uint32_
                                   uint32_t soff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(voff), "s"(r), "s"(soff) : "memory", "m0");
+  load_lds16_m0(r, m0, voff, soff);
 }
 
 template <int B_NK, int KIND>
@@ -573,24 +634,326 @@ struct Tile8w {
       kloop(std::false_type{});
     if (!split_epilogue<NT>(p, tl, acc, s_flag)) return;
 
-    // ---- epilogue: fp32 to C, one 32-bit lane offset plus per-element
-    // constants; edge tiles masked ----
-    int lane_off = (wm * WM + 4 * (lane >> 5)) * static_cast<int>(p.ldc) + wn * WN + (lane & 31);
-    asm volatile("" : "+v"(lane_off));
-    float* cbase = p.c + static_cast<int64_t>(tl.m0) * p.ldc + tl.n0;
-    const bool full = tl.m_rows == BM && tl.n_cols == BN;
-    const int lrow = wm * WM + 4 * (lane >> 5), lcol = wn * WN + (lane & 31);
+    store_tile<KIND, WM, WN, FM, FN>(p, tl, acc, wm, wn, lane);
+    notify_dests<KIND>(p, tl);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// 256 x 256 core, 4 wavefronts (2 x 2), 128 x 128 per wavefront: one
+// wavefront per SIMD with its 256 accumulators in the accumulation registers.
+// Against the 8-wavefront core it reads a third fewer LDS bytes per MFMA
+// (each fragment read feeds four MFMAs instead of two or four) and leaves
+// part of every SIMD's register file free, so that a copy kernel on another
+// stream can run beside it on the same compute unit.  Same LDS layout, same
+// loads, same K-step pipeline.
+// ---------------------------------------------------------------------------
+template <int B_NK, int KIND>
+struct Tile4w {
+  static constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4, NT = 256;
+  __device__ static int swz(int row) { return (row >> 1) & 7; }
+
+  __device__ static void run(const GemmParams& p, const tlc_tile& tl, TLC_LDS u32x4* A0,
+                             TLC_LDS u32x4* A1, TLC_LDS u32x4* B0, TLC_LDS u32x4* B1,
+                             int* s_flag) {
+    // the thread index is made opaque per tile, so that the lane-dependent
+    // offsets below are formed per tile instead of being kept (and spilled)
+    // across the whole persistent loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t lda2 = static_cast<uint32_t>(p.lda) * 2, ldb2 = static_cast<uint32_t>(p.ldb) * 2;
+
+    // ---- global sources of the 8 A blocks and 8 B blocks (1 KB each) this
+    // wave fills per stage; rows outside the tile are clamped into it ----
+    rsrc_words ra;
+    uint32_t a_off[8];
+    if (KIND == KIND_MOE) {
+      ra = rsrc_raw(p.a, static_cast<uint32_t>(p.a_rows) * lda2);
+    } else {
+      ra = rsrc_raw(p.a + static_cast<int64_t>(tl.m0) * p.lda, static_cast<uint32_t>(tl.m_rows) * lda2);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      int row = (wave * 8 + q) * 8 + (lane >> 3);
+      const int kc = (lane & 7) ^ swz(row);
+      row = row < tl.m_rows ? row : tl.m_rows - 1;
+      const uint32_t src_row = KIND == KIND_MOE ? static_cast<uint32_t>(p.row_token[tl.m0 + row])
+                                                 : static_cast<uint32_t>(row);
+      a_off[q] = src_row * lda2 + kc * 16;
+    }
+    const uint16_t* bexp = p.b + (KIND == KIND_MOE ? tl.expert * p.b_expert_stride : 0);
+    rsrc_words rb;
+    uint32_t b_off[8];
+    if constexpr (B_NK) {
+      rb = rsrc_raw(bexp + static_cast<int64_t>(tl.n0) * p.ldb, static_cast<uint32_t>(tl.n_cols) * ldb2);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        int row = (wave * 8 + q) * 8 + (lane >> 3);
+        const int kc = (lane & 7) ^ swz(row);
+        row = row < tl.n_cols ? row : tl.n_cols - 1;
+        b_off[q] = row * ldb2 + kc * 16;
+      }
+    } else {
+      rb = rsrc_raw(bexp + tl.n0, static_cast<uint32_t>(p.K) * ldb2);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int k = (wave * 8 + q) * 2 + (lane >> 5);
+        int n = ((lane & 31) ^ (2 * (k & 15))) * 8;
+        n = n < tl.n_cols ? n : tl.n_cols - 8;
+        b_off[q] = k * ldb2 + n * 2;
+      }
+    }
+    const uint32_t b_step = B_NK ? 128u : 64u * ldb2;
+    auto issue = [&](int kt, TLC_LDS u32x4* As, TLC_LDS u32x4* Bs) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        load_lds16(ra, (const TLC_LDS void*)(As + (wave * 8 + q) * 64), a_off[q], kt * 128u);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        load_lds16(rb, (const TLC_LDS void*)(Bs + (wave * 8 + q) * 64), b_off[q], kt * b_step);
+    };
+
+    f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    const int h = lane >> 5;
+    const int s_lane = swz(lane & 31);
+    bf16x8 fa[2][FM], fb[2][FN];
+    // Rows of the unit this wave computes: 32-row blocks i < fm_act hold rows
+    // below m_rows.  In a tile with fewer rows (the ragged last m-tile of an
+    // expert, or of M) a wave skips the fragment reads and MFMAs of its empty
+    // blocks -- a wave with no rows only loads and meets the barriers -- in a
+    // second copy of the K loop, so the loop of a full tile is unchanged.  The
+    // stored rows' results do not change.
+    int kt0, kt1;
+    unit_k_range(tl.split, p.K / 64, &kt0, &kt1);
+    const int nk = kt1 - kt0;
+    const int rows_left = tl.m_rows - __builtin_amdgcn_readfirstlane(wm) * WM;
+    const int fm_act = rows_left <= 0 ? 0 : (rows_left >= FM * 32 ? FM : (rows_left + 31) >> 5);
+    // One BK = 64 step on stage (Ac, Bc), whose first fragments are already in
+    // registers: the fragments of sub-step ks+1 are requested before the MFMAs
+    // of sub-step ks (the scheduling barriers keep that order).  Before the
+    // last sub-step's MFMAs -- their fragments are in registers -- the wave
+    // waits for its LDS reads and its loads of the next stage, and the
+    // workgroup barrier makes the next stage whole and this one free; under
+    // those MFMAs go the next stage's first fragment reads and the loads of
+    // the step after next into this stage.
+    auto kloop = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      auto fread = [&](const TLC_LDS u32x4* As, const TLC_LDS u32x4* Bs, int ks, int slot) {
+        const int phys = (ks * 2 + h) ^ s_lane;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int rr = i * 32 + 8 * (e >> 2) + (e & 3);
-          const int cc = j * 32;
-          if (full || (lrow + rr < tl.m_rows && lcol + cc < tl.n_cols))
-            store_c<KIND>(cbase + lane_off + rr * static_cast<int>(p.ldc) + cc, acc[i][j][e]);
+        for (int i = 0; i < FM; ++i) {
+          if (!FULL && i >= fm_act) continue;
+          fa[slot][i] = __builtin_bit_cast(
+              bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)As +
+                                              (wm * WM + i * 32 + (lane & 31)) * 128 + phys * 16));
         }
+        if (!FULL && fm_act == 0) return;
+        if constexpr (B_NK) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            fb[slot][j] = __builtin_bit_cast(
+                bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)Bs +
+                                                (wn * WN + j * 32 + (lane & 31)) * 128 + phys * 16));
+        } else {
+          // Lane l needs B[k = 16 ks + 8 (l / 32) + t][n] for t = 0..7 (n = l % 32 of the block):
+          // two transposing reads, each giving 4 consecutive k of one column.
+          const int g = lane >> 4, i16 = lane & 15;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            v4i16 hv[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int k = ks * 16 + 8 * (g >> 1) + 4 * hh + (i16 >> 2);
+              const int n = wn * WN + j * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+              const int pc = (n >> 3) ^ (2 * (k & 15));
+              hv[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (TLC_LDS v4i16*)((const TLC_LDS char*)Bs + k * 512 + pc * 16 + (n & 7) * 2));
+            }
+            const v8i16 v = {hv[0][0], hv[0][1], hv[0][2], hv[0][3], hv[1][0], hv[1][1], hv[1][2], hv[1][3]};
+            fb[slot][j] = __builtin_bit_cast(bf16x8, v);
+          }
+        }
+      };
+      auto mfmas = [&](int sl) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          if (!FULL && i >= fm_act) continue;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0);
+        }
+      };
+      auto step = [&](int i, const TLC_LDS u32x4* Ac, const TLC_LDS u32x4* Bc, TLC_LDS u32x4* Aw,
+                      TLC_LDS u32x4* Bw, const TLC_LDS u32x4* An, const TLC_LDS u32x4* Bn) {
+#pragma unroll
+        for (int ks = 0; ks < 3; ++ks) {
+          fread(Ac, Bc, ks + 1, (ks + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          mfmas(ks & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < nk) fread(An, Bn, 0, 0);
+        if (i + 2 < nk) issue(kt0 + i + 2, Aw, Bw);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(1);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      if (nk > 0) {
+        issue(kt0, A0, B0);
+        if (nk > 1) {
+          issue(kt0 + 1, A1, B1);
+          asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // stage 0's sixteen loads done
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        fread(A0, B0, 0, 0);
+        for (int i = 0; i < nk; i += 2) {
+          step(i, A0, B0, A0, B0, A1, B1);
+          if (i + 1 < nk) step(i + 1, A1, B1, A1, B1, A0, B0);
+        }
+      } else {
+        __syncthreads();
+      }
+    };
+    // Full tiles: the K loop with the place of every instruction fixed.  One
+    // wavefront per SIMD has no second wavefront to fill its gaps, so the
+    // other instructions are threaded between the MFMAs (each keeps the MFMA
+    // pipe busy for 32 cycles): during sub-step ks the fragment reads of
+    // sub-step ks+1 follow the first MFMAs one by one, in the order their
+    // MFMAs need them.  Before the last sub-step the wave waits for its reads
+    // and for its loads of the next stage and meets the barrier; the first
+    // instruction after it is an MFMA, and the next stage's first fragment
+    // reads and the sixteen loads of the step after next into this stage are
+    // threaded through the last sub-step's MFMAs.
+    constexpr int NRB = B_NK ? FN : 2 * FN;  // B reads per sub-step
+    constexpr int NR = FM + NRB;             // fragment reads per sub-step
+    v4i16 fbh[2][FN][2];                     // K x N weight: fragment halves
+    const uint32_t wave_s = __builtin_amdgcn_readfirstlane(wave);
+    // read R of sub-step ks from stage (As, Bs) into slot SL; reads in the
+    // order of first use: A block 0, the B fragments, then A blocks 1..3
+    auto read_one = [&](const TLC_LDS u32x4* As, const TLC_LDS u32x4* Bs, int ks, auto sl_c,
+                        auto r_c) __attribute__((always_inline)) {
+      constexpr int SL = decltype(sl_c)::value, R = decltype(r_c)::value;
+      constexpr int AI = R == 0 ? 0 : (R <= NRB ? -1 : R - NRB);
+      constexpr int BJ = R == 0 || R > NRB ? -1 : (B_NK ? R - 1 : (R - 1) >> 1);
+      constexpr int HH = B_NK ? 0 : (R - 1) & 1;
+      const int phys = (ks * 2 + h) ^ s_lane;
+      if constexpr (AI >= 0) {
+        fa[SL][AI] = __builtin_bit_cast(
+            bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)As +
+                                            (wm * WM + AI * 32 + (lane & 31)) * 128 + phys * 16));
+      } else if constexpr (B_NK) {
+        fb[SL][BJ] = __builtin_bit_cast(
+            bf16x8, *(const TLC_LDS u32x4*)((const TLC_LDS char*)Bs +
+                                            (wn * WN + BJ * 32 + (lane & 31)) * 128 + phys * 16));
+      } else {
+        const int g = lane >> 4, i16 = lane & 15;
+        const int k = ks * 16 + 8 * (g >> 1) + 4 * HH + (i16 >> 2);
+        const int n = wn * WN + BJ * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+        const int pc = (n >> 3) ^ (2 * (k & 15));
+        fbh[SL][BJ][HH] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (TLC_LDS v4i16*)((const TLC_LDS char*)Bs + k * 512 + pc * 16 + (n & 7) * 2));
+      }
+    };
+    // MFMA M of a sub-step on slot SL: row block M / FN, column block M % FN
+    auto mfma_one = [&](auto sl_c, auto m_c) __attribute__((always_inline)) {
+      constexpr int SL = decltype(sl_c)::value, M = decltype(m_c)::value;
+      constexpr int I = M / FN, J = M % FN;
+      bf16x8 bv;
+      if constexpr (B_NK) {
+        bv = fb[SL][J];
+      } else {
+        const v8i16 v = {fbh[SL][J][0][0], fbh[SL][J][0][1], fbh[SL][J][0][2], fbh[SL][J][0][3],
+                         fbh[SL][J][1][0], fbh[SL][J][1][1], fbh[SL][J][1][2], fbh[SL][J][1][3]};
+        bv = __builtin_bit_cast(bf16x8, v);
+      }
+      acc[I][J] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SL][I], bv, acc[I][J], 0, 0, 0);
+    };
+    // load Q of the sixteen that fill stage (As, Bs) with K step kt
+    auto load_one = [&](int kt, TLC_LDS u32x4* As, TLC_LDS u32x4* Bs, auto q_c)
+        __attribute__((always_inline)) {
+      constexpr int Q = decltype(q_c)::value;
+      if constexpr (Q < 8)
+        load_lds16_m0(ra, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(As)) + (wave_s * 8 + Q) * 1024,
+                      a_off[Q], kt * 128u);
+      else
+        load_lds16_m0(rb, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(Bs)) + (wave_s * 8 + Q - 8) * 1024,
+                      b_off[Q - 8], kt * b_step);
+    };
+    // one K step on stage (Ac, Bc): reads the next stage (An, Bn) at its end
+    // and loads the step after next into this stage
+    auto fstep = [&](int i, TLC_LDS u32x4* Ac, TLC_LDS u32x4* Bc, const TLC_LDS u32x4* An,
+                     const TLC_LDS u32x4* Bn) __attribute__((always_inline)) {
+      static_for<3>([&](auto ks_c) __attribute__((always_inline)) {
+        constexpr int KS = decltype(ks_c)::value;
+        static_for<FM * FN>([&](auto m_c) __attribute__((always_inline)) {
+          constexpr int M = decltype(m_c)::value;
+          mfma_one(std::integral_constant<int, KS & 1>{}, m_c);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (M < NR) {
+            read_one(Ac, Bc, KS + 1, std::integral_constant<int, (KS + 1) & 1>{}, m_c);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        });
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<FM * FN>([&](auto m_c) __attribute__((always_inline)) {
+        constexpr int M = decltype(m_c)::value;
+        mfma_one(std::integral_constant<int, 1>{}, m_c);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (M < NR) {
+          read_one(An, Bn, 0, std::integral_constant<int, 0>{}, m_c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        load_one(kt0 + i + 2, Ac, Bc, m_c);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // Every step reads the next stage and loads the step after next, also the
+    // last two: their loads fall past the unit's K range (the next row, or
+    // zeros past the end of the operand, which a buffer load returns) into a
+    // stage nobody reads any more, and they complete before the next unit's
+    // loads, vector memory operations completing in order.  An even number of
+    // steps keeps the loop body one pair of steps.
+    auto fast_loop = [&]() __attribute__((always_inline)) {
+      static_assert(FM * FN == 16, "sixteen MFMAs and sixteen loads per sub-step");
+      static_for<16>([&](auto q_c) __attribute__((always_inline)) { load_one(kt0, A0, B0, q_c); });
+      static_for<16>([&](auto q_c) __attribute__((always_inline)) { load_one(kt0 + 1, A1, B1, q_c); });
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // stage 0's sixteen loads done
+      __syncthreads();
+      static_for<NR>([&](auto r_c) __attribute__((always_inline)) {
+        read_one(A0, B0, 0, std::integral_constant<int, 0>{}, r_c);
+      });
+      for (int i = 0; i < nk; i += 2) {
+        fstep(i, A0, B0, A1, B1);
+        fstep(i + 1, A1, B1, A0, B0);
+      }
+    };
+    // the same loop for every wavefront of the workgroup: the fast loop's
+    // barriers and LDS layout differ from the other loop's
+    if (tl.m_rows >= BM && nk > 0 && (nk & 1) == 0)
+      fast_loop();
+    else if (fm_act == FM)
+      kloop(std::true_type{});
+    else
+      kloop(std::false_type{});
+    if (!split_epilogue<NT>(p, tl, acc, s_flag)) return;
+
+    store_tile<KIND, WM, WN, FM, FN>(p, tl, acc, wm, wn, lane);
     notify_dests<KIND>(p, tl);
   }
 };
@@ -712,6 +1075,19 @@ __global__ __launch_bounds__(512) void gemm_kernel_8w(GemmParams p) {
   });
 }
 
+template <int B_NK, int KIND, int WAIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel_4w(
+    GemmParams p) {
+  __shared__ u32x4 A0[2048], A1[2048], B0[2048], B1[2048];
+  __shared__ LoopShared sh;
+  tile_loop<256, 256, KIND, WAIT>(p, &sh, [&](const tlc_tile& tl, int* s_flag) {
+    Tile4w<B_NK, KIND>::run(p, tl, (TLC_LDS u32x4*)A0, (TLC_LDS u32x4*)A1, (TLC_LDS u32x4*)B0,
+                            (TLC_LDS u32x4*)B1, s_flag);
+  });
+  // the last unit's loads past its K range land before the wave ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <int BM, int BN, int B_NK, int KIND, int WAIT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
   __shared__ u32x4 lds[2 * (BM + BN) * 8];
@@ -723,9 +1099,18 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
 
 template <int BM, int BN, int B_NK, int KIND, int WAIT>
 void launch_kernel(const GemmParams& p, int grid, void* stream) {
-  if constexpr (BM == 256 && BN == 256)
-    hipLaunchKernelGGL((gemm_kernel_8w<B_NK, KIND, WAIT>), dim3(grid), dim3(512), 0,
-                       static_cast<hipStream_t>(stream), p);
+  // 256 x 256 tiles: the 4-wavefront core for whole-matrix GEMMs (3-5 %
+  // faster than the 8-wavefront one on their shapes), the 8-wavefront core
+  // for the grouped GEMM, whose ragged last tile of every expert the
+  // 4-wavefront core runs in its slower general loop
+  if constexpr (BM == 256 && BN == 256) {
+    if constexpr (KIND == KIND_MOE)
+      hipLaunchKernelGGL((gemm_kernel_8w<B_NK, KIND, WAIT>), dim3(grid), dim3(512), 0,
+                         static_cast<hipStream_t>(stream), p);
+    else
+      hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT>), dim3(grid), dim3(256), 0,
+                         static_cast<hipStream_t>(stream), p);
+  }
   else
     hipLaunchKernelGGL((gemm_kernel<BM, BN, B_NK, KIND, WAIT>), dim3(grid), dim3(THREADS), 0,
                        static_cast<hipStream_t>(stream), p);
