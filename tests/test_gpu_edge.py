@@ -153,3 +153,27 @@ def test_moe_tile_count_beyond_plan_capacity_reported():
     assert st[0] == tlc.ERR_BAD_PLAN and st[1] == n, st
     assert bool((prob.y == 7.0).all().item())
     prob.sig.clear_status(prob.streams.compute)
+
+
+@pytest.mark.parametrize("layout", [0, 1], ids=["KN", "NK"])
+def test_whole_tiles_even_and_odd_k_steps(layout):
+    """Whole 256 x 256 tiles go to the kernel with only the fixed-order loop
+    when the number of 64-wide K steps is even (K = 384, 5120) and to the
+    general loop when it is odd (K = 320, 448); integer inputs bit for bit,
+    every landing that waits."""
+    bl = tlc.B_KN if layout == 0 else tlc.B_NK
+    for K in (320, 384, 448):
+        inp = si.ag_inputs(170 + K, 2, 256, 264, K, integer=True)
+        ref = og.ag_gemm(inp.a_chunks, inp.b)
+        for land in (tlc.LAND_NONE, tlc.LAND_MEMCPY, tlc.LAND_COLOCATED):
+            log(f"[edge] whole tiles K={K} layout={layout} land={land}")
+            prob = AGProblem(inp.a_chunks, inp.b, 1, 256, 256, bl, schedule=tlc.SCHED_STATIC)
+            if land == tlc.LAND_NONE:
+                prob.place_all()
+            else:
+                prob.poison_remote()
+            prob.c.fill_(float("nan"))
+            prob.run(land)
+            torch.cuda.synchronize()
+            assert prob.sig.read_status()[0] == 0
+            check_exact(prob.c.cpu().numpy(), ref, f"whole tiles K={K}")

@@ -648,7 +648,7 @@ struct Tile8w {
 // stream can run beside it on the same compute unit.  Same LDS layout, same
 // loads, same K-step pipeline.
 // ---------------------------------------------------------------------------
-template <int B_NK, int KIND>
+template <int B_NK, int KIND, int FAST>
 struct Tile4w {
   static constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4, NT = 256;
   __device__ static int swz(int row) { return (row >> 1) & 7; }
@@ -944,14 +944,24 @@ struct Tile4w {
       }
     };
     // the same loop for every wavefront of the workgroup: the fast loop's
-    // barriers and LDS layout differ from the other loop's
-    if (tl.m_rows >= BM && nk > 0 && (nk & 1) == 0)
+    // barriers and LDS layout differ from the other loop's.  The FAST kernel
+    // has only the fast loop: the host picks it when every unit is a whole
+    // tile with an even number of K steps and no unit is split.
+    if constexpr (FAST) {
       fast_loop();
-    else if (fm_act == FM)
-      kloop(std::true_type{});
-    else
-      kloop(std::false_type{});
-    if (!split_epilogue<NT>(p, tl, acc, s_flag)) return;
+    } else {
+      if (tl.m_rows >= BM && nk > 0 && (nk & 1) == 0)
+        fast_loop();
+      else if (fm_act == FM)
+        kloop(std::true_type{});
+      else
+        kloop(std::false_type{});
+    }
+    if constexpr (!FAST) {
+      if (!split_epilogue<NT>(p, tl, acc, s_flag)) return;
+    } else {
+      (void)s_flag;
+    }
 
     store_tile<KIND, WM, WN, FM, FN>(p, tl, acc, wm, wn, lane);
     notify_dests<KIND>(p, tl);
@@ -1075,14 +1085,14 @@ __global__ __launch_bounds__(512) void gemm_kernel_8w(GemmParams p) {
   });
 }
 
-template <int B_NK, int KIND, int WAIT>
+template <int B_NK, int KIND, int WAIT, int FAST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel_4w(
     GemmParams p) {
   __shared__ u32x4 A0[2048], A1[2048], B0[2048], B1[2048];
   __shared__ LoopShared sh;
   tile_loop<256, 256, KIND, WAIT>(p, &sh, [&](const tlc_tile& tl, int* s_flag) {
-    Tile4w<B_NK, KIND>::run(p, tl, (TLC_LDS u32x4*)A0, (TLC_LDS u32x4*)A1, (TLC_LDS u32x4*)B0,
-                            (TLC_LDS u32x4*)B1, s_flag);
+    Tile4w<B_NK, KIND, FAST>::run(p, tl, (TLC_LDS u32x4*)A0, (TLC_LDS u32x4*)A1,
+                                  (TLC_LDS u32x4*)B0, (TLC_LDS u32x4*)B1, s_flag);
   });
   // the last unit's loads past its K range land before the wave ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1107,8 +1117,11 @@ void launch_kernel(const GemmParams& p, int grid, void* stream) {
     if constexpr (KIND == KIND_MOE)
       hipLaunchKernelGGL((gemm_kernel_8w<B_NK, KIND, WAIT>), dim3(grid), dim3(512), 0,
                          static_cast<hipStream_t>(stream), p);
+    else if (p.fast)
+      hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 1>), dim3(grid), dim3(256), 0,
+                         static_cast<hipStream_t>(stream), p);
     else
-      hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT>), dim3(grid), dim3(256), 0,
+      hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 0>), dim3(grid), dim3(256), 0,
                          static_cast<hipStream_t>(stream), p);
   }
   else
@@ -1147,8 +1160,16 @@ tlc_status launch_shape(const GemmParams& p, int b_layout, int kind, int grid, v
 
 }  // namespace
 
-tlc_status launch_gemm(const GemmParams& p, int bm, int bn, int b_layout, int kind, int grid,
+tlc_status launch_gemm(const GemmParams& p_in, int bm, int bn, int b_layout, int kind, int grid,
                        void* stream) {
+  GemmParams p = p_in;
+  // The kernel with only the fixed-order loop (and no split epilogue), for
+  // plans whose units are all whole 256-row tiles with an even number of
+  // K steps: M a multiple of 256, K / 64 even, no split workspace (a split
+  // unit without one is reported as a bad plan).  It keeps a third of the
+  // register file free, so that other kernels' wavefronts (a side stream's
+  // copies) can run beside it on the same compute units.
+  p.fast = kind != KIND_MOE && p.M % 256 == 0 && (p.K / 64) % 2 == 0 && p.split_bytes == 0;
   if (bm == 256 && bn == 256) return launch_shape<256, 256>(p, b_layout, kind, grid, stream);
   if (bm == 128 && bn == 128) return launch_shape<128, 128>(p, b_layout, kind, grid, stream);
   return fail(TLC_ERR_UNSUPPORTED, "tile %dx%d not built (256x256, 128x128)", bm, bn);

@@ -70,6 +70,9 @@ struct GemmParams {
   int32_t rows_per_chunk;
   uint32_t notify_mask;
   uint32_t dest_total;
+  // set by launch_gemm: every unit is a whole tile with an even number of K
+  // steps and none is split (the kernel with only the fast loop)
+  int32_t fast;
 };
 
 // Bytes of one split tile's workspace block (counter header + split_k partials).
