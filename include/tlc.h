@@ -486,6 +486,22 @@ int64_t tlc_moe_plan_capacity(int32_t T, int32_t topk, int32_t experts, int32_t 
 int64_t tlc_moe_workspace_bytes(int32_t T, int32_t topk, int32_t experts, int32_t bm);
 tlc_status tlc_moe_route(const tlc_moe_route_args* args, void* stream);
 
+/* tlc_moe_route for callers that cannot allocate memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Identical
+ * results; args->workspace is ignored (may be NULL) and the routing's
+ * workspace is instead a static array in each device's memory, of
+ * tlc_moe_static_workspace_bytes() bytes (4 MiB), which every call on that
+ * device shares and which stays allocated until the process ends.  Nothing
+ * is allocated: no hipMalloc, hipFree or allocating library call.  A problem
+ * whose tlc_moe_workspace_bytes(...) exceeds the array is refused with
+ * TLC_ERR_CAPACITY before anything is enqueued (e.g. T = 4096, k = 8,
+ * E = 64, bm = 256 needs about 51 KB).  The workspace needs no
+ * initialisation, and each call leaves the last call's contents in it.
+ * Calls that overlap in time on one device (on different streams, or from
+ * different threads) race on the array; the caller orders them. */
+tlc_status tlc_moe_route_static(const tlc_moe_route_args* args, void* stream);
+int64_t tlc_moe_static_workspace_bytes(void);
+
 /* Y[(T*k) x N] (f32): Y[i] = X[row_token[i]] (bf16, 1 x H) @ W_e (bf16, H x N)
  * for the expert e whose row segment holds i.  X is the gathered token matrix
  * (T x H, chunk c = rows [c Tc, (c+1) Tc)); chunks land as in tlc_ag_gemm.

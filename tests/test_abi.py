@@ -260,3 +260,20 @@ def test_ag_moe_grid_and_topk_errors():
         a = args(**over)
         assert tlc.lib().tlc_ag_moe(C.byref(a), None, streams, 1) == want, (over, tlc.last_error())
         assert text in tlc.last_error(), tlc.last_error()
+
+
+def test_moe_route_static_refuses_oversize_on_the_host():
+    """The routing variant without allocation refuses a problem whose workspace
+    exceeds its static array, before any device call."""
+    assert tlc.moe_static_workspace_bytes() == 4 << 20
+    T, E, k = 1 << 20, 64, 16
+    need = tlc.moe_workspace_bytes(T, k, E, 128)
+    assert need > tlc.moe_static_workspace_bytes()
+    a = tlc.MoERouteArgs(logits=16, tokens_per_chunk=T // 8, world=8, rank=0, experts=E, topk=k,
+                         N=128, bm=128, bn=128, order=1, topk_idx=16, gates=16, counts=16,
+                         offsets=16, row_token=16, slot=16, plan=16,
+                         plan_cap=tlc.moe_plan_capacity(T, k, E, 128, 128, 128), n_tiles_dev=16,
+                         workspace=None, x=None, x_src=None, H=64, sig=None, epoch=1)
+    assert tlc.lib().tlc_moe_route_static(C.byref(a), None) == tlc.ERR_CAPACITY
+    assert "static one holds" in tlc.last_error(), tlc.last_error()
+    assert tlc.lib().tlc_moe_route_static(None, None) == tlc.ERR_INVALID_ARG

@@ -726,8 +726,10 @@ int64_t tlc_moe_workspace_bytes(int32_t T, int32_t topk, int32_t experts, int32_
          up((T + 63) / 64 * static_cast<int64_t>(experts) * 4);
 }
 
-tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
-  if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: NULL args");
+}  // extern "C"
+
+// The routing with its workspace at `workspace` (caller's, or the static one).
+static tlc_status moe_route_impl(const tlc_moe_route_args* a, void* workspace, void* stream) {
   if (a->world < 1 || a->world > TLC_MAX_WORLD || a->rank < 0 || a->rank >= a->world)
     return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: world/rank");
   if (a->experts < 1 || a->experts > 64 || a->topk < 1 || a->topk > a->experts || a->topk > 16)
@@ -741,13 +743,13 @@ tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
   if (a->order != TLC_ORDER_NATURAL && a->order != TLC_ORDER_RANK_OFFSET)
     return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: order");
   if (!a->logits || !a->topk_idx || !a->gates || !a->counts || !a->offsets || !a->row_token ||
-      !a->slot || !a->plan || !a->n_tiles_dev || !a->workspace)
+      !a->slot || !a->plan || !a->n_tiles_dev || !workspace)
     return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: NULL array");
   const int64_t cap = tlc_moe_plan_capacity(static_cast<int32_t>(T), a->topk, a->experts, a->N, a->bm, a->bn);
   if (a->plan_cap < cap)
     return fail(TLC_ERR_CAPACITY, "tlc_moe_route: plan_cap %lld < %lld", static_cast<long long>(a->plan_cap),
                 static_cast<long long>(cap));
-  if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0)
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(TLC_ERR_MISALIGNED, "tlc_moe_route: workspace not 256-byte aligned");
   // optional co-located landing of the token chunks by the top-k kernel
   void* dst[TLC_MAX_WORLD];
@@ -799,7 +801,7 @@ tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
   d.plan = a->plan;
   d.n_tiles = a->n_tiles_dev;
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  char* ws = static_cast<char*>(a->workspace);
+  char* ws = static_cast<char*>(workspace);
   d.member = reinterpret_cast<unsigned long long*>(ws);
   ws += up(T * 8);
   d.pstart = reinterpret_cast<int32_t*>(ws);
@@ -815,6 +817,33 @@ tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
   st = launch_moe_route(d, stream);
   return st ? st : ok();
 }
+
+extern "C" {
+
+tlc_status tlc_moe_route(const tlc_moe_route_args* a, void* stream) {
+  if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route: NULL args");
+  return moe_route_impl(a, a->workspace, stream);
+}
+
+tlc_status tlc_moe_route_static(const tlc_moe_route_args* a, void* stream) {
+  if (!a) return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route_static: NULL args");
+  if (a->world < 1 || a->world > TLC_MAX_WORLD || a->tokens_per_chunk < 1 || a->topk < 1 ||
+      a->experts < 1 || a->bm < 1)
+    return fail(TLC_ERR_INVALID_ARG, "tlc_moe_route_static: sizes must be >= 1");
+  const int64_t T = static_cast<int64_t>(a->world) * a->tokens_per_chunk;
+  if (T > (1 << 20)) return fail(TLC_ERR_UNSUPPORTED, "tlc_moe_route_static: T > 2^20");
+  const int64_t need = tlc_moe_workspace_bytes(static_cast<int32_t>(T), a->topk, a->experts, a->bm);
+  if (need > kMoeStaticScratchBytes)
+    return fail(TLC_ERR_CAPACITY, "tlc_moe_route_static: the routing needs %lld bytes of workspace, "
+                "the static one holds %lld (use tlc_moe_route with a workspace)",
+                static_cast<long long>(need), static_cast<long long>(kMoeStaticScratchBytes));
+  void* ws = nullptr;
+  tlc_status st = moe_static_scratch(&ws);
+  if (st) return st;
+  return moe_route_impl(a, ws, stream);
+}
+
+int64_t tlc_moe_static_workspace_bytes(void) { return kMoeStaticScratchBytes; }
 
 tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* copy_streams,
                       int32_t n_copy_streams) {

@@ -33,6 +33,8 @@
 //                   batches of pairs), expanded over the n-tiles.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "colocated_copy.h"
 #include "tlc_internal.h"
 
@@ -354,6 +356,34 @@ tlc_status launch_moe_route(const MoeDev& d, void* stream) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TLC_ERR_HIP, "moe route launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Workspace of the routing variant that allocates nothing (tlc_moe_route_static):
+// one array in every device's memory, kept until the process ends.  In host
+// code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) char scratch[kMoeStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+}  // namespace
+
+tlc_status moe_static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TLC_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(TLC_ERR_UNSUPPORTED, "device id %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(TLC_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TLC_OK;
 }
 
 }  // namespace tlc

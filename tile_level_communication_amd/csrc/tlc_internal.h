@@ -156,6 +156,11 @@ struct MoeDev {
 int64_t moe_max_pairs(int32_t T, int32_t topk, int32_t experts, int32_t bm);
 tlc_status launch_moe_route(const MoeDev& d, void* stream);
 
+// The static routing workspace (tlc_moe_route_static): its size, and its
+// device address on the current device (looked up once per device).
+constexpr int64_t kMoeStaticScratchBytes = int64_t{4} << 20;
+tlc_status moe_static_scratch(void** out);
+
 // Default persistent grid: the fewest rounds of tiles over the CUs, with the
 // tiles spread evenly over that many rounds (rounded up to a multiple of 8).
 int default_grid(int64_t n_tiles, int cus);

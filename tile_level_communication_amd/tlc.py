@@ -32,7 +32,8 @@ EXPORTS = [
     "tlc_signals_clear_status", "tlc_read_status", "tlc_ag_gemm", "tlc_gemm_rs", "tlc_rs_reduce",
     "tlc_moe_plan_capacity", "tlc_moe_workspace_bytes", "tlc_moe_route", "tlc_ag_moe", "tlc_land",
     "tlc_status_string", "tlc_last_error", "tlc_version", "tlc_split_workspace_bytes", "tlc_gemm_ar",
-    "tlc_wall_clock_khz", "tlc_read_signals", "tlc_signals_rewind",
+    "tlc_wall_clock_khz", "tlc_read_signals", "tlc_signals_rewind", "tlc_moe_route_static",
+    "tlc_moe_static_workspace_bytes",
 ]
 
 
@@ -160,6 +161,10 @@ def lib() -> C.CDLL:
         L.tlc_moe_workspace_bytes.restype = C.c_int64
         L.tlc_moe_route.argtypes = [C.POINTER(MoERouteArgs), vp]
         L.tlc_moe_route.restype = st
+        L.tlc_moe_route_static.argtypes = [C.POINTER(MoERouteArgs), vp]
+        L.tlc_moe_route_static.restype = st
+        L.tlc_moe_static_workspace_bytes.argtypes = []
+        L.tlc_moe_static_workspace_bytes.restype = C.c_int64
         L.tlc_ag_moe.argtypes = [C.POINTER(MoEArgs), vp, C.POINTER(vp), C.c_int32]
         L.tlc_ag_moe.restype = st
         L.tlc_land.argtypes = [C.POINTER(vp), C.POINTER(vp), C.c_int64, C.c_int32, C.c_int32, vp,
@@ -400,6 +405,25 @@ def moe_route(logits, tokens_per_chunk, world, rank, experts, topk, N, bm, bn, o
                         _ptr(workspace), _ptr(x) if x is not None else None, src, H,
                         sig.ptr if sig is not None else None, epoch)
     _check(lib().tlc_moe_route(C.byref(args), _stream(stream)), "tlc_moe_route")
+
+
+def moe_route_static(logits, tokens_per_chunk, world, rank, experts, topk, N, bm, bn, order,
+                     topk_idx, gates, counts, offsets, row_token, slot, plan, plan_cap,
+                     n_tiles_dev, stream=None, x=None, x_src=None, H=0, sig: "Signals" = None,
+                     epoch=0):
+    """tlc_moe_route_static: tlc_moe_route with the library's static workspace
+    (allocates nothing)."""
+    src = _ptr_array(x_src, world) if x_src is not None else None
+    args = MoERouteArgs(_ptr(logits), tokens_per_chunk, world, rank, experts, topk, N, bm, bn,
+                        order, _ptr(topk_idx), _ptr(gates), _ptr(counts), _ptr(offsets),
+                        _ptr(row_token), _ptr(slot), _ptr(plan), plan_cap, _ptr(n_tiles_dev),
+                        None, _ptr(x) if x is not None else None, src, H,
+                        sig.ptr if sig is not None else None, epoch)
+    _check(lib().tlc_moe_route_static(C.byref(args), _stream(stream)), "tlc_moe_route_static")
+
+
+def moe_static_workspace_bytes() -> int:
+    return int(lib().tlc_moe_static_workspace_bytes())
 
 
 def ag_moe(plan, n_tiles_dev, plan_cap, row_token, tokens_per_chunk, world, rank, experts, topk, H,
