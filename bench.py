@@ -49,11 +49,11 @@ PEAK_HBM_GBS = 8000.0
 # WRITE_SCALE.  None where the kernel changed since the counters were taken.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE) or None
-    "ag": {"gemm": None},
+    "ag": {"gemm": (222444.6, 102404.9)},
     "moe": {"gemm": (266866.2, 99328.0)},
     "rs": {"gemm": None, "reduce": (32795.8, 16423.9)},
     "ar": {"gemm": None, "reduce": (32795.8, 16423.9)},
-    "rs_long": {"gemm": None, "reduce": (1310750.4, 327680.1)},
+    "rs_long": {"gemm": (3154005.4, 2621440.0), "reduce": (1310743.8, 327680.0)},
 }
 
 
@@ -65,7 +65,7 @@ def traffic_bytes(workload, kernel):
     return round((f * FETCH_SCALE + w * WRITE_SCALE) * 1024)
 
 
-WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4, "ar": 1}
+WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4, "ar": 1, "fetch_calibration": None}
 LANDINGS = {"memcpy": 3, "copy_engine": 1, "cu": 2, "colocated": 4}  # tlc.LAND_*
 ORDERS = {"natural": 0, "rank_offset": 1}  # tlc.ORDER_*
 
@@ -92,7 +92,7 @@ def parse(argv=None):
                     help="colocated: workgroups that copy (0 = the library's default)")
     ap.add_argument("--layout", default="KN", choices=["KN", "NK"])
     ap.add_argument("--tile", type=int, default=256)
-    ap.add_argument("--group-m", type=int, default=4)
+    ap.add_argument("--group-m", type=int, default=8)
     ap.add_argument("--grid", type=int, default=0)
     ap.add_argument("--copy-streams", type=int, default=1)
     ap.add_argument("--split-k", type=int, default=None,
@@ -819,6 +819,32 @@ def run_moe(args, torch, tlc, si, workloads):
     return line
 
 
+def run_fetch_calibration(args, torch, tlc, si, workloads):
+    """Known traffic for the memory counters: one workgroup computes one 256 x
+    256 tile over K = 65536, so every byte of A (256 x K) and B (K x 256) is
+    loaded exactly once, by the GEMM's own direct-to-LDS loads, and C (256 x
+    256 fp32) is written once.  rocprofv3's FETCH_SIZE and WRITE_SIZE for these
+    launches against the bytes below give the counters' scale for this kernel."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    K, R, N = 65536, 256, 256
+    inp = si.ag_inputs(900, 1, R, N, K)
+    prob = workloads.AGProblem(inp.a_chunks, inp.b, 0, 256, 256, tlc.B_KN, device=dev,
+                               schedule=tlc.SCHED_STATIC)
+    prob.place_all()
+    s = prob.streams.compute
+    kt = KernelTimer(torch, s)
+    fn = lambda: kt(lambda: tlc.ag_gemm(prob.plan, prob.n_tiles, prob.M, prob.N, prob.K, 1, 0, R,
+                                        256, 256, prob.a, None, prob.b, tlc.B_KN, prob.c, prob.sig,
+                                        0, tlc.LAND_NONE, s, None, 1, schedule=tlc.SCHED_STATIC))
+    t, st = run_leg(prob, fn, args.steps, args.warmup, torch, s)
+    return {"metric": "memory-counter calibration: bytes a one-workgroup GEMM moves",
+            "workload": f"AG-GEMM M={R} N={N} K={K}, grid 1, one tile",
+            "bytes_loaded": 2 * R * K + 2 * K * N, "bytes_stored": 4 * R * N,
+            "launches": args.warmup + args.steps, "kernel_ms": round(kt.mean_ms(args.steps), 4),
+            "device_status": st}
+
+
 def main():
     global WARM_SECONDS
     args = parse()
@@ -833,6 +859,9 @@ def main():
     from tile_level_communication_amd import tlc, workloads
 
     torch.cuda.set_device(0)
+    if args.workload == "fetch_calibration":
+        print(json.dumps(run_fetch_calibration(args, torch, tlc, si, workloads)), flush=True)
+        return
     if args.workload == "ag":
         line = run_ag(args, torch, tlc, si, workloads)
         if not args.no_rs:

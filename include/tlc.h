@@ -96,7 +96,12 @@ enum { TLC_B_KN = 0, TLC_B_NK = 1 };
  *                  chunk's shares raises its flag with a release store, and the
  *                  GEMM's units wait on the flags as in the other modes.
  *                  A share of 2 GiB or more (chunk bytes / copy_wgs) returns
- *                  TLC_ERR_UNSUPPORTED.
+ *                  TLC_ERR_UNSUPPORTED.  Deadlock freedom rests on the copying
+ *                  workgroups having the lowest ids: the dispatcher makes them
+ *                  resident first and they wait for nothing before copying.
+ *                  So all of them must fit the device at once: more copying
+ *                  workgroups than compute units (one GEMM workgroup per
+ *                  compute unit) is refused with TLC_ERR_INVALID_ARG.
  *                  GEMM-RS: the reduce loads the peers' partials from
  *                  remote_src itself (no landing buffers, no flags).  The copy
  *                  streams are not used (they may be NULL / 0).            */

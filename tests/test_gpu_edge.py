@@ -177,3 +177,27 @@ def test_whole_tiles_even_and_odd_k_steps(layout):
             torch.cuda.synchronize()
             assert prob.sig.read_status()[0] == 0
             check_exact(prob.c.cpu().numpy(), ref, f"whole tiles K={K}")
+
+
+def test_colocated_copiers_must_fit_the_device():
+    """The co-located landing is deadlock-free because its copying workgroups
+    (the lowest ids) are resident before any workgroup that waits on their
+    flags: a grid above the compute-unit count is fine while the copiers fit
+    (bit for bit), and more copiers than compute units are refused."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    W, R, K, N = 4, 256, 256, 512
+    inp = si.ag_inputs(180, W, R, N, K, integer=True)
+    ref = og.ag_gemm(inp.a_chunks, inp.b)
+    for sched in (tlc.SCHED_STATIC, tlc.SCHED_DYNAMIC):
+        log(f"[edge] co-located grid {2 * cus} with 64 copiers, schedule {sched}")
+        prob = AGProblem(inp.a_chunks, inp.b, 2, 256, 256, tlc.B_KN, schedule=sched)
+        prob.poison_remote()
+        prob.run(tlc.LAND_COLOCATED, grid=2 * cus, copy_wgs=64)
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        check_exact(prob.c.cpu().numpy(), ref, "co-located, grid above the CU count")
+    prob = AGProblem(inp.a_chunks, inp.b, 2, 256, 256, tlc.B_KN)
+    for grid, copy_wgs in ((2 * cus, 0), (2 * cus, cus + 8)):
+        with pytest.raises(tlc.TLCError) as e:
+            prob.run(tlc.LAND_COLOCATED, grid=grid, copy_wgs=copy_wgs)
+        assert e.value.status == tlc.ERR_INVALID_ARG and "resident" in str(e.value)

@@ -245,9 +245,17 @@ void fill_copy_chunks(CopyPlan* cp, void* const* dst, const void* const* src, in
   }
 }
 
+// The copying workgroups have the lowest ids, so the dispatcher makes them
+// resident first; they wait for nothing before they copy, and the workgroups
+// that wait on their flags are dispatched after them.  That holds only while
+// every copying workgroup can be resident at the same time: at most one
+// 256 x 256 GEMM workgroup fits a compute unit (its LDS stages alone take 128
+// KB), so copy_wgs is limited to the compute units (`resident`); more could
+// leave copying workgroups waiting for compute units that workgroups spinning
+// on their flags hold, until the wait times out.
 tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src, int64_t bytes,
-                         int world, int rank, int n_local, int copy_wgs, int grid, const char* who,
-                         int flag_base = 0, int64_t n_units = -1) {
+                         int world, int rank, int n_local, int copy_wgs, int grid, int resident,
+                         const char* who, int flag_base = 0, int64_t n_units = -1) {
   if (copy_wgs < 0 || copy_wgs > grid)
     return fail(TLC_ERR_INVALID_ARG, "%s: copy_wgs %d outside 0..grid %d", who, copy_wgs, grid);
   int cw = copy_wgs;
@@ -262,6 +270,10 @@ tlc_status set_colocated(GemmParams* p, void* const* dst, const void* const* src
     }
   }
   p->copy.wgs = world > n_local ? cw : 0;
+  if (p->copy.wgs > resident)
+    return fail(TLC_ERR_INVALID_ARG, "%s: %d co-located copying workgroups, more than the %d that "
+                "can be resident at once (one per compute unit): pass copy_wgs <= %d, or a grid "
+                "of at most %d", who, p->copy.wgs, resident, resident, resident);
   fill_copy_chunks(&p->copy, dst, src, bytes, world, rank, n_local, flag_base);
   // a workgroup's share is addressed with 32-bit byte offsets
   if (p->copy.wgs > 0 && (p->copy.vec + p->copy.wgs - 1) / p->copy.wgs >= (int64_t{1} << 27))
@@ -383,7 +395,8 @@ tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_
     p.do_wait = 1;
     p.sig = sig;
     p.epoch = epoch;
-    st = set_colocated(&p, dst, src, bytes_per_chunk, world, rank, 1, 0, info.cus, "tlc_land");
+    st = set_colocated(&p, dst, src, bytes_per_chunk, world, rank, 1, 0, info.cus, info.cus,
+                       "tlc_land");
     if (st) return st;
     st = launch_gemm(p, 256, 256, TLC_B_KN, KIND_DENSE, p.copy.wgs,
                      copy_streams && n_copy_streams > 0 ? copy_streams[0] : nullptr);
@@ -469,7 +482,8 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   int grid = a->n_tiles > 0 ? pick_grid(a->grid, p.dynamic, a->n_tiles, avail)
                             : (a->grid > 0 ? a->grid : avail);
   if (coloc) {
-    st = set_colocated(&p, dst, src, chunk_bytes, Wf, rf, S, a->copy_wgs, grid, "tlc_ag_gemm", 0,
+    st = set_colocated(&p, dst, src, chunk_bytes, Wf, rf, S, a->copy_wgs, grid, info.cus,
+                       "tlc_ag_gemm", 0,
                        a->n_tiles);
     if (st) return st;
     if (a->n_tiles == 0) grid = p.copy.wgs;
@@ -643,7 +657,8 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
       p.do_wait = 1;
       p.no_wait_mask = 0xFFFFFFFFu;
       st = set_colocated(&p, const_cast<void* const*>(g->dst), g->src, slice_bytes, a->world,
-                         a->rank, 1, g->copy_wgs, grid, "tlc_gemm_ar", a->world, a->n_tiles);
+                         a->rank, 1, g->copy_wgs, grid, info.cus, "tlc_gemm_ar", a->world,
+                         a->n_tiles);
       if (st) return st;
       if (a->n_tiles == 0) grid = p.copy.wgs;
     }
@@ -914,7 +929,7 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
   int grid = a->grid > 0 ? a->grid : (avail >= 8 ? avail / 8 * 8 : avail);
   if (a->land == TLC_LAND_COLOCATED) {
     st = set_colocated(&p, dst, a->x_src, chunk_bytes, a->world, a->rank, 1, a->copy_wgs, grid,
-                       "tlc_ag_moe");
+                       info.cus, "tlc_ag_moe");
     if (st) return st;
   }
   p.xcd_remap = grid % 8 == 0;
