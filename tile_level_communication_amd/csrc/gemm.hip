@@ -652,6 +652,8 @@ template <int B_NK, int KIND, int FAST>
 struct Tile4w {
   static constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4, NT = 256;
   __device__ static int swz(int row) { return (row >> 1) & 7; }
+  // one load of the next stage every LSTRIDE MFMAs (see the fast loop)
+  static constexpr int LSTRIDE = 2;
 
   __device__ static void run(const GemmParams& p, const tlc_tile& tl, TLC_LDS u32x4* A0,
                              TLC_LDS u32x4* A1, TLC_LDS u32x4* B0, TLC_LDS u32x4* B1,
@@ -834,8 +836,17 @@ struct Tile4w {
     // MFMAs need them.  Before the last sub-step the wave waits for its reads
     // and for its loads of the next stage and meets the barrier; the first
     // instruction after it is an MFMA, and the next stage's first fragment
-    // reads and the sixteen loads of the step after next into this stage are
-    // threaded through the last sub-step's MFMAs.
+    // reads are threaded through the last sub-step's MFMAs.
+    //   The sixteen loads that refill a stage go one every LSTRIDE MFMAs from
+    // the moment the stage is free (the barrier) on: the first 16 / LSTRIDE
+    // under the last sub-step of the step that frees it, the rest under the
+    // first sub-steps of the next step, which waits for all of them at its
+    // own barrier.  A CU's loads then reach the texture path at an even rate
+    // (64 per step from its four wavefronts) instead of in one burst behind
+    // which each wavefront's MFMAs stall: the whole-tile step took 3450
+    // cycles with the sixteen loads in the last sub-step, 2950 with them
+    // spread over three (the MFMAs alone take 2048).  LSTRIDE 2 leaves the
+    // last load about a thousand cycles before its wait.
     constexpr int NRB = B_NK ? FN : 2 * FN;  // B reads per sub-step
     constexpr int NR = FM + NRB;             // fragment reads per sub-step
     v4i16 fbh[2][FN][2];                     // K x N weight: fragment halves
@@ -891,10 +902,11 @@ struct Tile4w {
         load_lds16_m0(rb, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(Bs)) + (wave_s * 8 + Q - 8) * 1024,
                       b_off[Q - 8], kt * b_step);
     };
-    // one K step on stage (Ac, Bc): reads the next stage (An, Bn) at its end
-    // and loads the step after next into this stage
-    auto fstep = [&](int i, TLC_LDS u32x4* Ac, TLC_LDS u32x4* Bc, const TLC_LDS u32x4* An,
-                     const TLC_LDS u32x4* Bn) __attribute__((always_inline)) {
+    // one K step on stage (Ac, Bc): finishes the loads of the next step into
+    // (An, Bn), reads that stage's first fragments at its end, and starts the
+    // loads of the step after next into this stage once it is free
+    auto fstep = [&](int i, TLC_LDS u32x4* Ac, TLC_LDS u32x4* Bc, TLC_LDS u32x4* An,
+                     TLC_LDS u32x4* Bn) __attribute__((always_inline)) {
       static_for<3>([&](auto ks_c) __attribute__((always_inline)) {
         constexpr int KS = decltype(ks_c)::value;
         static_for<FM * FN>([&](auto m_c) __attribute__((always_inline)) {
@@ -903,6 +915,11 @@ struct Tile4w {
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (M < NR) {
             read_one(Ac, Bc, KS + 1, std::integral_constant<int, (KS + 1) & 1>{}, m_c);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          constexpr int G = 16 + KS * 16 + M;
+          if constexpr (G % LSTRIDE == 0 && G / LSTRIDE < 16) {
+            load_one(kt0 + i + 1, An, Bn, std::integral_constant<int, G / LSTRIDE>{});
             __builtin_amdgcn_sched_barrier(0);
           }
         });
@@ -919,8 +936,10 @@ struct Tile4w {
           read_one(An, Bn, 0, std::integral_constant<int, 0>{}, m_c);
           __builtin_amdgcn_sched_barrier(0);
         }
-        load_one(kt0 + i + 2, Ac, Bc, m_c);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (M % LSTRIDE == 0) {
+          load_one(kt0 + i + 2, Ac, Bc, std::integral_constant<int, M / LSTRIDE>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
       });
     };
     // Every step reads the next stage and loads the step after next, also the
@@ -932,8 +951,12 @@ struct Tile4w {
     auto fast_loop = [&]() __attribute__((always_inline)) {
       static_assert(FM * FN == 16, "sixteen MFMAs and sixteen loads per sub-step");
       static_for<16>([&](auto q_c) __attribute__((always_inline)) { load_one(kt0, A0, B0, q_c); });
-      static_for<16>([&](auto q_c) __attribute__((always_inline)) { load_one(kt0 + 1, A1, B1, q_c); });
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // stage 0's sixteen loads done
+      // step 1's loads that the steady state issues before the first step
+      static_assert(LSTRIDE == 2, "the wait below counts 16 / LSTRIDE loads");
+      static_for<16 / LSTRIDE>([&](auto q_c) __attribute__((always_inline)) {
+        load_one(kt0 + 1, A1, B1, q_c);
+      });
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0's sixteen loads done
       __syncthreads();
       static_for<NR>([&](auto r_c) __attribute__((always_inline)) {
         read_one(A0, B0, 0, std::integral_constant<int, 0>{}, r_c);
