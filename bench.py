@@ -45,15 +45,19 @@ PEAK_HBM_GBS = 8000.0
 # Memory traffic per launch of each workload's dominant kernels (256 x 256 tiles,
 # K x N weight), from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (KiB per
 # dispatch) recorded under profiles/, each scaled by what the same counter reads
-# for a plain copy kernel of known size: FETCH_SIZE x FETCH_SCALE, WRITE_SIZE x
-# WRITE_SCALE.  None where the kernel changed since the counters were taken.
+# for work of known size: FETCH_SIZE x FETCH_SCALE, WRITE_SIZE x WRITE_SCALE.
+# The one-workgroup GEMM of --workload fetch_calibration, which loads its 64 MiB
+# of A and B once through the GEMM's own direct-to-LDS loads, reads FETCH_SIZE
+# 32 830 KiB and WRITE_SIZE 256 KiB for its 256 KiB tile (the runtime's copy
+# kernel reads half its loads too).  None where the kernel changed since the
+# counters were taken.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE) or None
-    "ag": {"gemm": (222444.6, 102404.9)},
-    "moe": {"gemm": (266866.2, 99328.0)},
-    "rs": {"gemm": None, "reduce": (32795.8, 16423.9)},
-    "ar": {"gemm": None, "reduce": (32795.8, 16423.9)},
-    "rs_long": {"gemm": (3154005.4, 2621440.0), "reduce": (1310743.8, 327680.0)},
+    "ag": {"gemm": (222439.1, 102404.9)},
+    "moe": {"gemm": (266411.7, 98304.0)},
+    "rs": {"gemm": (50662.4, 65536.0), "reduce": (32788.7, 16384.5)},
+    "ar": {"gemm": (50662.4, 65536.0), "reduce": (32788.7, 16384.5)},
+    "rs_long": {"gemm": (3153999.9, 2621440.0), "reduce": (1310743.9, 327680.0)},
 }
 
 
