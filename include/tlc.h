@@ -230,7 +230,10 @@ int64_t tlc_split_workspace_bytes(int64_t n_split_tiles, int32_t split_k, int32_
 /* ------------------------------------------------------------- signals ---- */
 
 /* Allocate / free one zeroed tlc_signals block in fine-grained device memory
- * (synchronous).  *out receives a device pointer. */
+ * (synchronous).  *out receives a device pointer.  The block holds the pages'
+ * per-chunk signals (talk, signal wait/notify between producer and consumer;
+ * DITRON §3.2, per-tile synchronisation of the communication and the GEMM) as
+ * device flags; allocating and freeing it is not from the pages. */
 tlc_status tlc_signals_alloc(tlc_signals** out);
 tlc_status tlc_signals_free(tlc_signals* sig);
 /* Enqueue on `stream`: flags[0..world-1] = value (a one-workgroup kernel; no
@@ -242,9 +245,11 @@ tlc_status tlc_signals_set(tlc_signals* sig, int32_t world, uint32_t value, void
  * epochs can restart at 1 (after TLC_EPOCH_MAX in copy-engine mode; not from
  * the pages). */
 tlc_status tlc_signals_rewind(tlc_signals* sig, void* stream);
-/* Enqueue on `stream`: status[0..3] = 0 and dest_done[0..31] = 0. */
+/* Enqueue on `stream`: status[0..3] = 0 and dest_done[0..31] = 0 (not from
+ * the pages: the status word is this library's error report). */
 tlc_status tlc_signals_clear_status(tlc_signals* sig, void* stream);
-/* Synchronize `stream`, then copy status[0..3] to the host array out[4]. */
+/* Synchronize `stream`, then copy status[0..3] to the host array out[4] (not
+ * from the pages). */
 tlc_status tlc_read_status(const tlc_signals* sig, void* stream, int32_t* out);
 /* Synchronize `stream`, then copy the whole block to the host struct *out
  * (not from the pages: an aid for tests and debugging, e.g. to check that
@@ -435,6 +440,9 @@ tlc_status tlc_gemm_ar(const tlc_ar_args* args, void* compute_stream, void* cons
 
 /* Routing for AG-MoE, on the device (DITRON §3.1 device level: chunk sizes
  * computed at run time for MoE routing; talk, "MoE dynamic sorting").
+ * This is also the MoE mode of the tile planner: the readiness-ordered tile
+ * list that tlc_chunk_plan gives on the host for dense GEMMs is built here on
+ * the device, where the experts' row counts are known.
  * For T = world * tokens_per_chunk tokens and E experts:
  *   topk[T x k]  experts with the largest logits, largest first, equal logits
  *                -> lower expert index first;
@@ -507,7 +515,10 @@ tlc_status tlc_moe_route(const tlc_moe_route_args* args, void* stream);
 tlc_status tlc_moe_route_static(const tlc_moe_route_args* args, void* stream);
 int64_t tlc_moe_static_workspace_bytes(void);
 
-/* Y[(T*k) x N] (f32): Y[i] = X[row_token[i]] (bf16, 1 x H) @ W_e (bf16, H x N)
+/* Grouped GEMM of AG-MoE (DITRON §4.1 AG-MoE; Triton-Distributed talk, MoE
+ * dynamic sorting: tiles in the order their tokens become ready; DITRON §3.1,
+ * shapes known only on the device).
+ * Y[(T*k) x N] (f32): Y[i] = X[row_token[i]] (bf16, 1 x H) @ W_e (bf16, H x N)
  * for the expert e whose row segment holds i.  X is the gathered token matrix
  * (T x H, chunk c = rows [c Tc, (c+1) Tc)); chunks land as in tlc_ag_gemm.
  * w: device bf16, E stacked matrices, layout w_layout (KN: E x H x N; NK:
@@ -544,7 +555,9 @@ tlc_status tlc_ag_moe(const tlc_moe_args* args, void* compute_stream, void* cons
 /* ------------------------------------------------------------ misc -------- */
 
 /* Land the peers' chunks only (the copy side of tlc_ag_gemm / tlc_gemm_rs,
- * no GEMM): for c in landing order (rank+1, ..., rank-1 mod W) copies
+ * no GEMM; the landing order is DITRON §3.2's rank-offset order; the call by
+ * itself is not a page operation but the copy-only leg of the overlap
+ * measurement): for c in landing order (rank+1, ..., rank-1 mod W) copies
  * `bytes_per_chunk` bytes from src[c] to dst[c] and then raises
  * sig->flags[c] to epoch.  dst, src: host arrays of `world` device pointers,
  * 16-byte aligned; entries `rank` are ignored.  bytes_per_chunk % 16 == 0.
@@ -558,7 +571,7 @@ tlc_status tlc_land(void* const* dst, const void* const* src, int64_t bytes_per_
 
 /* Rate in kHz of the device clock that timeouts and the debug traces count in
  * (hipDeviceAttributeWallClockRate of the current device); 0 if it cannot be
- * queried. */
+ * queried.  Not from the pages; neither are the three calls below. */
 int64_t tlc_wall_clock_khz(void);
 
 const char* tlc_status_string(tlc_status s);
