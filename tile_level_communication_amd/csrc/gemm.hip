@@ -23,7 +23,8 @@
 //    accumulators in the accumulation registers (whole-matrix GEMMs).  Its
 //    K loop for whole tiles fixes the place of every instruction: fragment
 //    reads and loads are threaded one by one between the MFMAs, since no
-//    second wavefront on the SIMD fills the gaps.
+//    second wavefront on the SIMD fills the gaps, and the loads that refill
+//    a stage go one every two MFMAs from the barrier that frees it.
 //  * 256 x 256, 8 wavefronts (2 x 4), 128 x 64 per wavefront, two per SIMD
 //    so that one wave's MFMAs cover the other's LDS reads (grouped MoE GEMM,
 //    whose ragged tiles it runs as fast as whole ones).
