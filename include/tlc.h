@@ -368,10 +368,11 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* args, void* compute_stream, void* cons
  * the GEMM leaves the CUs of a copy-stream landing free (grid limit below),
  * and the caller orders send_stream after earlier readers of send_dst and
  * later readers after it.  The GEMM is always enqueued before the gates.
- * Grid: a caller grid greater than (compute units - 32) is refused with
- * INVALID_ARG whenever a copy-stream landing (COPY_ENGINE, CU, MEMCPY) or a
- * send runs beside the GEMM: the landing's and the sends' kernels need CUs no
- * GEMM workgroup holds. */
+ * Grid: the GEMM never waits, so by default it takes every compute unit and
+ * the runtime's copies (MEMCPY and COPY_ENGINE landings and sends) share them.
+ * A caller grid greater than (compute units - 32) is refused with INVALID_ARG
+ * only with the CU landing or CU sends, whose copy kernels are sized for
+ * compute units no GEMM workgroup holds. */
 typedef struct {
   const tlc_tile* plan;
   int64_t n_tiles;

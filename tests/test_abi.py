@@ -226,9 +226,9 @@ def test_gemm_rs_send_and_grid_argument_errors():
         (dict(send_dst=C.cast(bad_dst, C.POINTER(C.c_void_p)), send_land=tlc.LAND_MEMCPY),
          tlc.ERR_INVALID_ARG, "send_dst[1]"),
         (dict(send_dst=dp, send_land=tlc.LAND_CU, n_tiles=0), tlc.ERR_INVALID_ARG, "CU sends"),
-        (dict(send_dst=dp, send_land=tlc.LAND_MEMCPY, grid=225), tlc.ERR_INVALID_ARG,
+        (dict(send_dst=dp, send_land=tlc.LAND_CU, grid=225), tlc.ERR_INVALID_ARG,
          "compute units free"),
-        (dict(land=tlc.LAND_MEMCPY, remote_src=lp, grid=240), tlc.ERR_INVALID_ARG,
+        (dict(land=tlc.LAND_CU, remote_src=lp, grid=240), tlc.ERR_INVALID_ARG,
          "compute units free"),
     ]:
         args = _rs_args(landing=lp, **over)

@@ -20,9 +20,11 @@ bool g_info_ok[64] = {};
 // landing's kernels -- the CU copy kernel, or on the copy-engine path the
 // runtime's kernel for each 4-byte flag transfer (1024-thread workgroups) --
 // have to find CUs that no GEMM workgroup holds while those workgroups spin
-// (a GEMM workgroup takes all the registers of its CU).  With fewer than one
-// free CU per shader engine (8 XCDs x 4) their placement stalled now and then
-// until the wait timed out, even when the landing kernel was dispatched first.
+// (a workgroup of the 8-wavefront core takes all the registers of its CU).
+// With fewer than one free CU per shader engine (8 XCDs x 4) their placement
+// stalled now and then until the wait timed out, even when the landing kernel
+// was dispatched first.  A GEMM that never waits (scatter mode) needs no such
+// reserve for the runtime's copies.
 constexpr int kReserveCUsLandCU = 32;
 constexpr int kReserveCUsCopyEngine = 32;
 // The compute units of the largest gfx950 part: a caller grid is checked
@@ -596,9 +598,15 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
         return fail(TLC_ERR_INVALID_ARG, "tlc_gemm_rs: send_dst[%d] NULL or misaligned", c);
     }
   }
-  // CUs the landing and the sends need beside the GEMM
-  int reserve = reserve_for(land);
-  if (sends && reserve < kReserveCUsCopyEngine) reserve = kReserveCUsCopyEngine;
+  // CUs the landing and the sends need beside the GEMM.  The scatter-mode GEMM
+  // never waits, so the runtime's copies (memcpy and copy-engine landings and
+  // sends) may share its CUs and it takes every one: a GEMM on all 256 CUs
+  // instead of 224 runs the 4096 x 4096 x 2048 GEMM-RS in one round of tiles
+  // instead of two.  Only the library's own copy kernels, sized for CUs of
+  // their own (the CU landing, the CU sends), keep them free.
+  int reserve = land == TLC_LAND_CU ? kReserveCUsLandCU : 0;
+  if (sends && a->send_land == TLC_LAND_CU && reserve < kReserveCUsLandCU)
+    reserve = kReserveCUsLandCU;
   if (run_gemm) {
     st = check_grid(a->grid, reserve, 0, "tlc_gemm_rs");
     if (st) return st;
@@ -649,7 +657,6 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
       p.notify_mask = ((a->world == 32) ? 0xFFFFFFFFu : ((1u << a->world) - 1u)) & ~(1u << a->rank);
       p.dest_total = static_cast<uint32_t>(slice);
     }
-    // the GEMM does not wait, but the landing and the sends beside it may need CUs
     const int avail = info.cus - reserve;
     int grid = a->n_tiles > 0 ? pick_grid(a->grid, p.dynamic, a->n_tiles, avail)
                               : (a->grid > 0 ? a->grid : avail);
