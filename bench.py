@@ -54,7 +54,7 @@ PEAK_HBM_GBS = 8000.0
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE) or None
     "ag": {"gemm": (222439.1, 102404.9)},
-    "moe": {"gemm": (266411.7, 98304.0)},
+    "moe": {"gemm": None},
     "rs": {"gemm": (50662.4, 65536.0), "reduce": (32788.7, 16384.5)},
     "ar": {"gemm": (50662.4, 65536.0), "reduce": (32788.7, 16384.5)},
     "rs_long": {"gemm": (3153999.9, 2621440.0), "reduce": (1310743.9, 327680.0)},
@@ -805,7 +805,7 @@ def run_moe(args, torch, tlc, si, workloads):
                      "traffic_unit": "bytes per launch past the L2 (calibrated FETCH_SIZE + WRITE_SIZE)",
                      "algorithmic_bytes": prob.T * prob.H * 2 + prob.E * prob.H * prob.N * 2
                      + prob.T * prob.k * prob.N * 4,
-                     "kernel": "gemm_kernel_8w<KN,moe,no-wait>: grouped GEMM, every chunk resident",
+                     "kernel": "gemm_kernel_4w<KN,moe,no-wait,whole-tile loop>: grouped GEMM, every chunk resident",
                      "device_status": comp_status},
         "route_ms": round(route_ms, 4),
         "pct_peak": head["pct_peak"],

@@ -1133,15 +1133,20 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
 
 template <int BM, int BN, int B_NK, int KIND, int WAIT>
 void launch_kernel(const GemmParams& p, int grid, void* stream) {
-  // 256 x 256 tiles: the 4-wavefront core for whole-matrix GEMMs (3-5 %
-  // faster than the 8-wavefront one on their shapes), the 8-wavefront core
-  // for the grouped GEMM, whose ragged last tile of every expert the
-  // 4-wavefront core runs in its slower general loop
+  // 256 x 256 tiles: the 4-wavefront core (3-5 % faster than the 8-wavefront
+  // one on the whole-matrix shapes, and its whole-tile kernel 5 % faster on the
+  // grouped GEMM); the grouped GEMM falls back to the 8-wavefront core when it
+  // cannot run the whole-tile kernel, since the 4-wavefront core's general
+  // loop is slower on its ragged tiles
   if constexpr (BM == 256 && BN == 256) {
-    if constexpr (KIND == KIND_MOE)
-      hipLaunchKernelGGL((gemm_kernel_8w<B_NK, KIND, WAIT>), dim3(grid), dim3(512), 0,
-                         static_cast<hipStream_t>(stream), p);
-    else if (p.fast)
+    if constexpr (KIND == KIND_MOE) {
+      if (p.fast)
+        hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 1>), dim3(grid), dim3(256), 0,
+                           static_cast<hipStream_t>(stream), p);
+      else
+        hipLaunchKernelGGL((gemm_kernel_8w<B_NK, KIND, WAIT>), dim3(grid), dim3(512), 0,
+                           static_cast<hipStream_t>(stream), p);
+    } else if (p.fast)
       hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 1>), dim3(grid), dim3(256), 0,
                          static_cast<hipStream_t>(stream), p);
     else
@@ -1192,8 +1197,11 @@ tlc_status launch_gemm(const GemmParams& p_in, int bm, int bn, int b_layout, int
   // K steps: M a multiple of 256, K / 64 even, no split workspace (a split
   // unit without one is reported as a bad plan).  It keeps a third of the
   // register file free, so that other kernels' wavefronts (a side stream's
-  // copies) can run beside it on the same compute units.
-  p.fast = kind != KIND_MOE && p.M % 256 == 0 && (p.K / 64) % 2 == 0 && p.split_bytes == 0;
+  // copies) can run beside it on the same compute units.  The grouped GEMM
+  // runs it on its ragged tiles too (never split): the rows past an expert's
+  // end load that expert's last row again and are not stored, and the fixed
+  // loop over all 256 rows still beats the general loop that skips them.
+  p.fast = (kind == KIND_MOE || p.M % 256 == 0) && (p.K / 64) % 2 == 0 && p.split_bytes == 0;
   if (bm == 256 && bn == 256) return launch_shape<256, 256>(p, b_layout, kind, grid, stream);
   if (bm == 128 && bn == 128) return launch_shape<128, 128>(p, b_layout, kind, grid, stream);
   return fail(TLC_ERR_UNSUPPORTED, "tile %dx%d not built (256x256, 128x128)", bm, bn);
