@@ -726,13 +726,14 @@ def run_moe(args, torch, tlc, si, workloads):
     layout = tlc.B_KN if args.layout == "KN" else tlc.B_NK
     land = LANDINGS[args.land]
     order = ORDERS[args.order]
-    # Schedule per landing unless one is given: with the full grid (co-located
-    # landings) static slots keep each XCD on a contiguous run of the
-    # expert-major plan (its weights and token rows stay in that XCD's L2), 3 %
-    # faster than the dynamic counter; with 32 CUs left to the side-stream
-    # landing, ~486 units no longer fit two static rounds of 224 and the
-    # dynamic counter balances them (0.5-1 % faster for the memcpy landing,
-    # 1-2 % for the CU landing).
+    # Schedule per landing unless one is given: with no landing or a co-located
+    # one, static slots keep each XCD on a contiguous run of the expert-major
+    # plan (its weights and token rows stay in that XCD's L2), 3 % faster than
+    # the dynamic counter; beside a side-stream landing the dynamic counter
+    # lets units whose chunks have landed go ahead (with the memcpy landing on
+    # every CU the two are equal; with 32 CUs left to the CU landing, ~486
+    # units no longer fit two static rounds of 224 and the counter balances
+    # them, 1-2 % faster).
     forced = {"static": tlc.SCHED_STATIC, "dynamic": tlc.SCHED_DYNAMIC}.get(args.schedule)
 
     def schedule_for(land_kind):

@@ -527,7 +527,13 @@ int64_t tlc_moe_static_workspace_bytes(void);
  * land = TLC_LAND_NONE and epoch >= 1 nothing is landed here but the tiles
  * still wait for their chunks' flags: chunks landed by tlc_moe_route's
  * co-located landing (or by the caller), with that epoch.
- * Requirements: H % 64 == 0, N % 8 == 0, 16-byte aligned pointers. */
+ * Requirements: H % 64 == 0, N % 8 == 0, 16-byte aligned pointers.
+ * grid (0 = every compute unit the landing leaves free): with H / 64 even the
+ * GEMM's workgroups leave room on their CUs for the runtime's copy and
+ * flag-transfer kernels, so beside a MEMCPY or COPY_ENGINE landing they take
+ * every CU; a grid above (compute units - 32) is refused with INVALID_ARG with
+ * the CU landing, and with any copy-stream landing when H / 64 is odd (that
+ * GEMM kernel fills its CUs while it waits on flags). */
 typedef struct {
   const tlc_tile* plan;
   const int32_t* n_tiles_dev;

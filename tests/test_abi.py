@@ -254,12 +254,21 @@ def test_ag_moe_grid_and_topk_errors():
         base.update(over)
         return tlc.MoEArgs(**base)
 
+    # H = 64: one K step, so the 8-wavefront kernel, which fills its CUs: the
+    # memcpy landing keeps 32 CUs free; the CU landing always does
     for over, want, text in [(dict(grid=230), tlc.ERR_INVALID_ARG, "compute units free"),
+                             (dict(H=128, land=tlc.LAND_CU, grid=230), tlc.ERR_INVALID_ARG,
+                              "compute units free"),
                              (dict(topk=9), tlc.ERR_UNSUPPORTED, "topk"),
                              (dict(plan_cap=-1), tlc.ERR_INVALID_ARG, "plan_cap")]:
         a = args(**over)
         assert tlc.lib().tlc_ag_moe(C.byref(a), None, streams, 1) == want, (over, tlc.last_error())
         assert text in tlc.last_error(), tlc.last_error()
+    # H = 128 (even number of K steps): the whole-tile kernel shares its CUs with
+    # the runtime's copies, so a grid of every CU passes the host check
+    a = args(H=128, grid=256)
+    s = tlc.lib().tlc_ag_moe(C.byref(a), None, streams, 1)
+    assert "compute units free" not in tlc.last_error(), tlc.last_error()
 
 
 def test_moe_route_static_refuses_oversize_on_the_host():

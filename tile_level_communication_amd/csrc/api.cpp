@@ -896,7 +896,14 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
   tlc_status st = check_land_args(a->land, a->x_src, dst, a->world, a->rank, chunk_bytes, "tlc_ag_moe",
                                   copy_streams, n_copy_streams, a->epoch);
   if (st) return st;
-  const int moe_reserve = a->world > 1 ? reserve_for(a->land) : 0;
+  // The grouped GEMM's whole-tile kernel (H / 64 even) leaves room on every CU
+  // for the runtime's copy and flag-transfer workgroups (a third of the
+  // registers, 32 KB of LDS, most wavefront slots), so beside the memcpy and
+  // copy-engine landings it waits on flags without a reserve and takes every
+  // CU; the 8-wavefront fallback (H / 64 odd) fills its CUs, and the CU landing
+  // kernel is sized for CUs of its own: those keep the reserve.
+  const bool shares_cus = (a->H / 64) % 2 == 0 && a->land != TLC_LAND_CU;
+  const int moe_reserve = (a->world > 1 && !shares_cus) ? reserve_for(a->land) : 0;
   st = check_grid(a->grid, moe_reserve, 0, "tlc_ag_moe");
   if (st) return st;
   DeviceInfo info;
@@ -931,7 +938,7 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
   p.epoch = a->epoch;
   p.timeout_ticks = ticks_for(a->timeout_ns, info);
   set_schedule(&p, a->schedule, nullptr, 0);
-  const int avail = info.cus - (p.do_wait ? reserve_for(a->land) : 0);
+  const int avail = info.cus - (p.do_wait ? moe_reserve : 0);
   // The tile count is only known on the device: use every available CU.
   int grid = a->grid > 0 ? a->grid : (avail >= 8 ? avail / 8 * 8 : avail);
   if (a->land == TLC_LAND_COLOCATED) {
