@@ -434,16 +434,21 @@ def run_ag(args, torch, tlc, si, workloads):
 
     t_comp, comp_status = run_leg(comp, compute_only, args.steps, args.warmup, torch, compute)
     gemm_comp_ms = comp_t.mean_ms(args.steps)
-    # one more compute-only launch with trace stamps, right after the timed
-    # ones (clocks settled): the shader clock the workgroups ran at, from
-    # their cycle counters against the constant-rate clock, and the MFMA peak
-    # at that clock
+    # five more compute-only launches with trace stamps, right after the
+    # timed ones (clocks settled): the shader clock the workgroups ran at, from
+    # their cycle counters against the constant-rate clock (the median of the
+    # five launches: one launch now and then reads a momentary dip), and the
+    # MFMA peak at that clock
     ctrace = torch.zeros((comp.n_tiles, 6), dtype=torch.int64, device=dev)
-    tlc.ag_gemm(**ccall, a_src=None, epoch=0, land=tlc.LAND_NONE, compute_stream=compute,
-                copy_stream=None, grid=0, trace=ctrace)
-    torch.cuda.synchronize()
-    ct = ctrace.cpu().numpy()
-    sclk_mhz = float((ct[:, 5] - ct[:, 4]).sum()) / max(float((ct[:, 3] - ct[:, 2]).sum()), 1.0) * khz / 1e3
+    sclk_samples = []
+    for _ in range(5):
+        tlc.ag_gemm(**ccall, a_src=None, epoch=0, land=tlc.LAND_NONE, compute_stream=compute,
+                    copy_stream=None, grid=0, trace=ctrace)
+        torch.cuda.synchronize()
+        ct = ctrace.cpu().numpy()
+        sclk_samples.append(float((ct[:, 5] - ct[:, 4]).sum())
+                            / max(float((ct[:, 3] - ct[:, 2]).sum()), 1.0) * khz / 1e3)
+    sclk_mhz = sorted(sclk_samples)[len(sclk_samples) // 2]
     achieved = flops / (gemm_comp_ms * 1e-3) / 1e12
     peak_at_sclk = PEAK_BF16_TFLOPS * sclk_mhz / PEAK_SCLK_MHZ
     head = leg_summary(flops, t_fused, t_comp, t_copy, status)
@@ -463,6 +468,7 @@ def run_ag(args, torch, tlc, si, workloads):
                      "kernel": "gemm_kernel_4w<KN,dense,no-wait>: compute-only launch, whole tiles, "
                                "static schedule, every chunk resident",
                      "sclk_mhz_measured": round(sclk_mhz, 1),
+                     "sclk_mhz_samples": [round(x, 1) for x in sclk_samples],
                      "peak_at_measured_sclk": round(peak_at_sclk, 1),
                      "frac_at_measured_sclk": round(achieved / peak_at_sclk, 4),
                      "device_status": comp_status},
