@@ -460,10 +460,13 @@ tlc_status tlc_gemm_ar(const tlc_ar_args* args, void* compute_stream, void* cons
  * Limits: E <= 64 (one expert per lane of a wavefront), k <= E, k <= 16,
  * T <= 2^20, bm in {128, 256}.  plan_cap >= tlc_moe_plan_capacity(...).
  * All arrays are device memory; `workspace` is device memory of at least
- * tlc_moe_workspace_bytes(T, k, E, bm) bytes (contents need not be initialised).
+ * tlc_moe_workspace_bytes(T, k, E, bm) bytes (contents need not be initialised;
+ * the size depends on T and E only: T token masks and the per-expert counts of
+ * the blocks of up to 16 tokens that each chunk is cut into).
  *
- * Optional co-located landing of the peers' token chunks (x_src != NULL): the
- * top-k kernel's first workgroups also copy chunk c (c != rank, tokens_per_chunk
+ * Optional co-located landing of the peers' token chunks (x_src != NULL):
+ * extra workgroups of the routing's first (top-k) kernel, beside the routing's
+ * own, copy chunk c (c != rank, tokens_per_chunk
  * x H bf16) from x_src[c] into rows [c Tc, (c+1) Tc) of x with load/store
  * instructions, a fixed number of workgroups per chunk, and the last of them
  * raises sig->flags[c] to `epoch` (AutoOverlap §5.3, backend 5, here beside
@@ -509,7 +512,7 @@ tlc_status tlc_moe_route(const tlc_moe_route_args* args, void* stream);
  * is allocated: no hipMalloc, hipFree or allocating library call.  A problem
  * whose tlc_moe_workspace_bytes(...) exceeds the array is refused with
  * TLC_ERR_CAPACITY before anything is enqueued (e.g. T = 4096, k = 8,
- * E = 64, bm = 256 needs about 51 KB).  The workspace needs no
+ * E = 64, bm = 256 needs 104 KB).  The workspace needs no
  * initialisation, and each call leaves the last call's contents in it.
  * Calls that overlap in time on one device (on different streams, or from
  * different threads) race on the array; the caller orders them. */

@@ -89,12 +89,13 @@ def test_moe_ties_route_to_lower_expert():
 
 
 def test_moe_route_long_block_scan():
-    """16512 tokens: 258 blocks of 64 arrival positions, so each of the scan's
-    sixteen wavefronts takes a run of 17 blocks and reads its counts twice
-    (the path runs of up to 16 blocks do not take)."""
-    W, Tc, H, N, E, k = 4, 4128, 64, 128, 16, 2
+    """16500 tokens in 4 chunks of 4125: each chunk is cut into 258 blocks of
+    up to 16 tokens (the last of 13), 1032 blocks in all, so each of the plan
+    kernel's sixteen wavefronts takes a run of 65 blocks and reads its counts
+    twice (the path runs of up to 16 blocks do not take)."""
+    W, Tc, H, N, E, k = 4, 4125, 64, 128, 16, 2
     inp = si.moe_inputs(321, W, Tc, H, N, E)
-    log("[moe long scan] T=16512")
+    log("[moe long scan] T=16500")
     ref = om.route(inp.logits, k, W, 2, Tc)
     prob = MoEProblem(inp.x_chunks, inp.logits, inp.w, 2, k, 256, 256)
     prob.route()

@@ -742,10 +742,8 @@ int64_t tlc_moe_plan_capacity(int32_t T, int32_t topk, int32_t experts, int32_t 
 
 int64_t tlc_moe_workspace_bytes(int32_t T, int32_t topk, int32_t experts, int32_t bm) {
   if (T < 1 || topk < 1 || experts < 1 || bm < 1) return 0;
-  const int64_t pairs = moe_max_pairs(T, topk, experts, bm);
   auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  return up(static_cast<int64_t>(T) * 8) + up((experts + 1) * 4LL) + up(pairs * 4) + up(pairs * 4) +
-         up((T + 63) / 64 * static_cast<int64_t>(experts) * 4);
+  return up(static_cast<int64_t>(T) * 8) + up(moe_max_blocks(T) * experts * 4);
 }
 
 }  // extern "C"
@@ -791,8 +789,8 @@ static tlc_status moe_route_impl(const tlc_moe_route_args* a, void* workspace, v
   memset(&d, 0, sizeof(d));
   if (a->x_src && a->world > 1) {
     fill_copy_chunks(&d.copy, dst, a->x_src, chunk_bytes, a->world, a->rank, 1, 0);
-    // about 64 KB per copying workgroup; the top-k kernel (one workgroup per
-    // four tokens) is launched with at least that many workgroups
+    // about 64 KB per copying workgroup; the routing's first kernel is
+    // launched with that many workgroups after its own
     const int64_t per = (chunk_bytes + 65535) / 65536;
     if (per * d.copy.chunks > (1 << 30))
       return fail(TLC_ERR_UNSUPPORTED, "tlc_moe_route: co-located landing of %lld-byte chunks",
@@ -813,7 +811,6 @@ static tlc_status moe_route_impl(const tlc_moe_route_args* a, void* workspace, v
   d.bn = a->bn;
   d.order = a->order;
   d.ntiles_n = (a->N + a->bn - 1) / a->bn;
-  d.max_pairs = static_cast<int32_t>(moe_max_pairs(d.T, d.k, d.E, d.bm));
   d.topk = a->topk_idx;
   d.gates = a->gates;
   d.counts = a->counts;
@@ -826,12 +823,6 @@ static tlc_status moe_route_impl(const tlc_moe_route_args* a, void* workspace, v
   char* ws = static_cast<char*>(workspace);
   d.member = reinterpret_cast<unsigned long long*>(ws);
   ws += up(T * 8);
-  d.pstart = reinterpret_cast<int32_t*>(ws);
-  ws += up((d.E + 1) * 4LL);
-  d.pair_key = reinterpret_cast<int32_t*>(ws);
-  ws += up(d.max_pairs * 4LL);
-  d.pair_mask = reinterpret_cast<uint32_t*>(ws);
-  ws += up(d.max_pairs * 4LL);
   d.blk = reinterpret_cast<int32_t*>(ws);
   DeviceInfo info;
   tlc_status st = device_info(&info);

@@ -75,10 +75,10 @@ __device__ inline void copy_in_landing_order(const CopyPlan& cp, tlc_signals* si
     copy_share(cp, i, lo, hi, static_cast<uint32_t>(cp.wgs), sig, epoch);
 }
 
-// All chunks at once: cp.wgs = per * cp.chunks workgroups, workgroup g copies
-// share g % per of chunk g / per (one wait and one arrival per workgroup).
-__device__ inline void copy_by_chunk(const CopyPlan& cp, tlc_signals* sig, uint32_t epoch) {
-  const int g = blockIdx.x;
+// All chunks at once: cp.wgs = per * cp.chunks copying workgroups, copying
+// workgroup g (0 <= g < cp.wgs) copies share g % per of chunk g / per (one
+// arrival per workgroup).
+__device__ inline void copy_by_chunk(const CopyPlan& cp, int g, tlc_signals* sig, uint32_t epoch) {
   const int per = cp.wgs / cp.chunks;
   const int i = g / per, s = g % per;
   copy_share(cp, i, cp.vec * s / per, cp.vec * (s + 1) / per, static_cast<uint32_t>(per), sig, epoch);

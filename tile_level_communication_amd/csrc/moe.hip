@@ -9,28 +9,32 @@
 // deterministic: no atomics whose order could change a result.
 //
 // Tokens are visited in arrival order: the local chunk first, then rank+1,
-// rank+2, ... (position a = p(c) * Tc + token offset), in blocks of 64.
+// rank+2, ... (the chunk consumed p-th is c = (rank + p) mod world).  Each
+// chunk's tokens split into blocks of up to 16 consecutive tokens (a block
+// never spans two chunks), numbered in arrival order.  Three kernels:
 //
-//   topk_kernel     (optionally, its first workgroups also land the peers'
-//                   token chunks: the co-located landing beside the routing)
-//                   one wavefront per token, one expert per lane (E <= 64):
-//                   k rounds of a wavefront maximum of order-preserving keys
-//                   and a ballot for the lowest expert holding it (ties ->
-//                   lower expert), softmax over the k winners, a 64-bit
-//                   membership mask.
-//   block_count     one wavefront per block of 64 arrival positions: for each
-//                   expert, how many of the block's tokens chose it.
-//   scan_kernel     sixteen wavefronts over runs of blocks: per expert, the
-//                   prefix of those counts over the blocks; counts, offsets and
-//                   m-tile starts over experts.
-//   scatter_kernel  one wavefront per (block, 16 experts): each (token, expert)
-//                   pair's row = offsets[e] + rows of e in earlier blocks +
-//                   earlier lanes of this block; row_token and slot.
-//   pair_kernel     one wavefront per (expert, m-tile): readiness key and chunk
-//                   mask over the tile's rows.
-//   sort_kernel     one workgroup: stable counting sort of the (expert, m-tile)
-//                   pairs by key (ballot ranks per wavefront, carried over
-//                   batches of pairs), expanded over the n-tiles.
+//   route_kernel    one workgroup per block, one wavefront per token, one
+//                   expert per lane (E <= 64), k rounds of a wavefront
+//                   maximum of order-preserving keys and a ballot for the
+//                   lowest expert holding it (ties -> lower expert); lane j
+//                   keeps winner j, so the softmax over the k winners and the
+//                   stores are lane-parallel; a 64-bit membership mask per
+//                   token; then the block's token count per expert.
+//                   Optionally, workgroups after the blocks' land the peers'
+//                   token chunks (the co-located landing beside the routing).
+//   plan_kernel     one workgroup of sixteen wavefronts, lane = expert: the
+//                   exclusive prefix of the block counts over the blocks (each
+//                   wavefront a contiguous run), the rows of every expert that
+//                   come before each chunk position, counts, offsets and
+//                   m-tile starts; then every (expert, m-tile) pair's
+//                   readiness key and chunk mask, read off those per-position
+//                   row ranges, and a stable counting sort of the pairs by key
+//                   (ballot ranks per wavefront, carried over batches),
+//                   expanded over the n-tiles.
+//   scatter_kernel  one wavefront per (four blocks, sixteen experts): each
+//                   (token, expert) pair's row = offsets[e] + rows of e in
+//                   earlier blocks + earlier tokens of its block; row_token and
+//                   slot.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -41,6 +45,8 @@
 namespace tlc {
 
 namespace {
+
+constexpr int BLK = 16;  // tokens per arrival block
 
 // Order-preserving map of a float to an unsigned key (-0 counts as +0, as in
 // a value comparison); 0 is below every finite float's key.
@@ -69,84 +75,117 @@ __device__ inline uint32_t wave_max(uint32_t x) {
   return max(max(r0, r1), max(r2, r3));
 }
 
-// Routing of token t by one wavefront (lane = expert): k rounds of the
-// largest remaining logit (wave maximum of the ordered keys) and the lowest
-// expert holding it (first set bit of the ballot), then the softmax over the k
-// winners in lane 0.  Returns the membership mask (the same in every lane).
-__device__ inline unsigned long long route_token(const MoeDev& d, int t, int lane) {
-  const bool mine = lane < d.E;
-  const uint32_t key = mine ? ordered_key(d.logits[static_cast<int64_t>(t) * d.E + lane]) : 0u;
-  bool taken = !mine;
-  float win_v[16];
-  int win_i[16];
+// Sum over the wavefront, the same in every lane: the steps of wave_max with
+// an addition (every step adds two disjoint sets of lanes), then the four
+// rows' sums.
+template <int CTRL>
+__device__ inline float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x),
+                                                                   __builtin_bit_cast(int, x), CTRL,
+                                                                   0xF, 0xF, false));
+}
+
+__device__ inline float lane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+__device__ inline float wave_sum(float x) {
+  x = dpp_add<0xB1>(x);
+  x = dpp_add<0x4E>(x);
+  x = dpp_add<0x141>(x);
+  x = dpp_add<0x140>(x);
+  return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
+}
+
+// Blocks per chunk position, and the token in slot i of block b (-1 past the
+// chunk's end).
+__device__ inline int blocks_per_chunk(const MoeDev& d) { return (d.Tc + BLK - 1) / BLK; }
+
+__device__ inline int block_token(const MoeDev& d, int bpc, int b, int i) {
+  const int p = b / bpc;
+  const int off = (b - p * bpc) * BLK + i;
+  if (off >= d.Tc) return -1;
+  return ((d.rank + p) % d.world) * d.Tc + off;
+}
+
+// Routing of token t by one wavefront (lane = expert, `key` the lane's
+// ordered logit key): k rounds of the largest remaining key (wave maximum)
+// and the lowest expert holding it (first set bit of the ballot); lane j keeps
+// winner j, then the softmax over the k winners.  Returns the membership mask
+// (the same in every lane).
+__device__ inline unsigned long long route_token(const MoeDev& d, int t, uint32_t key, int lane) {
+  bool taken = lane >= d.E;
+  uint32_t top = 0, my_key = 0;
+  int my_e = 0;
   unsigned long long member = 0;
   for (int j = 0; j < d.k; ++j) {
     const uint32_t kk = taken ? 0u : key;
     const uint32_t mx = wave_max(kk);
     int bi = __ffsll(static_cast<unsigned long long>(__ballot(kk == mx))) - 1;
     bi = bi < 0 ? 0 : bi;  // a lane always holds the maximum; keeps the mask shift defined
-    win_v[j] = key_value(mx);
-    win_i[j] = bi;
+    if (j == 0) top = mx;
+    if (lane == j) {
+      my_key = mx;
+      my_e = bi;
+    }
     member |= 1ull << bi;
     if (lane == bi) taken = true;
   }
-  if (lane == 0) {
-    const float mx = win_v[0];
-    float e[16];
-    float sum = 0.0f;
-    for (int j = 0; j < d.k; ++j) {
-      e[j] = expf(win_v[j] - mx);
-      sum += e[j];
-    }
-    for (int j = 0; j < d.k; ++j) {
-      d.topk[static_cast<int64_t>(t) * d.k + j] = win_i[j];
-      d.gates[static_cast<int64_t>(t) * d.k + j] = e[j] / sum;
-    }
-    d.member[t] = member;
+  const bool win = lane < d.k;
+  const float ex = win ? expf(key_value(my_key) - key_value(top)) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (win) {
+    d.topk[static_cast<int64_t>(t) * d.k + lane] = my_e;
+    d.gates[static_cast<int64_t>(t) * d.k + lane] = ex / sum;
   }
   return member;
 }
 
-// Token at arrival position a (0 <= a < T).
-__device__ inline int arrival_token(const MoeDev& d, int a) {
-  const int pos = a / d.Tc;
-  const int c = (d.rank + pos) % d.world;
-  return c * d.Tc + (a - pos * d.Tc);
-}
-
-__global__ __launch_bounds__(256) void topk_kernel(MoeDev d) {
-  // co-located landing of the token chunks (d.copy.wgs = 0: none); the
-  // routing waits for nothing, so the copy overlaps it
-  if (static_cast<int>(blockIdx.x) < d.copy.wgs) copy_by_chunk(d.copy, d.sig, d.epoch);
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t < d.T) route_token(d, t, threadIdx.x & 63);
-}
-
-__global__ __launch_bounds__(64) void block_count_kernel(MoeDev d) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const int a = b * 64 + lane;
-  const unsigned long long m = a < d.T ? d.member[arrival_token(d, a)] : 0ull;
-  int mine = 0;
-  for (int e = 0; e < d.E; ++e) {
-    const int n = __popcll(__ballot((m >> e) & 1ull));
-    if (lane == e) mine = n;
+__global__ __launch_bounds__(64 * BLK) void route_kernel(MoeDev d, int nb) {
+  const int g = blockIdx.x;
+  if (g >= nb) {
+    // co-located landing of the token chunks, after the blocks' workgroups;
+    // the routing waits for nothing, so the copy overlaps it
+    copy_by_chunk(d.copy, g - nb, d.sig, d.epoch);
+    return;
   }
-  if (lane < d.E) d.blk[static_cast<int64_t>(b) * d.E + lane] = mine;
+  __shared__ unsigned long long s_member[BLK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wavefront w routes the block's token w
+  const int t = block_token(d, blocks_per_chunk(d), g, wave);
+  unsigned long long m = 0;
+  if (t >= 0) {
+    const uint32_t key = lane < d.E ? ordered_key(d.logits[static_cast<int64_t>(t) * d.E + lane]) : 0u;
+    m = route_token(d, t, key, lane);
+    if (lane == 0) d.member[t] = m;
+  }
+  if (lane == 0) s_member[wave] = m;
+  __syncthreads();
+  if (wave == 0 && lane < d.E) {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < BLK; ++i) n += static_cast<int>((s_member[i] >> lane) & 1ull);
+    d.blk[static_cast<int64_t>(g) * d.E + lane] = n;
+  }
 }
 
-// Sixteen wavefronts: wavefront w takes a contiguous run of blocks, lane =
-// expert.  Its per-expert total goes through LDS; each wavefront then rewrites
-// its blocks with the exclusive prefix (the totals of the runs before it plus
-// its own running sum), and wavefront 0 forms counts, offsets and m-tile starts.
-constexpr int SCAN_WAVES = 16;
+constexpr int PLAN_WAVES = 16;
 
-__global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(MoeDev d) {
-  __shared__ int part[SCAN_WAVES][64];
-  const int e = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int NB = (d.T + 63) / 64;
-  const int per = (NB + SCAN_WAVES - 1) / SCAN_WAVES;
-  const int b_lo = min(NB, w * per), b_hi = min(NB, b_lo + per);
+__global__ __launch_bounds__(64 * PLAN_WAVES) void plan_kernel(MoeDev d, int nb) {
+  __shared__ int part[PLAN_WAVES][64];
+  __shared__ int pos_pre[TLC_MAX_WORLD + 1][64];  // rows of expert e before chunk position p
+  __shared__ int s_cnt[64], s_off[65], s_pst[65];
+  __shared__ int key_cnt[TLC_MAX_WORLD];  // pairs per readiness key, then the first slot of each
+  __shared__ int carry[TLC_MAX_WORLD];
+  __shared__ int wave_cnt[PLAN_WAVES][TLC_MAX_WORLD];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int e = lane;
+  const int bpc = blocks_per_chunk(d);
+  const int W = d.world;
   const bool lane_ok = e < d.E;
+  // per-expert totals of each wavefront's run of blocks
+  const int per = (nb + PLAN_WAVES - 1) / PLAN_WAVES;
+  const int b_lo = min(nb, w * per), b_hi = min(nb, b_lo + per);
   int v[16];
   int tot = 0;
   for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
@@ -157,169 +196,145 @@ __global__ __launch_bounds__(64 * SCAN_WAVES) void scan_kernel(MoeDev d) {
     for (int i = 0; i < 16; ++i) tot += v[i];
   }
   part[w][e] = tot;
+  if (tid < TLC_MAX_WORLD) {
+    key_cnt[tid] = 0;
+    carry[tid] = 0;
+  }
   __syncthreads();
+  // each block's counts become their exclusive prefix; the first block of a
+  // chunk position gives the rows before that position
   int run = 0;
   for (int u = 0; u < w; ++u) run += part[u][e];
-  // a run of at most 16 blocks is still in v[]; longer runs are read again
+  int pos = (b_lo + bpc - 1) / bpc, pos_b = pos * bpc;  // next position's first block
   for (int b0 = b_lo; b0 < b_hi; b0 += 16) {
-    if (per > 16) {
+    if (per > 16) {  // a run of at most 16 blocks is still in v[]
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         v[i] = (lane_ok && b0 + i < b_hi) ? d.blk[static_cast<int64_t>(b0 + i) * d.E + e] : 0;
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if (lane_ok && b0 + i < b_hi) d.blk[static_cast<int64_t>(b0 + i) * d.E + e] = run;
+      const int b = b0 + i;
+      if (lane_ok && b < b_hi) {
+        d.blk[static_cast<int64_t>(b) * d.E + e] = run;
+        if (b == pos_b) {
+          pos_pre[pos][e] = run;
+          ++pos;
+          pos_b += bpc;
+        }
+      }
       run += v[i];
     }
   }
-  if (w != 0) return;
-  run = 0;
-  for (int u = 0; u < SCAN_WAVES; ++u) run += part[u][e];
-  const int cnt = e < d.E ? run : 0;
-  const int tiles = (cnt + d.bm - 1) / d.bm;
-  // exclusive scans over the experts (lanes)
-  int off = cnt, pst = tiles;
+  if (w == 0) {
+    run = 0;
+    for (int u = 0; u < PLAN_WAVES; ++u) run += part[u][e];
+    const int cnt = lane_ok ? run : 0;
+    const int tiles = (cnt + d.bm - 1) / d.bm;
+    // exclusive scans over the experts (lanes)
+    int off = cnt, pst = tiles;
 #pragma unroll
-  for (int sh = 1; sh < 64; sh <<= 1) {
-    const int o = __shfl_up(off, sh), q = __shfl_up(pst, sh);
-    if (e >= sh) {
-      off += o;
-      pst += q;
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int o = __shfl_up(off, sh), q = __shfl_up(pst, sh);
+      if (e >= sh) {
+        off += o;
+        pst += q;
+      }
+    }
+    if (lane_ok) {
+      pos_pre[W][e] = cnt;
+      s_cnt[e] = cnt;
+      s_off[e] = off - cnt;
+      s_pst[e] = pst - tiles;
+      d.counts[e] = cnt;
+      d.offsets[e] = off - cnt;
+      if (e == d.E - 1) {
+        s_off[d.E] = off;
+        s_pst[d.E] = pst;
+        d.offsets[d.E] = off;
+      }
     }
   }
-  if (e < d.E) {
-    d.counts[e] = cnt;
-    d.offsets[e] = off - cnt;
-    d.pstart[e] = pst - tiles;
-    if (e == d.E - 1) {
-      d.offsets[d.E] = off;
-      d.pstart[d.E] = pst;
-    }
-  }
-}
-
-// One wavefront per (block of 64 arrival positions, group of 16 experts).
-constexpr int SCATTER_GROUP = 16;
-
-__global__ __launch_bounds__(64) void scatter_kernel(MoeDev d) {
-  const int b = blockIdx.x, g0 = blockIdx.y * SCATTER_GROUP, lane = threadIdx.x;
-  const int a = b * 64 + lane;
-  const bool valid = a < d.T;
-  const int t = valid ? arrival_token(d, a) : 0;
-  const unsigned long long m = valid ? d.member[t] : 0ull;
-  // lane j < 16 holds the first row of expert g0 + j for this block
-  const int ej = g0 + lane;
-  const int base = (lane < SCATTER_GROUP && ej < d.E)
-                       ? d.offsets[ej] + d.blk[static_cast<int64_t>(b) * d.E + ej]
-                       : 0;
-  int sel[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    sel[j] = (valid && j < d.k) ? d.topk[static_cast<int64_t>(t) * d.k + j] : -1;
-  const unsigned long long below = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int j = 0; j < SCATTER_GROUP; ++j) {
-    const int e = g0 + j;
-    const bool in = e < d.E && ((m >> e) & 1ull);
-    const unsigned long long bal = __ballot(in);
-    const int first = __shfl(base, j);
-    if (in) {
-      const int r = first + __popcll(bal & below);
-      d.row_token[r] = t;
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (sel[q] == e) d.slot[static_cast<int64_t>(t) * d.k + q] = r;
-    }
-  }
-}
-
-// Pair q = (expert e, m-tile mt) by one wavefront: the readiness key (latest
-// consume position of the chunks its rows come from) and the chunk mask.
-__device__ inline void pair_one(const MoeDev& d, int q, int lane) {
-  int lo = 0, hi = d.E - 1;  // expert e with pstart[e] <= q < pstart[e+1]
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (d.pstart[mid] <= q) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int mt = q - d.pstart[e];
-  const int first = d.offsets[e] + mt * d.bm;
-  const int rows = min(d.bm, d.counts[e] - mt * d.bm);
-  uint32_t mask = 0;
-  int key = 0;
-  for (int i = lane; i < rows; i += 64) {
-    const int c = d.row_token[first + i] / d.Tc;
-    mask |= 1u << c;
-    key = max(key, (c - d.rank + d.world) % d.world);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    mask |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(mask), off));
-    key = max(key, __shfl_xor(key, off));
-  }
-  if (lane == 0) {
-    d.pair_key[q] = d.order == TLC_ORDER_NATURAL ? 0 : key;
-    d.pair_mask[q] = mask;
-  }
-}
-
-__global__ __launch_bounds__(256) void pair_kernel(MoeDev d) {
-  const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (q < d.pstart[d.E]) pair_one(d, q, threadIdx.x & 63);
-}
-
-__global__ __launch_bounds__(1024) void sort_kernel(MoeDev d) {
-  constexpr int NW = 16;  // wavefronts per workgroup
-  __shared__ int bucket[TLC_MAX_WORLD + 1];
-  __shared__ int carry[TLC_MAX_WORLD];
-  __shared__ int wave_cnt[NW][TLC_MAX_WORLD];
-  const int P = d.pstart[d.E];
-  const int W = d.world;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid <= TLC_MAX_WORLD) bucket[tid] = 0;
-  if (tid < TLC_MAX_WORLD) carry[tid] = 0;
   __syncthreads();
-  for (int q = tid; q < P; q += blockDim.x) atomicAdd(&bucket[d.pair_key[q] + 1], 1);
+  const int P = s_pst[d.E];
+  // pair q = (expert e, m-tile mt): its expert, readiness key (the latest
+  // chunk position among its rows; 0 in natural order) and chunk mask, read
+  // off the expert's rows per position (rows pos_pre[p][e] .. pos_pre[p+1][e]
+  // - 1 come from the chunk consumed p-th)
+  auto pair_info = [&](int q, int* pe, uint32_t* pmask) __attribute__((always_inline)) {
+    int lo = 0, hi = d.E - 1;  // expert with s_pst[e] <= q < s_pst[e+1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pst[mid] <= q) lo = mid; else hi = mid - 1;
+    }
+    const int ex = lo;
+    const int r0 = (q - s_pst[ex]) * d.bm, r1 = min(r0 + d.bm, s_cnt[ex]);
+    uint32_t mask = 0;
+    int key = 0;
+    int c = d.rank;  // chunk consumed p-th
+    for (int p = 0; p < W; ++p) {
+      if (max(pos_pre[p][ex], r0) < min(pos_pre[p + 1][ex], r1)) {
+        mask |= 1u << c;
+        key = p;
+      }
+      c = c + 1 == W ? 0 : c + 1;
+    }
+    *pe = ex;
+    *pmask = mask;
+    return d.order == TLC_ORDER_NATURAL ? 0 : key;
+  };
+  // the first batch of pairs keeps its information in registers
+  int ex0 = 0;
+  uint32_t mask0 = 0;
+  const int key0 = tid < P ? pair_info(tid, &ex0, &mask0) : -1;
+  if (key0 >= 0) atomicAdd(&key_cnt[key0], 1);
+  for (int q = tid + blockDim.x; q < P; q += blockDim.x) {
+    int ex;
+    uint32_t mask;
+    atomicAdd(&key_cnt[pair_info(q, &ex, &mask)], 1);
+  }
   __syncthreads();
-  if (tid == 0) {
-    for (int w = 0; w < W; ++w) bucket[w + 1] += bucket[w];
-    *d.n_tiles = P * d.ntiles_n;
+  if (w == 0) {
+    // exclusive scan of the key counts: the first pair slot of each key
+    const int kc = lane < W ? key_cnt[lane] : 0;
+    int incl = kc;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) {
+      const int o = __shfl_up(incl, sh);
+      if (lane >= sh) incl += o;
+    }
+    if (lane < W) key_cnt[lane] = incl - kc;
+    if (lane == 0) *d.n_tiles = P * d.ntiles_n;
   }
   __syncthreads();
   // stable ranks: pairs in q order, a batch of blockDim.x pairs at a time
   for (int q0 = 0; q0 < P; q0 += blockDim.x) {
     const int q = q0 + tid;
-    const bool valid = q < P;
-    const int key = valid ? d.pair_key[q] : -1;
+    int ex = ex0;
+    uint32_t mask = mask0;
+    const int key = q0 == 0 ? key0 : (q < P ? pair_info(q, &ex, &mask) : -1);
     int local = 0;
-    for (int w = 0; w < W; ++w) {
-      const unsigned long long bal = __ballot(key == w);
-      if (key == w) local = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) wave_cnt[wave][w] = __popcll(bal);
+    for (int u = 0; u < W; ++u) {
+      const unsigned long long bal = __ballot(key == u);
+      if (key == u) local = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wave_cnt[w][u] = __popcll(bal);
     }
     __syncthreads();
-    if (valid) {
+    if (key >= 0) {
       int rank = carry[key] + local;
-      for (int v = 0; v < wave; ++v) rank += wave_cnt[v][key];
-      int lo = 0, hi = d.E - 1;  // expert e with pstart[e] <= q < pstart[e+1]
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (d.pstart[mid] <= q) lo = mid; else hi = mid - 1;
-      }
-      const int e = lo;
-      const int mt = q - d.pstart[e];
-      const int m0 = d.offsets[e] + mt * d.bm;
-      const int rows = min(d.bm, d.counts[e] - mt * d.bm);
-      const int out = (bucket[key] + rank) * d.ntiles_n;
+      for (int u = 0; u < w; ++u) rank += wave_cnt[u][key];
+      const int mt = q - s_pst[ex];
+      const int m0 = s_off[ex] + mt * d.bm;
+      const int rows = min(d.bm, s_cnt[ex] - mt * d.bm);
+      const int out = (key_cnt[key] + rank) * d.ntiles_n;
       for (int nt = 0; nt < d.ntiles_n; ++nt) {
         tlc_tile tl;
         tl.m0 = m0;
         tl.n0 = nt * d.bn;
         tl.m_rows = rows;
         tl.n_cols = min(d.bn, d.N - nt * d.bn);
-        tl.expert = e;
-        tl.chunk_mask = d.pair_mask[q];
+        tl.expert = ex;
+        tl.chunk_mask = mask;
         tl.key = key;
         tl.split = 0;
         d.plan[out + nt] = tl;
@@ -328,11 +343,51 @@ __global__ __launch_bounds__(1024) void sort_kernel(MoeDev d) {
     __syncthreads();
     if (tid < W) {
       int add = 0;
-      for (int v = 0; v < NW; ++v) add += wave_cnt[v][tid];
+      for (int u = 0; u < PLAN_WAVES; ++u) add += wave_cnt[u][tid];
       carry[tid] += add;
     }
     __syncthreads();
   }
+}
+
+// One wavefront per (four blocks, group of 16 experts): lanes 16 s .. 16 s + 15
+// hold the tokens of block 4 x + s.
+constexpr int SCATTER_GROUP = 16;
+
+__global__ __launch_bounds__(64) void scatter_kernel(MoeDev d, int nb) {
+  const int lane = threadIdx.x, g0 = blockIdx.y * SCATTER_GROUP;
+  const int seg = lane >> 4, i = lane & 15;
+  const int b = blockIdx.x * 4 + seg;
+  const int t = b < nb ? block_token(d, blocks_per_chunk(d), b, i) : -1;
+  const bool valid = t >= 0;
+  const unsigned long long m = valid ? d.member[t] : 0ull;
+  // lane (seg, j) holds the first row of expert g0 + j for block b
+  const int ej = g0 + i;
+  const int base = (b < nb && ej < d.E) ? d.offsets[ej] + d.blk[static_cast<int64_t>(b) * d.E + ej] : 0;
+  int sel[16], row[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    sel[q] = (valid && q < d.k) ? d.topk[static_cast<int64_t>(t) * d.k + q] : -1;
+    row[q] = 0;
+  }
+  const unsigned long long before = ((1ull << lane) - 1ull) & (0xFFFFull << (16 * seg));
+#pragma unroll
+  for (int j = 0; j < SCATTER_GROUP; ++j) {
+    const int e = g0 + j;
+    const bool in = e < d.E && ((m >> e) & 1ull);
+    const unsigned long long bal = __ballot(in);
+    const int first = __shfl(base, 16 * seg + j);
+    if (in) {
+      const int r = first + __popcll(bal & before);
+      d.row_token[r] = t;
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (sel[q] == e) row[q] = r;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (sel[q] >= g0 && sel[q] < g0 + SCATTER_GROUP) d.slot[static_cast<int64_t>(t) * d.k + q] = row[q];
 }
 
 }  // namespace
@@ -341,18 +396,15 @@ int64_t moe_max_pairs(int32_t T, int32_t topk, int32_t experts, int32_t bm) {
   return static_cast<int64_t>(T) * topk / bm + experts;
 }
 
+int64_t moe_max_blocks(int64_t T) { return (T + BLK - 1) / BLK + TLC_MAX_WORLD; }
+
 tlc_status launch_moe_route(const MoeDev& d, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int nb = (d.T + 63) / 64;
-  const int topk_grid = (d.T + 3) / 4;
-  hipLaunchKernelGGL(topk_kernel, dim3(topk_grid > d.copy.wgs ? topk_grid : d.copy.wgs), dim3(256), 0,
-                     s, d);
-  hipLaunchKernelGGL(block_count_kernel, dim3(nb), dim3(64), 0, s, d);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(64 * SCAN_WAVES), 0, s, d);
-  hipLaunchKernelGGL(scatter_kernel, dim3(nb, (d.E + SCATTER_GROUP - 1) / SCATTER_GROUP), dim3(64),
-                     0, s, d);
-  hipLaunchKernelGGL(pair_kernel, dim3((d.max_pairs + 3) / 4), dim3(256), 0, s, d);
-  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(1024), 0, s, d);
+  const int nb = d.world * ((d.Tc + BLK - 1) / BLK);
+  hipLaunchKernelGGL(route_kernel, dim3(nb + d.copy.wgs), dim3(64 * BLK), 0, s, d, nb);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64 * PLAN_WAVES), 0, s, d, nb);
+  hipLaunchKernelGGL(scatter_kernel, dim3((nb + 3) / 4, (d.E + SCATTER_GROUP - 1) / SCATTER_GROUP), dim3(64),
+                     0, s, d, nb);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TLC_ERR_HIP, "moe route launch: %s", hipGetErrorString(e));
   return ok();

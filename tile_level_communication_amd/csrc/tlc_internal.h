@@ -132,7 +132,7 @@ tlc_status launch_signals_rewind(tlc_signals* sig, void* stream);
 
 struct MoeDev {
   const float* logits;
-  int32_t T, E, k, Tc, world, rank, N, bm, bn, order, ntiles_n, max_pairs;
+  int32_t T, E, k, Tc, world, rank, N, bm, bn, order, ntiles_n;
   int32_t* topk;
   float* gates;
   int32_t* counts;
@@ -142,10 +142,7 @@ struct MoeDev {
   tlc_tile* plan;
   int32_t* n_tiles;
   unsigned long long* member;  // workspace: T masks
-  int32_t* pstart;             // workspace: E + 1
-  int32_t* pair_key;           // workspace: max_pairs
-  uint32_t* pair_mask;         // workspace: max_pairs
-  int32_t* blk;                // workspace: ceil(T/64) x E block counts, then their prefixes
+  int32_t* blk;                // workspace: blocks x E block counts, then their prefixes
   // Optional landing of the peers' token chunks by the top-k kernel's first
   // copy.wgs workgroups (copy.wgs = 0: none), flags raised to `epoch` in sig.
   CopyPlan copy;
@@ -154,6 +151,8 @@ struct MoeDev {
 };
 
 int64_t moe_max_pairs(int32_t T, int32_t topk, int32_t experts, int32_t bm);
+// Arrival blocks of the routing for T tokens, at most (any world and chunk size).
+int64_t moe_max_blocks(int64_t T);
 tlc_status launch_moe_route(const MoeDev& d, void* stream);
 
 // The static routing workspace (tlc_moe_route_static): its size, and its
