@@ -103,6 +103,33 @@ def test_moe_route_long_block_scan():
     _check_routing(prob, ref, tlc.ORDER_RANK_OFFSET)
 
 
+ROUTE_EDGES = [
+    # name, W, Tc, E, k, tile
+    ("w1_tc70_e64_k16", 1, 70, 64, 16, 128),     # one rank, the largest k, a partial block
+    ("w3_tc5_e10_k3", 3, 5, 10, 3, 256),         # chunks shorter than a block, a partial expert group
+    ("w32_tc7_e33_k16", 32, 7, 33, 16, 128),     # the largest world, 33 experts
+    ("w5_tc17_e1_k1", 5, 17, 1, 1, 256),         # a single expert
+]
+
+
+@pytest.mark.parametrize("shape", ROUTE_EDGES, ids=[s[0] for s in ROUTE_EDGES])
+def test_moe_route_edge_shapes(shape):
+    """The routing alone at the edges of its blocking (chunks of fewer or more
+    than 16 tokens, expert counts that do not fill a group of 16, one or 32
+    ranks, k = 1 and 16, one expert): every routing array and the tile list bit
+    for bit, at the first and last rank, in both orders."""
+    name, W, Tc, E, k, tile = shape
+    inp = si.moe_inputs(340 + W, W, Tc, 64, 128, E)
+    for rank in sorted({0, W - 1}):
+        for order in (tlc.ORDER_RANK_OFFSET, tlc.ORDER_NATURAL):
+            log(f"[moe route edge] {name} rank={rank} order={order}")
+            ref = om.route(inp.logits, k, W, rank, Tc)
+            prob = MoEProblem(inp.x_chunks, inp.logits, inp.w, rank, k, tile, tile, tlc.B_KN, order)
+            prob.route()
+            torch.cuda.synchronize()
+            _check_routing(prob, ref, order)
+
+
 @pytest.mark.parametrize("rank", [0, 5])
 def test_moe_full_size(rank):
     wl = si.WORKLOADS[4]
