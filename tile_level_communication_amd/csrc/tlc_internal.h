@@ -143,8 +143,9 @@ struct MoeDev {
   int32_t* n_tiles;
   unsigned long long* member;  // workspace: T masks
   int32_t* blk;                // workspace: blocks x E block counts, then their prefixes
-  // Optional landing of the peers' token chunks by the top-k kernel's first
-  // copy.wgs workgroups (copy.wgs = 0: none), flags raised to `epoch` in sig.
+  // Optional landing of the peers' token chunks by copy.wgs workgroups of the
+  // top-k kernel after the routing's own (copy.wgs = 0: none), flags raised to
+  // `epoch` in sig.
   CopyPlan copy;
   tlc_signals* sig;
   uint32_t epoch;
