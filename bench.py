@@ -25,6 +25,9 @@ a leg whose flag waits failed on the device reports no derived figure.
 
 Inputs are seeded synthetic data resident in HBM when the timed region starts.
 The CPU oracle is timed on a bounded sample of the same workload (cpu_baseline).
+The dense lines also time the same product through the vendor library
+(vendor_gemm: hipBLASLt behind torch, bf16 and fp32 outputs, both weight
+layouts) as context for the GEMM's roofline fraction; --no-vendor skips it.
 """
 from __future__ import annotations
 
@@ -109,6 +112,8 @@ def parse(argv=None):
                     help="work distribution (default: static for ag, rs and ar; per landing for moe)")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip timing the same dense product through the vendor library")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--warm-seconds", type=float, default=0.5,
                     help="minimum busy time of each leg's warm-up (after the W warm-up steps)")
@@ -294,6 +299,39 @@ def cpu_baseline(kind, inp, budget_s, rank=0, topk=0):
         with threadpool_limits(limits=1):
             v1, what1, dt1 = _oracle_sample(kind, inp, budget_s / 2, rank, topk)
         out["one_thread"] = {"value": round(v1, 6), "cores": 1, "sample": f"{what1}, float64, {dt1:.1f} s"}
+    return out
+
+
+def vendor_gemm(torch, tlc, a, b, b_layout, gemm_ms):
+    """The same product through the vendor library (hipBLASLt behind torch.matmul,
+    and torch.mm with an fp32 output as this library writes), for a K x N and an
+    N x K weight: context for the roofline fraction, never the measured path."""
+    M, K = a.shape
+    b_kn = (b if b_layout == tlc.B_KN else b.t()).contiguous()
+    b_nk = b_kn.t().contiguous()
+    flops = 2.0 * M * b_kn.shape[1] * K
+    out = {"library": "hipBLASLt through torch.matmul (bf16 output) and torch.mm(out_dtype=float32)",
+           "this_kernel_tflops": round(flops / gemm_ms / 1e9, 1)}
+    variants = {"KN_bf16_out": lambda: torch.matmul(a, b_kn),
+                "NK_bf16_out": lambda: torch.matmul(a, b_nk.t()),
+                "KN_f32_out": lambda: torch.mm(a, b_kn, out_dtype=torch.float32),
+                "NK_f32_out": lambda: torch.mm(a, b_nk.t(), out_dtype=torch.float32)}
+    for name, fn in variants.items():
+        try:
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            out[name] = round(flops / (e0.elapsed_time(e1) / 20) / 1e9, 1)
+        except Exception as e:  # an older torch without out_dtype
+            out[name] = f"unavailable: {type(e).__name__}"
+    del b_kn, b_nk
+    torch.cuda.empty_cache()
     return out
 
 
@@ -486,6 +524,8 @@ def run_ag(args, torch, tlc, si, workloads):
         "device_status": status,
         "other_landings": other_landings(flops, t_comp, others, t_copy_others),
     }
+    if not args.no_vendor:
+        extra["vendor_gemm"] = vendor_gemm(torch, tlc, prob.a, prob.b, prob.b_layout, gemm_comp_ms)
     line = base_line(args, head["value"], t_fused, extra)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline("ag", inp, args.cpu_seconds)
@@ -713,6 +753,8 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False, sub_object=False):
     }
     if sends is not None:
         extra["sends"] = sends
+    if not args.no_vendor:
+        extra["vendor_gemm"] = vendor_gemm(torch, tlc, prob.a, prob.b, prob.b_layout, gemm_ms)
     if other_kinds:
         extra["other_landings"] = other_landings(flops, t_comp, others, t_copy_others)
     if sub_object:
