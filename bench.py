@@ -56,11 +56,11 @@ PEAK_HBM_GBS = 8000.0
 # counters were taken.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE) or None
-    "ag": {"gemm": (222439.1, 102404.9)},
-    "moe": {"gemm": (249471.8, 98304.0)},
-    "rs": {"gemm": (50662.4, 65536.0), "reduce": (32788.7, 16384.5)},
-    "ar": {"gemm": (50662.4, 65536.0), "reduce": (32788.7, 16384.5)},
-    "rs_long": {"gemm": (3153999.9, 2621440.0), "reduce": (1310743.9, 327680.0)},
+    "ag": {"gemm": (222355.7, 102416.2)},
+    "moe": {"gemm": (249350.8, 98304.0)},
+    "rs": {"gemm": (50578.9, 65536.0), "reduce": (32788.6, 16385.6)},
+    "ar": {"gemm": (50578.9, 65536.0), "reduce": (32788.6, 16385.6)},
+    "rs_long": {"gemm": (3153954.0, 2621440.0), "reduce": (1310743.8, 327680.0)},
 }
 
 
