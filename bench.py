@@ -58,9 +58,9 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE) or None
     "ag": {"gemm": (222355.7, 102416.2)},
     "moe": {"gemm": (249350.8, 98304.0)},
-    "rs": {"gemm": (50578.9, 65536.0), "reduce": (32788.6, 16385.6)},
-    "ar": {"gemm": (50578.9, 65536.0), "reduce": (32788.6, 16385.6)},
-    "rs_long": {"gemm": (3153954.0, 2621440.0), "reduce": (1310743.8, 327680.0)},
+    "rs": {"gemm": (50581.4, 65536.0), "reduce": (32788.6, 16384.7)},
+    "ar": {"gemm": (50581.4, 65536.0), "reduce": (32788.6, 16384.7)},
+    "rs_long": {"gemm": (3153921.1, 2621440.0), "reduce": (1310743.9, 327680.0)},
 }
 
 

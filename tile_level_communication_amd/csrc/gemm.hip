@@ -429,16 +429,20 @@ typedef float f32x4_st __attribute__((ext_vector_type(4)));
 // 8, so that the two halves of a wavefront, four rows apart, write different
 // banks.  The caller makes the stages idle first (every wavefront's loads in,
 // a workgroup barrier) and keeps the next unit's loads out until every
-// wavefront has read its staging area back (a barrier after).
+// wavefront has read its staging area back (a barrier after).  In scatter
+// mode with sends the stores are device-coherent (write-through) 16-byte
+// buffer stores.
 __device__ inline int stage_index(int r, int c) {
   return r * 128 + ((((c >> 2) ^ (((r >> 2) & 1) << 3))) << 2) + (c & 3);
 }
 
+template <int KIND>
 __device__ inline void store_tile_rows(const GemmParams& p, const tlc_tile& tl, f32x16 (&acc)[4][4],
                                        int wm, int wn, int lane, TLC_LDS float* st) {
   const int64_t ldc = p.ldc;
   float* cbase = p.c + static_cast<int64_t>(tl.m0 + wm * 128) * ldc + tl.n0 + wn * 128;
   const int rows_left = tl.m_rows - wm * 128, cols_left = tl.n_cols - wn * 128;
+
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -453,8 +457,17 @@ __device__ inline void store_tile_rows(const GemmParams& p, const tlc_tile& tl, 
     for (int rr = 0; rr < 32; ++rr) {
       const int r = 2 * rr + (lane >> 5), c = (lane & 31) * 4;
       const f32x4_st v = *reinterpret_cast<const TLC_LDS f32x4_st*>(st + stage_index(r, c));
-      if (h * 64 + r < rows_left && c < cols_left)
+      if constexpr (KIND == KIND_RS_NOTIFY) {
+        // scatter mode with sends: device-coherent stores (written through past
+        // this XCD's L2), through a buffer resource over the instruction's two rows
+        const __amdgpu_buffer_rsrc_t rc =
+            copy_rsrc(cbase + static_cast<int64_t>(h * 64 + 2 * rr) * ldc, static_cast<uint32_t>(2 * ldc * 4));
+        if (h * 64 + r < rows_left && c < cols_left)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(copy_vec, v), rc,
+                                                 static_cast<int>(((lane >> 5) * ldc + c) * 4), 0, CPOL_SC1);
+      } else if (h * 64 + r < rows_left && c < cols_left) {
         *reinterpret_cast<f32x4_st*>(cbase + static_cast<int64_t>(h * 64 + r) * ldc + c) = v;
+      }
     }
   }
 }
@@ -1033,13 +1046,13 @@ struct Tile4w {
       (void)s_flag;
     }
 
-    if constexpr (FAST && KIND != KIND_RS_NOTIFY) {
+    if constexpr (FAST) {
       // every wavefront's loads (also those past the K range) are in and
       // every wavefront is done with the stages: they hold the staging areas
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       TLC_LDS u32x4* mine = wave == 0 ? A0 : (wave == 1 ? A1 : (wave == 2 ? B0 : B1));
-      store_tile_rows(p, tl, acc, wm, wn, lane, reinterpret_cast<TLC_LDS float*>(mine));
+      store_tile_rows<KIND>(p, tl, acc, wm, wn, lane, reinterpret_cast<TLC_LDS float*>(mine));
       __syncthreads();  // the next unit's loads refill the stages
     } else {
       store_tile<KIND, WM, WN, FM, FN>(p, tl, acc, wm, wn, lane);
