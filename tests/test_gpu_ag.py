@@ -31,6 +31,9 @@ SHAPES = [
     ("w2_256x256x512_t256_straddle", 2, 128, 512, 256, 256),
     ("w3_ragged_600x392x320_t256", 3, 200, 320, 392, 256),
     ("w5_ragged_385x136x128_t128", 5, 77, 128, 136, 128),
+    # whole-tile kernel (M % 256 == 0, an even number of K steps) with a ragged
+    # last column tile of 136: one wavefront column stores 8 of its 128 columns
+    ("w2_whole_512x392x256_t256", 2, 256, 256, 392, 256),
 ]
 
 

@@ -25,6 +25,9 @@ SHAPES = [
     ("w2_256x256x512_t128", 2, 128, 512, 256, 128),
     ("w4_ragged_400x264x192_t256", 4, 100, 192, 264, 256),
     ("w3_ragged_600x392x320_t128", 3, 200, 320, 392, 128),
+    # whole-tile kernel (M % 256 == 0, an even number of K steps) with a last
+    # column tile of 8: one wavefront column stores nothing
+    ("w2_whole_512x264x256_t256", 2, 256, 256, 264, 256),
 ]
 
 
