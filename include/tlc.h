@@ -227,6 +227,17 @@ tlc_status tlc_chunk_plan(const tlc_plan_desc* desc, tlc_tile* tiles, int64_t ca
  * error (TIMEOUT, BAD_PLAN), after which it must be zero-filled before reuse. */
 int64_t tlc_split_workspace_bytes(int64_t n_split_tiles, int32_t split_k, int32_t bm, int32_t bn);
 
+/* Bytes of the workspace the stream-K tail (TLC_SCHED_STREAMK) needs on a
+ * grid of `grid` workgroups (0: the largest gfx950 part's 256 compute units,
+ * enough for any grid): grid blocks of 256 + 4 * 256 * 256 * 4 bytes, an
+ * arrival counter and up to four fp32 partial tiles per tail tile (a tail
+ * has fewer tiles than the grid has workgroups).  Negative grid: -1.
+ * The caller allocates it in device memory (256-byte aligned) and zero-fills it
+ * once; each call leaves the counters at zero again, except after a device
+ * error, after which it must be zero-filled before reuse.  Not from the
+ * pages: a work-sharing device of this library (see TLC_SCHED_STREAMK). */
+int64_t tlc_streamk_workspace_bytes(int32_t grid);
+
 /* ------------------------------------------------------------- signals ---- */
 
 /* Allocate / free one zeroed tlc_signals block in fine-grained device memory
@@ -281,7 +292,8 @@ tlc_status tlc_read_signals(const tlc_signals* sig, void* stream, tlc_signals* o
  *   workspace  device, tlc_split_workspace_bytes(...) bytes for the plan's
  *          split tiles (zero-filled before first use), or NULL / 0 bytes if the
  *          plan splits no tile.  A split tile whose slot lies beyond
- *          workspace_bytes is reported as BAD_PLAN.
+ *          workspace_bytes is reported as BAD_PLAN.  With TLC_SCHED_STREAMK:
+ *          the tail's workspace (tlc_streamk_workspace_bytes) instead.
  * Streams: the GEMM runs on `compute_stream`, the landing on the copy streams.
  * grid: persistent workgroups (0 = every compute unit the landing leaves free).
  *   With a COPY_ENGINE, CU or MEMCPY landing a grid above (compute units - 32)
@@ -291,9 +303,32 @@ tlc_status tlc_read_signals(const tlc_signals* sig, void* stream, tlc_signals* o
  * schedule: TLC_SCHED_DYNAMIC -- workgroups take the next unit in plan order
  *   from a counter in `sig` as they become free (units that wait for a late
  *   chunk then do not hold back the ones behind them); TLC_SCHED_STATIC --
- *   workgroup slot g runs units g, g + grid, g + 2 grid, ...
+ *   workgroup slot g runs units g, g + grid, g + 2 grid, ...; TLC_SCHED_STREAMK
+ *   -- static slots for the first floor(n_tiles / grid) * grid units, then the
+ *   remaining tiles (the last chunks' tiles, in plan order) split along K into
+ *   S pieces each (2 <= S <= 4; piece s covers the 64-wide K steps from
+ *   s * KT / S to (s + 1) * KT / S, each rounded down to even, KT = K / 64),
+ *   piece s of the j-th such tile being item s * (tiles in the tail) + j of the
+ *   slots' walk: pieces over the same K steps of neighbouring tiles run side
+ *   by side, so that they share their operands in the caches as whole tiles
+ *   do.  S is chosen on the host so that the slot with the most tail steps
+ *   has the fewest; without a gain over one more round of whole tiles there is
+ *   no tail.  A tile's pieces are summed in the workspace
+ *   (tlc_streamk_workspace_bytes(grid) bytes) by the piece that completes it,
+ *   in K order, so the result does not depend on which workgroup finishes
+ *   first (it may differ from the other schedules' in rounding, since the K
+ *   sums are grouped differently).  The last round then ends together on every
+ *   compute unit instead of leaving units idle (wave quantization: AutoOverlap
+ *   §2.1 and Fig. 2(a); the split into K pieces is this library's, not the
+ *   pages').  Default grid: every compute unit the landing leaves free.  The
+ *   tail is used when the kernel that runs only whole 256 x 256 tiles applies
+ *   (M % 256 == 0, K / 64 even, bm = bn = 256) and the tiles do not fill the
+ *   grid evenly; otherwise the schedule is TLC_SCHED_STATIC and the workspace
+ *   is not touched.  The plan must not split tiles (split_k 0): the workspace
+ *   serves the tail alone.  A workspace smaller than needed is refused with
+ *   INVALID_ARG.
  * timeout_ns: per-wait limit (0 = 2 s). */
-enum { TLC_SCHED_DYNAMIC = 0, TLC_SCHED_STATIC = 1 };
+enum { TLC_SCHED_DYNAMIC = 0, TLC_SCHED_STATIC = 1, TLC_SCHED_STREAMK = 2 };
 typedef struct {
   const tlc_tile* plan; /* device, n_tiles entries, execution order */
   int64_t n_tiles;
@@ -555,7 +590,9 @@ typedef struct {
   int32_t land;
   int32_t grid;
   int64_t timeout_ns;
-  int32_t schedule; /* TLC_SCHED_* as in tlc_ag_args (MoE tiles are never split) */
+  int32_t schedule; /* TLC_SCHED_* as in tlc_ag_args (MoE tiles are never split;
+                       TLC_SCHED_STREAMK runs as TLC_SCHED_STATIC: the unit count
+                       is known only on the device) */
   int32_t copy_wgs; /* as in tlc_ag_args */
 } tlc_moe_args;
 

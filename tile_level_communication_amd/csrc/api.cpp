@@ -2,10 +2,12 @@
 // See include/tlc.h for the contract of every function.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "tlc_internal.h"
 
@@ -211,7 +213,7 @@ tlc_status check_dense(const char* who, int32_t M, int32_t N, int32_t K, int32_t
 // Work distribution and split-tile workspace of one GEMM launch: checked with
 // the other arguments, applied when the launch parameters are filled in.
 tlc_status check_schedule(int32_t schedule, const void* ws, int64_t ws_bytes, const char* who) {
-  if (schedule != TLC_SCHED_DYNAMIC && schedule != TLC_SCHED_STATIC)
+  if (schedule != TLC_SCHED_DYNAMIC && schedule != TLC_SCHED_STATIC && schedule != TLC_SCHED_STREAMK)
     return fail(TLC_ERR_INVALID_ARG, "%s: schedule %d unknown", who, schedule);
   if (ws_bytes < 0 || (ws_bytes > 0 && !ws))
     return fail(TLC_ERR_INVALID_ARG, "%s: workspace NULL with %lld bytes", who,
@@ -223,8 +225,63 @@ tlc_status check_schedule(int32_t schedule, const void* ws, int64_t ws_bytes, co
 
 void set_schedule(GemmParams* p, int32_t schedule, void* ws, int64_t ws_bytes) {
   p->dynamic = schedule == TLC_SCHED_DYNAMIC;
-  p->split_ws = static_cast<char*>(ws);
-  p->split_bytes = ws ? ws_bytes : 0;
+  // stream-K: the workspace serves the tail (configure_tail), not split tiles
+  const bool sk = schedule == TLC_SCHED_STREAMK;
+  p->split_ws = sk ? nullptr : static_cast<char*>(ws);
+  p->split_bytes = (ws && !sk) ? ws_bytes : 0;
+}
+
+// The most K steps one of G static slots runs when the t_sk tail tiles are
+// split into S pieces (piece s of tile j is item s * t_sk + j, slot item % G).
+int64_t tail_cost(int64_t t_sk, int64_t G, int KT, int S) {
+  std::vector<int64_t> per(static_cast<size_t>(G), 0);
+  for (int64_t q = 0; q < S * t_sk; ++q) {
+    const int sp = static_cast<int>(q / t_sk);
+    per[static_cast<size_t>(q % G)] += (((sp + 1) * KT / S) & ~1) - ((sp * KT / S) & ~1);
+  }
+  return *std::max_element(per.begin(), per.end());
+}
+
+// Stream-K tail (TLC_SCHED_STREAMK) for a launch of `grid` workgroups: the
+// first floor(T / G) * G units whole, then each remaining tile in S pieces
+// along K (2 <= S <= kSkMaxSplit, at least two K steps each), S chosen so
+// that the slot with the most tail steps has the fewest, counting two steps
+// of fix-up per extra piece; no tail unless that beats a round of whole
+// tiles.  Only the kernel that runs whole 256 x 256 tiles has the tail;
+// without it, or when the units fill the grid evenly, the schedule stays
+// static.
+tlc_status configure_tail(GemmParams* p, int32_t schedule, void* ws, int64_t ws_bytes, int grid,
+                          int bm, int bn, int kind, const char* who) {
+  p->sk_split = 0;
+  if (schedule != TLC_SCHED_STREAMK || grid < 1 || p->n_tiles <= 0) return TLC_OK;
+  const int KT = p->K / 64;
+  const bool whole_tile_kernel = kind != KIND_MOE && bm == 256 && bn == 256 && p->M % 256 == 0 &&
+                                 p->K % 64 == 0 && KT % 2 == 0 && p->split_bytes == 0;
+  if (!whole_tile_kernel) return TLC_OK;
+  const int64_t T = p->n_tiles, G = grid;
+  const int64_t t_dp = T / G * G, t_sk = T - t_dp;
+  if (t_sk == 0) return TLC_OK;
+  int best = 0;
+  int64_t best_cost = KT;
+  for (int S = 2; S <= kSkMaxSplit && 2 * S <= KT; ++S) {
+    const int64_t cost = tail_cost(t_sk, G, KT, S) + 2 * (S - 1);
+    if (cost < best_cost) {
+      best = S;
+      best_cost = cost;
+    }
+  }
+  if (best == 0) return TLC_OK;
+  const int64_t need = t_sk * kSkBlockBytes;
+  if (!ws || ws_bytes < need)
+    return fail(TLC_ERR_INVALID_ARG, "%s: the stream-K tail of %lld tiles on %d workgroups needs a "
+                "workspace of %lld bytes (tlc_streamk_workspace_bytes), got %lld", who,
+                static_cast<long long>(t_sk), grid, static_cast<long long>(need),
+                static_cast<long long>(ws ? ws_bytes : 0));
+  p->sk_from = t_dp;
+  p->sk_tiles = static_cast<int32_t>(t_sk);
+  p->sk_split = best;
+  p->sk_ws = static_cast<char*>(ws);
+  return TLC_OK;
 }
 
 // Co-located landing: the chunks in landing order (rank+n_local, ... mod W)
@@ -300,11 +357,14 @@ tlc_status check_grid(int grid, int reserve, int cus, const char* who) {
 }
 
 // Persistent grid: every CU left free (dynamic: no more workgroups than
-// units), or the evenly spread static default.
-int pick_grid(int requested, int dynamic, int64_t n_units, int avail) {
+// units; stream-K: every CU, the tail spreads the last tiles over them), or
+// the evenly spread static default.
+int pick_grid(int requested, int32_t schedule, int64_t n_units, int avail) {
   if (requested > 0) return requested;
   if (avail < 1) avail = 1;
-  if (dynamic) return static_cast<int>(n_units < avail ? (n_units > 0 ? n_units : 1) : avail);
+  if (schedule == TLC_SCHED_DYNAMIC)
+    return static_cast<int>(n_units < avail ? (n_units > 0 ? n_units : 1) : avail);
+  if (schedule == TLC_SCHED_STREAMK) return avail;
   return default_grid(n_units, avail);
 }
 
@@ -481,7 +541,7 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
   const int avail = info.cus - (p.do_wait ? reserve_for(a->land) : 0);
   // no units (copy-only run of the co-located landing): one workgroup per
   // copying workgroup of a full grid
-  int grid = a->n_tiles > 0 ? pick_grid(a->grid, p.dynamic, a->n_tiles, avail)
+  int grid = a->n_tiles > 0 ? pick_grid(a->grid, a->schedule, a->n_tiles, avail)
                             : (a->grid > 0 ? a->grid : avail);
   if (coloc) {
     st = set_colocated(&p, dst, src, chunk_bytes, Wf, rf, S, a->copy_wgs, grid, info.cus,
@@ -490,6 +550,9 @@ tlc_status tlc_ag_gemm(const tlc_ag_args* a, void* compute_stream, void* const* 
     if (st) return st;
     if (a->n_tiles == 0) grid = p.copy.wgs;
   }
+  st = configure_tail(&p, a->schedule, a->workspace, a->workspace_bytes, grid, a->bm, a->bn,
+                      KIND_DENSE, "tlc_ag_gemm");
+  if (st) return st;
   p.xcd_remap = grid % 8 == 0;
   st = launch_gemm(p, a->bm, a->bn, a->b_layout, KIND_DENSE, grid, compute_stream);
   return st ? st : ok();
@@ -658,7 +721,7 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
       p.dest_total = static_cast<uint32_t>(slice);
     }
     const int avail = info.cus - reserve;
-    int grid = a->n_tiles > 0 ? pick_grid(a->grid, p.dynamic, a->n_tiles, avail)
+    int grid = a->n_tiles > 0 ? pick_grid(a->grid, a->schedule, a->n_tiles, avail)
                               : (a->grid > 0 ? a->grid : avail);
     if (coloc_gather) {
       p.do_wait = 1;
@@ -669,6 +732,9 @@ static tlc_status rs_common(const tlc_rs_args* a, void* compute_stream, void* co
       if (st) return st;
       if (a->n_tiles == 0) grid = p.copy.wgs;
     }
+    st = configure_tail(&p, a->schedule, a->workspace, a->workspace_bytes, grid, a->bm, a->bn,
+                        sends ? KIND_RS_NOTIFY : KIND_DENSE, g ? "tlc_gemm_ar" : "tlc_gemm_rs");
+    if (st) return st;
     p.xcd_remap = grid % 8 == 0;
     st = launch_gemm(p, a->bm, a->bn, a->b_layout, sends ? KIND_RS_NOTIFY : KIND_DENSE, grid,
                      compute_stream);

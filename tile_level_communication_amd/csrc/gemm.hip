@@ -170,6 +170,57 @@ __device__ inline bool split_epilogue(const GemmParams& p, const tlc_tile& tl,
   return true;
 }
 
+// One piece of a tile of the stream-K tail: K steps [kt0, kt1) of the tile,
+// piece `self` in K order of `count` (count = 0: a unit of the plan, its K
+// range given by its split field).  `block`: the tile's workspace block, its
+// arrival counter at the start and piece u's partial at 256 + u * 256 KB.
+struct SkPiece {
+  int kt0, kt1;
+  int count, self;
+  char* block;
+};
+
+typedef float f32x4_st __attribute__((ext_vector_type(4)));
+
+// Tail epilogue of the whole-tile core (256 threads, 4 x 4 blocks of 32 x 32
+// per thread).  Every piece writes its fp32 partial (16-byte device-coherent
+// stores, written through past this XCD's L2: the pieces of a tile may run on
+// different XCDs), waits for the stores and counts itself in.  The piece that
+// counts itself in last rewinds the counter and returns true: it stores the
+// tile, adding the other pieces to its own while it stages them (SkAddPieces).
+__device__ inline bool sk_epilogue(const GemmParams& p, const SkPiece& pc, f32x16 (&acc)[4][4],
+                                   int* s_flag) {
+  // an opaque copy of the thread index: keeps the compiler from forming the
+  // addresses before the K loop and holding them across it
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const uint32_t voff = static_cast<uint32_t>(tid) * 16u;
+  (void)p;
+  // vector V (0..63) of the thread: block (V / 16, V / 4 % 4), elements 4 (V % 4) ..
+  {
+    const __amdgpu_buffer_rsrc_t rs =
+        copy_rsrc(pc.block + 256 + pc.self * kSkTileBytes, static_cast<uint32_t>(kSkTileBytes));
+    static_for<64>([&](auto v_c) __attribute__((always_inline)) {
+      constexpr int V = decltype(v_c)::value, I = V / 16, J = (V / 4) % 4, Q = V % 4;
+      const f32x4_st x = {acc[I][J][4 * Q], acc[I][J][4 * Q + 1], acc[I][J][4 * Q + 2],
+                          acc[I][J][4 * Q + 3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(copy_vec, x), rs, voff + V * 4096u,
+                                             0, CPOL_SC1);
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial (and loads) are in
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t* counter = reinterpret_cast<uint32_t*>(pc.block);
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == static_cast<uint32_t>(pc.count) - 1;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
 // One element of C.  Scatter mode with sends: a device-coherent store (written
 // through past this XCD's L2), so that the slice is complete in memory when
 // the notification below is raised and a copy on another engine or XCD reads
@@ -413,8 +464,6 @@ typedef short v8i16 __attribute__((ext_vector_type(8)));
 // format flags) for the LDS-writing loads below.
 typedef unsigned int rsrc_words __attribute__((ext_vector_type(4)));
 
-typedef float f32x4_st __attribute__((ext_vector_type(4)));
-
 // Epilogue of the whole-tile kernel: the wavefront's 128 x 128 fp32 sub-tile
 // to C through LDS, so that each store instruction writes 16 bytes per lane
 // and two 512-byte row pieces.  All CUs store their tiles at once at the end
@@ -436,15 +485,15 @@ __device__ inline int stage_index(int r, int c) {
   return r * 128 + ((((c >> 2) ^ (((r >> 2) & 1) << 3))) << 2) + (c & 3);
 }
 
-template <int KIND>
+template <int KIND, typename Adjust>
 __device__ inline void store_tile_rows(const GemmParams& p, const tlc_tile& tl, f32x16 (&acc)[4][4],
-                                       int wm, int wn, int lane, TLC_LDS float* st) {
+                                       Adjust adjust, int wm, int wn, int lane, TLC_LDS float* st) {
   const int64_t ldc = p.ldc;
   float* cbase = p.c + static_cast<int64_t>(tl.m0 + wm * 128) * ldc + tl.n0 + wn * 128;
   const int rows_left = tl.m_rows - wm * 128, cols_left = tl.n_cols - wn * 128;
 
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  static_for<2>([&](auto h_c) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -453,6 +502,8 @@ __device__ inline void store_tile_rows(const GemmParams& p, const tlc_tile& tl, 
         for (int j = 0; j < 4; ++j)
           st[stage_index(ii * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3), j * 32 + (lane & 31))] =
               acc[2 * h + ii][j][e];
+    // a stream-K tail tile adds the other pieces to the staged half here
+    adjust(h_c, st);
 #pragma unroll
     for (int rr = 0; rr < 32; ++rr) {
       const int r = 2 * rr + (lane >> 5), c = (lane & 31) * 4;
@@ -469,8 +520,78 @@ __device__ inline void store_tile_rows(const GemmParams& p, const tlc_tile& tl, 
         *reinterpret_cast<f32x4_st*>(cbase + static_cast<int64_t>(h * 64 + r) * ldc + c) = v;
       }
     }
-  }
+  });
 }
+
+// store_tile_rows as it is: a whole tile.
+struct NoAdjust {
+  template <int H>
+  __device__ void operator()(std::integral_constant<int, H>, TLC_LDS float*) const {}
+};
+
+// Half H (row blocks 2H and 2H + 1) of a tail tile for store_tile_rows,
+// staged in LDS with this piece's own partial: replaced by the pieces summed
+// in K order, ((x0 + x1) + x2) + ..., whichever piece completed the tile.  So
+// the result depends on the grid (where the pieces start) but not on which
+// workgroup finishes when.  The pieces before this one are summed in
+// registers and added to the staged value (t + own == own + t); the later
+// ones are added to the staged value one by one.  Element k of vector
+// w = 4 j + q of row block i is element e = 4 q + k of block (i, j).
+struct SkAddPieces {
+  const GemmParams& p;
+  const SkPiece& pc;
+  int lane;
+  template <int H>
+  __device__ void operator()(std::integral_constant<int, H>, TLC_LDS float* st) const {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const uint32_t voff = static_cast<uint32_t>(tid) * 16u;
+    // eight vectors (half a row block) at a time
+    auto load = [&](int u, int v0, f32x4_st (&x)[8]) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t rs =
+          copy_rsrc(pc.block + 256 + u * kSkTileBytes, static_cast<uint32_t>(kSkTileBytes));
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+        x[w] = __builtin_bit_cast(
+            f32x4_st, __builtin_amdgcn_raw_buffer_load_b128(
+                          rs, voff + static_cast<uint32_t>(v0 + w) * 4096u, 0, CPOL_SC1));
+    };
+    auto add_staged = [&](int ii, int w0, const f32x4_st (&x)[8]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int ww = w0 + w;
+          const int idx = stage_index(ii * 32 + 8 * (ww % 4) + 4 * (lane >> 5) + k, (ww / 4) * 32 + (lane & 31));
+          st[idx] = x[w][k] + st[idx];
+        }
+    };
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
+      for (int w0 = 0; w0 < 16; w0 += 8) {
+        const int v0 = (2 * H + ii) * 16 + w0;
+        if (pc.self > 0) {
+          f32x4_st t[8];
+          load(0, v0, t);
+          for (int u = 1; u < pc.self; ++u) {
+            f32x4_st x[8];
+            load(u, v0, x);
+#pragma unroll
+            for (int w = 0; w < 8; ++w) t[w] += x[w];
+          }
+          add_staged(ii, w0, t);
+        }
+        for (int u = pc.self + 1; u < pc.count; ++u) {
+          f32x4_st x[8];
+          load(u, v0, x);
+          add_staged(ii, w0, x);
+        }
+      }
+    }
+  }
+};
+
 __device__ inline rsrc_words rsrc_raw(const void* base, uint32_t bytes) {
   const uint64_t v = reinterpret_cast<uint64_t>(base);
   rsrc_words d;
@@ -708,16 +829,16 @@ struct Tile8w {
 // stream can run beside it on the same compute unit.  Same LDS layout, same
 // loads, same K-step pipeline.
 // ---------------------------------------------------------------------------
-template <int B_NK, int KIND, int FAST>
+template <int B_NK, int KIND, int FAST, int SK>
 struct Tile4w {
   static constexpr int BM = 256, BN = 256, WM = 128, WN = 128, FM = 4, FN = 4, NT = 256;
   __device__ static int swz(int row) { return (row >> 1) & 7; }
   // one load of the next stage every LSTRIDE MFMAs (see the fast loop)
   static constexpr int LSTRIDE = 2;
 
-  __device__ static void run(const GemmParams& p, const tlc_tile& tl, TLC_LDS u32x4* A0,
-                             TLC_LDS u32x4* A1, TLC_LDS u32x4* B0, TLC_LDS u32x4* B1,
-                             int* s_flag) {
+  __device__ static void run(const GemmParams& p, const tlc_tile& tl, const SkPiece& pc,
+                             TLC_LDS u32x4* A0, TLC_LDS u32x4* A1, TLC_LDS u32x4* B0,
+                             TLC_LDS u32x4* B1, int* s_flag) {
     // the thread index is made opaque per tile, so that the lane-dependent
     // offsets below are formed per tile instead of being kept (and spilled)
     // across the whole persistent loop
@@ -791,8 +912,15 @@ struct Tile4w {
     // blocks -- a wave with no rows only loads and meets the barriers -- in a
     // second copy of the K loop, so the loop of a full tile is unchanged.  The
     // stored rows' results do not change.
+    // a piece of a stream-K tail tile runs its own K steps (the whole-tile
+    // kernel only); a unit of the plan runs the range of its split field
     int kt0, kt1;
-    unit_k_range(tl.split, p.K / 64, &kt0, &kt1);
+    if (SK && pc.count > 0) {
+      kt0 = pc.kt0;
+      kt1 = pc.kt1;
+    } else {
+      unit_k_range(tl.split, p.K / 64, &kt0, &kt1);
+    }
     const int nk = kt1 - kt0;
     const int rows_left = tl.m_rows - __builtin_amdgcn_readfirstlane(wm) * WM;
     const int fm_act = rows_left <= 0 ? 0 : (rows_left >= FM * 32 ? FM : (rows_left + 31) >> 5);
@@ -1047,12 +1175,26 @@ struct Tile4w {
     }
 
     if constexpr (FAST) {
+      // a piece of a shared tile: its partial out, and the tile stored only by
+      // the piece that completes it
+      const bool shared = SK && pc.count > 1;
+      if constexpr (SK) {
+        if (shared && !sk_epilogue(p, pc, acc, s_flag)) return;
+      }
       // every wavefront's loads (also those past the K range) are in and
       // every wavefront is done with the stages: they hold the staging areas
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       TLC_LDS u32x4* mine = wave == 0 ? A0 : (wave == 1 ? A1 : (wave == 2 ? B0 : B1));
-      store_tile_rows<KIND>(p, tl, acc, wm, wn, lane, reinterpret_cast<TLC_LDS float*>(mine));
+      TLC_LDS float* st = reinterpret_cast<TLC_LDS float*>(mine);
+      if constexpr (SK) {
+        if (shared)
+          store_tile_rows<KIND>(p, tl, acc, SkAddPieces{p, pc, lane}, wm, wn, lane, st);
+        else
+          store_tile_rows<KIND>(p, tl, acc, NoAdjust{}, wm, wn, lane, st);
+      } else {
+        store_tile_rows<KIND>(p, tl, acc, NoAdjust{}, wm, wn, lane, st);
+      }
       __syncthreads();  // the next unit's loads refill the stages
     } else {
       store_tile<KIND, WM, WN, FM, FN>(p, tl, acc, wm, wn, lane);
@@ -1069,7 +1211,7 @@ struct LoopShared {
   int64_t next[2];
 };
 
-template <int BM, int BN, int KIND, int WAIT, typename RunTile>
+template <int BM, int BN, int KIND, int WAIT, int SK, typename RunTile>
 __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile run_tile) {
   const int G = gridDim.x;
   // co-located landing: the first copy.wgs workgroups copy every chunk's
@@ -1088,7 +1230,56 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
       n_tiles = nd;
     }
   }
+  // stream-K tail: the work items past sk_from are pieces of the last tiles
+  const bool tail = SK && p.sk_split > 0;
+  const int64_t n_work = tail ? p.sk_from + static_cast<int64_t>(p.sk_split) * p.sk_tiles : n_tiles;
   uint32_t seen = p.no_wait_mask;
+  // A unit's checks and chunk wait; false: stop (a bad unit was reported, or
+  // a wait was aborted).
+  auto admit = [&](int64_t t, const tlc_tile& tl) -> bool {
+    const uint32_t S = tl.split & 0xFFu;
+    const bool bad_split =
+        tl.split != 0 &&
+        (S < 2 || ((tl.split >> 8) & 0xFFu) >= S ||
+         static_cast<int64_t>((tl.split >> 16) + 1) * (256 + static_cast<int64_t>(S) * BM * BN * 4) >
+             p.split_bytes);
+    const bool bad = tl.m_rows < 1 || tl.n_cols < 1 || tl.m0 < 0 || tl.n0 < 0 ||
+                     tl.m0 + tl.m_rows > p.M || tl.n0 + tl.n_cols > p.N || tl.m_rows > BM ||
+                     tl.n_cols > BN || (tl.n_cols & 7) != 0 || (KIND == KIND_MOE && tl.expert < 0) ||
+                     bad_split;
+    if (bad) {
+      if (threadIdx.x == 0) report(p.sig, TLC_ERR_BAD_PLAN, t);
+      return false;
+    }
+    // trace stamps go to memory as they are taken, so that nothing is kept
+    // in registers across the unit
+    if (p.trace && threadIdx.x == 0) p.trace[6 * t + 1] = static_cast<int64_t>(wall_clock64());
+    if (WAIT) {
+      const uint32_t need = tl.chunk_mask & ~seen;
+      if (need) {
+        if (threadIdx.x == 0) sh->abort = wait_chunks(p.sig, need, p.epoch, p.timeout_ticks, t);
+        __syncthreads();
+        if (sh->abort) return false;
+        seen |= need;
+      }
+    }
+    return true;
+  };
+  auto stamp_start = [&](int64_t t) {
+    if (p.trace && threadIdx.x == 0) {
+      int64_t* e = p.trace + 6 * t;
+      e[2] = static_cast<int64_t>(wall_clock64());
+      e[4] = static_cast<int64_t>(__builtin_amdgcn_s_memtime());
+    }
+  };
+  auto stamp_end = [&](int64_t t) {
+    if (p.trace && threadIdx.x == 0) {
+      int64_t* e = p.trace + 6 * t;
+      e[0] = blockIdx.x;
+      e[3] = static_cast<int64_t>(wall_clock64());
+      e[5] = static_cast<int64_t>(__builtin_amdgcn_s_memtime());
+    }
+  };
   // The first unit of every workgroup is its slot (no counter traffic while all
   // workgroups start at once); the dynamic schedule then hands out units
   // G, G+1, ... from the counter as workgroups become free.  Slots are spread
@@ -1104,50 +1295,41 @@ __device__ inline void tile_loop(const GemmParams& p, LoopShared* sh, RunTile ru
   } else {
     t = p.xcd_remap ? (g & 7) * (G >> 3) + (g >> 3) : g;
   }
-  for (int it = 1; t < n_tiles; ++it) {
+  for (int it = 1; t < n_work; ++it) {
+    if (tail && t >= p.sk_from) {
+      // Piece s of tail tile j (static slots only): pieces s of consecutive
+      // tiles go to consecutive slots, so the workgroups of an XCD run one K
+      // range of a run of neighbouring tiles at the same time.
+      const int KT = p.K / 64, S = p.sk_split;
+      const int64_t q = t - p.sk_from;
+      const int s = static_cast<int>(q / p.sk_tiles);
+      const int64_t j = q - static_cast<int64_t>(s) * p.sk_tiles;
+      const int64_t tt = p.sk_from + j;
+      const tlc_tile tl = p.plan[tt];
+      if (!admit(tt, tl)) break;
+      SkPiece pc;
+      pc.kt0 = (s * KT / S) & ~1;
+      pc.kt1 = ((s + 1) * KT / S) & ~1;
+      pc.count = S;
+      pc.self = s;
+      pc.block = p.sk_ws + j * kSkBlockBytes;
+      stamp_start(tt);
+      run_tile(tl, pc, &sh->split_last);
+      stamp_end(tt);
+      t += G;
+      continue;
+    }
     const tlc_tile tl = p.plan[t];
-    const uint32_t S = tl.split & 0xFFu;
-    const bool bad_split =
-        tl.split != 0 &&
-        (S < 2 || ((tl.split >> 8) & 0xFFu) >= S ||
-         static_cast<int64_t>((tl.split >> 16) + 1) * (256 + static_cast<int64_t>(S) * BM * BN * 4) >
-             p.split_bytes);
-    const bool bad = tl.m_rows < 1 || tl.n_cols < 1 || tl.m0 < 0 || tl.n0 < 0 ||
-                     tl.m0 + tl.m_rows > p.M || tl.n0 + tl.n_cols > p.N || tl.m_rows > BM ||
-                     tl.n_cols > BN || (tl.n_cols & 7) != 0 || (KIND == KIND_MOE && tl.expert < 0) ||
-                     bad_split;
-    if (bad) {
-      if (threadIdx.x == 0) report(p.sig, TLC_ERR_BAD_PLAN, t);
-      break;
-    }
-    // trace stamps go to memory as they are taken, so that nothing is kept
-    // in registers across the unit
-    if (p.trace && threadIdx.x == 0) p.trace[6 * t + 1] = static_cast<int64_t>(wall_clock64());
-    if (WAIT) {
-      const uint32_t need = tl.chunk_mask & ~seen;
-      if (need) {
-        if (threadIdx.x == 0) sh->abort = wait_chunks(p.sig, need, p.epoch, p.timeout_ticks, t);
-        __syncthreads();
-        if (sh->abort) break;
-        seen |= need;
-      }
-    }
+    if (!admit(t, tl)) break;
     // claim the next unit now: the counter's round trip overlaps this unit
     if (p.dynamic && threadIdx.x == 0)
       sh->next[it & 1] = G + static_cast<int64_t>(__hip_atomic_fetch_add(
                                  &p.sig->work_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (p.trace && threadIdx.x == 0) {
-      int64_t* e = p.trace + 6 * t;
-      e[2] = static_cast<int64_t>(wall_clock64());
-      e[4] = static_cast<int64_t>(__builtin_amdgcn_s_memtime());
-    }
-    run_tile(tl, &sh->split_last);  // has workgroup barriers: next[] is visible after it
-    if (p.trace && threadIdx.x == 0) {
-      int64_t* e = p.trace + 6 * t;
-      e[0] = blockIdx.x;
-      e[3] = static_cast<int64_t>(wall_clock64());
-      e[5] = static_cast<int64_t>(__builtin_amdgcn_s_memtime());
-    }
+    stamp_start(t);
+    SkPiece whole;
+    whole.count = 0;
+    run_tile(tl, whole, &sh->split_last);  // has workgroup barriers: next[] is visible after it
+    stamp_end(t);
     t = p.dynamic ? sh->next[it & 1] : t + G;
   }
   if (p.dynamic) {
@@ -1172,20 +1354,22 @@ template <int B_NK, int KIND, int WAIT>
 __global__ __launch_bounds__(512) void gemm_kernel_8w(GemmParams p) {
   __shared__ u32x4 A0[2048], A1[2048], B0[2048], B1[2048];
   __shared__ LoopShared sh;
-  tile_loop<256, 256, KIND, WAIT>(p, &sh, [&](const tlc_tile& tl, int* s_flag) {
+  tile_loop<256, 256, KIND, WAIT, 0>(p, &sh, [&](const tlc_tile& tl, const SkPiece&, int* s_flag) {
     Tile8w<B_NK, KIND>::run(p, tl, (TLC_LDS u32x4*)A0, (TLC_LDS u32x4*)A1, (TLC_LDS u32x4*)B0,
                             (TLC_LDS u32x4*)B1, s_flag);
   });
 }
 
-template <int B_NK, int KIND, int WAIT, int FAST>
+// SK: the variant with the stream-K tail (more vector registers in its
+// epilogue, so it is launched only when the plan has a tail).
+template <int B_NK, int KIND, int WAIT, int FAST, int SK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel_4w(
     GemmParams p) {
   __shared__ u32x4 A0[2048], A1[2048], B0[2048], B1[2048];
   __shared__ LoopShared sh;
-  tile_loop<256, 256, KIND, WAIT>(p, &sh, [&](const tlc_tile& tl, int* s_flag) {
-    Tile4w<B_NK, KIND, FAST>::run(p, tl, (TLC_LDS u32x4*)A0, (TLC_LDS u32x4*)A1,
-                                  (TLC_LDS u32x4*)B0, (TLC_LDS u32x4*)B1, s_flag);
+  tile_loop<256, 256, KIND, WAIT, SK>(p, &sh, [&](const tlc_tile& tl, const SkPiece& pc, int* s_flag) {
+    Tile4w<B_NK, KIND, FAST, SK>::run(p, tl, pc, (TLC_LDS u32x4*)A0, (TLC_LDS u32x4*)A1,
+                                      (TLC_LDS u32x4*)B0, (TLC_LDS u32x4*)B1, s_flag);
   });
   // the last unit's loads past its K range land before the wave ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1195,7 +1379,7 @@ template <int BM, int BN, int B_NK, int KIND, int WAIT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(GemmParams p) {
   __shared__ u32x4 lds[2 * (BM + BN) * 8];
   __shared__ LoopShared sh;
-  tile_loop<BM, BN, KIND, WAIT>(p, &sh, [&](const tlc_tile& tl, int* s_flag) {
+  tile_loop<BM, BN, KIND, WAIT, 0>(p, &sh, [&](const tlc_tile& tl, const SkPiece&, int* s_flag) {
     Tile<BM, BN, B_NK, KIND>::run(p, tl, lds, s_flag);
   });
 }
@@ -1210,16 +1394,19 @@ void launch_kernel(const GemmParams& p, int grid, void* stream) {
   if constexpr (BM == 256 && BN == 256) {
     if constexpr (KIND == KIND_MOE) {
       if (p.fast)
-        hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 1>), dim3(grid), dim3(256), 0,
+        hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 1, 0>), dim3(grid), dim3(256), 0,
                            static_cast<hipStream_t>(stream), p);
       else
         hipLaunchKernelGGL((gemm_kernel_8w<B_NK, KIND, WAIT>), dim3(grid), dim3(512), 0,
                            static_cast<hipStream_t>(stream), p);
-    } else if (p.fast)
-      hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 1>), dim3(grid), dim3(256), 0,
+    } else if (p.fast && p.sk_split > 0)
+      hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 1, 1>), dim3(grid), dim3(256), 0,
+                         static_cast<hipStream_t>(stream), p);
+    else if (p.fast)
+      hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 1, 0>), dim3(grid), dim3(256), 0,
                          static_cast<hipStream_t>(stream), p);
     else
-      hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 0>), dim3(grid), dim3(256), 0,
+      hipLaunchKernelGGL((gemm_kernel_4w<B_NK, KIND, WAIT, 0, 0>), dim3(grid), dim3(256), 0,
                          static_cast<hipStream_t>(stream), p);
   }
   else

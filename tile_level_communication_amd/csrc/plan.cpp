@@ -143,6 +143,11 @@ extern "C" int64_t tlc_split_workspace_bytes(int64_t n_split_tiles, int32_t spli
   return n_split_tiles * tlc::split_block_bytes(split_k, bm, bn);
 }
 
+extern "C" int64_t tlc_streamk_workspace_bytes(int32_t grid) {
+  if (grid < 0) return -1;
+  return static_cast<int64_t>(grid == 0 ? 256 : grid) * tlc::kSkBlockBytes;
+}
+
 namespace tlc {
 int64_t split_block_bytes(int32_t split_k, int32_t bm, int32_t bn) {
   return 256 + static_cast<int64_t>(split_k) * bm * bn * 4;

@@ -73,7 +73,26 @@ struct GemmParams {
   // set by launch_gemm: every unit is a whole tile with an even number of K
   // steps and none is split (the kernel with only the fast loop)
   int32_t fast;
+  // Stream-K tail (the whole-tile kernel, static slots): work items
+  // [0, sk_from) are the plan's first units, run whole; the sk_tiles tiles
+  // from sk_from on are each split into sk_split pieces along K, piece s of
+  // a tile covering the 64-wide K steps [b(s), b(s + 1)), b(s) = s * KT /
+  // sk_split rounded down to even (KT = K / 64, even), and item
+  // sk_from + s * sk_tiles + j is piece s of tile sk_from + j: pieces with
+  // the same K range of neighbouring tiles run side by side, as whole tiles
+  // do.  sk_split = 0: no tail.
+  int64_t sk_from;
+  int32_t sk_tiles;
+  int32_t sk_split;
+  // per tail tile a block of kSkBlockBytes: a 256-byte header (the tile's
+  // arrival counter) and one fp32 partial tile per piece
+  char* sk_ws;
 };
+
+// Stream-K tail workspace: pieces per tile at most, bytes per tile.
+constexpr int kSkMaxSplit = 4;
+constexpr int64_t kSkTileBytes = int64_t{256} * 256 * 4;
+constexpr int64_t kSkBlockBytes = 256 + kSkMaxSplit * kSkTileBytes;
 
 // Bytes of one split tile's workspace block (counter header + split_k partials).
 int64_t split_block_bytes(int32_t split_k, int32_t bm, int32_t bn);

@@ -23,7 +23,7 @@ MODE_AG, MODE_RS, MODE_MOE = 0, 1, 2
 ORDER_NATURAL, ORDER_RANK_OFFSET = 0, 1
 B_KN, B_NK = 0, 1
 LAND_NONE, LAND_COPY_ENGINE, LAND_CU, LAND_MEMCPY, LAND_COLOCATED = 0, 1, 2, 3, 4
-SCHED_DYNAMIC, SCHED_STATIC = 0, 1
+SCHED_DYNAMIC, SCHED_STATIC, SCHED_STREAMK = 0, 1, 2
 MAX_WORLD = 32
 EPOCH_MAX = 4096
 
@@ -31,7 +31,7 @@ EXPORTS = [
     "tlc_chunk_plan", "tlc_signals_alloc", "tlc_signals_free", "tlc_signals_set",
     "tlc_signals_clear_status", "tlc_read_status", "tlc_ag_gemm", "tlc_gemm_rs", "tlc_rs_reduce",
     "tlc_moe_plan_capacity", "tlc_moe_workspace_bytes", "tlc_moe_route", "tlc_ag_moe", "tlc_land",
-    "tlc_status_string", "tlc_last_error", "tlc_version", "tlc_split_workspace_bytes", "tlc_gemm_ar",
+    "tlc_status_string", "tlc_last_error", "tlc_version", "tlc_split_workspace_bytes", "tlc_streamk_workspace_bytes", "tlc_gemm_ar",
     "tlc_wall_clock_khz", "tlc_read_signals", "tlc_signals_rewind", "tlc_moe_route_static",
     "tlc_moe_static_workspace_bytes",
 ]
@@ -180,6 +180,8 @@ def lib() -> C.CDLL:
         L.tlc_version.restype = C.c_int32
         L.tlc_split_workspace_bytes.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32]
         L.tlc_split_workspace_bytes.restype = C.c_int64
+        L.tlc_streamk_workspace_bytes.argtypes = [C.c_int32]
+        L.tlc_streamk_workspace_bytes.restype = C.c_int64
         _lib = L
     return _lib
 
@@ -265,6 +267,10 @@ def split_tiles(plan) -> int:
 
 def split_workspace_bytes(n_split_tiles, split_k, bm, bn) -> int:
     return int(lib().tlc_split_workspace_bytes(n_split_tiles, split_k, bm, bn))
+
+
+def streamk_workspace_bytes(grid=0) -> int:
+    return int(lib().tlc_streamk_workspace_bytes(grid))
 
 
 # --------------------------------------------------------------- signals ----

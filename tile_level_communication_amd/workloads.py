@@ -93,6 +93,19 @@ def split_workspace(tiles, split_k, bm, bn, device):
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
+def streamk_workspace(device, grid=0):
+    """Zeroed workspace of the stream-K tail for any grid (or `grid` workgroups)."""
+    return torch.zeros(tlc.streamk_workspace_bytes(grid), dtype=torch.uint8, device=device)
+
+
+def schedule_workspace(tiles, split_k, bm, bn, schedule, device):
+    """The workspace a plan needs under `schedule`: the stream-K tail's, or the
+    split tiles' (None if neither)."""
+    if schedule == tlc.SCHED_STREAMK:
+        return streamk_workspace(device)
+    return split_workspace(tiles, split_k, bm, bn, device)
+
+
 class AGProblem:
     def __init__(self, a_chunks, b_kn, rank, bm=256, bn=256, b_layout=tlc.B_KN,
                  order=tlc.ORDER_RANK_OFFSET, group_m=4, device="cuda", split_k=0, split_from=0,
@@ -116,7 +129,7 @@ class AGProblem:
         self.tiles = tiles
         self.plan = torch.from_numpy(tiles).to(self.device)
         self.n_tiles = int(tiles.shape[0])
-        self.workspace = split_workspace(tiles, split_k, bm, bn, self.device)
+        self.workspace = schedule_workspace(tiles, split_k, bm, bn, schedule, self.device)
         self.schedule = schedule
         self.sig = tlc.Signals()
         self.epoch = 0
@@ -189,7 +202,7 @@ class RSProblem:
         self.tiles = tiles
         self.plan = torch.from_numpy(tiles).to(self.device)
         self.n_tiles = int(tiles.shape[0])
-        self.workspace = split_workspace(tiles, split_k, bm, bn, self.device)
+        self.workspace = schedule_workspace(tiles, split_k, bm, bn, schedule, self.device)
         self.schedule = schedule
         self.sig = tlc.Signals()
         self.epoch = 0
