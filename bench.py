@@ -56,11 +56,11 @@ PEAK_HBM_GBS = 8000.0
 # counters were taken.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE) or None
-    "ag": {"gemm": (222355.7, 102416.2)},
-    "moe": {"gemm": (249350.8, 98304.0)},
-    "rs": {"gemm": (50581.4, 65536.0), "reduce": (32788.6, 16384.7)},
-    "ar": {"gemm": (50581.4, 65536.0), "reduce": (32788.6, 16384.7)},
-    "rs_long": {"gemm": (3153921.1, 2621440.0), "reduce": (1310743.9, 327680.0)},
+    "ag": {"gemm": None},
+    "moe": {"gemm": None},
+    "rs": {"gemm": None, "reduce": (32788.6, 16384.7)},
+    "ar": {"gemm": None, "reduce": (32788.6, 16384.7)},
+    "rs_long": {"gemm": None, "reduce": (1310743.9, 327680.0)},
 }
 
 
@@ -75,6 +75,7 @@ def traffic_bytes(workload, kernel):
 WORKLOAD_ID = {"ag": 2, "rs": 1, "rs_long": 3, "moe": 4, "ar": 1, "fetch_calibration": None}
 LANDINGS = {"memcpy": 3, "copy_engine": 1, "cu": 2, "colocated": 4}  # tlc.LAND_*
 ORDERS = {"natural": 0, "rank_offset": 1}  # tlc.ORDER_*
+SCHEDULES = {"dynamic": 0, "static": 1, "streamk": 2}  # tlc.SCHED_*
 
 
 def parse(argv=None):
@@ -108,7 +109,7 @@ def parse(argv=None):
                     help="first key (chunk position) whose tiles are split (default 7)")
     ap.add_argument("--sub-chunks", type=int, default=None,
                     help="ag: land every peer chunk as S pieces with their own flags (default 1)")
-    ap.add_argument("--schedule", default=None, choices=["dynamic", "static"],
+    ap.add_argument("--schedule", default=None, choices=["dynamic", "static", "streamk"],
                     help="work distribution (default: static for ag, rs and ar; per landing for moe)")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -370,7 +371,9 @@ def run_ag(args, torch, tlc, si, workloads):
     # static slots: faster than the dynamic counter for the memcpy and the
     # co-located landings (one process each, two runs)
     args.schedule = args.schedule or "static"
-    schedule = tlc.SCHED_DYNAMIC if args.schedule == "dynamic" else tlc.SCHED_STATIC
+    schedule = SCHEDULES[args.schedule]
+    if schedule == tlc.SCHED_STREAMK:
+        split_k = 0  # the tail's workspace replaces the split tiles'
     sub = 1 if args.sub_chunks is None else args.sub_chunks
     prob = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
                                order=order, group_m=args.group_m, device=dev, split_k=split_k,
@@ -524,12 +527,58 @@ def run_ag(args, torch, tlc, si, workloads):
         "device_status": status,
         "other_landings": other_landings(flops, t_comp, others, t_copy_others),
     }
+    if args.legs == "all":
+        extra["full_grid"] = full_grid(args, torch, tlc, workloads, inp, layout, order, dev, compute,
+                                       call, flops, khz, gemm_comp_ms, sclk_mhz)
     if not args.no_vendor:
         extra["vendor_gemm"] = vendor_gemm(torch, tlc, prob.a, prob.b, prob.b_layout, gemm_comp_ms)
     line = base_line(args, head["value"], t_fused, extra)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline("ag", inp, args.cpu_seconds)
     return line
+
+
+def full_grid(args, torch, tlc, workloads, inp, layout, order, dev, compute, call, flops, khz,
+              base_ms, base_mhz):
+    """The compute-only GEMM on every compute unit instead of the default grid
+    (two even rounds of whole tiles): whole tiles on static slots (the second
+    round part-filled), and the stream-K tail (one round of whole tiles, the
+    rest split along K over every CU).  Each with the kernel's mean time (HIP
+    events) and the shader clock its workgroups ran at (cycle counters of the
+    whole-tile units in five traced launches, median), beside the default."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {"default": {"grid": "default", "gemm_ms": round(base_ms, 4),
+                       "tflops": round(flops / base_ms / 1e9, 1), "sclk_mhz": round(base_mhz, 1)}}
+    for name, sched in [("static", tlc.SCHED_STATIC), ("streamk", tlc.SCHED_STREAMK)]:
+        comp = workloads.AGProblem(inp.a_chunks, inp.b, args.rank, args.tile, args.tile, layout,
+                                   order=order, group_m=args.group_m, device=dev, schedule=sched)
+        comp.place_all()
+        torch.cuda.synchronize()
+        timer = KernelTimer(torch, compute)
+        kw = dict(call, plan=comp.plan, n_tiles=comp.n_tiles, a=comp.a, c=comp.c, sig=comp.sig,
+                  workspace=comp.workspace, schedule=sched, sub_chunks=0)
+
+        def launch(trace=None):
+            tlc.ag_gemm(**kw, a_src=None, epoch=0, land=tlc.LAND_NONE, compute_stream=compute,
+                        copy_stream=None, grid=cus, trace=trace)
+
+        _, st = run_leg(comp, lambda: timer(launch), args.steps, args.warmup, torch, compute)
+        ms = timer.mean_ms(args.steps)
+        whole = comp.n_tiles // cus * cus if sched == tlc.SCHED_STREAMK else comp.n_tiles
+        tr = torch.zeros((comp.n_tiles, 6), dtype=torch.int64, device=dev)
+        mhz = []
+        for _ in range(5):
+            launch(tr)
+            torch.cuda.synchronize()
+            t = tr[:whole].cpu().numpy()
+            mhz.append(float((t[:, 5] - t[:, 4]).sum()) / max(float((t[:, 3] - t[:, 2]).sum()), 1.0)
+                       * khz / 1e3)
+        ok = st[0] == 0
+        out[name] = {"grid": cus, "gemm_ms": round(ms, 4) if ok else None,
+                     "tflops": round(flops / ms / 1e9, 1) if ok else None,
+                     "sclk_mhz": round(sorted(mhz)[2], 1), "device_status": st}
+        del comp
+    return out
 
 
 def run_rs(args, torch, tlc, si, workloads, wid, ar=False, sub_object=False):
@@ -549,7 +598,9 @@ def run_rs(args, torch, tlc, si, workloads, wid, ar=False, sub_object=False):
     split_k = 0 if (args.split_k is None or sub_object) else args.split_k
     split_from = 1 if args.split_from is None else args.split_from
     schedule_name = "static" if sub_object else (args.schedule or "static")
-    schedule = tlc.SCHED_DYNAMIC if schedule_name == "dynamic" else tlc.SCHED_STATIC
+    schedule = SCHEDULES[schedule_name]
+    if schedule == tlc.SCHED_STREAMK:
+        split_k = 0
     if ar:
         prob = workloads.ARProblem(inp.a, inp.b, inp.remote, inp.gathered, wl.world, args.rank,
                                    args.tile, args.tile, layout, order=order, group_m=args.group_m,

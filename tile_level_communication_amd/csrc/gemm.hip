@@ -1093,15 +1093,24 @@ struct Tile4w {
     // one K step on stage (Ac, Bc): finishes the loads of the next step into
     // (An, Bn), reads that stage's first fragments at its end, and starts the
     // loads of the step after next into this stage once it is free
+    // C (compute): false for a wavefront whose 128 x 128 share of the unit
+    // lies wholly outside its rows or columns (the empty half of a 128-wide
+    // last column tile, or of an expert's unit of 128 rows or fewer): it
+    // issues its share of the stage loads and meets the barriers, but makes
+    // no fragment reads and no MFMAs, which saves their power on a part whose
+    // clock the power limit sets.
     auto fstep = [&](int i, TLC_LDS u32x4* Ac, TLC_LDS u32x4* Bc, TLC_LDS u32x4* An,
-                     TLC_LDS u32x4* Bn) __attribute__((always_inline)) {
+                     TLC_LDS u32x4* Bn, auto c_c) __attribute__((always_inline)) {
+      constexpr bool C = decltype(c_c)::value;
       static_for<3>([&](auto ks_c) __attribute__((always_inline)) {
         constexpr int KS = decltype(ks_c)::value;
         static_for<FM * FN>([&](auto m_c) __attribute__((always_inline)) {
           constexpr int M = decltype(m_c)::value;
-          mfma_one(std::integral_constant<int, KS & 1>{}, m_c);
-          __builtin_amdgcn_sched_barrier(0);
-          if constexpr (M < NR) {
+          if constexpr (C) {
+            mfma_one(std::integral_constant<int, KS & 1>{}, m_c);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if constexpr (C && M < NR) {
             read_one(Ac, Bc, KS + 1, std::integral_constant<int, (KS + 1) & 1>{}, m_c);
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -1118,9 +1127,11 @@ struct Tile4w {
       __builtin_amdgcn_sched_barrier(0);
       static_for<FM * FN>([&](auto m_c) __attribute__((always_inline)) {
         constexpr int M = decltype(m_c)::value;
-        mfma_one(std::integral_constant<int, 1>{}, m_c);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (M < NR) {
+        if constexpr (C) {
+          mfma_one(std::integral_constant<int, 1>{}, m_c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (C && M < NR) {
           read_one(An, Bn, 0, std::integral_constant<int, 0>{}, m_c);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -1136,7 +1147,8 @@ struct Tile4w {
     // stage nobody reads any more, and they complete before the next unit's
     // loads, vector memory operations completing in order.  An even number of
     // steps keeps the loop body one pair of steps.
-    auto fast_loop = [&]() __attribute__((always_inline)) {
+    auto fast_loop = [&](auto c_c) __attribute__((always_inline)) {
+      constexpr bool C = decltype(c_c)::value;
       static_assert(FM * FN == 16, "sixteen MFMAs and sixteen loads per sub-step");
       static_for<16>([&](auto q_c) __attribute__((always_inline)) { load_one(kt0, A0, B0, q_c); });
       // step 1's loads that the steady state issues before the first step
@@ -1146,23 +1158,34 @@ struct Tile4w {
       });
       asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 0's sixteen loads done
       __syncthreads();
-      static_for<NR>([&](auto r_c) __attribute__((always_inline)) {
-        read_one(A0, B0, 0, std::integral_constant<int, 0>{}, r_c);
-      });
-      for (int i = 0; i < nk; i += 2) {
-        fstep(i, A0, B0, A1, B1);
-        fstep(i + 1, A1, B1, A0, B0);
+      if constexpr (C) {
+        static_for<NR>([&](auto r_c) __attribute__((always_inline)) {
+          read_one(A0, B0, 0, std::integral_constant<int, 0>{}, r_c);
+        });
       }
+      for (int i = 0; i < nk; i += 2) {
+        fstep(i, A0, B0, A1, B1, c_c);
+        fstep(i + 1, A1, B1, A0, B0, c_c);
+      }
+    };
+    // a wavefront with nothing to compute in this unit (wave-uniform)
+    const bool idle = __builtin_amdgcn_readfirstlane(
+                          static_cast<int>(wm * WM >= tl.m_rows || wn * WN >= tl.n_cols)) != 0;
+    auto fast_loop_any = [&]() __attribute__((always_inline)) {
+      if (idle)
+        fast_loop(std::false_type{});
+      else
+        fast_loop(std::true_type{});
     };
     // the same loop for every wavefront of the workgroup: the fast loop's
     // barriers and LDS layout differ from the other loop's.  The FAST kernel
     // has only the fast loop: the host picks it when every unit is a whole
     // tile with an even number of K steps and no unit is split.
     if constexpr (FAST) {
-      fast_loop();
+      fast_loop_any();
     } else {
       if (tl.m_rows >= BM && nk > 0 && (nk & 1) == 0)
-        fast_loop();
+        fast_loop_any();
       else if (fm_act == FM)
         kloop(std::true_type{});
       else
