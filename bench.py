@@ -56,11 +56,11 @@ PEAK_HBM_GBS = 8000.0
 # counters were taken.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE) or None
-    "ag": {"gemm": None},
-    "moe": {"gemm": None},
-    "rs": {"gemm": None, "reduce": (32788.6, 16384.7)},
-    "ar": {"gemm": None, "reduce": (32788.6, 16384.7)},
-    "rs_long": {"gemm": None, "reduce": (1310743.9, 327680.0)},
+    "ag": {"gemm": (222482.5, 102416.3)},
+    "moe": {"gemm": (249696.4, 98304.0)},
+    "rs": {"gemm": (50582.2, 65536.0), "reduce": (32788.8, 16385.8)},
+    "ar": {"gemm": (50582.2, 65536.0), "reduce": (32788.8, 16385.8)},
+    "rs_long": {"gemm": (3153934.1, 2621440.0), "reduce": (1310742.8, 327680.0)},
 }
 
 
