@@ -203,3 +203,42 @@ def test_streamk_workspace_too_small_is_refused():
     with pytest.raises(RuntimeError, match="stream-K"):
         prob.run(tlc.LAND_NONE, grid=8)
     torch.cuda.synchronize()
+
+
+def test_streamk_bad_tail_tile_reported():
+    """A tail tile whose plan entry lies outside the output is reported as
+    BAD_PLAN with its plan index by the pieces that reach it, every workgroup
+    exits, and after the status and the workspace are cleared the call with the
+    plan restored is correct.  Under the tail schedule the workspace serves the
+    tail only, so a plan with split units is reported as BAD_PLAN too."""
+    W, R, K, N = 2, 512, 1024, 648
+    inp = si.ag_inputs(650, W, R, N, K)
+    ref = og.ag_gemm(inp.a_chunks, inp.b)
+    prob = AGProblem(inp.a_chunks, inp.b, 0, 256, 256, tlc.B_KN, schedule=tlc.SCHED_STREAMK)
+    prob.place_all()
+    good = prob.plan.clone()
+    # 12 tiles on 8 workgroups: tiles 8..11 form the tail, two K pieces each
+    bad = 9
+    prob.plan[bad, 0] = prob.M
+    log("[sk ag] tail tile 9 outside the output, grid 8")
+    prob.run(tlc.LAND_NONE, grid=8)
+    torch.cuda.synchronize()
+    st = prob.sig.read_status()
+    assert st[0] == tlc.ERR_BAD_PLAN and st[1] == bad, st
+    prob.sig.clear_status()
+    prob.workspace.zero_()
+    prob.plan.copy_(good)
+    prob.run(tlc.LAND_NONE, grid=8)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    assert _counters_zero(prob.workspace)
+    check_close(prob.c.cpu().numpy(), ref, K, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b),
+                "after a bad tail tile")
+    del prob
+    log("[sk ag] split units under the tail schedule, grid 8")
+    prob = AGProblem(inp.a_chunks, inp.b, 0, 256, 256, tlc.B_KN, split_k=2, split_from=0,
+                     schedule=tlc.SCHED_STREAMK)
+    prob.place_all()
+    prob.run(tlc.LAND_NONE, grid=8)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == tlc.ERR_BAD_PLAN
