@@ -286,3 +286,14 @@ def test_moe_route_static_refuses_oversize_on_the_host():
     assert tlc.lib().tlc_moe_route_static(C.byref(a), None) == tlc.ERR_CAPACITY
     assert "static one holds" in tlc.last_error(), tlc.last_error()
     assert tlc.lib().tlc_moe_route_static(None, None) == tlc.ERR_INVALID_ARG
+
+
+def test_streamk_schedule_accepted_and_sized():
+    """TLC_SCHED_STREAMK passes the schedule check (the call then fails on its NULL
+    operands, not on the schedule), and its workspace query covers any grid."""
+    args = _ag_args(schedule=tlc.SCHED_STREAMK)
+    assert tlc.lib().tlc_ag_gemm(C.byref(args), None, None, 0) == tlc.ERR_INVALID_ARG
+    assert "schedule" not in tlc.last_error(), tlc.last_error()
+    block = 256 + 4 * 256 * 256 * 4
+    assert tlc.streamk_workspace_bytes(0) == 256 * block
+    assert tlc.streamk_workspace_bytes(1) == block

@@ -88,3 +88,11 @@ def test_cpu_baseline_moe_reports_the_oracle_sample():
     # the host it ran on, and the same oracle on one thread
     assert r["nproc"] == os.cpu_count() and r["cpu_model"]
     assert r["one_thread"]["cores"] == 1 and r["one_thread"]["value"] > 0
+
+
+def test_schedule_option_maps_to_the_library():
+    from tile_level_communication_amd import tlc
+    for name, want in (("static", tlc.SCHED_STATIC), ("dynamic", tlc.SCHED_DYNAMIC),
+                       ("streamk", tlc.SCHED_STREAMK)):
+        a = bench.parse(["--schedule", name])
+        assert bench.SCHEDULES[a.schedule] == want
