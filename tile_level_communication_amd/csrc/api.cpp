@@ -954,8 +954,8 @@ tlc_status tlc_ag_moe(const tlc_moe_args* a, void* compute_stream, void* const* 
                                   copy_streams, n_copy_streams, a->epoch);
   if (st) return st;
   // The grouped GEMM's whole-tile kernel (H / 64 even) leaves room on every CU
-  // for the runtime's copy and flag-transfer workgroups (a third of the
-  // registers, 32 KB of LDS, most wavefront slots), so beside the memcpy and
+  // for the runtime's copy and flag-transfer workgroups (a fifth of the
+  // registers or more, 32 KB of LDS, most wavefront slots), so beside the memcpy and
   // copy-engine landings it waits on flags without a reserve and takes every
   // CU; the 8-wavefront fallback (H / 64 odd) fills its CUs, and the CU landing
   // kernel is sized for CUs of its own: those keep the reserve.

@@ -1474,9 +1474,10 @@ tlc_status launch_gemm(const GemmParams& p_in, int bm, int bn, int b_layout, int
   // The kernel with only the fixed-order loop (and no split epilogue), for
   // plans whose units are all whole 256-row tiles with an even number of
   // K steps: M a multiple of 256, K / 64 even, no split workspace (a split
-  // unit without one is reported as a bad plan).  It keeps a third of the
-  // register file free, so that other kernels' wavefronts (a side stream's
-  // copies) can run beside it on the same compute units.  The grouped GEMM
+  // unit without one is reported as a bad plan).  It keeps a fifth of the
+  // register file free or more (405 of 512 registers per lane with a K x N
+  // weight), so that other kernels' wavefronts (a side stream's copies) can
+  // run beside it on the same compute units.  The grouped GEMM
   // runs it on its ragged tiles too (never split): the rows past an expert's
   // end load that expert's last row again and are not stored, and the fixed
   // loop over all 256 rows still beats the general loop that skips them.
