@@ -55,6 +55,8 @@ PEAK_HBM_GBS = 8000.0
 # kernel reads half its loads too).  None where the kernel changed since the
 # counters were taken.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+# fused steps queued ahead of the one whose units are traced (flag_spin)
+TRACE_LEAD_STEPS = 4
 TRAFFIC_KIB = {  # workload -> kernel -> (FETCH_SIZE, WRITE_SIZE) or None
     "ag": {"gemm": (222482.5, 102416.3)},
     "moe": {"gemm": (249696.4, 98304.0)},
@@ -407,10 +409,16 @@ def run_ag(args, torch, tlc, si, workloads):
     t_fused, status = run_leg(prob, fused_step(land, fused_t), args.steps, args.warmup, torch, compute)
     gemm_fused_ms = fused_t.mean_ms(args.steps)
 
-    # one more fused step with per-unit trace stamps: time the workgroups spent
-    # spinning on chunk flags (the exposed part of the landing inside the GEMM)
+    # per-unit trace stamps of a fused step: time the workgroups spent spinning
+    # on chunk flags (the exposed part of the landing inside the GEMM).  The
+    # traced step is the last of several queued back to back, as in the timed
+    # loop: a step started from an idle GPU finds its copies already under way
+    # and waits less.
     trace = torch.zeros((prob.n_tiles, 6), dtype=torch.int64, device=dev)
     prob.sig.clear_status(compute)
+    torch.cuda.synchronize()
+    for _ in range(TRACE_LEAD_STEPS):
+        fused_step(land)()
     workloads.next_epoch(prob)
     for c in copies:
         c.wait_stream(compute)
@@ -429,10 +437,16 @@ def run_ag(args, torch, tlc, si, workloads):
         wait_us = (tr[:, 2] - tr[:, 1]) * 1e3 / khz
         span_us = float(tr[:, 3].max() - tr[:, 1].min()) * 1e3 / khz
         n_wg = len(set(tr[:, 0].tolist()))
+        import numpy as np
+        keys = prob.tiles[:, 6]
         spin = {"wait_us_total": round(float(wait_us.sum()), 1),
                 "units_that_waited": int((wait_us > 1.0).sum()),
                 "wait_fraction_of_workgroup_time": round(float(wait_us.sum()) / (n_wg * span_us), 4),
-                "kernel_span_us": round(span_us, 1)}
+                "kernel_span_us": round(span_us, 1),
+                # median wait of the units keyed by each landing position (0: the local chunk)
+                "median_wait_us_by_position": [round(float(np.median(wait_us[keys == k])), 1)
+                                               for k in range(int(keys.max()) + 1) if (keys == k).any()],
+                "traced_step": f"the last of {TRACE_LEAD_STEPS + 1} steps queued back to back"}
 
     # the same step with the other landing backends (reported beside the headline)
     other_kinds = [o for o in LANDINGS.values() if o != land] if args.legs == "all" else []
