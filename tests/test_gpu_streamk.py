@@ -242,3 +242,42 @@ def test_streamk_bad_tail_tile_reported():
     prob.run(tlc.LAND_NONE, grid=8)
     torch.cuda.synchronize()
     assert prob.sig.read_status()[0] == tlc.ERR_BAD_PLAN
+
+
+def test_streamk_rs_ffn_down_128k_full_with_sends():
+    """The long-context FFN-down GEMM-RS (131072 x 5120 x 3200, 8 slices) with the tail
+    on 240 workgroups: 42 rounds of whole tiles, then 160 tiles in three K pieces, the
+    tile that completes a destination's slice possibly a tail piece.  Integer inputs
+    (K * 16 < 2^24: every fp32 sum exact), so the whole partial product, the reduced
+    slice and every sent slice are compared bit for bit with the oracle."""
+    wl = si.WORKLOADS[3]
+    rank = 0
+    log(f"[sk rs 128k] {wl.name}: integer inputs")
+    ii = si.workload_inputs(3, rank=rank, integer=True)
+    R = wl.rows_per_chunk
+    prob = RSProblem(ii.a, ii.b, ii.remote, wl.world, rank, 256, 256, tlc.B_KN,
+                     schedule=tlc.SCHED_STREAMK, sends=True)
+    prob.poison_remote()
+    prob.partials.fill_(float("nan"))
+    for c in range(wl.world):
+        if c != rank:
+            prob.send_dst[c].fill_(float("nan"))
+    log("[sk rs 128k] memcpy landing, memcpy sends, grid 240")
+    prob.run(tlc.LAND_MEMCPY, grid=240, send_land=tlc.LAND_MEMCPY)
+    torch.cuda.synchronize()
+    blk = prob.sig.read_block()
+    assert blk.status[0] == 0, list(blk.status)
+    assert all(v == 0 for v in blk.dest_done)
+    assert _counters_zero(prob.workspace)
+    for c in range(wl.world):
+        if c != rank:
+            assert blk.dest_ready[c] == prob.epoch
+            assert torch.equal(prob.send_dst[c].view(torch.int32),
+                               prob.partials[c * R:(c + 1) * R].view(torch.int32)), c
+    log("[sk rs 128k] oracle: reduced slice and every row block of P")
+    _, out_ref = og.gemm_rs_rows(ii.a, ii.b, ii.remote, wl.world, rank, np.arange(R))
+    check_exact(prob.out.cpu().numpy(), out_ref, "integer out, tail")
+    for r0 in range(0, prob.M, 8192):
+        idx = np.arange(r0, min(r0 + 8192, prob.M))
+        check_exact(prob.partials[r0:r0 + len(idx)].cpu().numpy(), og.gemm_partial(ii.a, ii.b, idx),
+                    f"integer P rows {r0}.., tail")
