@@ -552,6 +552,21 @@ def run_ag(args, torch, tlc, si, workloads):
     return line
 
 
+def moe_hbm_view(gemm_s, prob, args):
+    """The grouped GEMM's launch against the HBM peak: its algorithmic bytes
+    (X read once, W once, Y written once) and its measured traffic past the L2
+    (the counters' figures) per second of the same launch."""
+    alg = prob.T * prob.H * 2 + prob.E * prob.H * prob.N * 2 + prob.T * prob.k * prob.N * 4
+    traffic = traffic_bytes("moe", "gemm") if args.tile == 256 and args.layout == "KN" else None
+    out = {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "achieved": round(alg / gemm_s / 1e9, 1), "frac": round(alg / gemm_s / 1e9 / PEAK_HBM_GBS, 4),
+           "algorithmic_bytes": alg}
+    if traffic is not None:
+        out["traffic_gbs"] = round(traffic / gemm_s / 1e9, 1)
+        out["traffic_frac"] = round(traffic / gemm_s / 1e9 / PEAK_HBM_GBS, 4)
+    return out
+
+
 def full_grid(args, torch, tlc, workloads, inp, layout, order, dev, compute, call, flops, khz,
               base_ms, base_mhz):
     """The compute-only GEMM on every compute unit instead of the default grid
@@ -921,6 +936,10 @@ def run_moe(args, torch, tlc, si, workloads):
                      + prob.T * prob.k * prob.N * 4,
                      "kernel": "gemm_kernel_4w<KN,moe,no-wait,whole-tile loop>: grouped GEMM, every chunk resident",
                      "device_status": comp_status},
+        # the grouped GEMM sits at the ridge point (2H flops per output element
+        # against the bytes of X, W and Y: 323 flop/B, the peaks' ratio 312), so
+        # the memory side of the same launch beside the MFMA fraction
+        "roofline_hbm": moe_hbm_view(flops / (achieved * 1e12), prob, args),
         "route_ms": round(route_ms, 4),
         "pct_peak": head["pct_peak"],
         "compute_only_ms": round(t_comp * 1e3, 4),

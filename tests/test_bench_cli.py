@@ -96,3 +96,16 @@ def test_schedule_option_maps_to_the_library():
                        ("streamk", tlc.SCHED_STREAMK)):
         a = bench.parse(["--schedule", name])
         assert bench.SCHEDULES[a.schedule] == want
+
+
+def test_moe_hbm_view_arithmetic():
+    """The grouped GEMM's memory-side figures: algorithmic bytes of X, W and Y per
+    second of the launch, and the calibrated counter traffic per second."""
+    import types
+    prob = types.SimpleNamespace(T=4096, H=2048, E=64, N=768, k=8)
+    args = bench.parse(["--workload", "moe"])
+    v = bench.moe_hbm_view(100e-6, prob, args)
+    alg = 4096 * 2048 * 2 + 64 * 2048 * 768 * 2 + 4096 * 8 * 768 * 4
+    assert v["algorithmic_bytes"] == alg and v["bound"] == "hbm" and v["peak"] == 8000.0
+    assert abs(v["achieved"] - alg / 100e-6 / 1e9) < 0.1
+    assert abs(v["traffic_gbs"] - bench.traffic_bytes("moe", "gemm") / 100e-6 / 1e9) < 0.1
