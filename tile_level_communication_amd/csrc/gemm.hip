@@ -188,14 +188,12 @@ typedef float f32x4_st __attribute__((ext_vector_type(4)));
 // different XCDs), waits for the stores and counts itself in.  The piece that
 // counts itself in last rewinds the counter and returns true: it stores the
 // tile, adding the other pieces to its own while it stages them (SkAddPieces).
-__device__ inline bool sk_epilogue(const GemmParams& p, const SkPiece& pc, f32x16 (&acc)[4][4],
-                                   int* s_flag) {
+__device__ inline bool sk_epilogue(const SkPiece& pc, f32x16 (&acc)[4][4], int* s_flag) {
   // an opaque copy of the thread index: keeps the compiler from forming the
   // addresses before the K loop and holding them across it
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const uint32_t voff = static_cast<uint32_t>(tid) * 16u;
-  (void)p;
   // vector V (0..63) of the thread: block (V / 16, V / 4 % 4), elements 4 (V % 4) ..
   {
     const __amdgpu_buffer_rsrc_t rs =
@@ -1202,7 +1200,7 @@ struct Tile4w {
       // the piece that completes it
       const bool shared = SK && pc.count > 1;
       if constexpr (SK) {
-        if (shared && !sk_epilogue(p, pc, acc, s_flag)) return;
+        if (shared && !sk_epilogue(pc, acc, s_flag)) return;
       }
       // every wavefront's loads (also those past the K range) are in and
       // every wavefront is done with the stages: they hold the staging areas
