@@ -354,3 +354,22 @@ def test_ag_trace_stamps():
     assert (tr[:, 4] < tr[:, 5]).all()
     mhz = (tr[:, 5] - tr[:, 4]).sum() / (tr[:, 3] - tr[:, 2]).sum() * tlc.wall_clock_khz() / 1e3
     assert 300 < mhz < 3000, mhz
+
+
+def test_ag_qwen3_ffn_up_every_cu_static():
+    """The launch the bench times as `full_grid.static`: the compute-only GEMM on
+    every compute unit with static slots (a round of 256 tiles, then 160), the
+    whole 8192 x 3200 output against the float64 oracle."""
+    wl = si.WORKLOADS[2]
+    inp = si.workload_inputs(2)
+    ref = og.ag_gemm(inp.a_chunks, inp.b)
+    prob = AGProblem(inp.a_chunks, inp.b, 0, 256, 256, tlc.B_KN, group_m=8, schedule=tlc.SCHED_STATIC)
+    prob.place_all()
+    prob.c.fill_(float("nan"))
+    cus = torch.cuda.get_device_properties(prob.c.device).multi_processor_count
+    log(f"[ag full] {wl.name}: compute only on {cus} workgroups, static slots")
+    prob.run(tlc.LAND_NONE, grid=cus)
+    torch.cuda.synchronize()
+    assert prob.sig.read_status()[0] == 0
+    check_close(prob.c.cpu().numpy(), ref, wl.k, absmax_bf16(inp.a_chunks), absmax_bf16(inp.b),
+                "every CU, static")
