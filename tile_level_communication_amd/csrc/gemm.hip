@@ -92,11 +92,11 @@ __device__ inline void unit_k_range(uint32_t split, int KT, int* kt0, int* kt1) 
   *kt1 = (s + 1) * KT / S;
 }
 
-// Split-tile epilogue.  Returns true when the caller is to store the tile:
-// always for a whole tile; for a split tile only in the workgroup that counted
-// itself in last, after acc has been replaced by the sum of the S partials in
-// ascending split index.  Partial slots hold each thread's accumulators at
-// index (element * NT + thread), so every store and load instruction of a
+// Split-tile epilogue, first half.  Returns true when the caller is to store
+// the tile: always for a whole tile; for a split tile only in the workgroup
+// that counted itself in last, which then stores the sum of the S partials
+// (split_sum_store).  Partial slots hold each thread's accumulators at index
+// (element * NT + thread), so every store and load instruction of a
 // wavefront covers 256 consecutive bytes.
 //
 // The units of one tile may run on different XCDs, whose L2 caches are not
@@ -115,7 +115,6 @@ __device__ inline bool split_epilogue(const GemmParams& p, const tlc_tile& tl,
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   constexpr int PER = FM * FN * 16;  // floats per thread = tile floats / NT
-  static_assert((FM * FN) % 2 == 0, "blocks are summed in pairs");
   char* block = p.split_ws + static_cast<int64_t>(f) * (256 + static_cast<int64_t>(S) * NT * PER * 4);
   uint32_t* counter = reinterpret_cast<uint32_t*>(block);
   float* slots = reinterpret_cast<float*>(block + 256);
@@ -138,36 +137,7 @@ __device__ inline bool split_epilogue(const GemmParams& p, const tlc_tile& tl,
     *s_flag = last;
   }
   __syncthreads();
-  if (!*s_flag) return false;
-  // Sum in ascending split index, two 32 x 32 blocks (32 values per thread)
-  // per batch of independent loads, so that each batch costs one round trip.
-  const float* all = slots + tid;
-#pragma unroll
-  for (int b = 0; b < FM * FN; b += 2) {
-    f32x16& x0 = acc[b / FN][b % FN];
-    f32x16& x1 = acc[(b + 1) / FN][(b + 1) % FN];
-    const float* p0 = all + static_cast<int64_t>(b) * 16 * NT;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      x0[e] = __hip_atomic_load(p0 + e * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      x1[e] = __hip_atomic_load(p0 + (16 + e) * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    for (uint32_t u = 1; u < S; ++u) {
-      const float* pu = p0 + static_cast<int64_t>(u) * NT * PER;
-      float t0[16], t1[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        t0[e] = __hip_atomic_load(pu + e * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        t1[e] = __hip_atomic_load(pu + (16 + e) * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        x0[e] += t0[e];
-        x1[e] += t1[e];
-      }
-    }
-  }
-  return true;
+  return *s_flag != 0;
 }
 
 // One piece of a tile of the stream-K tail: K steps [kt0, kt1) of the tile,
@@ -229,6 +199,63 @@ __device__ inline void store_c(float* dst, float v) {
     __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else
     *dst = v;
+}
+
+// Split-tile epilogue, second half, in the workgroup that counted itself in
+// last: each 32 x 32 block of the tile is the sum of the S partials in
+// ascending split index (its own partial read back like the others, so the
+// sum does not depend on which unit came last), stored through the
+// accumulators' element map (element e of block (i, j): row i*32 + 8*(e/4) +
+// 4*(lane/32) + e%4, column j*32 + lane%32 of the wavefront's sub-tile) and
+// masked at the tile's edges.  Two blocks are summed per batch of independent
+// loads, so that each batch costs one round trip; the sums live in vector
+// registers and the accumulators are not written, which keeps them in the
+// accumulation registers.
+template <int KIND, int NT, int WM, int WN, int FM, int FN>
+__device__ inline void split_sum_store(const GemmParams& p, const tlc_tile& tl, int wm, int wn,
+                                       int lane) {
+  static_assert((FM * FN) % 2 == 0, "blocks are summed in pairs");
+  const uint32_t S = tl.split & 0xFFu, f = tl.split >> 16;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  constexpr int PER = FM * FN * 16;
+  const float* all = reinterpret_cast<const float*>(
+      p.split_ws + static_cast<int64_t>(f) * (256 + static_cast<int64_t>(S) * NT * PER * 4) + 256) + tid;
+  float* cbase = p.c + static_cast<int64_t>(tl.m0) * p.ldc + tl.n0;
+  for (int b = 0; b < FM * FN; b += 2) {
+    const float* p0 = all + static_cast<int64_t>(b) * 16 * NT;
+    float x0[16], x1[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      x0[e] = __hip_atomic_load(p0 + e * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      x1[e] = __hip_atomic_load(p0 + (16 + e) * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (uint32_t u = 1; u < S; ++u) {
+      const float* pu = p0 + static_cast<int64_t>(u) * NT * PER;
+      float t0[16], t1[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        t0[e] = __hip_atomic_load(pu + e * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t1[e] = __hip_atomic_load(pu + (16 + e) * NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x0[e] += t0[e];
+        x1[e] += t1[e];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = (b + h) / FN, j = (b + h) % FN;
+      const int col = wn * WN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = wm * WM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (row < tl.m_rows && col < tl.n_cols)
+          store_c<KIND>(cbase + static_cast<int64_t>(row) * p.ldc + col, h ? x1[e] : x0[e]);
+      }
+    }
+  }
 }
 
 // Per-destination notification after a tile is stored (scatter mode with
@@ -432,6 +459,11 @@ struct Tile {
       __syncthreads();
     }
     if (!split_epilogue<THREADS>(p, tl, acc, s_flag)) return;
+    if ((tl.split & 0xFFu) >= 2) {
+      split_sum_store<KIND, THREADS, WM, WN, FM, FN>(p, tl, wm, wn, lane);
+      notify_dests<KIND>(p, tl);
+      return;
+    }
 
     // ---- epilogue: fp32 tile to C, masked at the tile's edges ----
     float* cbase = p.c + static_cast<int64_t>(tl.m0) * p.ldc + tl.n0;
@@ -813,7 +845,10 @@ struct Tile8w {
       kloop(std::false_type{});
     if (!split_epilogue<NT>(p, tl, acc, s_flag)) return;
 
-    store_tile<KIND, WM, WN, FM, FN>(p, tl, acc, wm, wn, lane);
+    if ((tl.split & 0xFFu) >= 2)
+      split_sum_store<KIND, NT, WM, WN, FM, FN>(p, tl, wm, wn, lane);
+    else
+      store_tile<KIND, WM, WN, FM, FN>(p, tl, acc, wm, wn, lane);
     notify_dests<KIND>(p, tl);
   }
 };
@@ -1217,6 +1252,8 @@ struct Tile4w {
         store_tile_rows<KIND>(p, tl, acc, NoAdjust{}, wm, wn, lane, st);
       }
       __syncthreads();  // the next unit's loads refill the stages
+    } else if ((tl.split & 0xFFu) >= 2) {
+      split_sum_store<KIND, NT, WM, WN, FM, FN>(p, tl, wm, wn, lane);
     } else {
       store_tile<KIND, WM, WN, FM, FN>(p, tl, acc, wm, wn, lane);
     }
