@@ -228,10 +228,12 @@ tlc_status tlc_chunk_plan(const tlc_plan_desc* desc, tlc_tile* tiles, int64_t ca
 int64_t tlc_split_workspace_bytes(int64_t n_split_tiles, int32_t split_k, int32_t bm, int32_t bn);
 
 /* Bytes of the workspace the stream-K tail (TLC_SCHED_STREAMK) needs on a
- * grid of `grid` workgroups (0: the largest gfx950 part's 256 compute units,
- * enough for any grid): grid blocks of 256 + 4 * 256 * 256 * 4 bytes, an
- * arrival counter and up to four fp32 partial tiles per tail tile (a tail
- * has fewer tiles than the grid has workgroups).  Negative grid: -1.
+ * grid of `grid` workgroups (0: 256, the largest gfx950 part's compute units,
+ * enough for the default grid and any grid of at most 256): grid blocks of
+ * 256 + 4 * 256 * 256 * 4 bytes, an arrival counter and up to four fp32
+ * partial tiles per tail tile (a tail has fewer tiles than the grid has
+ * workgroups).  A call whose tail needs more blocks than the workspace holds
+ * is refused with INVALID_ARG.  Negative grid: -1.
  * The caller allocates it in device memory (256-byte aligned) and zero-fills it
  * once; each call leaves the counters at zero again, except after a device
  * error, after which it must be zero-filled before reuse.  Not from the
