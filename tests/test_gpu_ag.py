@@ -136,6 +136,26 @@ def test_ag_split_parity(land, split, sched):
                 assert np.array_equal(c2.view(np.uint32), c.view(np.uint32))
 
 
+@pytest.mark.parametrize("sched", ["dynamic", "static"])
+def test_ag_split_parity_nk_weight(sched):
+    """Split units with an N x K weight (its own kernel instances): three
+    splits from the second key on, integer inputs, bit for bit, twice."""
+    schedule = tlc.SCHED_DYNAMIC if sched == "dynamic" else tlc.SCHED_STATIC
+    for (name, W, R, K, N, tile) in SHAPES:
+        inp = si.ag_inputs(180 + W, W, R, N, K, integer=True)
+        ref = og.ag_gemm(inp.a_chunks, inp.b)
+        rank = W - 1
+        log(f"[ag split nk] {name} sched={sched} rank={rank}")
+        prob, c = _run(inp, rank, tile, tlc.B_NK, tlc.LAND_COPY_ENGINE, split_k=3, split_from=1,
+                       schedule=schedule)
+        check_exact(c, ref, name)
+        prob.poison_remote()
+        prob.run(tlc.LAND_COPY_ENGINE)
+        torch.cuda.synchronize()
+        assert prob.sig.read_status()[0] == 0
+        check_exact(prob.c.cpu().numpy(), ref, name + " second call")
+
+
 def test_ag_split_result_independent_of_schedule():
     """With a fixed split, the output bits do not depend on schedule, grid or
     which workgroup finished a tile's units last."""

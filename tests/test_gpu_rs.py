@@ -16,6 +16,8 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from tile_level_communication_amd import tlc
     from tile_level_communication_amd.workloads import RSProblem
+else:  # collected on CPU-only hosts, never run there
+    from tile_level_communication_amd import tlc  # noqa: F401
 
 LANDS = {"none": 0, "copy_engine": 1, "cu": 2, "memcpy": 3, "colocated": 4}
 SEND_LANDS = {"memcpy": 3, "copy_engine": 1, "cu": 2}
@@ -259,17 +261,19 @@ def test_rs_sends(send, order):
 
 
 @pytest.mark.parametrize("sched", ["dynamic", "static"])
-def test_rs_sends_split_tiles(sched):
-    """Split tiles: only the unit that stores the summed tile counts it in."""
+@pytest.mark.parametrize("layout", [tlc.B_KN, tlc.B_NK], ids=["KN", "NK"])
+def test_rs_sends_split_tiles(sched, layout):
+    """Split tiles: only the unit that stores the summed tile counts it in; the
+    weight K x N or N x K."""
     schedule = tlc.SCHED_DYNAMIC if sched == "dynamic" else tlc.SCHED_STATIC
     for (name, W, R, K, N, tile) in SHAPES:
         rank = W - 1
         inp = si.rs_inputs(240 + W, W, rank, R, N, K, remote_std=0.5, integer=True)
         p_ref, _ = og.gemm_rs(inp.a, inp.b, inp.remote, W, rank)
-        prob = RSProblem(inp.a, inp.b, inp.remote, W, rank, tile, tile, tlc.B_KN, split_k=3,
+        prob = RSProblem(inp.a, inp.b, inp.remote, W, rank, tile, tile, layout, split_k=3,
                          split_from=0, schedule=schedule, sends=True)
         for call in range(2):
-            log(f"[rs sends split] {name} sched={sched} call={call}")
+            log(f"[rs sends split] {name} sched={sched} layout={layout} call={call}")
             prob.partials.fill_(float("nan"))
             for c in range(W):
                 if c != rank:

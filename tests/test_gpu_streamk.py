@@ -119,22 +119,24 @@ def test_streamk_ag_qwen3_ffn_up_full_size():
         check_exact(prob.c.cpu().numpy(), iref, f"stream-K full integer, land {land}")
 
 
-def test_streamk_rs_with_sends():
+@pytest.mark.parametrize("layout", [tlc.B_KN, tlc.B_NK], ids=["KN", "NK"])
+def test_streamk_rs_with_sends(layout):
     """GEMM-RS with the tail: 8 x 5 tiles (the last column 128 wide) on 9 and 16
-    workgroups (tails of 4 and 8 tiles in two K pieces); the partial product,
-    the reduced slice and every sent slice (the tile that completes a
-    destination's slice may be completed by a tail piece)."""
+    workgroups (tails of 4 and 8 tiles in two K pieces), the weight K x N or
+    N x K; the partial product, the reduced slice and every sent slice (the
+    tile that completes a destination's slice may be completed by a tail
+    piece)."""
     W, R, K, N = 4, 512, 512, 1152
     for integer in (True, False):
         for rank in (0, 3):
             inp = si.rs_inputs(620, W, rank, R, N, K, remote_std=0.5, integer=integer)
             p_ref, out_ref = og.gemm_rs(inp.a, inp.b, inp.remote, W, rank)
             am, bm = absmax_bf16(inp.a), absmax_bf16(inp.b)
-            prob = RSProblem(inp.a, inp.b, inp.remote, W, rank, 256, 256, tlc.B_KN,
+            prob = RSProblem(inp.a, inp.b, inp.remote, W, rank, 256, 256, layout,
                              schedule=tlc.SCHED_STREAMK, sends=True)
             for grid in (9, 16):
                 for send in (None, tlc.LAND_MEMCPY, tlc.LAND_CU):
-                    log(f"[sk rs] int={integer} rank={rank} grid={grid} send={send}")
+                    log(f"[sk rs] layout={layout} int={integer} rank={rank} grid={grid} send={send}")
                     prob.poison_remote()
                     prob.partials.fill_(float("nan"))
                     if send is not None:
