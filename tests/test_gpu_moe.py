@@ -44,6 +44,9 @@ SMALL = [
     ("w4_t64_e16_k4_h128_n136_t128", 4, 16, 128, 136, 16, 4, 128),
     ("w2_t80_e64_k8_h192_n256_t256", 2, 40, 192, 256, 64, 8, 256),
     ("w8_t256_e8_k2_h64_n512_t128", 8, 32, 64, 512, 8, 2, 128),
+    # the whole-tile kernel (256 tiles, H / 64 even) on ragged experts, with a
+    # last column tile of 136: one wavefront column of each unit stores 8 columns
+    ("w4_t96_e16_k4_h256_n392_t256", 4, 24, 256, 392, 16, 4, 256),
 ]
 
 
