@@ -86,6 +86,30 @@ def test_colocated_landing_argument_errors():
     assert s == tlc.ERR_INVALID_ARG and "epoch" in tlc.last_error()
 
 
+def test_empty_sizes_are_refused():
+    """Zero rows, columns, K or tokens: refused on the host with INVALID_ARG
+    before anything is enqueued (no GPU is touched)."""
+    for over in (dict(M=0, rows_per_chunk=0), dict(N=0), dict(K=0), dict(rows_per_chunk=0)):
+        args = _ag_args(a=16, b=32, c=48, sig=64, **over)
+        assert tlc.lib().tlc_ag_gemm(C.byref(args), None, None, 0) == tlc.ERR_INVALID_ARG, over
+        assert tlc.last_error()
+    for over in (dict(M=0, rows_per_chunk=0), dict(N=0), dict(K=0)):
+        base = dict(plan=None, n_tiles=0, M=256, N=256, K=512, world=2, rank=0, rows_per_chunk=128,
+                    bm=128, bn=128, a=16, b=32, b_layout=tlc.B_KN, partials=48, sig=64, epoch=1,
+                    land=tlc.LAND_NONE)
+        base.update(over)
+        r = tlc.RSArgs(**base)
+        assert tlc.lib().tlc_gemm_rs(C.byref(r), None, None, 0) == tlc.ERR_INVALID_ARG, over
+        assert tlc.last_error()
+    E, k, N = 8, 2, 128
+    a = tlc.MoERouteArgs(logits=16, tokens_per_chunk=0, world=2, rank=0, experts=E, topk=k, N=N,
+                         bm=128, bn=128, order=1, topk_idx=16, gates=16, counts=16, offsets=16,
+                         row_token=16, slot=16, plan=16, plan_cap=16, n_tiles_dev=16,
+                         workspace=4096, x=None, x_src=None, H=64, sig=None, epoch=1)
+    assert tlc.lib().tlc_moe_route(C.byref(a), None) == tlc.ERR_INVALID_ARG
+    assert "tokens_per_chunk" in tlc.last_error(), tlc.last_error()
+
+
 def test_gemm_ar_argument_errors():
     rs = tlc.RSArgs(plan=None, n_tiles=0, M=256, N=256, K=512, world=2, rank=0, rows_per_chunk=128,
                     bm=128, bn=128, a=16, b=32, b_layout=tlc.B_KN, partials=48, sig=64, epoch=1,
